@@ -1,0 +1,334 @@
+// libhswd: C ABI of hybrid sliding-window decode attention for gfx950.
+// Host side: argument checks (before any launch), workspace layout, split
+// count, kernel dispatch.  Declarations and contracts: include/hswd.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hswd.h"
+#include "kernels/attn.hpp"
+#include "kernels/small.hpp"
+
+namespace {
+
+using namespace hswd;
+
+constexpr int kVersion = (0 << 16) | 3;
+constexpr int kDefaultKeysPerSplit = 512;
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int32_t launch_status() {
+    return hipGetLastError() == hipSuccess ? HSWD_OK : HSWD_ERR_HIP;
+}
+
+// Workspace: [error word | counters (B*Hkv) | part_ml (B*H*n*2) | part_o (B*H*n*D)]
+struct WsLayout {
+    size_t counters, part_ml, part_o, total;
+};
+
+int32_t desc_check(const hswd_attn_desc* d) {
+    if (!d) return HSWD_ERR_INVALID;
+    if (d->batch < 1 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_slots < 1)
+        return HSWD_ERR_INVALID;
+    if (d->n_heads % d->n_kv_heads != 0) return HSWD_ERR_INVALID;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+        return d->head_dim > 0 && d->head_dim % 8 == 0 ? HSWD_ERR_UNSUPPORTED : HSWD_ERR_INVALID;
+    if (d->kv_dtype < HSWD_F32 || d->kv_dtype > HSWD_BF16) return HSWD_ERR_INVALID;
+    if (!(d->scale > 0.f) || !isfinite(d->scale)) return HSWD_ERR_INVALID;
+    if (d->keys_per_split < 0 || d->keys_per_split % 64 != 0) return HSWD_ERR_INVALID;
+    return HSWD_OK;
+}
+
+int keys_per_split(const hswd_attn_desc* d) {
+    return d->keys_per_split > 0 ? d->keys_per_split : kDefaultKeysPerSplit;
+}
+
+// Splits over the key range: a function of the cache geometry and max_pos
+// only, never of the batch (the split size is part of the summation order).
+int num_splits(const hswd_attn_desc* d, int ring, int max_pos) {
+    const int kps = keys_per_split(d);
+    const long keys = ring ? d->n_slots : (max_pos > 0 ? max_pos : 0);
+    const long n = (keys + kps - 1) / kps;
+    return n < 1 ? 1 : (int)n;
+}
+
+WsLayout ws_layout(const hswd_attn_desc* d, int n_split) {
+    WsLayout L;
+    const size_t pairs = (size_t)d->batch * d->n_kv_heads;
+    const size_t bh = (size_t)d->batch * d->n_heads;
+    L.counters = kAlign;
+    L.part_ml = L.counters + round_up(pairs * sizeof(int32_t), kAlign);
+    const size_t parts = n_split > 1 ? (size_t)n_split : 0;
+    L.part_o = L.part_ml + round_up(bh * parts * 2 * sizeof(float), kAlign);
+    L.total = L.part_o + round_up(bh * parts * d->head_dim * sizeof(float), kAlign);
+    return L;
+}
+
+template <int D, int DT, bool RING, int MODE>
+void launch_attn(const AttnParams& P, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((attn_kernel<D, DT, RING, MODE>), dim3(grid), dim3(kAttnThreads), 0, st, P);
+}
+
+template <int MODE>
+int32_t dispatch_attn(const AttnParams& P, int D, int DT, int grid, hipStream_t st) {
+#define HSWD_CASE(DV, TV)                                                            \
+    if (D == DV && DT == TV) {                                                       \
+        if (P.ring) launch_attn<DV, TV, true, MODE>(P, grid, st);                    \
+        else launch_attn<DV, TV, false, MODE>(P, grid, st);                          \
+        return launch_status();                                                      \
+    }
+    HSWD_CASE(256, kBF16) HSWD_CASE(256, kF16) HSWD_CASE(256, kF32)
+    HSWD_CASE(128, kBF16) HSWD_CASE(128, kF16) HSWD_CASE(128, kF32)
+    HSWD_CASE(64, kBF16) HSWD_CASE(64, kF16) HSWD_CASE(64, kF32)
+#undef HSWD_CASE
+    return HSWD_ERR_UNSUPPORTED;
+}
+
+// Shared argument checks and parameter set-up of the attention entries.
+int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, int max_pos,
+                   void* ws, size_t ws_bytes, bool need_ws) {
+    int32_t st = desc_check(d);
+    if (st != HSWD_OK) return st;
+    if (d->n_heads != d->n_kv_heads) return HSWD_ERR_UNSUPPORTED;
+    if (!ring) {
+        if (max_pos < 0) return HSWD_ERR_INVALID;
+        if ((long)max_pos + 1 > d->n_slots) return HSWD_ERR_CAPACITY;
+    }
+    const int n_split = num_splits(d, ring, max_pos);
+    if (n_split > kMaxSplits) return HSWD_ERR_INVALID;
+    if (need_ws) {
+        if (!ws) return HSWD_ERR_WORKSPACE;
+        if (!aligned16(ws)) return HSWD_ERR_ALIGN;
+        const WsLayout L = ws_layout(d, n_split);
+        if (ws_bytes < L.total) return HSWD_ERR_WORKSPACE;
+        char* base = static_cast<char*>(ws);
+        P.err = reinterpret_cast<int32_t*>(base);
+        P.counters = reinterpret_cast<int32_t*>(base + L.counters);
+        P.part_ml = reinterpret_cast<float*>(base + L.part_ml);
+        P.part_o = reinterpret_cast<float*>(base + L.part_o);
+    }
+    P.B = d->batch;
+    P.H = d->n_heads;
+    P.Hkv = d->n_kv_heads;
+    P.S = d->n_slots;
+    P.kps = keys_per_split(d);
+    P.n_split = n_split;
+    P.ring = ring ? 1 : 0;
+    P.max_pos = ring ? d->n_slots : max_pos;
+    P.qscale = d->scale * 1.4426950408889634f;
+    grid = d->batch * d->n_kv_heads * n_split;
+    return HSWD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hswd_version(void) { return kVersion; }
+
+const char* hswd_status_string(int32_t s) {
+    switch (s) {
+        case HSWD_OK: return "ok";
+        case HSWD_ERR_INVALID: return "invalid argument";
+        case HSWD_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case HSWD_ERR_WORKSPACE: return "workspace missing or too small";
+        case HSWD_ERR_CAPACITY: return "position does not fit the cache";
+        case HSWD_ERR_HIP: return "HIP runtime error";
+        case HSWD_ERR_UNSUPPORTED: return "unsupported configuration";
+        default: return "unknown status";
+    }
+}
+
+size_t hswd_workspace_bytes(const hswd_attn_desc* d, int32_t ring, int32_t max_pos) {
+    if (desc_check(d) != HSWD_OK) return 0;
+    return ws_layout(d, num_splits(d, ring, max_pos)).total;
+}
+
+int32_t hswd_num_splits(const hswd_attn_desc* d, int32_t ring, int32_t max_pos) {
+    int32_t st = desc_check(d);
+    if (st != HSWD_OK) return st;
+    return num_splits(d, ring, max_pos);
+}
+
+int32_t hswd_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws || ws_bytes < 4) return HSWD_ERR_WORKSPACE;
+    if (!aligned16(ws)) return HSWD_ERR_ALIGN;
+    const size_t n = ws_bytes / 4;
+    const int grid = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, as_stream(stream),
+                       static_cast<int32_t*>(ws), n);
+    return launch_status();
+}
+
+int32_t hswd_ring_mask(uint8_t* mask, int32_t* slot, const int32_t* pos, int32_t B,
+                       int32_t n_slots, int32_t ring, void* stream) {
+    if (!pos || (!mask && !slot) || B < 1 || n_slots < 1) return HSWD_ERR_INVALID;
+    hipLaunchKernelGGL(ring_mask_kernel, dim3(B), dim3(256), 0, as_stream(stream), mask, slot,
+                       pos, n_slots, ring ? 1 : 0);
+    return launch_status();
+}
+
+int32_t hswd_rope_apply(float* q, float* k, const int32_t* pos, int32_t B, int32_t H,
+                        int32_t Hkv, int32_t D, int32_t rot_dim, double theta, void* stream) {
+    if (!q || !pos || B < 1 || H < 1 || D < 2 || (k && Hkv < 1)) return HSWD_ERR_INVALID;
+    if (rot_dim <= 0 || rot_dim > D || (rot_dim & 1)) return HSWD_ERR_INVALID;
+    if (!(theta > 0.0) || !isfinite(theta)) return HSWD_ERR_INVALID;
+    const size_t lds = (size_t)(H + (k ? Hkv : 0)) * D * sizeof(float);
+    if (lds > 64 * 1024) return HSWD_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(rope_kernel, dim3(B), dim3(256), lds, as_stream(stream), q, k, pos, H,
+                       k ? Hkv : 0, D, rot_dim, log2(theta));
+    return launch_status();
+}
+
+int32_t hswd_kv_slot_write(void* k_cache, void* v_cache, const float* k_rot, const float* v,
+                           const int32_t* pos, const hswd_attn_desc* d, int32_t ring,
+                           int32_t* slot_out, void* ws, void* stream) {
+    int32_t st = desc_check(d);
+    if (st != HSWD_OK) return st;
+    if (!k_cache || !v_cache || !k_rot || !v || !pos) return HSWD_ERR_INVALID;
+    if (!ws) return HSWD_ERR_WORKSPACE;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_rot) || !aligned16(v) ||
+        !aligned16(ws))
+        return HSWD_ERR_ALIGN;
+    const int grid = d->batch * d->n_kv_heads;
+    hipStream_t s = as_stream(stream);
+    int32_t* err = static_cast<int32_t*>(ws);
+    switch (d->kv_dtype) {
+        case HSWD_F32:
+            hipLaunchKernelGGL(kv_write_kernel<kF32>, dim3(grid), dim3(256), 0, s, k_cache, v_cache,
+                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring ? 1 : 0,
+                               slot_out, err);
+            break;
+        case HSWD_F16:
+            hipLaunchKernelGGL(kv_write_kernel<kF16>, dim3(grid), dim3(256), 0, s, k_cache, v_cache,
+                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring ? 1 : 0,
+                               slot_out, err);
+            break;
+        default:
+            hipLaunchKernelGGL(kv_write_kernel<kBF16>, dim3(grid), dim3(256), 0, s, k_cache, v_cache,
+                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring ? 1 : 0,
+                               slot_out, err);
+    }
+    return launch_status();
+}
+
+static int32_t decode_attn(float* o, const float* q_rot, const float* k_rot, const float* v,
+                           const void* kc, const void* vc, const int32_t* pos, int32_t ring,
+                           int32_t max_pos, const hswd_attn_desc* d, void* ws, size_t ws_bytes,
+                           void* stream) {
+    if (!o || !q_rot || !k_rot || !v || !kc || !vc || !pos) return HSWD_ERR_INVALID;
+    if (!aligned16(o) || !aligned16(q_rot) || !aligned16(k_rot) || !aligned16(v) ||
+        !aligned16(kc) || !aligned16(vc))
+        return HSWD_ERR_ALIGN;
+    AttnParams P{};
+    int grid = 0;
+    int32_t st = attn_setup(P, grid, d, ring, max_pos, ws, ws_bytes, true);
+    if (st != HSWD_OK) return st;
+    P.out = o;
+    P.q = q_rot;
+    P.k = k_rot;
+    P.v = v;
+    P.kc = const_cast<void*>(kc);
+    P.vc = const_cast<void*>(vc);
+    P.pos = pos;
+    return dispatch_attn<kModeAttend>(P, d->head_dim, d->kv_dtype, grid, as_stream(stream));
+}
+
+int32_t hswd_decode_attn_sliding(float* o, const float* q_rot, const float* k_rot,
+                                 const float* v, const void* k_ring, const void* v_ring,
+                                 const int32_t* pos, const hswd_attn_desc* d, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    return decode_attn(o, q_rot, k_rot, v, k_ring, v_ring, pos, 1, 0, d, ws, ws_bytes, stream);
+}
+
+int32_t hswd_decode_attn_full(float* o, const float* q_rot, const float* k_rot,
+                              const float* v, const void* k_cache, const void* v_cache,
+                              const int32_t* pos, int32_t max_pos, const hswd_attn_desc* d,
+                              void* ws, size_t ws_bytes, void* stream) {
+    return decode_attn(o, q_rot, k_rot, v, k_cache, v_cache, pos, 0, max_pos, d, ws, ws_bytes,
+                       stream);
+}
+
+int32_t hswd_decode_attn_partials(float* part_o, float* part_ml, const float* q_rot,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* pos, int32_t ring, int32_t max_pos,
+                                  const hswd_attn_desc* d, void* stream) {
+    if (!part_o || !part_ml || !q_rot || !k_cache || !v_cache || !pos) return HSWD_ERR_INVALID;
+    if (!aligned16(part_o) || !aligned16(part_ml) || !aligned16(q_rot) || !aligned16(k_cache) ||
+        !aligned16(v_cache))
+        return HSWD_ERR_ALIGN;
+    AttnParams P{};
+    int grid = 0;
+    int32_t st = attn_setup(P, grid, d, ring, max_pos, nullptr, 0, false);
+    if (st != HSWD_OK) return st;
+    P.q = q_rot;
+    P.kc = const_cast<void*>(k_cache);
+    P.vc = const_cast<void*>(v_cache);
+    P.pos = pos;
+    P.part_o = part_o;
+    P.part_ml = part_ml;
+    return dispatch_attn<kModePartials>(P, d->head_dim, d->kv_dtype, grid, as_stream(stream));
+}
+
+int32_t hswd_lse_merge(float* o, const float* part_o, const float* part_ml, int32_t B,
+                       int32_t H, int32_t D, int32_t n, void* stream) {
+    if (!o || !part_o || !part_ml || B < 1 || H < 1 || D < 1 || n < 1) return HSWD_ERR_INVALID;
+    if (n > kMaxSplits) return HSWD_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3(B * H), dim3(256), 0, as_stream(stream), o, part_o,
+                       part_ml, D, n);
+    return launch_status();
+}
+
+int32_t hswd_head_gate(float* out, const float* o, const float* gate, int32_t B, int32_t H,
+                       int32_t D, void* stream) {
+    if (!out || !o || !gate || B < 1 || H < 1 || D < 1) return HSWD_ERR_INVALID;
+    hipLaunchKernelGGL(head_gate_kernel, dim3(B * H), dim3(256), 0, as_stream(stream), out, o,
+                       gate, D);
+    return launch_status();
+}
+
+int32_t hswd_layer_step(float* out, const float* q, const float* k, const float* v,
+                        const float* gate, void* k_cache, void* v_cache, const int32_t* pos,
+                        int32_t ring, int32_t rot_dim, double theta, int32_t max_pos,
+                        const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
+    if (!out || !q || !k || !v || !k_cache || !v_cache || !pos) return HSWD_ERR_INVALID;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        !aligned16(k_cache) || !aligned16(v_cache))
+        return HSWD_ERR_ALIGN;
+    if (!d || rot_dim <= 0 || rot_dim > d->head_dim || (rot_dim & 1)) return HSWD_ERR_INVALID;
+    if (!(theta > 0.0) || !isfinite(theta)) return HSWD_ERR_INVALID;
+    AttnParams P{};
+    int grid = 0;
+    int32_t st = attn_setup(P, grid, d, ring, max_pos, ws, ws_bytes, true);
+    if (st != HSWD_OK) return st;
+    P.out = out;
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.gate = gate;
+    P.kc = k_cache;
+    P.vc = v_cache;
+    P.pos = pos;
+    P.rot = rot_dim;
+    P.log2_theta = log2(theta);
+    return dispatch_attn<kModeStep>(P, d->head_dim, d->kv_dtype, grid, as_stream(stream));
+}
+
+int32_t hswd_check_errors(const void* ws, int32_t* flags_out, void* stream) {
+    if (!ws) return HSWD_ERR_WORKSPACE;
+    int32_t flags = 0;
+    if (hipMemcpyAsync(&flags, ws, sizeof(int32_t), hipMemcpyDeviceToHost, as_stream(stream)) !=
+        hipSuccess)
+        return HSWD_ERR_HIP;
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return HSWD_ERR_HIP;
+    if (flags_out) *flags_out = flags;
+    return flags ? HSWD_ERR_CAPACITY : HSWD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+// Device helpers shared by the hswd kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hswd {
+
+constexpr int kWave = 64;
+
+// Cache element type codes (hswd_dtype).
+constexpr int kF32 = 0;
+constexpr int kF16 = 1;
+constexpr int kBF16 = 2;
+
+template <int DT> struct Storage { using type = uint16_t; };
+template <> struct Storage<kF32> { using type = float; };
+
+// ---------------------------------------------------------------------------
+// float32 -> cache element, IEEE round to nearest, ties to even, by integer
+// arithmetic on the bit pattern.  NaN stays NaN: sign kept, quiet bit set,
+// the leading payload bits kept.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    // Adding 0x7fff plus the kept lsb carries into the kept bits exactly when
+    // the dropped half is above the midpoint, or at it with an odd lsb; a
+    // carry out of the significand bumps the exponent (up to infinity).
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t sign = (u >> 16) & 0x8000u;
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u | ((a & 0x7fffffu) >> 13));
+    if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);   // |x| >= 65520: rounds to inf
+    if (a >= 0x38800000u) {                                     // |x| >= 2^-14: normal result
+        uint32_t r = a - 0x38000000u;                           // exponent bias 127 -> 15
+        r += 0x0fffu + ((r >> 13) & 1u);                        // ties to even on 13 dropped bits
+        return (uint16_t)(sign | (r >> 13));
+    }
+    if (a < 0x33000000u) return (uint16_t)sign;                 // |x| < 2^-25: rounds to 0
+    // subnormal result: value / 2^-24 = significand >> (126 - exponent)
+    uint32_t e = a >> 23;
+    uint32_t m = (a & 0x7fffffu) | 0x800000u;
+    uint32_t sh = 126u - e;                                     // 14 .. 24
+    uint32_t q = m >> sh;
+    uint32_t rem = m & ((1u << sh) - 1u);
+    uint32_t half = 1u << (sh - 1u);
+    if (rem > half || (rem == half && (q & 1u))) ++q;
+    return (uint16_t)(sign | q);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    _Float16 f = __builtin_bit_cast(_Float16, h);
+    return (float)f;
+}
+
+template <int DT>
+__device__ __forceinline__ typename Storage<DT>::type round_to_elt(float x) {
+    if constexpr (DT == kF32) return x;
+    else if constexpr (DT == kF16) return f32_to_f16_rne(x);
+    else return f32_to_bf16_rne(x);
+}
+
+template <int DT>
+__device__ __forceinline__ float elt_to_f32(typename Storage<DT>::type s) {
+    if constexpr (DT == kF32) return s;
+    else if constexpr (DT == kF16) return f16_bits_to_f32(s);
+    else return bf16_bits_to_f32(s);
+}
+
+// Unpack one 16-byte chunk of cache elements into floats (EPC of them).
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4& w, float* f) {
+    if constexpr (DT == kF32) {
+        f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+        f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+    } else if constexpr (DT == kBF16) {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[2 * j] = __uint_as_float(u[j] << 16);
+            f[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+        }
+    } else {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[2 * j] = f16_bits_to_f32((uint16_t)(u[j] & 0xffffu));
+            f[2 * j + 1] = f16_bits_to_f32((uint16_t)(u[j] >> 16));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave exchanges: value of lane (lane ^ mask).
+//   masks 1, 2: DPP quad permutations;  4, 8, 16: ds_swizzle bit mode
+//   (within 32-lane halves);  32: ds_bpermute.
+// ---------------------------------------------------------------------------
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "mask");
+    int x = __float_as_int(v);
+    int r;
+    if constexpr (M == 1) {
+        r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false);        // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false);        // quad_perm [2,3,0,1]
+    } else if constexpr (M == 32) {
+        r = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2), x);
+    } else {
+        r = __builtin_amdgcn_ds_swizzle(x, 0x1f | (M << 10));          // and 0x1f, xor M
+    }
+    return __int_as_float(r);
+}
+
+__device__ __forceinline__ float xor_lane_rt(float v, int m) {
+    switch (m) {
+        case 1: return xor_lane<1>(v);
+        case 2: return xor_lane<2>(v);
+        case 4: return xor_lane<4>(v);
+        case 8: return xor_lane<8>(v);
+        case 16: return xor_lane<16>(v);
+        default: return xor_lane<32>(v);
+    }
+}
+
+// Value of lane `src` (any lane of the wave).
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += xor_lane<32>(v); v += xor_lane<16>(v); v += xor_lane<8>(v);
+    v += xor_lane<4>(v); v += xor_lane<2>(v); v += xor_lane<1>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, xor_lane<32>(v)); v = fmaxf(v, xor_lane<16>(v)); v = fmaxf(v, xor_lane<8>(v));
+    v = fmaxf(v, xor_lane<4>(v)); v = fmaxf(v, xor_lane<2>(v)); v = fmaxf(v, xor_lane<1>(v));
+    return v;
+}
+
+// Agent-scope (whole GPU) relaxed atomic store / load of a float.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// RoPE of element t of one head vector x[0..D) at position p: the pair
+// (x[i], x[i + rot/2]) turns by p * theta^(-2i/rot); dims >= rot pass.  The
+// inverse frequency is 2^(-(2i/rot) * log2(theta)); angle, sine, cosine and
+// rotation are in double precision, rounded once to float.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float rope_elem(const float* x, int t, int rot, double log2_theta,
+                                           int p) {
+    if (t >= rot) return x[t];
+    int half = rot >> 1;
+    int i = t < half ? t : t - half;
+    double inv = exp2(-(2.0 * (double)i / (double)rot) * log2_theta);
+    double a = (double)p * inv;
+    double sn, cs;
+    sincos(a, &sn, &cs);
+    double x0 = (double)x[i];
+    double x1 = (double)x[i + half];
+    double r = t < half ? x0 * cs - x1 * sn : x1 * cs + x0 * sn;
+    return (float)r;
+}
+
+}  // namespace hswd

@@ -1,0 +1,141 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, and rejects bad arguments on the host before anything is
+launched (no GPU needed: every call here fails its host checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_sliding_window_decode_amd as hswd
+from hybrid_sliding_window_decode_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hswd.h")
+
+A = ctypes.c_void_p(0x10000)       # aligned stand-in pointer (never dereferenced)
+MIS = ctypes.c_void_p(0x10004)     # misaligned stand-in pointer
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int32_t|size_t)\s+(hswd_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def desc(**kw):
+    d = dict(batch=2, n_heads=8, n_kv_heads=8, head_dim=256, n_slots=511, kv_dtype=2,
+             scale=1 / 16, keys_per_split=0)
+    d.update(kw)
+    return binding.AttnDesc(**d)
+
+
+def test_exports_every_declared_symbol():
+    L = binding.lib()
+    names = declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(binding.SIGNATURES), set(names) ^ set(binding.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    assert hswd.version() >= 3
+    for s in range(-6, 1):
+        assert hswd.status_string(s) == binding.STATUS[s]
+    assert hswd.status_string(-99) == "unknown status"
+
+
+def test_workspace_and_splits():
+    L = binding.lib()
+    d = desc()
+    assert hswd.num_splits(d, 1) == 1
+    assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 8
+    assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 256
+    assert hswd.num_splits(desc(n_slots=4097, keys_per_split=1024), 0, 4096) == 4
+    # splits never depend on the batch
+    assert hswd.num_splits(desc(batch=1, n_slots=4097), 0, 4096) == \
+        hswd.num_splits(desc(batch=64, n_slots=4097), 0, 4096)
+    ring = hswd.workspace_bytes(d, 1)
+    full = hswd.workspace_bytes(desc(n_slots=4097), 0, 4096)
+    assert ring >= 256 + 2 * 8 * 4
+    assert full >= 2 * 8 * 8 * (256 + 2) * 4
+    assert L.hswd_workspace_bytes(ctypes.byref(desc(head_dim=0)), 1, 0) == 0
+    assert L.hswd_num_splits(ctypes.byref(desc(keys_per_split=100)), 1, 0) == -1
+
+
+@pytest.mark.parametrize("case,kw,want", [
+    ("H % Hkv", dict(n_heads=6, n_kv_heads=4), -1),
+    ("head_dim", dict(head_dim=96), -6),
+    ("head_dim odd", dict(head_dim=7), -1),
+    ("dtype", dict(kv_dtype=3), -1),
+    ("scale", dict(scale=0.0), -1),
+    ("kps", dict(keys_per_split=100), -1),
+    ("batch", dict(batch=0), -1),
+    ("GQA not built", dict(n_heads=16, n_kv_heads=8), -6),
+])
+def test_sliding_rejects_bad_descriptor(case, kw, want):
+    L = binding.lib()
+    d = desc(**kw)
+    st = L.hswd_decode_attn_sliding(A, A, A, A, A, A, A, ctypes.byref(d), A, 1 << 20, None)
+    assert st == want, case
+
+
+def test_attention_host_checks():
+    L = binding.lib()
+    d = desc()
+    big = 1 << 30
+    assert L.hswd_decode_attn_sliding(None, A, A, A, A, A, A, ctypes.byref(d), A, big, None) == -1
+    assert L.hswd_decode_attn_sliding(A, A, A, A, MIS, A, A, ctypes.byref(d), A, big, None) == -2
+    assert L.hswd_decode_attn_sliding(A, A, A, A, A, A, A, ctypes.byref(d), None, big, None) == -3
+    assert L.hswd_decode_attn_sliding(A, A, A, A, A, A, A, ctypes.byref(d), A, 16, None) == -3
+    assert L.hswd_decode_attn_sliding(A, A, A, A, A, A, A, ctypes.byref(d), MIS, big, None) == -2
+    assert L.hswd_decode_attn_sliding(A, A, A, A, A, A, A, None, A, big, None) == -1
+    f = desc(n_slots=4097)
+    # max_pos + 1 must fit the append capacity
+    assert L.hswd_decode_attn_full(A, A, A, A, A, A, A, 4096 + 1, ctypes.byref(f), A, big, None) == -4
+    assert L.hswd_decode_attn_full(A, A, A, A, A, A, A, -1, ctypes.byref(f), A, big, None) == -1
+    # more than 1024 splits is refused
+    huge = desc(n_slots=1 << 20, keys_per_split=64)
+    assert L.hswd_decode_attn_full(A, A, A, A, A, A, A, (1 << 20) - 1, ctypes.byref(huge), A, big,
+                                   None) == -1
+    need = hswd.workspace_bytes(f, 0, 4096)
+    assert L.hswd_decode_attn_full(A, A, A, A, A, A, A, 4096, ctypes.byref(f), A, need - 1,
+                                   None) == -3
+
+
+def test_other_entries_host_checks():
+    L = binding.lib()
+    d = desc()
+    # rope: rot_dim odd / zero / above D, theta <= 0, null q
+    assert L.hswd_rope_apply(A, A, A, 2, 8, 8, 256, 255, 1e4, None) == -1
+    assert L.hswd_rope_apply(A, A, A, 2, 8, 8, 256, 0, 1e4, None) == -1
+    assert L.hswd_rope_apply(A, A, A, 2, 8, 8, 256, 258, 1e4, None) == -1
+    assert L.hswd_rope_apply(A, A, A, 2, 8, 8, 256, 64, 0.0, None) == -1
+    assert L.hswd_rope_apply(None, A, A, 2, 8, 8, 256, 64, 5e6, None) == -1
+    assert L.hswd_rope_apply(A, A, A, 2, 64, 64, 256, 64, 5e6, None) == -6   # LDS bound
+    # kv write
+    assert L.hswd_kv_slot_write(A, A, A, A, A, ctypes.byref(d), 1, None, None, None) == -3
+    assert L.hswd_kv_slot_write(A, MIS, A, A, A, ctypes.byref(d), 1, None, A, None) == -2
+    assert L.hswd_kv_slot_write(A, None, A, A, A, ctypes.byref(d), 1, None, A, None) == -1
+    # merge, gate, mask
+    assert L.hswd_lse_merge(A, A, A, 2, 8, 256, 0, None) == -1
+    assert L.hswd_lse_merge(A, A, A, 2, 8, 256, 2048, None) == -6
+    assert L.hswd_head_gate(A, A, None, 2, 8, 256, None) == -1
+    assert L.hswd_ring_mask(None, None, A, 2, 511, 1, None) == -1
+    assert L.hswd_ring_mask(A, A, A, 2, 0, 1, None) == -1
+    # layer step
+    assert L.hswd_layer_step(A, A, A, A, A, A, A, A, 1, 255, 1e4, 0, ctypes.byref(d), A,
+                             1 << 20, None) == -1
+    assert L.hswd_layer_step(A, A, A, A, A, A, A, A, 1, 256, -1.0, 0, ctypes.byref(d), A,
+                             1 << 20, None) == -1
+    assert L.hswd_workspace_init(None, 64, None) == -3
+    assert L.hswd_workspace_init(MIS, 64, None) == -2
+    assert L.hswd_check_errors(None, None, None) == -3
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 8, 256)
+    with pytest.raises(ValueError):
+        hswd.rope_apply(q, None, torch.zeros(1, dtype=torch.int32), 256, 1e4)

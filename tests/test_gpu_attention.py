@@ -1,0 +1,296 @@
+"""GPU parity of the decode attention entry points against the oracle, at
+sizes the oracle finishes in seconds that still span several tiles, several
+splits and ragged tails, plus the method's degenerate cases."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_sliding_window_decode_amd as hswd
+import oracle
+from oracle import brute
+from hybrid_sliding_window_decode_amd import inputs
+from gpu_util import (CODE, assert_parity, cache_to_dev, cache_to_host, f32_dev, i32_dev, say,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def spec_for(kind, B, dtype, S=None, H=8, D=256):
+    if kind == "sliding":
+        return inputs.sliding_spec(B, dtype, H=H, Hkv=H, D=D, n_slots=S or 511)
+    return inputs.full_spec(B, S, dtype, H=H, Hkv=H, D=D)
+
+
+def oracle_step(x, write=False):
+    kc, vc = x.k_cache.copy(), x.v_cache.copy()
+    return oracle.layer_step(x.q, x.k, x.v, x.gate, kc, vc, x.pos, CODE[x.spec.dtype],
+                             x.spec.kind == "sliding", x.spec.rot, x.spec.theta, write=write)
+
+
+def gpu_unfused(x, kps=0, max_pos=None):
+    """rope_apply -> decode_attn_* (pre-gate o) on device; returns (o, q_rot, k_rot)."""
+    d = to_dev(x)
+    ring = x.spec.kind == "sliding"
+    desc = hswd.make_desc(d["k_cache"], keys_per_split=kps)
+    hswd.rope_apply(d["q"], d["k"], d["pos"], x.spec.rot, x.spec.theta)
+    mp = int(x.pos.max()) if max_pos is None else max_pos
+    ws = hswd.workspace(desc, ring, mp)
+    if ring:
+        o = hswd.decode_attn_sliding(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"],
+                                     d["pos"], ws, desc=desc)
+    else:
+        o = hswd.decode_attn_full(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["pos"],
+                                  mp, ws, desc=desc)
+    assert hswd.check_errors(ws) == 0
+    return o.cpu().numpy(), d["q"].cpu().numpy(), d["k"].cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# the named small workloads
+# ---------------------------------------------------------------------------
+CASES = [
+    # 1 stream, sliding, fp32 ring, position 600 (ring wrapped)
+    ("sliding_1x600_f32", "sliding", 1, "f32", [600], None, 0),
+    # 1 stream, full, fp16 cache, context 1024
+    ("full_1x1024_f16", "full", 1, "f16", [1024], 1025, 0),
+    # 64 streams, sliding, bf16, ragged positions in [1, 4096]
+    ("sliding_64xragged_bf16", "sliding", 64, "bf16", "ragged", None, 0),
+    # ragged full layer over several splits, with empty splits
+    ("full_16xragged_bf16_kps128", "full", 16, "bf16", "ragged", 2049, 128),
+    ("full_8xragged_f32_kps64", "full", 8, "f32", "ragged", 700, 64),
+    ("sliding_8xragged_f16_kps128", "sliding", 8, "f16", "ragged", None, 128),
+    ("full_4x_f16_d128", "full", 4, "f16", [5, 300, 1000, 77], 1001, 0),
+]
+
+
+@pytest.mark.parametrize("name,kind,B,dtype,pos,S,kps", CASES, ids=[c[0] for c in CASES])
+def test_decode_attn_parity(name, kind, B, dtype, pos, S, kps):
+    D = 128 if name.endswith("d128") else 256
+    spec = spec_for(kind, B, dtype, S=S, D=D)
+    if pos == "ragged":
+        hi = 4096 if kind == "sliding" else spec.n_slots - 1
+        pos = inputs.ragged_positions(B, 1, hi, seed=3)
+        pos[0] = 1                                  # a nearly empty cache
+    x = inputs.make_step(spec, pos, seed=zlib.crc32(name.encode()) % 1000)
+    say("decode_attn %s pos=%s" % (name, list(x.pos[:8])))
+    ref = oracle_step(x)
+    o, q_rot, k_rot = gpu_unfused(x, kps=kps)
+    assert_parity(o, ref["o_pre"], x, name)
+
+
+def test_sliding_equals_full_on_same_history():
+    """pos <= 511: a ring that never wrapped holds the same rows as an append
+    cache; with one RoPE setting both kernels must agree."""
+    B, S = 4, 511
+    spec = inputs.sliding_spec(B, "bf16")
+    x = inputs.make_step(spec, [1, 100, 300, 511], seed=7)
+    ring_o, _, _ = gpu_unfused(x)
+    y = inputs.make_step(spec, [1, 100, 300, 511], seed=7)
+    y.spec = inputs.LayerSpec("full", B, 8, 8, 256, S + 1, "bf16", rot=256, theta=1e4)
+    pad = np.full((B, 8, 1, 256), 0x7fc0, np.uint16)
+    y.k_cache = np.concatenate([y.k_cache, pad], 2)
+    y.v_cache = np.concatenate([y.v_cache, pad], 2)
+    full_o, _, _ = gpu_unfused(y, max_pos=511)
+    say("sliding vs full max diff %.3e" % np.max(np.abs(ring_o - full_o)))
+    assert np.max(np.abs(ring_o - full_o)) < 1e-5
+
+
+def test_single_key_returns_rounded_value():
+    """pos 0: nothing cached; the output is the new entry's value, bit for bit."""
+    for kind, dtype in [("sliding", "bf16"), ("full", "f16"), ("sliding", "f32")]:
+        spec = spec_for(kind, 3, dtype, S=8 if kind == "full" else None)
+        x = inputs.make_step(spec, [0, 0, 0], seed=9)
+        say("single key %s %s" % (kind, dtype))
+        o, _, _ = gpu_unfused(x, max_pos=0)
+        vh = oracle.decode(CODE[dtype], oracle.round_to(CODE[dtype], x.v))
+        assert np.array_equal(o.astype(np.float64), vh)
+
+
+def test_zero_query_gives_mean():
+    """q = 0: all scores equal; the output is the mean of the attended values."""
+    spec = inputs.sliding_spec(4, "bf16")
+    x = inputs.make_step(spec, [3, 511, 700, 100], seed=10)
+    x.q[:] = 0
+    say("zero query")
+    o, _, _ = gpu_unfused(x)
+    ref = oracle_step(x)["o_pre"]
+    assert_parity(o, ref, x, "zero query")
+
+
+def test_partials_and_merge_match_oracle_split_form():
+    """Split partials of the cached keys (a5) and their merge (a7)."""
+    B, S, kps = 4, 1300, 256
+    spec = inputs.full_spec(B, S, "bf16")
+    x = inputs.make_step(spec, [1299, 5, 700, 256], seed=11)
+    d = to_dev(x)
+    hswd.rope_apply(d["q"], d["k"], d["pos"], spec.rot, spec.theta)
+    desc = hswd.make_desc(d["k_cache"], keys_per_split=kps)
+    say("partials B=%d kps=%d" % (B, kps))
+    po, pml = hswd.decode_attn_partials(d["q"], d["k_cache"], d["v_cache"], d["pos"], 0,
+                                        max_pos=1299, desc=desc)
+    po, pml = po.cpu().numpy(), pml.cpu().numpy()
+    n = po.shape[2]
+    assert n == math.ceil(1299 / kps)
+    q_rot = d["q"].cpu().numpy().astype(np.float64)
+    for b in range(B):
+        p = int(x.pos[b])
+        for h in range(spec.H):
+            for c in range(n):
+                j0, j1 = c * kps, min((c + 1) * kps, p)
+                m, l, o = oracle.partial(q_rot[b, h], x.k_cache[b, h], x.v_cache[b, h],
+                                         CODE["bf16"], j0, j1, 1 / 16)
+                if j1 <= j0:
+                    assert pml[b, h, c, 0] == -np.inf and pml[b, h, c, 1] == 0
+                    assert np.all(po[b, h, c] == 0)
+                    continue
+                assert abs(pml[b, h, c, 0] - m) < 1e-5 * (1 + abs(m))
+                # o and l are relative to each side's own max; rescale to compare
+                scale = math.exp(pml[b, h, c, 0] - m)
+                assert abs(pml[b, h, c, 1] * scale - l) < 1e-5 * l
+                assert np.max(np.abs(po[b, h, c] * scale - o)) < 1e-5 * np.max(np.abs(o))
+    merged = hswd.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pml).cuda())
+    merged = merged.cpu().numpy()
+    for b in range(B):
+        if int(x.pos[b]) == 0:
+            continue
+        for h in range(spec.H):
+            ref = oracle.merge(pml[b, h, :, 0].astype(np.float64), pml[b, h, :, 1], po[b, h])
+            assert np.max(np.abs(merged[b, h] - ref)) < 1e-5 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("kind,dtype,pos,S,kps", [
+    ("sliding", "bf16", "ragged", None, 0),
+    ("sliding", "f32", [600, 3], None, 128),
+    ("full", "bf16", "ragged", 3000, 0),
+    ("full", "f16", [1024, 1, 0, 2999], 3000, 256),
+])
+def test_layer_step_fused_matches_oracle_and_unfused(kind, dtype, pos, S, kps):
+    """The one-launch layer step: gated output against the oracle, the stored
+    entry bit for bit, and the same bits as the four separate entries."""
+    B = 12 if pos == "ragged" else len(pos)
+    spec = spec_for(kind, B, dtype, S=S)
+    if pos == "ragged":
+        pos = inputs.ragged_positions(B, 0, 4096 if kind == "sliding" else S - 1, seed=12)
+    x = inputs.make_step(spec, pos, seed=13)
+    ring = kind == "sliding"
+    ref = oracle_step(x, write=True)
+    d = to_dev(x)
+    desc = hswd.make_desc(d["k_cache"], keys_per_split=kps)
+    mp = int(x.pos.max())
+    ws = hswd.workspace(desc, ring, mp)
+    say("layer_step fused %s %s pos=%s" % (kind, dtype, list(x.pos[:6])))
+    out = hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
+                          d["pos"], ring, spec.rot, spec.theta, ws, max_pos=mp, desc=desc)
+    assert hswd.check_errors(ws) == 0
+    out = out.cpu().numpy()
+    assert_parity(out, ref["out"], x, "fused step")
+    kc, vc = cache_to_host(d["k_cache"]), cache_to_host(d["v_cache"])
+
+    # unfused sequence on fresh copies: rope -> attend -> gate -> write
+    e = to_dev(x)
+    hswd.rope_apply(e["q"], e["k"], e["pos"], spec.rot, spec.theta)
+    ws2 = hswd.workspace(desc, ring, mp)
+    if ring:
+        o = hswd.decode_attn_sliding(e["q"], e["k"], e["v"], e["k_cache"], e["v_cache"],
+                                     e["pos"], ws2, desc=desc)
+    else:
+        o = hswd.decode_attn_full(e["q"], e["k"], e["v"], e["k_cache"], e["v_cache"], e["pos"],
+                                  mp, ws2, desc=desc)
+    g = hswd.head_gate(o, e["gate"])
+    hswd.kv_slot_write(e["k_cache"], e["v_cache"], e["k"], e["v"], e["pos"], ring, ws2,
+                       desc=desc)
+    assert hswd.check_errors(ws2) == 0
+    assert np.array_equal(g.cpu().numpy(), out), "fused and unfused outputs differ"
+    kc2, vc2 = cache_to_host(e["k_cache"]), cache_to_host(e["v_cache"])
+    assert np.array_equal(kc.view(np.uint16) if dtype != "f32" else kc.view(np.uint32),
+                          kc2.view(np.uint16) if dtype != "f32" else kc2.view(np.uint32))
+
+    # the stored entry equals the oracle's rounding of the GPU's rotated key
+    k_rot = e["k"].cpu().numpy()
+    for b in range(B):
+        p = int(x.pos[b])
+        row = p % spec.n_slots if ring else p
+        want_k = oracle.round_to(CODE[dtype], k_rot[b])
+        want_v = oracle.round_to(CODE[dtype], x.v[b])
+        if dtype == "f32":
+            assert np.array_equal(kc[b, :, row].view(np.uint32), want_k.view(np.uint32))
+            assert np.array_equal(vc[b, :, row].view(np.uint32), want_v.view(np.uint32))
+        else:
+            assert np.array_equal(kc[b, :, row], want_k)
+            assert np.array_equal(vc[b, :, row], want_v)
+        # every other row is untouched
+        others = np.ones(spec.n_slots, bool)
+        others[row] = False
+        kb = kc[b][:, others].view(np.uint16 if dtype != "f32" else np.uint32)
+        xb = x.k_cache[b][:, others].view(np.uint16 if dtype != "f32" else np.uint32)
+        assert np.array_equal(kb, xb)
+
+
+@pytest.mark.parametrize("kind,dtype", [("sliding", "f32"), ("sliding", "bf16"),
+                                        ("full", "f16")])
+def test_multistep_against_brute_force(kind, dtype):
+    """Several steps through the ring's wrap, driven on the GPU with the fused
+    layer step (read, then write), against the brute force over the raw
+    history: a 4-token window (3 slots), D = 256."""
+    rng = np.random.default_rng(50)
+    H, D, steps, W = 2, 256, 12, 4
+    ring = kind == "sliding"
+    S = W - 1 if ring else steps
+    rot, theta = (D, 1e4) if ring else (D // 4, 5e6)
+    hist = [(rng.standard_normal((H, D)).astype(np.float32),
+             rng.standard_normal((H, D)).astype(np.float32),
+             rng.standard_normal((H, D)).astype(np.float32)) for _ in range(steps)]
+    gate = rng.standard_normal(H).astype(np.float32)
+    hist_py = [(q.tolist(), k.tolist(), v.tolist()) for q, k, v in hist]
+    sd = oracle.storage_dtype(CODE[dtype])
+    nan = {"f32": np.float32(np.nan), "f16": np.uint16(0x7e00), "bf16": np.uint16(0x7fc0)}[dtype]
+    kc = cache_to_dev(np.full((1, H, S, D), nan, sd), dtype)
+    vc = cache_to_dev(np.full((1, H, S, D), nan, sd), dtype)
+    desc = hswd.make_desc(kc)
+    ws = hswd.workspace(desc, ring, S - 1)
+    say("multistep %s %s" % (kind, dtype))
+    for p in range(steps):
+        q, k, v = hist[p]
+        out = hswd.layer_step(f32_dev(q[None]), f32_dev(k[None]), f32_dev(v[None]),
+                              f32_dev(gate[None]), kc, vc, i32_dev([p]), ring, rot, theta, ws,
+                              max_pos=0 if ring else S - 1, desc=desc)
+        ref = np.array(brute.step(hist_py, p, W if ring else None, H, H, rot, theta, dtype,
+                                  1 / 16, gate.tolist()))
+        got = out.cpu().numpy()[0]
+        err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+        assert err < (1e-5 if dtype == "f32" else 2e-3 / 4), (p, err)
+    assert hswd.check_errors(ws) == 0
+
+
+def test_deterministic_and_batch_invariant():
+    """Same inputs twice: same bits.  A stream alone and inside a batch of
+    64: same bits (the split count never depends on the batch)."""
+    spec = inputs.full_spec(64, 2100, "bf16")
+    pos = inputs.ragged_positions(64, 1, 2099, seed=14)
+    x = inputs.make_step(spec, pos, seed=15)
+    say("determinism")
+    a, _, _ = gpu_unfused(x, max_pos=2099)
+    b, _, _ = gpu_unfused(x, max_pos=2099)
+    assert np.array_equal(a, b)
+    for s in (0, 17, 63):
+        one = inputs.StepInputs(inputs.full_spec(1, 2100, "bf16"), x.pos[s:s + 1], x.q[s:s + 1],
+                                x.k[s:s + 1], x.v[s:s + 1], x.gate[s:s + 1],
+                                x.k_cache[s:s + 1], x.v_cache[s:s + 1])
+        solo, _, _ = gpu_unfused(one, max_pos=2099)
+        assert np.array_equal(solo[0], a[s]), s
+
+
+def test_max_pos_flag():
+    """A device position above the host bound is reported, not silently used."""
+    spec = inputs.full_spec(2, 2000, "bf16")
+    x = inputs.make_step(spec, [100, 1500], seed=16)
+    d = to_dev(x)
+    desc = hswd.make_desc(d["k_cache"])
+    ws = hswd.workspace(desc, 0, 600)
+    say("max_pos flag")
+    hswd.decode_attn_full(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["pos"], 600, ws,
+                          desc=desc)
+    assert hswd.check_errors(ws) & hswd.binding.FLAG_MAX_POS

@@ -1,0 +1,140 @@
+"""GPU parity of the per-token kernels: slot/mask, RoPE, entry write, head
+gate and split merge, each through the C ABI against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_sliding_window_decode_amd as hswd
+import oracle
+import pins
+from gpu_util import CODE, cache_to_dev, cache_to_host, f32_dev, i32_dev, say
+
+pytestmark = pytest.mark.gpu
+
+POS = np.array([0, 1, 2, 89, 510, 511, 512, 600, 1021, 1022, 1023, 4095, 4096, 131072],
+               np.int32)
+
+
+@pytest.mark.parametrize("ring", [1, 0])
+def test_ring_mask_bit_exact(ring):
+    S = 511 if ring else 131073
+    say("ring_mask ring=%d S=%d" % (ring, S))
+    mask, slot = hswd.ring_mask(i32_dev(POS), S, ring)
+    om_slot, om_mask = oracle.slot_mask(POS, S, ring)
+    assert np.array_equal(slot.cpu().numpy(), om_slot)
+    assert np.array_equal(mask.cpu().numpy(), om_mask)
+
+
+@pytest.mark.parametrize("rot,theta", [(256, 1e4), (64, 5e6), (128, 1e4)])
+def test_rope(rot, theta):
+    rng = np.random.default_rng(40 + rot)
+    B, H, Hkv, D = len(POS), 8, 8, 256
+    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, D), dtype=np.float32)
+    say("rope rot=%d theta=%g B=%d" % (rot, theta, B))
+    qd, kd = f32_dev(q), f32_dev(k)
+    hswd.rope_apply(qd, kd, i32_dev(POS), rot, theta)
+    gq, gk = qd.cpu().numpy(), kd.cpu().numpy()
+    for got, x, nh in [(gq, q, H), (gk, k, Hkv)]:
+        ref = oracle.rope(x, POS, rot, theta)
+        # the GPU rounds its double-precision rotation once to float32
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= ulp), np.max(np.abs(got - ref) / ulp)
+        assert np.array_equal(got[0], x[0])                    # pos 0: identity
+        assert np.array_equal(got[..., rot:], x[..., rot:])    # untouched dims
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_kv_slot_write_rounding_bit_exact(dtype):
+    """Entry rounding on the GPU equals the oracle's, bit for bit, on 2^20
+    random float32 patterns and on every tie and edge of the target grid."""
+    rng = np.random.default_rng(41)
+    vals = np.concatenate([
+        rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32),
+        pins.rne_special_inputs()])
+    Hkv, D = 8, 256
+    per = Hkv * D
+    B = -(-vals.size // per)
+    vals = np.resize(vals, B * per).astype(np.float32)
+    k = vals.reshape(B, Hkv, D)
+    v = np.roll(vals, 12345).reshape(B, Hkv, D)
+    sd = oracle.storage_dtype(CODE[dtype])
+    kc = np.zeros((B, Hkv, 3, D), sd)
+    say("kv_slot_write %s B=%d" % (dtype, B))
+    kd, vd = cache_to_dev(kc, dtype), cache_to_dev(kc.copy(), dtype)
+    pos = np.arange(B, dtype=np.int32)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    slot = torch.empty(B, dtype=torch.int32, device="cuda")
+    hswd.kv_slot_write(kd, vd, f32_dev(k), f32_dev(v), i32_dev(pos), 1, ws, slot_out=slot)
+    assert hswd.check_errors(ws) == 0
+    kh, vh = cache_to_host(kd), cache_to_host(vd)
+    assert np.array_equal(slot.cpu().numpy(), pos % 3)
+    for b in range(0, B, 97):
+        assert np.all(kh[b, :, [s for s in range(3) if s != b % 3]] == 0)
+    ref_k = oracle.round_to(CODE[dtype], k)
+    ref_v = oracle.round_to(CODE[dtype], v)
+    rows = pos % 3
+    got_k = kh[np.arange(B), :, rows]
+    got_v = vh[np.arange(B), :, rows]
+    if dtype == "f32":
+        assert np.array_equal(got_k.view(np.uint32), ref_k.view(np.uint32))
+        assert np.array_equal(got_v.view(np.uint32), ref_v.view(np.uint32))
+    else:
+        assert np.array_equal(got_k, ref_k)
+        assert np.array_equal(got_v, ref_v)
+
+
+def test_kv_slot_write_capacity_flag():
+    B, Hkv, S, D = 4, 8, 10, 256
+    rng = np.random.default_rng(42)
+    k = rng.standard_normal((B, Hkv, D), dtype=np.float32)
+    pos = np.array([3, 10, 9, 11], np.int32)       # 10 and 11 do not fit 10 rows
+    kc = torch.zeros(B, Hkv, S, D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    slot = torch.empty(B, dtype=torch.int32, device="cuda")
+    say("kv_slot_write capacity")
+    hswd.kv_slot_write(kc, vc, f32_dev(k), f32_dev(k), i32_dev(pos), 0, ws, slot_out=slot)
+    assert hswd.check_errors(ws) == hswd.binding.FLAG_CAPACITY
+    assert slot.cpu().tolist() == [3, -1, 9, -1]
+    assert float(kc[1].abs().sum()) == 0 and float(kc[3].abs().sum()) == 0
+    hswd.workspace_init(ws)
+    assert hswd.check_errors(ws) == 0
+
+
+def test_head_gate():
+    rng = np.random.default_rng(43)
+    B, H, D = 64, 8, 256
+    o = rng.standard_normal((B, H, D), dtype=np.float32)
+    g = rng.standard_normal((B, H), dtype=np.float32) * 4
+    g[0, :4] = [0, 40, -40, 88]
+    say("head_gate")
+    got = hswd.head_gate(f32_dev(o), f32_dev(g)).cpu().numpy()
+    ref = oracle.head_gate(o.astype(np.float64), g)
+    assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)) < 2e-6
+    assert np.array_equal(got[0, 0], o[0, 0] * np.float32(0.5))
+    # in place
+    od = f32_dev(o)
+    hswd.head_gate(od, f32_dev(g), out=od)
+    assert np.array_equal(od.cpu().numpy(), got)
+
+
+@pytest.mark.parametrize("n", [1, 7, 16, 40, 256])
+def test_lse_merge(n):
+    rng = np.random.default_rng(44 + n)
+    B, H, D = 3, 8, 256
+    m = rng.standard_normal((B, H, n)).astype(np.float32) * 3
+    l = rng.uniform(0.5, 50, (B, H, n)).astype(np.float32)
+    o = (rng.standard_normal((B, H, n, D)) * 5).astype(np.float32)
+    if n > 1:                                      # empty partials are skipped
+        m[:, :, ::3] = -np.inf
+        l[:, :, ::3] = 0
+        o[:, :, ::3] = 0
+    ml = np.stack([m, l], -1)
+    say("lse_merge n=%d" % n)
+    got = hswd.lse_merge(f32_dev(o), f32_dev(ml)).cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.merge(m[b, h], l[b, h], o[b, h])
+            err = np.max(np.abs(got[b, h] - ref)) / np.max(np.abs(ref))
+            assert err < 1e-5, (b, h, err)
