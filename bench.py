@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of hybrid sliding-window decode attention on one MI355X.
+
+Workload (one "step"): one decode step of a 28-layer hybrid stack -- 21
+sliding-window layers (511-slot rings) and 7 full-attention layers (append
+caches at context 4096), layer l full iff l % 4 == 3 -- for 64 streams, 8
+heads of 256 dims, bf16 KV caches, each layer with its own buffers.  Every
+layer runs the whole path (RoPE, attention over the cache plus the new entry,
+head gate, entry write) as one launch of hswd_layer_step.  Inputs are seeded
+synthetic N(0,1) data resident in HBM before timing starts.
+
+Reported `value`: algorithmic HBM bytes of the step (valid K/V rows plus
+per-token input/output) / step time, in GB/s.  `roofline` covers the
+dominant kernel, the full-layer launch, timed with HIP events on the stream
+it runs on, inside the timed region.  `cpu_baseline` is the fp64 CPU oracle
+timed on two layers of the same step on the host cores (rank 0 only).
+
+    python bench.py [--steps K] [--warmup W] [--mode fused|unfused]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/layer-step + achieved HBM GB/s (% peak), 64 streams × 4k ctx"
+PEAK_HBM_GBS = 8000.0                 # MI355X HBM3E, vendor figure
+B, H, HKV, D, S_RING, CTX, LAYERS = 64, 8, 8, 256, 511, 4096, 28
+ELT = 2                               # bf16
+
+
+def layer_bytes(kind, B=B, pos=CTX):
+    """Algorithmic bytes of one layer step: valid K and V rows plus the
+    per-stream q in, output out, k and v in, rounded entry out, gate, pos."""
+    n_keys = min(pos, S_RING) if kind == "sliding" else pos
+    cache = B * HKV * n_keys * D * ELT * 2
+    per_stream = H * D * 4 * 2 + HKV * D * 4 * 2 + HKV * D * ELT * 2 + H * 4 + 4
+    return cache + B * per_stream
+
+
+def is_full(l):
+    return l % 4 == 3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", choices=["fused", "unfused"], default="fused")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter scaling)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
+              "(the path shards by stream with no exchange, see DESIGN.md)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import hybrid_sliding_window_decode_amd as hswd
+    from hybrid_sliding_window_decode_amd import inputs
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read, %d bytes written" % (n, n))
+        return
+
+    # ---- inputs: 28 layers, each with its own buffers, all streams at 4096
+    log("generating 28-layer workload (%.1f GB of KV caches)" % (
+        sum(2 * B * HKV * (S_RING if not is_full(l) else CTX + 1) * D * ELT
+            for l in range(LAYERS)) / 1e9))
+    layers = []
+    for l in range(LAYERS):
+        full = is_full(l)
+        spec = inputs.full_spec(B, CTX + 1, "bf16") if full else inputs.sliding_spec(B, "bf16")
+        t = inputs.device_step(spec, CTX, seed=4000 + l, device=dev)
+        desc = hswd.make_desc(t["k_cache"])
+        t.update(spec=spec, ring=not full, desc=desc, out=torch.empty_like(t["q"]),
+                 ws=hswd.workspace(desc, not full, CTX, device=dev))
+        if args.mode == "unfused":
+            t["q_rot"] = torch.empty_like(t["q"])
+            t["k_rot"] = torch.empty_like(t["k"])
+            t["o"] = torch.empty_like(t["q"])
+        layers.append(t)
+    torch.cuda.synchronize()
+
+    def run_layer(t):
+        if args.mode == "fused":
+            hswd.layer_step(t["q"], t["k"], t["v"], t["gate"], t["k_cache"], t["v_cache"],
+                            t["pos"], t["ring"], t["spec"].rot, t["spec"].theta, t["ws"],
+                            max_pos=CTX, out=t["out"], desc=t["desc"])
+            return
+        t["q_rot"].copy_(t["q"])
+        t["k_rot"].copy_(t["k"])
+        hswd.rope_apply(t["q_rot"], t["k_rot"], t["pos"], t["spec"].rot, t["spec"].theta)
+        if t["ring"]:
+            hswd.decode_attn_sliding(t["q_rot"], t["k_rot"], t["v"], t["k_cache"], t["v_cache"],
+                                     t["pos"], t["ws"], out=t["o"], desc=t["desc"])
+        else:
+            hswd.decode_attn_full(t["q_rot"], t["k_rot"], t["v"], t["k_cache"], t["v_cache"],
+                                  t["pos"], CTX, t["ws"], out=t["o"], desc=t["desc"])
+        hswd.head_gate(t["o"], t["gate"], out=t["out"])
+        hswd.kv_slot_write(t["k_cache"], t["v_cache"], t["k_rot"], t["v"], t["pos"], t["ring"],
+                           t["ws"], desc=t["desc"])
+
+    # ---- parity before timing: layers 0 (sliding) and 3 (full) vs the oracle
+    sample = [0, 3]
+    host = {}
+    for l in sample:
+        t = layers[l]
+        host[l] = {k: (t[k].view(torch.int16).cpu().numpy().view(np.uint16)
+                       if t[k].dtype == torch.bfloat16 else t[k].cpu().numpy())
+                   for k in ("q", "k", "v", "gate", "k_cache", "v_cache", "pos")}
+    for t in layers:
+        run_layer(t)
+    torch.cuda.synchronize()
+    for t in layers:
+        flags = hswd.check_errors(t["ws"])
+        assert flags == 0, "error flags %d" % flags
+    gpu_out = {l: layers[l]["out"].cpu().numpy() for l in sample}
+
+    cpu = None
+    parity = {}
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        times = {}
+        for l in sample:
+            h = host[l]
+            spec = layers[l]["spec"]
+            best = None
+            for rep in range(3):
+                kc, vc = h["k_cache"], h["v_cache"]
+                t0 = time.perf_counter()
+                r = oracle.layer_step(h["q"], h["k"], h["v"], h["gate"], kc, vc, h["pos"],
+                                      oracle.BF16, spec.kind == "sliding", spec.rot,
+                                      spec.theta, write=False)
+                dt = time.perf_counter() - t0
+                best = dt if best is None else min(best, dt)
+                times.setdefault(l, []).append(dt)
+            vmax = np.abs(oracle.decode(oracle.BF16, h["v_cache"]))
+            vmax = float(np.nanmax(np.where(np.isnan(vmax), 0.0, vmax)))
+            err = float(np.max(np.abs(gpu_out[l] - r["out"])) / max(vmax, 1e-30))
+            parity["layer%d_%s" % (l, spec.kind)] = err
+            assert err <= 2e-3, ("parity", l, err)
+            log("oracle layer %d (%s): %s s, GPU parity %.2e" % (
+                l, spec.kind, ", ".join("%.2f" % x for x in times[l]), err))
+        t_sl = float(np.median(times[0]))
+        t_fu = float(np.median(times[3]))
+        step_cpu = 21 * t_sl + 7 * t_fu
+        step_bytes = 21 * layer_bytes("sliding") + 7 * layer_bytes("full")
+        cpu = {"value": round(step_bytes / step_cpu / 1e9, 3), "unit": "GB/s",
+               "cores": threads, "kind": "oracle",
+               "sample": ("fp64 oracle on layer 0 (sliding) and layer 3 (full) of the same "
+                          "step, 64 streams x 4096, median of 3 runs each (%.2f s, %.2f s), "
+                          "extrapolated to 21 sliding + 7 full layers; %d OpenMP threads"
+                          % (t_sl, t_fu, threads))}
+
+    # ---- warmup, then the timed region
+    for _ in range(args.warmup):
+        for t in layers:
+            run_layer(t)
+    torch.cuda.synchronize()
+
+    full_ev = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        for l, t in enumerate(layers):
+            if is_full(l):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run_layer(t)
+                e1.record(stream)
+                full_ev.append((e0, e1))
+            else:
+                run_layer(t)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    full_us = float(np.mean([a.elapsed_time(b) for a, b in full_ev])) * 1e3
+    step_bytes = 21 * layer_bytes("sliding") + 7 * layer_bytes("full")
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    full_bytes = layer_bytes("full")
+    achieved = full_bytes / (full_us * 1e-6) / 1e9
+    sl_us_est = (ms_step * 1e3 - 7 * full_us) / 21
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) caches and projections, no model weights)",
+        "config": {"workload": "step28_64x4096_bf16", "layers": "21 sliding (511-slot ring) "
+                   "+ 7 full (context 4096), l%4==3 full", "streams": B, "heads": H,
+                   "head_dim": D, "kv_dtype": "bf16", "launch": args.mode},
+        "us_per_layer_step": round(ms_step * 1e3 / LAYERS, 2),
+        "us_full_layer": round(full_us, 2),
+        "us_sliding_layer_est": round(sl_us_est, 2),
+        "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None,
+                     "kernel": "attn_kernel<256, bf16, append, step> (full layer, one launch)",
+                     "bytes_per_launch": full_bytes},
+        "cpu_baseline": cpu,
+        "parity_max_err": parity,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -307,24 +307,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     }
 
     if (P.n_split > 1) {
-        // Partials cross workgroups (and possibly XCDs): agent-scope atomic
-        // stores and loads, ordered by fences around the arrival count.
+        // Partials cross workgroups (and possibly XCDs).  They are written and
+        // read only with agent-scope atomic stores and loads, which go to the
+        // device-coherent level themselves, so no L2 write-back or invalidate
+        // is needed: each thread waits for its own stores to complete, the
+        // barrier makes that true for the whole workgroup, and only then is
+        // the arrival counted.  The merging workgroup reads the partials after
+        // it has seen the final count.
         const size_t idx = (size_t)bh * P.n_split + split;
         if (t < D) st_agent(P.part_o + idx * D + t, o_t);
         if (tid == 0) {
             st_agent(P.part_ml + idx * 2 + 0, M);
             st_agent(P.part_ml + idx * 2 + 1, L);
         }
-        __threadfence();
+        wait_stores_complete();
         __syncthreads();
         if (tid == 0) {
-            const int prev = __hip_atomic_fetch_add(&P.counters[pair], 1, __ATOMIC_ACQ_REL,
+            const int prev = __hip_atomic_fetch_add(&P.counters[pair], 1, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
             sm_last = prev == P.n_split - 1;
         }
         __syncthreads();
         if (!sm_last) return;
-        __threadfence();
 
         // Last arrival merges every split of this (stream, head).
         const float* pml = P.part_ml + (size_t)bh * P.n_split * 2;

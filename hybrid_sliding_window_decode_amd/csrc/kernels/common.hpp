@@ -155,6 +155,13 @@ __device__ __forceinline__ float ld_agent(const float* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wait until every vector memory operation this thread issued, stores
+// included, has completed.  The asm's memory clobber also keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void wait_stores_complete() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
