@@ -45,6 +45,31 @@ def is_full(l):
     return l % 4 == 3
 
 
+KERNEL_SOURCES = ["hybrid_sliding_window_decode_amd/csrc/kernels/attn.hpp",
+                  "hybrid_sliding_window_decode_amd/csrc/kernels/common.hpp",
+                  "hybrid_sliding_window_decode_amd/csrc/hswd.hip"]
+COUNTERS = os.path.join(ROOT, "profiles", "attn_step28_64x4096_bf16_counters.json")
+FULL_KERNEL = "hswd::attn_kernel<256, 2, false, 1>(...)"
+
+
+def measured_traffic():
+    """HBM bytes per full-layer launch from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs (scaled by a 1 GiB copy), or None when the kernel
+    sources have changed since those counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest() or FULL_KERNEL not in rec["kernels"]:
+        return None
+    k = rec["kernels"][FULL_KERNEL]
+    return int(round(k["read_bytes"] + k["write_bytes"]))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,7 +262,7 @@ def main():
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "kernel": "attn_kernel<256, bf16, append, step> (full layer, one launch)",
                      "bytes_per_launch": full_bytes},
         "cpu_baseline": cpu,

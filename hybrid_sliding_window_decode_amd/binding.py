@@ -36,7 +36,8 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_slots", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("keys_per_split", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("keys_per_split", ctypes.c_int32),
+                ("chunks_per_workgroup", ctypes.c_int32)]
 
 
 _P, _I, _Z, _D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
@@ -107,14 +108,15 @@ def _need(t, name, dtype=None, shape=None):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
-def make_desc(k_cache, n_heads=None, scale=None, keys_per_split=0):
+def make_desc(k_cache, n_heads=None, scale=None, keys_per_split=0, chunks_per_workgroup=0):
     """Descriptor of a layer from its cache tensor [B, Hkv, n_slots, D]."""
     B, Hkv, S, D = k_cache.shape
     if k_cache.dtype not in _TORCH_CODE:
         raise ValueError("cache dtype must be float32, float16 or bfloat16")
     H = Hkv if n_heads is None else n_heads
     sc = (1.0 / D ** 0.5) if scale is None else float(scale)
-    return AttnDesc(B, H, Hkv, D, S, _TORCH_CODE[k_cache.dtype], sc, keys_per_split)
+    return AttnDesc(B, H, Hkv, D, S, _TORCH_CODE[k_cache.dtype], sc, keys_per_split,
+                    chunks_per_workgroup)
 
 
 def version():

@@ -1,11 +1,13 @@
 // libhswd: C ABI of hybrid sliding-window decode attention for gfx950.
-// Host side: argument checks (before any launch), workspace layout, split
-// count, kernel dispatch.  Declarations and contracts: include/hswd.h.
+// Host side: argument checks (before any launch), workspace layout, chunk
+// count and work split, kernel dispatch.  Declarations and contracts: include/hswd.h.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "../../include/hswd.h"
 #include "kernels/attn.hpp"
@@ -15,9 +17,10 @@ namespace {
 
 using namespace hswd;
 
-constexpr int kVersion = (0 << 16) | 3;
-constexpr int kDefaultKeysPerSplit = 512;
+constexpr int kVersion = (0 << 16) | 4;
+constexpr int kDefaultChunk = 512;
 constexpr size_t kAlign = 256;
+constexpr int kWgsPerCu = 2;          // resident attention workgroups per CU (VGPR bound)
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -41,30 +44,61 @@ int32_t desc_check(const hswd_attn_desc* d) {
         return d->head_dim > 0 && d->head_dim % 8 == 0 ? HSWD_ERR_UNSUPPORTED : HSWD_ERR_INVALID;
     if (d->kv_dtype < HSWD_F32 || d->kv_dtype > HSWD_BF16) return HSWD_ERR_INVALID;
     if (!(d->scale > 0.f) || !isfinite(d->scale)) return HSWD_ERR_INVALID;
-    if (d->keys_per_split < 0 || d->keys_per_split % 64 != 0) return HSWD_ERR_INVALID;
+    if (d->keys_per_split < 0 || d->chunks_per_workgroup < 0) return HSWD_ERR_INVALID;
+    if (d->keys_per_split > 0 &&
+        d->keys_per_split % chunk_quantum(d->head_dim, d->kv_dtype) != 0)
+        return HSWD_ERR_INVALID;
     return HSWD_OK;
 }
 
-int keys_per_split(const hswd_attn_desc* d) {
-    return d->keys_per_split > 0 ? d->keys_per_split : kDefaultKeysPerSplit;
+int chunk_keys(const hswd_attn_desc* d) {
+    return d->keys_per_split > 0 ? d->keys_per_split : kDefaultChunk;
 }
 
-// Splits over the key range: a function of the cache geometry and max_pos
-// only, never of the batch (the split size is part of the summation order).
-int num_splits(const hswd_attn_desc* d, int ring, int max_pos) {
-    const int kps = keys_per_split(d);
+// Chunks over the key range: a function of the cache geometry and max_pos
+// only, never of the batch (the chunk size is part of the summation order).
+int num_chunks(const hswd_attn_desc* d, int ring, int max_pos) {
+    const long K = chunk_keys(d);
     const long keys = ring ? d->n_slots : (max_pos > 0 ? max_pos : 0);
-    const long n = (keys + kps - 1) / kps;
+    const long n = (keys + K - 1) / K;
     return n < 1 ? 1 : (int)n;
 }
 
-WsLayout ws_layout(const hswd_attn_desc* d, int n_split) {
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+        v = 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// Chunks per workgroup: enough workgroups to fill the GPU once
+// (kWgsPerCu per CU), each streaming as long a range as that allows.  Only
+// the work split depends on this, never the arithmetic.
+int chunks_per_workgroup(const hswd_attn_desc* d, int n_chunk) {
+    if (d->chunks_per_workgroup > 0)
+        return d->chunks_per_workgroup < n_chunk ? d->chunks_per_workgroup : n_chunk;
+    const long pairs = (long)d->batch * d->n_kv_heads;
+    const long target = (long)device_cus() * kWgsPerCu;
+    long wpp = (target + pairs - 1) / pairs;
+    if (wpp < 1) wpp = 1;
+    if (wpp > n_chunk) wpp = n_chunk;
+    return (int)((n_chunk + wpp - 1) / wpp);
+}
+
+WsLayout ws_layout(const hswd_attn_desc* d, int n_chunk) {
     WsLayout L;
     const size_t pairs = (size_t)d->batch * d->n_kv_heads;
     const size_t bh = (size_t)d->batch * d->n_heads;
     L.counters = kAlign;
     L.part_ml = L.counters + round_up(pairs * sizeof(int32_t), kAlign);
-    const size_t parts = n_split > 1 ? (size_t)n_split : 0;
+    const size_t parts = n_chunk > 1 ? (size_t)n_chunk : 0;
     L.part_o = L.part_ml + round_up(bh * parts * 2 * sizeof(float), kAlign);
     L.total = L.part_o + round_up(bh * parts * d->head_dim * sizeof(float), kAlign);
     return L;
@@ -100,12 +134,12 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
         if (max_pos < 0) return HSWD_ERR_INVALID;
         if ((long)max_pos + 1 > d->n_slots) return HSWD_ERR_CAPACITY;
     }
-    const int n_split = num_splits(d, ring, max_pos);
-    if (n_split > kMaxSplits) return HSWD_ERR_INVALID;
+    const int n_chunk = num_chunks(d, ring, max_pos);
+    if (n_chunk > kMaxChunks) return HSWD_ERR_INVALID;
     if (need_ws) {
         if (!ws) return HSWD_ERR_WORKSPACE;
         if (!aligned16(ws)) return HSWD_ERR_ALIGN;
-        const WsLayout L = ws_layout(d, n_split);
+        const WsLayout L = ws_layout(d, n_chunk);
         if (ws_bytes < L.total) return HSWD_ERR_WORKSPACE;
         char* base = static_cast<char*>(ws);
         P.err = reinterpret_cast<int32_t*>(base);
@@ -113,16 +147,19 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
         P.part_ml = reinterpret_cast<float*>(base + L.part_ml);
         P.part_o = reinterpret_cast<float*>(base + L.part_o);
     }
+    const int cpw = chunks_per_workgroup(d, n_chunk);
     P.B = d->batch;
     P.H = d->n_heads;
     P.Hkv = d->n_kv_heads;
     P.S = d->n_slots;
-    P.kps = keys_per_split(d);
-    P.n_split = n_split;
+    P.K = chunk_keys(d);
+    P.n_chunk = n_chunk;
+    P.cpw = cpw;
+    P.wpp = (n_chunk + cpw - 1) / cpw;
     P.ring = ring ? 1 : 0;
     P.max_pos = ring ? d->n_slots : max_pos;
     P.qscale = d->scale * 1.4426950408889634f;
-    grid = d->batch * d->n_kv_heads * n_split;
+    grid = d->batch * d->n_kv_heads * P.wpp;
     return HSWD_OK;
 }
 
@@ -147,13 +184,13 @@ const char* hswd_status_string(int32_t s) {
 
 size_t hswd_workspace_bytes(const hswd_attn_desc* d, int32_t ring, int32_t max_pos) {
     if (desc_check(d) != HSWD_OK) return 0;
-    return ws_layout(d, num_splits(d, ring, max_pos)).total;
+    return ws_layout(d, num_chunks(d, ring, max_pos)).total;
 }
 
 int32_t hswd_num_splits(const hswd_attn_desc* d, int32_t ring, int32_t max_pos) {
     int32_t st = desc_check(d);
     if (st != HSWD_OK) return st;
-    return num_splits(d, ring, max_pos);
+    return num_chunks(d, ring, max_pos);
 }
 
 int32_t hswd_workspace_init(void* ws, size_t ws_bytes, void* stream) {
@@ -279,7 +316,7 @@ int32_t hswd_decode_attn_partials(float* part_o, float* part_ml, const float* q_
 int32_t hswd_lse_merge(float* o, const float* part_o, const float* part_ml, int32_t B,
                        int32_t H, int32_t D, int32_t n, void* stream) {
     if (!o || !part_o || !part_ml || B < 1 || H < 1 || D < 1 || n < 1) return HSWD_ERR_INVALID;
-    if (n > kMaxSplits) return HSWD_ERR_UNSUPPORTED;
+    if (n > 1024) return HSWD_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(lse_merge_kernel, dim3(B * H), dim3(256), 0, as_stream(stream), o, part_o,
                        part_ml, D, n);
     return launch_status();

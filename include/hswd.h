@@ -94,9 +94,16 @@ typedef struct {
     int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows */
     int32_t kv_dtype;       /* hswd_dtype of the cache */
     float scale;            /* softmax scale, > 0; 1/sqrt(D) by convention */
-    int32_t keys_per_split; /* keys per workgroup; 0 = library default (512).
-                               A multiple of 64.  Part of the summation order
-                               [split]: never chosen from B. */
+    int32_t keys_per_split; /* keys per chunk, the unit of summation order [split]:
+                               the valid keys are cut into chunks of this many,
+                               each chunk's softmax partial is formed alone and
+                               the partials are folded in chunk order.  0 = 512.
+                               A multiple of 64 (D = 256, 16-bit cache), 32
+                               (D = 256, f32) or of 4 tiles otherwise.  Results
+                               depend on it; never on the batch. */
+    int32_t chunks_per_workgroup; /* work split only, never the bits: how many
+                               consecutive chunks one workgroup streams.  0 =
+                               library choice (from B and the CU count). */
 } hswd_attn_desc;
 
 /* Library version, (major << 16) | minor. */
@@ -108,7 +115,7 @@ const char* hswd_status_string(int32_t status);
 /* Workspace bytes needed by the attention entries for this layer and the
  * largest position `max_pos` any stream will have (append caches; rings
  * ignore it).  The workspace holds the error word, per-(stream, kv head)
- * arrival counters and the split partials.  It must be zeroed once before
+ * arrival counters and the chunk partials.  It must be zeroed once before
  * first use (hswd_workspace_init); the library leaves the counters at zero
  * after every call, so it can be reused without clearing. */
 size_t hswd_workspace_bytes(const hswd_attn_desc* d, int32_t ring, int32_t max_pos);
@@ -116,7 +123,8 @@ size_t hswd_workspace_bytes(const hswd_attn_desc* d, int32_t ring, int32_t max_p
 /* Zero a workspace (error word and counters) with a fill kernel. */
 int32_t hswd_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
-/* Number of key splits the attention entries use for this layer. */
+/* Number of chunks of keys_per_split keys per (stream, kv head): ceil(n_slots
+ * / K) for a ring, ceil(max_pos / K) for an append cache (at least 1). */
 int32_t hswd_num_splits(const hswd_attn_desc* d, int32_t ring, int32_t max_pos);
 
 /* Slot and mask [join].  slot[b] = pos[b] mod n_slots (ring) or pos[b]
@@ -172,8 +180,8 @@ int32_t hswd_decode_attn_full(float* o, const float* q_rot, const float* k_rot,
                               const int32_t* pos, int32_t max_pos, const hswd_attn_desc* d,
                               void* ws, size_t ws_bytes, void* stream);
 
-/* Split partials of the cached keys alone (no new entry) [split]: for split
- * c covering cache rows [c*kps, (c+1)*kps) of the valid range,
+/* Chunk partials of the cached keys alone (no new entry) [split]: for chunk
+ * c covering cache rows [c*K, (c+1)*K) of the valid range (K = keys_per_split),
  *   part_ml[b][h][c] = (m, l): m = max scale*q.K (natural-log units, -inf if
  *                      the split is empty), l = sum exp(score - m) (0 if empty);
  *   part_o[b][h][c][:] = sum exp(score - m) * V  (not divided by l).
@@ -184,7 +192,7 @@ int32_t hswd_decode_attn_partials(float* part_o, float* part_ml, const float* q_
                                   const int32_t* pos, int32_t ring, int32_t max_pos,
                                   const hswd_attn_desc* d, void* stream);
 
-/* Log-sum-exp merge of n partials [split]:
+/* Log-sum-exp merge of n partials [split] (n <= 1024):
  *   M = max m_i over partials with l_i > 0,
  *   o[b][h][:] = sum part_o_i * exp(m_i - M) / sum l_i * exp(m_i - M).
  * Partials with l_i == 0 are skipped; at least one must be non-empty. */

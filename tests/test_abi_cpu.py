@@ -25,7 +25,7 @@ def declared():
 
 def desc(**kw):
     d = dict(batch=2, n_heads=8, n_kv_heads=8, head_dim=256, n_slots=511, kv_dtype=2,
-             scale=1 / 16, keys_per_split=0)
+             scale=1 / 16, keys_per_split=0, chunks_per_workgroup=0)
     d.update(kw)
     return binding.AttnDesc(**d)
 
@@ -53,6 +53,7 @@ def test_workspace_and_splits():
     assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 8
     assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 256
     assert hswd.num_splits(desc(n_slots=4097, keys_per_split=1024), 0, 4096) == 4
+    assert hswd.num_splits(desc(n_slots=4097, chunks_per_workgroup=3), 0, 4096) == 8
     # splits never depend on the batch
     assert hswd.num_splits(desc(batch=1, n_slots=4097), 0, 4096) == \
         hswd.num_splits(desc(batch=64, n_slots=4097), 0, 4096)
@@ -71,6 +72,9 @@ def test_workspace_and_splits():
     ("dtype", dict(kv_dtype=3), -1),
     ("scale", dict(scale=0.0), -1),
     ("kps", dict(keys_per_split=100), -1),
+    ("kps quantum bf16", dict(keys_per_split=96), -1),
+    ("kps quantum d128", dict(head_dim=128, keys_per_split=64), -1),
+    ("cpw", dict(chunks_per_workgroup=-1), -1),
     ("batch", dict(batch=0), -1),
     ("GQA not built", dict(n_heads=16, n_kv_heads=8), -6),
 ])
@@ -95,7 +99,7 @@ def test_attention_host_checks():
     # max_pos + 1 must fit the append capacity
     assert L.hswd_decode_attn_full(A, A, A, A, A, A, A, 4096 + 1, ctypes.byref(f), A, big, None) == -4
     assert L.hswd_decode_attn_full(A, A, A, A, A, A, A, -1, ctypes.byref(f), A, big, None) == -1
-    # more than 1024 splits is refused
+    # more than 4096 chunks is refused
     huge = desc(n_slots=1 << 20, keys_per_split=64)
     assert L.hswd_decode_attn_full(A, A, A, A, A, A, A, (1 << 20) - 1, ctypes.byref(huge), A, big,
                                    None) == -1

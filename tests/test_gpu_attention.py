@@ -294,3 +294,45 @@ def test_max_pos_flag():
     hswd.decode_attn_full(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["pos"], 600, ws,
                           desc=desc)
     assert hswd.check_errors(ws) & hswd.binding.FLAG_MAX_POS
+
+
+@pytest.mark.parametrize("kind,dtype,S,kps", [("full", "bf16", 3000, 256),
+                                              ("sliding", "f32", None, 128),
+                                              ("full", "f16", 2100, 0)])
+def test_work_split_never_changes_bits(kind, dtype, S, kps):
+    """Chunks per workgroup only moves work between workgroups: one
+    workgroup per chunk, several chunks each, or the whole range in one must
+    give the same bits, in both the attention entry and the fused step."""
+    B = 6
+    spec = spec_for(kind, B, dtype, S=S)
+    hi = 4096 if kind == "sliding" else S - 1
+    pos = inputs.ragged_positions(B, 0, hi, seed=17)
+    x = inputs.make_step(spec, pos, seed=18)
+    ring = kind == "sliding"
+    mp = int(x.pos.max())
+    outs, steps, caches = [], [], []
+    for cpw in (1, 2, 5, 64, 0):
+        d = to_dev(x)
+        desc = hswd.make_desc(d["k_cache"], keys_per_split=kps, chunks_per_workgroup=cpw)
+        say("work split %s %s cpw=%d" % (kind, dtype, cpw))
+        ws = hswd.workspace(desc, ring, mp)
+        out = hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
+                              d["pos"], ring, spec.rot, spec.theta, ws, max_pos=mp, desc=desc)
+        steps.append(out.cpu().numpy())
+        caches.append(cache_to_host(d["k_cache"]))
+        e = to_dev(x)
+        hswd.rope_apply(e["q"], e["k"], e["pos"], spec.rot, spec.theta)
+        if ring:
+            o = hswd.decode_attn_sliding(e["q"], e["k"], e["v"], e["k_cache"], e["v_cache"],
+                                         e["pos"], ws, desc=desc)
+        else:
+            o = hswd.decode_attn_full(e["q"], e["k"], e["v"], e["k_cache"], e["v_cache"],
+                                      e["pos"], mp, ws, desc=desc)
+        assert hswd.check_errors(ws) == 0
+        outs.append(o.cpu().numpy())
+    for i in range(1, len(outs)):
+        assert np.array_equal(outs[0], outs[i]), i
+        assert np.array_equal(steps[0], steps[i]), i
+        assert np.array_equal(caches[0].view(np.uint8), caches[i].view(np.uint8)), i
+    ref = oracle_step(x)
+    assert_parity(outs[0], ref["o_pre"], x, "work split")
