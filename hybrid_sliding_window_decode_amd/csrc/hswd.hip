@@ -18,7 +18,6 @@ namespace {
 using namespace hswd;
 
 constexpr int kVersion = (0 << 16) | 4;
-constexpr int kDefaultChunk = 512;
 constexpr size_t kAlign = 256;
 constexpr int kWgsPerCu = 2;          // resident attention workgroups per CU (VGPR bound)
 
@@ -51,8 +50,17 @@ int32_t desc_check(const hswd_attn_desc* d) {
     return HSWD_OK;
 }
 
+// Default keys per chunk, from the cache geometry only (never the batch):
+// 2^floor(log2(n_slots / 32)) clamped to [128, 512], and at least one tile
+// per wave.  Short caches (rings, a few thousand rows) get 128-key chunks, so
+// a small batch still spreads over many workgroups; long caches get 512-key
+// chunks, so the merge folds fewer partials.
 int chunk_keys(const hswd_attn_desc* d) {
-    return d->keys_per_split > 0 ? d->keys_per_split : kDefaultChunk;
+    if (d->keys_per_split > 0) return d->keys_per_split;
+    int k = 128;
+    while (k < 512 && (long)k * 2 * 32 <= d->n_slots) k *= 2;
+    const int q = chunk_quantum(d->head_dim, d->kv_dtype);
+    return k < q ? q : k;
 }
 
 // Chunks over the key range: a function of the cache geometry and max_pos

@@ -3,9 +3,10 @@
 // layer step, the head gate and the entry write in the epilogue.
 //
 // Summation order.  The valid key range of each (stream, kv head) is cut into
-// chunks of K keys (K = keys_per_split, 512 by default).  A chunk's partial
-// (max m, sum l, unnormalised o) is computed the same way wherever it runs:
-// the workgroup's waves take the chunk's tiles round robin, keep an online
+// chunks of K keys (K = keys_per_split; by default 128 to 512 from the cache
+// length).  A chunk's partial (max m, sum l, unnormalised o) is computed the
+// same way wherever it runs: the workgroup's waves take the chunk's tiles
+// round robin, keep an online
 // softmax each, and merge through LDS in wave order.  Chunk partials are then
 // folded in chunk order, and the new entry last.  The bits therefore depend
 // on K and the positions only -- not on the batch, nor on how many chunks a
@@ -15,18 +16,20 @@
 // one (stream, kv head).  Each wave reads whole 16-key (bf16/f16) or 8-key
 // (f32) tiles with 128-bit non-temporal loads, lanes over head dims, and
 // keeps the next tile in flight while it scores the current one (register
-// double buffering); the prefetch runs across chunk boundaries, so the only
-// cost of a boundary is one barrier and a fold.  The first tile is requested
+// double buffering); the prefetch runs across chunk boundaries, and chunk
+// partials wait in registers so the waves meet at a barrier only every four
+// chunks.  The first tile is requested
 // before the query prologue.  Dot products are reduced across lanes with a
 // transposed butterfly (about one exchange per key).  Softmax is in base 2
 // with log2(e) folded into the query scale.
 //
 // Several workgroups per (stream, kv head) (long contexts, small batches):
 // each stores its chunk partials with agent-scope atomic stores, counts its
-// arrival, and the last to arrive folds all chunk partials, joins the new
-// entry, gates, and writes the entry into the cache -- after every read of
-// that cache block, which the ring needs (its slot pos mod n_slots still
-// holds position pos - n_slots, inside the window).
+// arrival, and the last to arrive folds all chunk partials (32 loads in
+// flight before folding), joins the new entry, gates, and writes the entry
+// into the cache -- after every read of that cache block, which the ring
+// needs (its slot pos mod n_slots still holds position pos - n_slots, inside
+// the window).
 //
 // Sources: vLLM-Omni fork commit log, score-space join commit (join scores,
 // not keys; ring without reordering, only a mask; 511 slots) and Spark-X2.5
@@ -169,8 +172,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     constexpr float kLn2 = 0.69314718055994531f;
 
     __shared__ float sm_q[D];
-    __shared__ float sm_o[2][kAttnWaves][D];          // wave partials, by chunk parity
-    __shared__ float sm_m[2][kAttnWaves], sm_l[2][kAttnWaves];
+    __shared__ float sm_o[2][4][kAttnWaves][D];       // stashed wave partials, by flush parity
+    __shared__ float sm_m[2][4][kAttnWaves], sm_l[2][4][kAttnWaves];
     __shared__ float sm_dot[kAttnWaves];
     __shared__ int sm_last;
 
@@ -309,56 +312,93 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         }
     };
 
-    // End of chunk ch (every wave, same point): wave partials -> LDS, one
-    // barrier, then each thread forms the chunk partial for its dim t and
-    // folds it (single workgroup per pair) or stores it.
+    // End of a chunk (every wave, same point): the wave's partial for it is
+    // reduced across lanes and pushed on a short register stash (a shift
+    // register, so every index is a compile-time one).  Every kStash chunks,
+    // and once at the end, the stash is flushed: wave partials -> LDS, one
+    // barrier, then each thread forms the chunk partials for its dim t, in
+    // chunk order, and folds (single workgroup per pair) or stores them.
+    // Deferring the barrier keeps small chunks cheap; the arithmetic and its
+    // order are those of a barrier per chunk.
+    constexpr int kStash = 4;
+    float st_m[kStash], st_l[kStash], st_o[kStash][EPC];
+    int n_st = 0, st_first = 0, n_flush = 0;
+
+    auto flush = [&]() {
+        const int buf = n_flush & 1;
+        ++n_flush;
+#pragma unroll
+        for (int s = 0; s < kStash; ++s) {
+            if (s < n_st) {
+                if (r == 0) {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) sm_o[buf][s][wid][c * EPC + e] = st_o[s][e];
+                }
+                if (lane == 0) {
+                    sm_m[buf][s][wid] = st_m[s];
+                    sm_l[buf][s][wid] = st_l[s];
+                }
+            }
+        }
+        __syncthreads();
+        for (int i = 0; i < n_st; ++i) {
+            const int s = n_st - 1 - i;             // slot 0 holds the newest chunk
+            const int ch = st_first + i;
+            const float Mc = lds_max<kAttnWaves>(sm_m[buf][s]);
+            float Lc = 0.f, Oc = 0.f;
+            if (Mc != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < kAttnWaves; ++w) {
+                    const float a = fast_exp2(sm_m[buf][s][w] - Mc);
+                    Lc = fmaf(sm_l[buf][s][w], a, Lc);
+                    if (t < D) Oc = fmaf(sm_o[buf][s][w][t], a, Oc);
+                }
+            }
+            const size_t idx = (size_t)bh * P.n_chunk + ch;
+            if (MODE == kModePartials) {
+                if (t < D) P.part_o[idx * D + t] = Oc;
+                if (tid == 0) {
+                    P.part_ml[idx * 2 + 0] = Mc == -INFINITY ? -INFINITY : Mc * kLn2;
+                    P.part_ml[idx * 2 + 1] = Lc;
+                }
+            } else if (P.wpp == 1) {
+                run.add(Mc, Lc, Oc);
+            } else {
+                if (t < D) st_agent(P.part_o + idx * D + t, Oc);
+                if (tid == 0) {
+                    st_agent(P.part_ml + idx * 2 + 0, Mc);
+                    st_agent(P.part_ml + idx * 2 + 1, Lc);
+                }
+            }
+        }
+        n_st = 0;
+    };
+
     auto end_chunk = [&](int ch) {
-        const int buf = ch & 1;
         const float l_w = wave_sum(l_lane);
 #pragma unroll
         for (int m = LPR; m < kWave; m <<= 1) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) o_acc[e] += xor_lane_rt(o_acc[e], m);
         }
-        if (r == 0) {
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) sm_o[buf][wid][c * EPC + e] = o_acc[e];
+        for (int s = kStash - 1; s > 0; --s) {
+            st_m[s] = st_m[s - 1];
+            st_l[s] = st_l[s - 1];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) st_o[s][e] = st_o[s - 1][e];
         }
-        if (lane == 0) {
-            sm_m[buf][wid] = m_run;
-            sm_l[buf][wid] = l_w;
-        }
+        st_m[0] = m_run;
+        st_l[0] = l_w;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) st_o[0][e] = o_acc[e];
+        if (n_st == 0) st_first = ch;
+        ++n_st;
         m_run = -INFINITY;
         l_lane = 0.f;
 #pragma unroll
         for (int e = 0; e < EPC; ++e) o_acc[e] = 0.f;
-        __syncthreads();
-        const float Mc = lds_max<kAttnWaves>(sm_m[buf]);
-        float Lc = 0.f, Oc = 0.f;
-        if (Mc != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) {
-                const float a = fast_exp2(sm_m[buf][w] - Mc);
-                Lc = fmaf(sm_l[buf][w], a, Lc);
-                if (t < D) Oc = fmaf(sm_o[buf][w][t], a, Oc);
-            }
-        }
-        const size_t idx = (size_t)bh * P.n_chunk + ch;
-        if (MODE == kModePartials) {
-            if (t < D) P.part_o[idx * D + t] = Oc;
-            if (tid == 0) {
-                P.part_ml[idx * 2 + 0] = Mc == -INFINITY ? -INFINITY : Mc * kLn2;
-                P.part_ml[idx * 2 + 1] = Lc;
-            }
-        } else if (P.wpp == 1) {
-            run.add(Mc, Lc, Oc);
-        } else {
-            if (t < D) st_agent(P.part_o + idx * D + t, Oc);
-            if (tid == 0) {
-                st_agent(P.part_ml + idx * 2 + 0, Mc);
-                st_agent(P.part_ml + idx * 2 + 1, Lc);
-            }
-        }
+        if (n_st == kStash) flush();
     };
 
     // The first tile's loads do not depend on the query: issue them before
@@ -403,6 +443,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         after(j);
     }
     if (c_valid > c_full) end_chunk(c_full);            // the partly valid chunk
+    if (n_st > 0) flush();
 
     if (MODE == kModePartials) {
         // chunks without a valid key are empty partials
@@ -436,20 +477,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         if (!sm_last) return;
 
         // Last arrival folds the valid chunks of this (stream, head) in chunk
-        // order, 16 partials' loads in flight before any is folded.
+        // order, 32 partials' loads in flight before any is folded.
         const float* pml = P.part_ml + (size_t)bh * P.n_chunk * 2;
         const float* po = P.part_o + (size_t)bh * P.n_chunk * D + (t < D ? t : 0);
+        constexpr int kBatch = 32;
         int i = 0;
-        for (; i + 16 <= n_valid_chunks; i += 16) {
-            float xm[16], xl[16], xo[16];
+        for (; i + kBatch <= n_valid_chunks; i += kBatch) {
+            float xm[kBatch], xl[kBatch], xo[kBatch];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < kBatch; ++u) {
                 xm[u] = ld_agent(pml + 2 * (i + u));
                 xl[u] = ld_agent(pml + 2 * (i + u) + 1);
                 xo[u] = ld_agent(po + (size_t)(i + u) * D);
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) run.add(xm[u], xl[u], xo[u]);
+            for (int u = 0; u < kBatch; ++u) run.add(xm[u], xl[u], xo[u]);
         }
         for (; i < n_valid_chunks; ++i)
             run.add(ld_agent(pml + 2 * i), ld_agent(pml + 2 * i + 1), ld_agent(po + (size_t)i * D));

@@ -49,11 +49,15 @@ def test_version_and_status_strings():
 def test_workspace_and_splits():
     L = binding.lib()
     d = desc()
-    assert hswd.num_splits(d, 1) == 1
-    assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 8
+    # default chunk: 128 keys up to 8191 slots, 256 below 16384, then 512
+    assert hswd.num_splits(d, 1) == 4
+    assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 32
+    assert hswd.num_splits(desc(n_slots=8192), 0, 8191) == 32
+    assert hswd.num_splits(desc(n_slots=16385), 0, 16384) == 32
     assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 256
+    assert hswd.num_splits(desc(n_slots=4097, head_dim=64), 0, 4096) == 16
     assert hswd.num_splits(desc(n_slots=4097, keys_per_split=1024), 0, 4096) == 4
-    assert hswd.num_splits(desc(n_slots=4097, chunks_per_workgroup=3), 0, 4096) == 8
+    assert hswd.num_splits(desc(n_slots=4097, chunks_per_workgroup=3), 0, 4096) == 32
     # splits never depend on the batch
     assert hswd.num_splits(desc(batch=1, n_slots=4097), 0, 4096) == \
         hswd.num_splits(desc(batch=64, n_slots=4097), 0, 4096)
