@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mode", choices=["fused", "unfused"], default="fused")
+    ap.add_argument("--gate", choices=["logits", "proj"], default="logits",
+                    help="gate logits given per layer (default), or projected in the "
+                         "launch from the layer input x [B, 2048] by w_g [2048, 8]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter scaling)")
@@ -199,6 +202,11 @@ def main():
         desc = hswd.make_desc(t["k_cache"])
         t.update(spec=spec, ring=not full, desc=desc, out=torch.empty_like(t["q"]),
                  ws=hswd.workspace(desc, not full, CTX, device=dev))
+        if args.gate == "proj":
+            gx, gw = inputs.gate_inputs(B, 2048, H, seed=7000 + l)
+            t["gx"] = torch.from_numpy(gx).to(dev)
+            t["gw"] = torch.from_numpy(gw).to(dev)
+            t["gate"] = torch.empty(B, H, device=dev)
         if args.mode == "unfused":
             t["q_rot"] = torch.empty_like(t["q"])
             t["k_rot"] = torch.empty_like(t["k"])
@@ -207,6 +215,14 @@ def main():
     torch.cuda.synchronize()
 
     def run_layer(t):
+        if args.mode == "fused" and args.gate == "proj":
+            hswd.layer_step_gproj(t["q"], t["k"], t["v"], t["gx"], t["gw"], t["k_cache"],
+                                  t["v_cache"], t["pos"], t["ring"], t["spec"].rot,
+                                  t["spec"].theta, t["ws"], max_pos=CTX, out=t["out"],
+                                  desc=t["desc"])
+            return
+        if args.gate == "proj":
+            hswd.gate_proj(t["gx"], t["gw"], out=t["gate"])
         if args.mode == "fused":
             hswd.layer_step(t["q"], t["k"], t["v"], t["gate"], t["k_cache"], t["v_cache"],
                             t["pos"], t["ring"], t["spec"].rot, t["spec"].theta, t["ws"],
@@ -254,9 +270,14 @@ def main():
             for rep in range(3):
                 kc, vc = h["k_cache"], h["v_cache"]
                 t0 = time.perf_counter()
-                r = oracle.layer_step(h["q"], h["k"], h["v"], h["gate"], kc, vc, h["pos"],
+                gate_h = None if args.gate == "proj" else h["gate"]
+                r = oracle.layer_step(h["q"], h["k"], h["v"], gate_h, kc, vc, h["pos"],
                                       oracle.BF16, spec.kind == "sliding", spec.rot,
                                       spec.theta, write=False)
+                if args.gate == "proj":
+                    lg = oracle.gate_proj(layers[l]["gx"].cpu().numpy(),
+                                          layers[l]["gw"].cpu().numpy())
+                    r["out"] = r["o_pre"] * (1.0 / (1.0 + np.exp(-lg)))[:, :, None]
                 dt = time.perf_counter() - t0
                 best = dt if best is None else min(best, dt)
                 times.setdefault(l, []).append(dt)
@@ -328,7 +349,9 @@ def main():
         "data": "synthetic (seeded N(0,1) caches and projections, no model weights)",
         "config": {"workload": "step28_64x4096_bf16", "layers": "21 sliding (511-slot ring) "
                    "+ 7 full (context 4096), l%4==3 full", "streams": B, "heads": H,
-                   "head_dim": D, "kv_dtype": "bf16", "launch": args.mode},
+                   "head_dim": D, "kv_dtype": "bf16", "launch": args.mode,
+                   "gate": "logits given" if args.gate == "logits" else
+                   "projected in-launch from x[64,2048] by w_g[2048,8]"},
         "us_per_layer_step": round(ms_step * 1e3 / LAYERS, 2),
         "us_full_layer": round(full_us, 2),
         "us_sliding_layer_est": round(sl_us_est, 2),

@@ -58,6 +58,9 @@ SIGNATURES = {
     "hswd_head_gate": ([_P, _P, _P, _I, _I, _I, _P], _I),
     "hswd_layer_step": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _D, _I, _DP, _P, _Z, _P], _I),
     "hswd_check_errors": ([_P, ctypes.POINTER(ctypes.c_int32), _P], _I),
+    "hswd_gate_proj": ([_P, _P, _P, _I, _I, _I, _P], _I),
+    "hswd_layer_step_gproj": ([_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _D, _I, _DP, _P,
+                               _Z, _P], _I),
 }
 
 _lib = None
@@ -286,6 +289,40 @@ def layer_step(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, ws, m
         _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(k_cache), _ptr(v_cache),
         _ptr(pos), int(ring), int(rot_dim), float(theta), int(max_pos), ctypes.byref(d),
         _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def gate_proj(x, w_g, out=None):
+    """Gate logits [B, H] = x [B, hidden] @ w_g [hidden, H] (float32)."""
+    _need(x, "x", torch.float32)
+    B, hidden = x.shape
+    _need(w_g, "w_g", torch.float32)
+    if w_g.shape[0] != hidden:
+        raise ValueError("w_g must be [hidden, H]")
+    H = w_g.shape[1]
+    out = torch.empty(B, H, dtype=torch.float32, device=x.device) if out is None else out
+    _need(out, "out", torch.float32, (B, H))
+    _check("hswd_gate_proj", lib().hswd_gate_proj(_ptr(out), _ptr(x), _ptr(w_g), B, hidden, H,
+                                                  _stream()))
+    return out
+
+
+def layer_step_gproj(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim, theta, ws,
+                     max_pos=0, out=None, desc=None):
+    """Layer step with the gate logits projected from x [B, hidden] by w_g."""
+    d = _attn_args(q, k, v, k_cache, v_cache, pos, desc)
+    B, H = q.shape[0], q.shape[1]
+    _need(x, "x", torch.float32)
+    hidden = x.shape[1]
+    _need(x, "x", torch.float32, (B, hidden))
+    _need(w_g, "w_g", torch.float32, (hidden, H))
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", torch.float32, q.shape)
+    _need(ws, "ws")
+    _check("hswd_layer_step_gproj", lib().hswd_layer_step_gproj(
+        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w_g), hidden, _ptr(k_cache),
+        _ptr(v_cache), _ptr(pos), int(ring), int(rot_dim), float(theta), int(max_pos),
+        ctypes.byref(d), _ptr(ws), ws.numel(), _stream()))
     return out
 
 

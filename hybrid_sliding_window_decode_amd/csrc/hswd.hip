@@ -338,10 +338,11 @@ int32_t hswd_head_gate(float* out, const float* o, const float* gate, int32_t B,
     return launch_status();
 }
 
-int32_t hswd_layer_step(float* out, const float* q, const float* k, const float* v,
-                        const float* gate, void* k_cache, void* v_cache, const int32_t* pos,
-                        int32_t ring, int32_t rot_dim, double theta, int32_t max_pos,
-                        const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
+static int32_t layer_step(float* out, const float* q, const float* k, const float* v,
+                          const float* gate, const float* gx, const float* gw, int32_t hidden,
+                          void* k_cache, void* v_cache, const int32_t* pos, int32_t ring,
+                          int32_t rot_dim, double theta, int32_t max_pos,
+                          const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
     if (!out || !q || !k || !v || !k_cache || !v_cache || !pos) return HSWD_ERR_INVALID;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
         !aligned16(k_cache) || !aligned16(v_cache))
@@ -357,12 +358,41 @@ int32_t hswd_layer_step(float* out, const float* q, const float* k, const float*
     P.k = k;
     P.v = v;
     P.gate = gate;
+    P.gx = gx;
+    P.gw = gw;
+    P.hidden = hidden;
     P.kc = k_cache;
     P.vc = v_cache;
     P.pos = pos;
     P.rot = rot_dim;
     P.log2_theta = log2(theta);
     return dispatch_attn<kModeStep>(P, d->head_dim, d->kv_dtype, grid, as_stream(stream));
+}
+
+int32_t hswd_layer_step(float* out, const float* q, const float* k, const float* v,
+                        const float* gate, void* k_cache, void* v_cache, const int32_t* pos,
+                        int32_t ring, int32_t rot_dim, double theta, int32_t max_pos,
+                        const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
+    return layer_step(out, q, k, v, gate, nullptr, nullptr, 0, k_cache, v_cache, pos, ring,
+                      rot_dim, theta, max_pos, d, ws, ws_bytes, stream);
+}
+
+int32_t hswd_layer_step_gproj(float* out, const float* q, const float* k, const float* v,
+                              const float* x, const float* w_g, int32_t hidden, void* k_cache,
+                              void* v_cache, const int32_t* pos, int32_t ring, int32_t rot_dim,
+                              double theta, int32_t max_pos, const hswd_attn_desc* d, void* ws,
+                              size_t ws_bytes, void* stream) {
+    if (!x || !w_g || hidden < 1) return HSWD_ERR_INVALID;
+    return layer_step(out, q, k, v, nullptr, x, w_g, hidden, k_cache, v_cache, pos, ring,
+                      rot_dim, theta, max_pos, d, ws, ws_bytes, stream);
+}
+
+int32_t hswd_gate_proj(float* logits, const float* x, const float* w_g, int32_t B,
+                       int32_t hidden, int32_t H, void* stream) {
+    if (!logits || !x || !w_g || B < 1 || hidden < 1 || H < 1) return HSWD_ERR_INVALID;
+    hipLaunchKernelGGL(gate_proj_kernel, dim3(B * H), dim3(256), 0, as_stream(stream), logits, x,
+                       w_g, hidden, H);
+    return launch_status();
 }
 
 int32_t hswd_check_errors(const void* ws, int32_t* flags_out, void* stream) {

@@ -65,7 +65,10 @@ struct AttnParams {
     const float* q;          // [B,H,D]: rotated (attend) or raw (step)
     const float* k;          // [B,Hkv,D]: rotated (attend) or raw (step); unused for partials
     const float* v;          // [B,Hkv,D]
-    const float* gate;       // [B,H] or null
+    const float* gate;       // [B,H] logits, or null
+    const float* gx;         // [B,hidden] gate-projection input, or null
+    const float* gw;         // [hidden,H] gate-projection weight (used when gx != null)
+    int hidden;
     void* kc;                // cache [B,Hkv,S,D]
     void* vc;
     const int32_t* pos;      // [B]
@@ -102,18 +105,13 @@ constexpr int chunk_quantum(int D, int DT) {
     return kAttnWaves * 8 * (kWave / (D / (16 / (DT == kF32 ? 4 : 2))));
 }
 
-// Max and pairwise-tree sum of N values in LDS (fixed order: deterministic).
+// Max of N values in LDS.
 template <int N>
 __device__ __forceinline__ float lds_max(const float* a) {
     float m = a[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) m = fmaxf(m, a[i]);
     return m;
-}
-template <int N>
-__device__ __forceinline__ float lds_tree_sum(const float* a) {
-    if constexpr (N == 1) return a[0];
-    else return lds_tree_sum<N / 2>(a) + lds_tree_sum<N / 2>(a + N / 2);
 }
 
 // Fold partial (m, l, o) into the running (M, L, O); base-2 exponents.  The
@@ -175,6 +173,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     __shared__ float sm_o[2][4][kAttnWaves][D];       // stashed wave partials, by flush parity
     __shared__ float sm_m[2][4][kAttnWaves], sm_l[2][4][kAttnWaves];
     __shared__ float sm_dot[kAttnWaves];
+    __shared__ float sm_gl[kAttnWaves];
     __shared__ int sm_last;
 
     const int tid = threadIdx.x;
@@ -514,12 +513,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     }
     prod = wave_sum(prod);
     if (lane == 0) sm_dot[wid] = prod;
+    const bool gproj = MODE == kModeStep && P.gx != nullptr;
+    if (gproj) {        // gate logit from the projection, same sum as hswd_gate_proj
+        float gs = gate_share(P.gx + (size_t)b * P.hidden, P.gw, P.hidden, P.H, h, tid,
+                              kAttnThreads);
+        gs = wave_sum(gs);
+        if (lane == 0) sm_gl[wid] = gs;
+    }
     __syncthreads();
     const float s_new = lds_tree_sum<kAttnWaves>(sm_dot);
     run.add(s_new, 1.f, vh);
     if (t < D) {
         float o = run.O / run.L;
-        if (MODE == kModeStep && P.gate != nullptr) o *= 1.f / (1.f + expf(-P.gate[bh]));
+        if (MODE == kModeStep && (gproj || P.gate != nullptr)) {
+            const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl) : P.gate[bh];
+            o *= 1.f / (1.f + expf(-logit));
+        }
         P.out[(size_t)bh * D + t] = o;
     }
 

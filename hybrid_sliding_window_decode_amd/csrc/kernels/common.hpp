@@ -181,6 +181,25 @@ __device__ __forceinline__ void wait_stores_complete() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Pairwise-tree sum of N values in LDS (fixed order: deterministic).
+template <int N>
+__device__ __forceinline__ float lds_tree_sum(const float* a) {
+    if constexpr (N == 1) return a[0];
+    else return lds_tree_sum<N / 2>(a) + lds_tree_sum<N / 2>(a + N / 2);
+}
+
+// This thread's share of one gate logit, x . w_g[:, h]: the terms i = tid,
+// tid + nthreads, ... in order.  The head-gate projection of the pages' model
+// maps the layer's post-norm input (hidden 2048) to one logit per head.
+// Callers sum the shares of 256 threads by wave_sum and a 4-wave tree, so the
+// standalone projection and the fused layer step give the same bits.
+__device__ __forceinline__ float gate_share(const float* x, const float* w, int hidden, int H,
+                                            int h, int tid, int nthreads) {
+    float acc = 0.f;
+    for (int i = tid; i < hidden; i += nthreads) acc = fmaf(x[i], w[(size_t)i * H + h], acc);
+    return acc;
+}
+
 // ---------------------------------------------------------------------------
 // RoPE of element t of one head vector x[0..D) at position p: the pair
 // (x[i], x[i + rot/2]) turns by p * theta^(-2i/rot); dims >= rot pass.  The

@@ -76,6 +76,21 @@ __global__ __launch_bounds__(256) void head_gate_kernel(float* out, const float*
     for (int t = threadIdx.x; t < D; t += blockDim.x) out[(size_t)bh * D + t] = o[(size_t)bh * D + t] * s;
 }
 
+// Gate logits: logits[b][h] = x[b] . w_g[:, h], one workgroup of 256
+// threads per (stream, head) (the same sum as the fused layer step).
+__global__ __launch_bounds__(256) void gate_proj_kernel(float* logits, const float* x,
+                                                        const float* w, int hidden, int H) {
+    __shared__ float sm[4];
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x;
+    float gs = gate_share(x + (size_t)b * hidden, w, hidden, H, h, tid, 256);
+    gs = wave_sum(gs);
+    if ((tid & 63) == 0) sm[tid >> 6] = gs;
+    __syncthreads();
+    if (tid == 0) logits[bh] = lds_tree_sum<4>(sm);
+}
+
 // Merge n partials (natural-log m, l, unnormalised o) of each (stream, head).
 __global__ __launch_bounds__(256) void lse_merge_kernel(float* out, const float* part_o,
                                                         const float* part_ml, int D, int n) {

@@ -103,6 +103,15 @@ def make_step(spec, pos, seed, poison=True):
     return StepInputs(spec, pos, q, k, v, gate, kc, vc)
 
 
+def gate_inputs(B, hidden, H, seed):
+    """Post-norm layer input x [B, hidden] ~ N(0,1) and gate weight
+    w_g [hidden, H] ~ N(0, 1/hidden) (float32), so logits are ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, hidden), dtype=np.float32)
+    w = (rng.standard_normal((hidden, H), dtype=np.float32) / np.float32(np.sqrt(hidden)))
+    return x, w.astype(np.float32)
+
+
 def ragged_positions(B, lo, hi, seed):
     """Integer positions uniform in [lo, hi], seeded."""
     rng = np.random.default_rng(seed)

@@ -8,9 +8,11 @@
  *   attend over the cached keys plus the new entry      hswd_decode_attn_sliding
  *     (ring of window-1 slots, or append cache),        hswd_decode_attn_full
  *     split over the key range and merged               hswd_lse_merge
+ *   gate logits from the layer input (g_proj)           hswd_gate_proj
  *   scale each head by the sigmoid of its gate logit    hswd_head_gate
  *   store the new entry in its ring slot / append row   hswd_kv_slot_write
- *   all of the above in one launch                      hswd_layer_step
+ *   all of the above in one launch                      hswd_layer_step,
+ *                                                       hswd_layer_step_gproj
  *
  * Sources (web pages; each citation names the page and its part):
  *   [join]   vLLM-Omni fork commit log (tea.kyle-merritt.com,
@@ -218,6 +220,23 @@ int32_t hswd_layer_step(float* out, const float* q, const float* k, const float*
                         const float* gate, void* k_cache, void* v_cache, const int32_t* pos,
                         int32_t ring, int32_t rot_dim, double theta, int32_t max_pos,
                         const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream);
+
+/* Gate projection g_proj [model], [export]: logits[b][h] = sum over i of
+ * x[b][i] * w_g[i][h], summed in a fixed order in float32.  x float32
+ * [B, hidden] is the layer's post-norm input (the same one the QKV
+ * projection reads), w_g float32 [hidden, H] ([2048, 8] in the pages' model).
+ * logits float32 [B, H]. */
+int32_t hswd_gate_proj(float* logits, const float* x, const float* w_g, int32_t B,
+                       int32_t hidden, int32_t H, void* stream);
+
+/* hswd_layer_step with the gate logits computed inside the launch from x
+ * [B, hidden] and w_g [hidden, H] (the same sum as hswd_gate_proj, so the
+ * same bits as hswd_gate_proj followed by hswd_layer_step). */
+int32_t hswd_layer_step_gproj(float* out, const float* q, const float* k, const float* v,
+                              const float* x, const float* w_g, int32_t hidden, void* k_cache,
+                              void* v_cache, const int32_t* pos, int32_t ring, int32_t rot_dim,
+                              double theta, int32_t max_pos, const hswd_attn_desc* d, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* Synchronise `stream`, then read the workspace error word.  Returns
  * HSWD_OK if it is zero, HSWD_ERR_CAPACITY otherwise; *flags_out (nullable,

@@ -61,6 +61,7 @@ def _bind(L):
     L.orc_layer_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f64, f64, i32,
                                  P, P, P, P, P, P, P, i32, P, P, P, P, P, P]
     L.orc_attend_block.argtypes = [P, P, P, P, i32, i32, i32, P, P, f64]
+    L.orc_gate_proj.argtypes = [P, P, P, i32, i32, i32]
     return L
 
 
@@ -189,6 +190,18 @@ def head_gate(o, g, L=None):
     B, H, D = o.shape
     out = np.empty_like(o)
     L.orc_head_gate(_p(out), _p(o), _p(g), B, H, D)
+    return out
+
+
+def gate_proj(x, w, L=None):
+    """Gate logits [B, H] = x [B, hidden] . w [hidden, H], in fp64."""
+    L = L or lib()
+    x = _c(x, np.float32)
+    w = _c(w, np.float32)
+    B, hidden = x.shape
+    H = w.shape[1]
+    out = np.empty((B, H))
+    L.orc_gate_proj(_p(out), _p(x), _p(w), B, hidden, H)
     return out
 
 

@@ -359,6 +359,17 @@ def pin_gate(L):
     assert np.max(np.abs(out[1, 0] - o[1, 0] * expit(1.0))) < 1e-15
 
 
+def pin_gate_proj(L):
+    """Per-layer-type KV export commit: the gate is [2048, 8], one logit per
+    head from the layer's input; against numpy's float64 matmul."""
+    x, w = inputs.gate_inputs(5, 2048, 8, seed=31)
+    got = oracle.gate_proj(x, w, L=L)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    assert np.max(np.abs(got - ref)) < 1e-12 * np.max(np.abs(x)) * np.abs(w).sum(0).max()
+    x2, w2 = inputs.gate_inputs(3, 100, 7, seed=32)     # non-square, odd sizes
+    assert np.max(np.abs(oracle.gate_proj(x2, w2, L=L) - x2.astype(np.float64) @ w2)) < 1e-12
+
+
 def pin_capacity_and_poison(L):
     """An append position at the capacity is reported (-4) and its write is
     skipped; NaN in unwritten slots never reaches the output."""
@@ -379,4 +390,4 @@ def pin_capacity_and_poison(L):
 QUICK_PINS = [pin_rne_quick, pin_decode, pin_rope, pin_slot_mask, pin_brute_multistep,
               pin_single_key, pin_equal_scores, pin_join_equals_concat,
               pin_split_invariance, pin_permutation, pin_ring_equals_roll, pin_merge,
-              pin_gate, pin_capacity_and_poison]
+              pin_gate, pin_gate_proj, pin_capacity_and_poison]
