@@ -78,7 +78,7 @@ def parse():
     ap.add_argument("--mode", choices=["fused", "unfused"], default="fused")
     ap.add_argument("--gate", choices=["logits", "proj"], default="logits",
                     help="gate logits given per layer (default), or projected in the "
-                         "launch from the layer input x [B, 2048] by w_g [2048, 8]")
+                         "launch from the layer input x [B, 2048] by w_g [8, 2048]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter scaling)")
@@ -351,7 +351,7 @@ def main():
                    "+ 7 full (context 4096), l%4==3 full", "streams": B, "heads": H,
                    "head_dim": D, "kv_dtype": "bf16", "launch": args.mode,
                    "gate": "logits given" if args.gate == "logits" else
-                   "projected in-launch from x[64,2048] by w_g[2048,8]"},
+                   "projected in-launch from x[64,2048] by w_g[8,2048]"},
         "us_per_layer_step": round(ms_step * 1e3 / LAYERS, 2),
         "us_full_layer": round(full_us, 2),
         "us_sliding_layer_est": round(sl_us_est, 2),

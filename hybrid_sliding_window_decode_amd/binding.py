@@ -293,13 +293,13 @@ def layer_step(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, ws, m
 
 
 def gate_proj(x, w_g, out=None):
-    """Gate logits [B, H] = x [B, hidden] @ w_g [hidden, H] (float32)."""
+    """Gate logits [B, H] = x [B, hidden] @ w_g[H, hidden].T (float32)."""
     _need(x, "x", torch.float32)
     B, hidden = x.shape
     _need(w_g, "w_g", torch.float32)
-    if w_g.shape[0] != hidden:
-        raise ValueError("w_g must be [hidden, H]")
-    H = w_g.shape[1]
+    if w_g.dim() != 2 or w_g.shape[1] != hidden:
+        raise ValueError("w_g must be [H, hidden]")
+    H = w_g.shape[0]
     out = torch.empty(B, H, dtype=torch.float32, device=x.device) if out is None else out
     _need(out, "out", torch.float32, (B, H))
     _check("hswd_gate_proj", lib().hswd_gate_proj(_ptr(out), _ptr(x), _ptr(w_g), B, hidden, H,
@@ -309,13 +309,13 @@ def gate_proj(x, w_g, out=None):
 
 def layer_step_gproj(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim, theta, ws,
                      max_pos=0, out=None, desc=None):
-    """Layer step with the gate logits projected from x [B, hidden] by w_g."""
+    """Layer step with the gate logits projected from x [B, hidden] by w_g [H, hidden]."""
     d = _attn_args(q, k, v, k_cache, v_cache, pos, desc)
     B, H = q.shape[0], q.shape[1]
     _need(x, "x", torch.float32)
     hidden = x.shape[1]
     _need(x, "x", torch.float32, (B, hidden))
-    _need(w_g, "w_g", torch.float32, (hidden, H))
+    _need(w_g, "w_g", torch.float32, (H, hidden))
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", torch.float32, q.shape)
     _need(ws, "ws")

@@ -67,7 +67,7 @@ struct AttnParams {
     const float* v;          // [B,Hkv,D]
     const float* gate;       // [B,H] logits, or null
     const float* gx;         // [B,hidden] gate-projection input, or null
-    const float* gw;         // [hidden,H] gate-projection weight (used when gx != null)
+    const float* gw;         // [H,hidden] gate-projection weight (used when gx != null)
     int hidden;
     void* kc;                // cache [B,Hkv,S,D]
     void* vc;
@@ -413,6 +413,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
             sm_q[i] = x * P.qscale;
         }
     }
+    // Gate logit from the projection (fused step with g_proj): it needs only
+    // the layer input, so it is summed here, under the first tile's latency,
+    // and used in the epilogue.  Same sum as hswd_gate_proj.
+    const bool gproj = MODE == kModeStep && P.gx != nullptr;
+    if (gproj) {
+        float gs = gate_share(P.gx + (size_t)b * P.hidden, P.gw + (size_t)h * P.hidden,
+                              P.hidden, tid, kAttnThreads);
+        gs = wave_sum(gs);
+        if (lane == 0) sm_gl[wid] = gs;
+    }
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < EPC; ++e) qs[e] = sm_q[c * EPC + e];
@@ -513,13 +523,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     }
     prod = wave_sum(prod);
     if (lane == 0) sm_dot[wid] = prod;
-    const bool gproj = MODE == kModeStep && P.gx != nullptr;
-    if (gproj) {        // gate logit from the projection, same sum as hswd_gate_proj
-        float gs = gate_share(P.gx + (size_t)b * P.hidden, P.gw, P.hidden, P.H, h, tid,
-                              kAttnThreads);
-        gs = wave_sum(gs);
-        if (lane == 0) sm_gl[wid] = gs;
-    }
     __syncthreads();
     const float s_new = lds_tree_sum<kAttnWaves>(sm_dot);
     run.add(s_new, 1.f, vh);

@@ -188,15 +188,29 @@ __device__ __forceinline__ float lds_tree_sum(const float* a) {
     else return lds_tree_sum<N / 2>(a) + lds_tree_sum<N / 2>(a + N / 2);
 }
 
-// This thread's share of one gate logit, x . w_g[:, h]: the terms i = tid,
+// This thread's share of one gate logit, x . w_g[h, :]: the terms i = tid,
 // tid + nthreads, ... in order.  The head-gate projection of the pages' model
 // maps the layer's post-norm input (hidden 2048) to one logit per head.
-// Callers sum the shares of 256 threads by wave_sum and a 4-wave tree, so the
-// standalone projection and the fused layer step give the same bits.
-__device__ __forceinline__ float gate_share(const float* x, const float* w, int hidden, int H,
-                                            int h, int tid, int nthreads) {
+// Loads go out 16 at a time before any is used, so the share costs about one
+// memory latency.  Callers sum the shares of 256 threads by wave_sum and a
+// 4-wave tree, so the standalone projection and the fused layer step give the
+// same bits.
+__device__ __forceinline__ float gate_share(const float* x, const float* w_row, int hidden,
+                                            int tid, int nthreads) {
+    constexpr int kBatch = 16;
     float acc = 0.f;
-    for (int i = tid; i < hidden; i += nthreads) acc = fmaf(x[i], w[(size_t)i * H + h], acc);
+    for (int i0 = tid; i0 < hidden; i0 += kBatch * nthreads) {
+        float xv[kBatch], wv[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = i0 + u * nthreads;
+            xv[u] = i < hidden ? x[i] : 0.f;
+            wv[u] = i < hidden ? w_row[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (i0 + u * nthreads < hidden) acc = fmaf(xv[u], wv[u], acc);
+    }
     return acc;
 }
 

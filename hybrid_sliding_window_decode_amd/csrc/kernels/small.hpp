@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void head_gate_kernel(float* out, const float*
     for (int t = threadIdx.x; t < D; t += blockDim.x) out[(size_t)bh * D + t] = o[(size_t)bh * D + t] * s;
 }
 
-// Gate logits: logits[b][h] = x[b] . w_g[:, h], one workgroup of 256
+// Gate logits: logits[b][h] = x[b] . w_g[h], one workgroup of 256
 // threads per (stream, head) (the same sum as the fused layer step).
 __global__ __launch_bounds__(256) void gate_proj_kernel(float* logits, const float* x,
                                                         const float* w, int hidden, int H) {
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void gate_proj_kernel(float* logits, const flo
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x;
-    float gs = gate_share(x + (size_t)b * hidden, w, hidden, H, h, tid, 256);
+    float gs = gate_share(x + (size_t)b * hidden, w + (size_t)h * hidden, hidden, tid, 256);
     gs = wave_sum(gs);
     if ((tid & 63) == 0) sm[tid >> 6] = gs;
     __syncthreads();

@@ -105,10 +105,10 @@ def make_step(spec, pos, seed, poison=True):
 
 def gate_inputs(B, hidden, H, seed):
     """Post-norm layer input x [B, hidden] ~ N(0,1) and gate weight
-    w_g [hidden, H] ~ N(0, 1/hidden) (float32), so logits are ~ N(0,1)."""
+    w_g [H, hidden] ~ N(0, 1/hidden) (float32), so logits are ~ N(0,1)."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((B, hidden), dtype=np.float32)
-    w = (rng.standard_normal((hidden, H), dtype=np.float32) / np.float32(np.sqrt(hidden)))
+    w = (rng.standard_normal((H, hidden), dtype=np.float32) / np.float32(np.sqrt(hidden)))
     return x, w.astype(np.float32)
 
 

@@ -222,15 +222,16 @@ int32_t hswd_layer_step(float* out, const float* q, const float* k, const float*
                         const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream);
 
 /* Gate projection g_proj [model], [export]: logits[b][h] = sum over i of
- * x[b][i] * w_g[i][h], summed in a fixed order in float32.  x float32
+ * x[b][i] * w_g[h][i], summed in a fixed order in float32.  x float32
  * [B, hidden] is the layer's post-norm input (the same one the QKV
- * projection reads), w_g float32 [hidden, H] ([2048, 8] in the pages' model).
- * logits float32 [B, H]. */
+ * projection reads); w_g float32 [H, hidden] is the projection's weight in
+ * the row-per-output layout of a linear layer (the pages' model maps hidden
+ * 2048 to 8 heads; each head's row is contiguous).  logits float32 [B, H]. */
 int32_t hswd_gate_proj(float* logits, const float* x, const float* w_g, int32_t B,
                        int32_t hidden, int32_t H, void* stream);
 
 /* hswd_layer_step with the gate logits computed inside the launch from x
- * [B, hidden] and w_g [hidden, H] (the same sum as hswd_gate_proj, so the
+ * [B, hidden] and w_g [H, hidden] (the same sum as hswd_gate_proj, so the
  * same bits as hswd_gate_proj followed by hswd_layer_step). */
 int32_t hswd_layer_step_gproj(float* out, const float* q, const float* k, const float* v,
                               const float* x, const float* w_g, int32_t hidden, void* k_cache,

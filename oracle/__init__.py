@@ -194,12 +194,12 @@ def head_gate(o, g, L=None):
 
 
 def gate_proj(x, w, L=None):
-    """Gate logits [B, H] = x [B, hidden] . w [hidden, H], in fp64."""
+    """Gate logits [B, H] = x [B, hidden] . w[H, hidden]^T, in fp64."""
     L = L or lib()
     x = _c(x, np.float32)
     w = _c(w, np.float32)
     B, hidden = x.shape
-    H = w.shape[1]
+    H = w.shape[0]
     out = np.empty((B, H))
     L.orc_gate_proj(_p(out), _p(x), _p(w), B, hidden, H)
     return out

@@ -332,15 +332,15 @@ void orc_head_gate(double* out, const double* o, const float* g, int B, int H, i
 }
 
 /* Gate projection  [vLLM-Omni/model], [vLLM-Omni/export]: g_proj maps the  */
-/* layer's post-norm input (hidden 2048) to one logit per head, weight      */
-/* [hidden, H]: logits[b][h] = sum_i x[b][i] * w[i][h].                      */
+/* layer's post-norm input (hidden 2048) to one logit per head; the weight   */
+/* is stored a row per head, [H, hidden]: logits[b][h] = sum_i x[b][i]*w[h][i].*/
 void orc_gate_proj(double* logits, const float* x, const float* w, int B, int hidden, int H)
 {
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < H; ++h) {
             double acc = 0.0;
             for (int i = 0; i < hidden; ++i)
-                acc += (double)x[(size_t)b * hidden + i] * (double)w[(size_t)i * H + h];
+                acc += (double)x[(size_t)b * hidden + i] * (double)w[(size_t)h * hidden + i];
             logits[(size_t)b * H + h] = acc;
         }
 }

@@ -364,10 +364,10 @@ def pin_gate_proj(L):
     head from the layer's input; against numpy's float64 matmul."""
     x, w = inputs.gate_inputs(5, 2048, 8, seed=31)
     got = oracle.gate_proj(x, w, L=L)
-    ref = x.astype(np.float64) @ w.astype(np.float64)
-    assert np.max(np.abs(got - ref)) < 1e-12 * np.max(np.abs(x)) * np.abs(w).sum(0).max()
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.max(np.abs(got - ref)) < 1e-12 * np.max(np.abs(x)) * np.abs(w).sum(1).max()
     x2, w2 = inputs.gate_inputs(3, 100, 7, seed=32)     # non-square, odd sizes
-    assert np.max(np.abs(oracle.gate_proj(x2, w2, L=L) - x2.astype(np.float64) @ w2)) < 1e-12
+    assert np.max(np.abs(oracle.gate_proj(x2, w2, L=L) - x2.astype(np.float64) @ w2.T)) < 1e-12
 
 
 def pin_capacity_and_poison(L):

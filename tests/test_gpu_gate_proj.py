@@ -16,12 +16,12 @@ def test_gate_proj_matches_oracle():
     say("gate_proj 64x2048x8")
     got = hswd.gate_proj(f32_dev(x), f32_dev(w)).cpu().numpy()
     ref = oracle.gate_proj(x, w)
-    scale = np.abs(x).astype(np.float64) @ np.abs(w).astype(np.float64)   # sum of |terms|
+    scale = np.abs(x).astype(np.float64) @ np.abs(w).astype(np.float64).T   # sum of |terms|
     assert np.all(np.abs(got - ref) <= 1e-6 * scale)
     x2, w2 = inputs.gate_inputs(3, 1000, 5, seed=61)                       # ragged sizes
     got2 = hswd.gate_proj(f32_dev(x2), f32_dev(w2)).cpu().numpy()
     ref2 = oracle.gate_proj(x2, w2)
-    assert np.all(np.abs(got2 - ref2) <= 1e-6 * (np.abs(x2) @ np.abs(w2)))
+    assert np.all(np.abs(got2 - ref2) <= 1e-6 * (np.abs(x2) @ np.abs(w2).T))
 
 
 @pytest.mark.parametrize("kind,dtype", [("sliding", "bf16"), ("full", "f16")])

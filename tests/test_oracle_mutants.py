@@ -55,7 +55,7 @@ MUTANTS = [
     ("f16 subnormal exponent", [("round_to_grid(ax, 10, -14);", "round_to_grid(ax, 10, -15);")]),
     ("f16 decode subnormal scale", [("else if (e == 0) v = ldexp((double)m, -24);",
                                      "else if (e == 0) v = ldexp((double)m, -25);")]),
-    ("gate weight transposed", [("(double)w[(size_t)i * H + h];", "(double)w[(size_t)h * hidden + i];")]),
+    ("gate weight transposed", [("(double)w[(size_t)h * hidden + i];", "(double)w[(size_t)i * H + h];")]),
     ("append capacity off by one", [("if (!ring && p >= n_slots) { status = -4; continue; }",
                                      "if (!ring && p > n_slots) { status = -4; continue; }")]),
 ]
