@@ -29,16 +29,16 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn µs/layer-step + achieved HBM GB/s (% peak), 64 streams × 4k ctx"
 PEAK_HBM_GBS = 8000.0                 # MI355X HBM3E, vendor figure
 B, H, HKV, D, S_RING, CTX, LAYERS = 64, 8, 8, 256, 511, 4096, 28
-ELT = 2                               # bf16
 
 
-def layer_bytes(kind, B=B, pos=CTX):
+def layer_bytes(kind, B=B, pos=CTX, elt=2):
     """Algorithmic bytes of one layer step: valid K and V rows plus the
-    per-stream q in, output out, k and v in, rounded entry out, gate, pos."""
+    per-stream q in, output out, k and v in, rounded entry out, gate, pos
+    (fp8 caches: plus the 2*Hkv per-head scales)."""
     n_keys = min(pos, S_RING) if kind == "sliding" else pos
-    cache = B * HKV * n_keys * D * ELT * 2
-    per_stream = H * D * 4 * 2 + HKV * D * 4 * 2 + HKV * D * ELT * 2 + H * 4 + 4
-    return cache + B * per_stream
+    cache = B * HKV * n_keys * D * elt * 2
+    per_stream = H * D * 4 * 2 + HKV * D * 4 * 2 + HKV * D * elt * 2 + H * 4 + 4
+    return cache + B * per_stream + (2 * HKV * 4 if elt == 1 else 0)
 
 
 def is_full(l):
@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--gate", choices=["logits", "proj"], default="logits",
                     help="gate logits given per layer (default), or projected in the "
                          "launch from the layer input x [B, 2048] by w_g [8, 2048]")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="cache element type of the 28-layer step (fp8: OCP e4m3 with "
+                         "per-head scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter scaling)")
@@ -191,15 +194,17 @@ def main():
         return
 
     # ---- inputs: 28 layers, each with its own buffers, all streams at 4096
+    kv = args.kv
+    elt = 1 if kv == "fp8" else 2
     log("generating 28-layer workload (%.1f GB of KV caches)" % (
-        sum(2 * B * HKV * (S_RING if not is_full(l) else CTX + 1) * D * ELT
+        sum(2 * B * HKV * (S_RING if not is_full(l) else CTX + 1) * D * elt
             for l in range(LAYERS)) / 1e9))
     layers = []
     for l in range(LAYERS):
         full = is_full(l)
-        spec = inputs.full_spec(B, CTX + 1, "bf16") if full else inputs.sliding_spec(B, "bf16")
+        spec = inputs.full_spec(B, CTX + 1, kv) if full else inputs.sliding_spec(B, kv)
         t = inputs.device_step(spec, CTX, seed=4000 + l, device=dev)
-        desc = hswd.make_desc(t["k_cache"])
+        desc = hswd.make_desc(t["k_cache"], kv_scale=t.get("kv_scale"))
         t.update(spec=spec, ring=not full, desc=desc, out=torch.empty_like(t["q"]),
                  ws=hswd.workspace(desc, not full, CTX, device=dev))
         if args.gate == "proj":
@@ -247,7 +252,9 @@ def main():
     for l in sample:
         t = layers[l]
         host[l] = {k: (t[k].view(torch.int16).cpu().numpy().view(np.uint16)
-                       if t[k].dtype == torch.bfloat16 else t[k].cpu().numpy())
+                       if t[k].dtype == torch.bfloat16 else
+                       t[k].view(torch.uint8).cpu().numpy()
+                       if t[k].dtype == torch.float8_e4m3fn else t[k].cpu().numpy())
                    for k in ("q", "k", "v", "gate", "k_cache", "v_cache", "pos")}
     for t in layers:
         run_layer(t)
@@ -272,8 +279,8 @@ def main():
                 t0 = time.perf_counter()
                 gate_h = None if args.gate == "proj" else h["gate"]
                 r = oracle.layer_step(h["q"], h["k"], h["v"], gate_h, kc, vc, h["pos"],
-                                      oracle.BF16, spec.kind == "sliding", spec.rot,
-                                      spec.theta, write=False)
+                                      oracle.DTYPES[kv], spec.kind == "sliding", spec.rot,
+                                      spec.theta, write=False, kv_scale=spec.kv_scale)
                 if args.gate == "proj":
                     lg = oracle.gate_proj(layers[l]["gx"].cpu().numpy(),
                                           layers[l]["gw"].cpu().numpy())
@@ -281,7 +288,9 @@ def main():
                 dt = time.perf_counter() - t0
                 best = dt if best is None else min(best, dt)
                 times.setdefault(l, []).append(dt)
-            vmax = np.abs(oracle.decode(oracle.BF16, h["v_cache"]))
+            vmax = np.abs(oracle.decode(oracle.DTYPES[kv], h["v_cache"]))
+            if spec.kv_scale is not None:
+                vmax = vmax * spec.kv_scale[1][None, :, None, None]
             vmax = float(np.nanmax(np.where(np.isnan(vmax), 0.0, vmax)))
             err = float(np.max(np.abs(gpu_out[l] - r["out"])) / max(vmax, 1e-30))
             parity["layer%d_%s" % (l, spec.kind)] = err
@@ -291,7 +300,7 @@ def main():
         t_sl = float(np.median(times[0]))
         t_fu = float(np.median(times[3]))
         step_cpu = 21 * t_sl + 7 * t_fu
-        step_bytes = 21 * layer_bytes("sliding") + 7 * layer_bytes("full")
+        step_bytes = 21 * layer_bytes("sliding", elt=elt) + 7 * layer_bytes("full", elt=elt)
         cpu = {"value": round(step_bytes / step_cpu / 1e9, 3), "unit": "GB/s",
                "cores": threads, "kind": "oracle",
                "sample": ("fp64 oracle on layer 0 (sliding) and layer 3 (full) of the same "
@@ -328,9 +337,9 @@ def main():
 
     ms_step = t_start.elapsed_time(t_end) / args.steps
     full_us = float(np.mean([a.elapsed_time(b) for a, b in full_ev])) * 1e3
-    step_bytes = 21 * layer_bytes("sliding") + 7 * layer_bytes("full")
+    step_bytes = 21 * layer_bytes("sliding", elt=elt) + 7 * layer_bytes("full", elt=elt)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    full_bytes = layer_bytes("full")
+    full_bytes = layer_bytes("full", elt=elt)
     achieved = full_bytes / (full_us * 1e-6) / 1e9
     sl_us_est = (ms_step * 1e3 - 7 * full_us) / 21
 
@@ -345,11 +354,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": kv,
         "data": "synthetic (seeded N(0,1) caches and projections, no model weights)",
-        "config": {"workload": "step28_64x4096_bf16", "layers": "21 sliding (511-slot ring) "
+        "config": {"workload": "step28_64x4096_" + kv, "layers": "21 sliding (511-slot ring) "
                    "+ 7 full (context 4096), l%4==3 full", "streams": B, "heads": H,
-                   "head_dim": D, "kv_dtype": "bf16", "launch": args.mode,
+                   "head_dim": D, "kv_dtype": kv, "launch": args.mode,
                    "gate": "logits given" if args.gate == "logits" else
                    "projected in-launch from x[64,2048] by w_g[8,2048]"},
         "us_per_layer_step": round(ms_step * 1e3 / LAYERS, 2),
@@ -358,8 +367,8 @@ def main():
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "attn_kernel<256, bf16, append, step> (full layer, one launch)",
+                     "traffic": measured_traffic() if kv == "bf16" else None,
+                     "kernel": "attn_kernel<256, %s, append, step> (full layer, one launch)" % kv,
                      "bytes_per_launch": full_bytes},
         "cpu_baseline": cpu,
         "parity_max_err": parity,

@@ -13,8 +13,9 @@ import torch
 
 from . import build as _build
 
-F32, F16, BF16 = 0, 1, 2
-_TORCH_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+F32, F16, BF16, FP8 = 0, 1, 2, 3
+_TORCH_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
+               torch.float8_e4m3fn: FP8}
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "pointer not 16-byte aligned",
           -3: "workspace missing or too small", -4: "position does not fit the cache",
@@ -37,7 +38,7 @@ class AttnDesc(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_slots", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("keys_per_split", ctypes.c_int32),
-                ("chunks_per_workgroup", ctypes.c_int32)]
+                ("chunks_per_workgroup", ctypes.c_int32), ("kv_scale", ctypes.c_void_p)]
 
 
 _P, _I, _Z, _D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
@@ -111,15 +112,24 @@ def _need(t, name, dtype=None, shape=None):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
-def make_desc(k_cache, n_heads=None, scale=None, keys_per_split=0, chunks_per_workgroup=0):
-    """Descriptor of a layer from its cache tensor [B, Hkv, n_slots, D]."""
+def make_desc(k_cache, n_heads=None, scale=None, keys_per_split=0, chunks_per_workgroup=0,
+              kv_scale=None):
+    """Descriptor of a layer from its cache tensor [B, Hkv, n_slots, D].
+
+    kv_scale: for a float8_e4m3fn cache, a float32 device tensor [2, Hkv] of
+    per-head K and V scales (the caller keeps it alive while the descriptor
+    is in use)."""
     B, Hkv, S, D = k_cache.shape
     if k_cache.dtype not in _TORCH_CODE:
-        raise ValueError("cache dtype must be float32, float16 or bfloat16")
+        raise ValueError("cache dtype must be float32, float16, bfloat16 or float8_e4m3fn")
     H = Hkv if n_heads is None else n_heads
     sc = (1.0 / D ** 0.5) if scale is None else float(scale)
+    ptr = None
+    if kv_scale is not None:
+        _need(kv_scale, "kv_scale", torch.float32, (2, Hkv))
+        ptr = kv_scale.data_ptr()
     return AttnDesc(B, H, Hkv, D, S, _TORCH_CODE[k_cache.dtype], sc, keys_per_split,
-                    chunks_per_workgroup)
+                    chunks_per_workgroup, ptr)
 
 
 def version():

@@ -41,7 +41,8 @@ int32_t desc_check(const hswd_attn_desc* d) {
     if (d->n_heads % d->n_kv_heads != 0) return HSWD_ERR_INVALID;
     if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
         return d->head_dim > 0 && d->head_dim % 8 == 0 ? HSWD_ERR_UNSUPPORTED : HSWD_ERR_INVALID;
-    if (d->kv_dtype < HSWD_F32 || d->kv_dtype > HSWD_BF16) return HSWD_ERR_INVALID;
+    if (d->kv_dtype < HSWD_F32 || d->kv_dtype > HSWD_FP8_E4M3) return HSWD_ERR_INVALID;
+    if (d->kv_dtype == HSWD_FP8_E4M3 && d->head_dim < 128) return HSWD_ERR_UNSUPPORTED;
     if (!(d->scale > 0.f) || !isfinite(d->scale)) return HSWD_ERR_INVALID;
     if (d->keys_per_split < 0 || d->chunks_per_workgroup < 0) return HSWD_ERR_INVALID;
     if (d->keys_per_split > 0 &&
@@ -128,6 +129,7 @@ int32_t dispatch_attn(const AttnParams& P, int D, int DT, int grid, hipStream_t 
     HSWD_CASE(256, kBF16) HSWD_CASE(256, kF16) HSWD_CASE(256, kF32)
     HSWD_CASE(128, kBF16) HSWD_CASE(128, kF16) HSWD_CASE(128, kF32)
     HSWD_CASE(64, kBF16) HSWD_CASE(64, kF16) HSWD_CASE(64, kF32)
+    HSWD_CASE(256, kFP8) HSWD_CASE(128, kFP8)
 #undef HSWD_CASE
     return HSWD_ERR_UNSUPPORTED;
 }
@@ -167,6 +169,7 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     P.ring = ring ? 1 : 0;
     P.max_pos = ring ? d->n_slots : max_pos;
     P.qscale = d->scale * 1.4426950408889634f;
+    P.kv_scale = d->kv_scale;
     grid = d->batch * d->n_kv_heads * P.wpp;
     return HSWD_OK;
 }
@@ -244,21 +247,27 @@ int32_t hswd_kv_slot_write(void* k_cache, void* v_cache, const float* k_rot, con
     const int grid = d->batch * d->n_kv_heads;
     hipStream_t s = as_stream(stream);
     int32_t* err = static_cast<int32_t*>(ws);
+    const int ring01 = ring ? 1 : 0;
     switch (d->kv_dtype) {
         case HSWD_F32:
             hipLaunchKernelGGL(kv_write_kernel<kF32>, dim3(grid), dim3(256), 0, s, k_cache, v_cache,
-                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring ? 1 : 0,
-                               slot_out, err);
+                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring01,
+                               slot_out, err, d->kv_scale);
             break;
         case HSWD_F16:
             hipLaunchKernelGGL(kv_write_kernel<kF16>, dim3(grid), dim3(256), 0, s, k_cache, v_cache,
-                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring ? 1 : 0,
-                               slot_out, err);
+                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring01,
+                               slot_out, err, d->kv_scale);
+            break;
+        case HSWD_FP8_E4M3:
+            hipLaunchKernelGGL(kv_write_kernel<kFP8>, dim3(grid), dim3(256), 0, s, k_cache, v_cache,
+                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring01,
+                               slot_out, err, d->kv_scale);
             break;
         default:
             hipLaunchKernelGGL(kv_write_kernel<kBF16>, dim3(grid), dim3(256), 0, s, k_cache, v_cache,
-                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring ? 1 : 0,
-                               slot_out, err);
+                               k_rot, v, pos, d->n_kv_heads, d->n_slots, d->head_dim, ring01,
+                               slot_out, err, d->kv_scale);
     }
     return launch_status();
 }

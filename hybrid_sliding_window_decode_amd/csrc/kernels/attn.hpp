@@ -69,6 +69,7 @@ struct AttnParams {
     const float* gx;         // [B,hidden] gate-projection input, or null
     const float* gw;         // [H,hidden] gate-projection weight (used when gx != null)
     int hidden;
+    const float* kv_scale;   // fp8 caches: [2,Hkv] per-head scales (K then V), or null
     void* kc;                // cache [B,Hkv,S,D]
     void* vc;
     const int32_t* pos;      // [B]
@@ -90,7 +91,7 @@ struct AttnParams {
 
 template <int D, int DT>
 struct AttnGeo {
-    static constexpr int EB = DT == kF32 ? 4 : 2;     // element bytes
+    static constexpr int EB = elt_bytes<DT>();        // element bytes
     static constexpr int EPC = 16 / EB;               // elements per 16-byte chunk
     static constexpr int LPR = D / EPC;               // lanes per cache row
     static constexpr int RPI = kWave / LPR;           // rows per wave-wide load
@@ -102,7 +103,7 @@ struct AttnGeo {
 
 // Keys per chunk must be a multiple of this: a whole tile for every wave.
 constexpr int chunk_quantum(int D, int DT) {
-    return kAttnWaves * 8 * (kWave / (D / (16 / (DT == kF32 ? 4 : 2))));
+    return kAttnWaves * 8 * (kWave / (D / (16 / (DT == kF32 ? 4 : (DT == kFP8 ? 1 : 2)))));
 }
 
 // Max of N values in LDS.
@@ -203,6 +204,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     const int h = g;                       // one query head per kv head
     const int bh = b * P.H + h;
     const int p = P.pos[b];
+    const float kscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[g] : 1.f;
+    const float vscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[P.Hkv + g] : 1.f;
 
     // Valid cache rows: ring slots s < min(p, S); append rows < p.
     int nv = p < 0 ? 0 : (p < P.S ? p : P.S);
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     // chunk order, and folds (single workgroup per pair) or stores them.
     // Deferring the barrier keeps small chunks cheap; the arithmetic and its
     // order are those of a barrier per chunk.
-    constexpr int kStash = 4;
+    constexpr int kStash = EPC > 8 ? 2 : 4;    // registers: 16 dims per lane for fp8
     float st_m[kStash], st_l[kStash], st_o[kStash][EPC];
     int n_st = 0, st_first = 0, n_flush = 0;
 
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
             }
             const size_t idx = (size_t)bh * P.n_chunk + ch;
             if (MODE == kModePartials) {
-                if (t < D) P.part_o[idx * D + t] = Oc;
+                if (t < D) P.part_o[idx * D + t] = Oc * vscale;
                 if (tid == 0) {
                     P.part_ml[idx * 2 + 0] = Mc == -INFINITY ? -INFINITY : Mc * kLn2;
                     P.part_ml[idx * 2 + 1] = Lc;
@@ -405,12 +408,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     // prologue runs under the memory latency.
     if (n_items > 0) load_tile(kA, vA, 0);
 
-    // Query (rotated in-kernel for the fused step), scaled by scale*log2(e).
+    // Query (rotated in-kernel for the fused step), scaled by scale*log2(e)
+    // and, for an fp8 cache, by the head's K scale (cached keys are scale *
+    // code, so the scale moves onto the query once).
     {
         const float* qv = P.q + (size_t)bh * D;
+        const float qmul = P.qscale * kscale;
         for (int i = tid; i < D; i += kAttnThreads) {
             float x = MODE == kModeStep ? rope_elem(qv, i, P.rot, P.log2_theta, p) : qv[i];
-            sm_q[i] = x * P.qscale;
+            sm_q[i] = x * qmul;
         }
     }
     // Gate logit from the projection (fused step with g_proj): it needs only
@@ -516,8 +522,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     float prod = 0.f, vh = 0.f;
     if (t < D) {
         const float kr = MODE == kModeStep ? rope_elem(kv, t, P.rot, P.log2_theta, p) : kv[t];
-        k_hat = round_to_elt<DT>(kr);
-        v_hat = round_to_elt<DT>(vv[t]);
+        // fp8: the code of x / scale, the quotient rounded once to float32
+        k_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(kr, kscale) : kr);
+        v_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(vv[t], vscale) : vv[t]);
         prod = sm_q[t] * elt_to_f32<DT>(k_hat);
         vh = elt_to_f32<DT>(v_hat);
     }
@@ -528,6 +535,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     run.add(s_new, 1.f, vh);
     if (t < D) {
         float o = run.O / run.L;
+        if (DT == kFP8) o *= vscale;
         if (MODE == kModeStep && (gproj || P.gate != nullptr)) {
             const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl) : P.gate[bh];
             o *= 1.f / (1.f + expf(-logit));

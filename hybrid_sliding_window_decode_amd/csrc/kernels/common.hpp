@@ -12,8 +12,13 @@ constexpr int kWave = 64;
 constexpr int kF32 = 0;
 constexpr int kF16 = 1;
 constexpr int kBF16 = 2;
+constexpr int kFP8 = 3;     // OCP fp8 e4m3 with a per-head scale
 
 template <int DT> struct Storage { using type = uint16_t; };
+template <> struct Storage<kF32> { using type = float; };
+template <> struct Storage<kFP8> { using type = uint8_t; };
+
+template <int DT> constexpr int elt_bytes() { return DT == kF32 ? 4 : (DT == kFP8 ? 1 : 2); }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -31,7 +36,6 @@ __device__ __forceinline__ u32x4 load_kv16(const T* p) {
     return *reinterpret_cast<const u32x4*>(p);
 #endif
 }
-template <> struct Storage<kF32> { using type = float; };
 
 // ---------------------------------------------------------------------------
 // float32 -> cache element, IEEE round to nearest, ties to even, by integer
@@ -70,6 +74,40 @@ __device__ __forceinline__ uint16_t f32_to_f16_rne(float x) {
     return (uint16_t)(sign | q);
 }
 
+// float32 -> OCP fp8 e4m3 (bias 7, 3 fraction bits, no infinities, largest
+// finite 448), round to nearest, ties to even, saturating: |x| >= 448 and
+// infinities become +-448.  NaN stays NaN (code 0x7f with the sign).
+__device__ __forceinline__ uint8_t f32_to_fp8_rne_sat(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return (uint8_t)(sign | 0x7fu);
+    if (a >= 0x43e00000u) return (uint8_t)(sign | 0x7eu);      // |x| >= 448
+    if (a >= 0x3c800000u) {                                     // |x| >= 2^-6: normal
+        uint32_t r = a - 0x3c000000u;                           // exponent bias 127 -> 7
+        r += 0x7ffffu + ((r >> 20) & 1u);                       // ties to even on 20 bits
+        uint32_t code = r >> 20;
+        return (uint8_t)(sign | (code > 0x7eu ? 0x7eu : code));
+    }
+    if (a < 0x39800000u) return (uint8_t)sign;                  // |x| < 2^-12: rounds to 0
+    // subnormal result: value / 2^-9 = significand >> (141 - exponent)
+    uint32_t e = a >> 23;
+    uint32_t m = (a & 0x7fffffu) | 0x800000u;
+    uint32_t sh = 141u - e;                                     // 21 .. 26
+    uint32_t q = m >> sh;
+    uint32_t rem = m & ((1u << sh) - 1u);
+    uint32_t half = 1u << (sh - 1u);
+    if (rem > half || (rem == half && (q & 1u))) ++q;
+    return (uint8_t)(sign | q);
+}
+
+// Two fp8 e4m3 codes (bytes 0-1 or 2-3 of w) to float32, by the hardware
+// conversion (gfx950 decodes the OCP format; checked on all 256 codes).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
@@ -81,6 +119,7 @@ template <int DT>
 __device__ __forceinline__ typename Storage<DT>::type round_to_elt(float x) {
     if constexpr (DT == kF32) return x;
     else if constexpr (DT == kF16) return f32_to_f16_rne(x);
+    else if constexpr (DT == kFP8) return f32_to_fp8_rne_sat(x);
     else return f32_to_bf16_rne(x);
 }
 
@@ -88,13 +127,21 @@ template <int DT>
 __device__ __forceinline__ float elt_to_f32(typename Storage<DT>::type s) {
     if constexpr (DT == kF32) return s;
     else if constexpr (DT == kF16) return f16_bits_to_f32(s);
+    else if constexpr (DT == kFP8) return fp8x2_to_f32((uint32_t)s, false).x;
     else return bf16_bits_to_f32(s);
 }
 
 // Unpack one 16-byte chunk of cache elements into floats (EPC of them).
 template <int DT>
 __device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
-    if constexpr (DT == kF32) {
+    if constexpr (DT == kFP8) {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x2 lo = fp8x2_to_f32(u[j], false), hi = fp8x2_to_f32(u[j], true);
+            f[4 * j] = lo.x; f[4 * j + 1] = lo.y; f[4 * j + 2] = hi.x; f[4 * j + 3] = hi.y;
+        }
+    } else if constexpr (DT == kF32) {
         f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
         f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
     } else if constexpr (DT == kBF16) {

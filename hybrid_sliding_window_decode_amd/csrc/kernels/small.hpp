@@ -44,7 +44,8 @@ template <int DT>
 __global__ __launch_bounds__(256) void kv_write_kernel(void* kc, void* vc, const float* k,
                                                        const float* v, const int32_t* pos,
                                                        int Hkv, int S, int D, int ring,
-                                                       int32_t* slot_out, int32_t* err) {
+                                                       int32_t* slot_out, int32_t* err,
+                                                       const float* kv_scale) {
     using St = typename Storage<DT>::type;
     const int pair = blockIdx.x;
     const int b = pair / Hkv;
@@ -62,9 +63,18 @@ __global__ __launch_bounds__(256) void kv_write_kernel(void* kc, void* vc, const
     if (row < 0) return;
     St* kd = reinterpret_cast<St*>(kc) + ((size_t)pair * S + row) * D;
     St* vd = reinterpret_cast<St*>(vc) + ((size_t)pair * S + row) * D;
-    for (int t = threadIdx.x; t < D; t += blockDim.x) {
-        kd[t] = round_to_elt<DT>(k[(size_t)pair * D + t]);
-        vd[t] = round_to_elt<DT>(v[(size_t)pair * D + t]);
+    if constexpr (DT == kFP8) {     // the code of x / scale (quotient rounded to float32)
+        const int g = pair % Hkv;
+        const float ks = kv_scale ? kv_scale[g] : 1.f, vs = kv_scale ? kv_scale[Hkv + g] : 1.f;
+        for (int t = threadIdx.x; t < D; t += blockDim.x) {
+            kd[t] = round_to_elt<DT>(__fdiv_rn(k[(size_t)pair * D + t], ks));
+            vd[t] = round_to_elt<DT>(__fdiv_rn(v[(size_t)pair * D + t], vs));
+        }
+    } else {
+        for (int t = threadIdx.x; t < D; t += blockDim.x) {
+            kd[t] = round_to_elt<DT>(k[(size_t)pair * D + t]);
+            vd[t] = round_to_elt<DT>(v[(size_t)pair * D + t]);
+        }
     }
 }
 

@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 
 
 @dataclass
@@ -33,16 +33,26 @@ class LayerSpec:
     dtype: str = "bf16"
     rot: int = 256
     theta: float = 1e4
+    kv_scale: object = None   # fp8: float32 [2, Hkv] per-head scales (K then V)
+
+
+def default_fp8_scales(Hkv):
+    """Per-head scales of an fp8 cache: different for every head and for K
+    and V, sized so N(0,1) data sits well inside the e4m3 range (+-448)."""
+    g = np.arange(Hkv, dtype=np.float32)
+    return np.stack([(1 + g / 8) / 64, (1 + g / 4) / 64]).astype(np.float32)
 
 
 def sliding_spec(B, dtype="bf16", H=8, Hkv=8, D=256, n_slots=511):
     """Sliding layer: 511-slot ring, all head dims rotated at theta 1e4."""
-    return LayerSpec("sliding", B, H, Hkv, D, n_slots, dtype, rot=D, theta=1e4)
+    return LayerSpec("sliding", B, H, Hkv, D, n_slots, dtype, rot=D, theta=1e4,
+                     kv_scale=default_fp8_scales(Hkv) if dtype == "fp8" else None)
 
 
 def full_spec(B, capacity, dtype="bf16", H=8, Hkv=8, D=256):
     """Full layer: append cache, first quarter of the head dims at theta 5e6."""
-    return LayerSpec("full", B, H, Hkv, D, capacity, dtype, rot=D // 4, theta=5e6)
+    return LayerSpec("full", B, H, Hkv, D, capacity, dtype, rot=D // 4, theta=5e6,
+                     kv_scale=default_fp8_scales(Hkv) if dtype == "fp8" else None)
 
 
 def written_rows(kind, n_slots, pos):
@@ -53,8 +63,17 @@ def written_rows(kind, n_slots, pos):
     return s < pos
 
 
-def cast_bits(x32, dtype):
-    """float32 array -> storage bits of `dtype` by a library cast."""
+def cast_bits(x32, dtype, scale=None):
+    """float32 array -> storage bits of `dtype` by a library cast.  fp8: the
+    code of x / scale (scale broadcast against x), clamped to +-448 first so
+    the cast saturates."""
+    if dtype == "fp8":
+        import torch
+        y = np.ascontiguousarray(x32, np.float32)
+        if scale is not None:
+            y = (y / np.asarray(scale, np.float32)).astype(np.float32)
+        t = torch.from_numpy(np.clip(y, -448.0, 448.0).astype(np.float32))
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
     if dtype == "f32":
         return np.ascontiguousarray(x32, np.float32)
     if dtype == "f16":
@@ -68,7 +87,7 @@ def cast_bits(x32, dtype):
 
 def nan_bits(dtype):
     return {"f32": np.float32(np.nan), "f16": np.uint16(0x7e00),
-            "bf16": np.uint16(0x7fc0)}[dtype]
+            "bf16": np.uint16(0x7fc0), "fp8": np.uint8(0x7f)}[dtype]
 
 
 @dataclass
@@ -93,8 +112,12 @@ def make_step(spec, pos, seed, poison=True):
     k = rng.standard_normal((B, Hkv, D), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, D), dtype=np.float32)
     gate = rng.standard_normal((B, H), dtype=np.float32)
-    kc = cast_bits(rng.standard_normal((B, Hkv, S, D), dtype=np.float32), spec.dtype)
-    vc = cast_bits(rng.standard_normal((B, Hkv, S, D), dtype=np.float32), spec.dtype)
+    ks = vs = None
+    if spec.dtype == "fp8":
+        ks = spec.kv_scale[0][None, :, None, None]
+        vs = spec.kv_scale[1][None, :, None, None]
+    kc = cast_bits(rng.standard_normal((B, Hkv, S, D), dtype=np.float32), spec.dtype, ks)
+    vc = cast_bits(rng.standard_normal((B, Hkv, S, D), dtype=np.float32), spec.dtype, vs)
     if poison:
         for b in range(B):
             dead = ~written_rows(spec.kind, S, int(pos[b]))
@@ -144,9 +167,19 @@ def layer_is_full(l):
 # ----------------------------------------------------------------------------
 # Device-side generation for the full-size workloads (torch, seeded Philox).
 # ----------------------------------------------------------------------------
-def device_normal_(t, gen, chunk_rows=1 << 16):
-    """Fill a CUDA tensor of any float dtype with N(0,1) drawn in float32."""
+def device_normal_(t, gen, chunk_rows=1 << 16, scale=None):
+    """Fill a CUDA tensor of any float dtype with N(0,1) drawn in float32.
+    fp8 tensors [B, Hkv, S, D] get the code of x / scale[g] (clamped to
+    +-448), scale a float32 [Hkv] array."""
     import torch
+    if t.dtype == torch.float8_e4m3fn:
+        sc = torch.as_tensor(np.asarray(scale, np.float32), device=t.device)
+        for b in range(t.shape[0]):
+            for g in range(t.shape[1]):
+                x = torch.randn(t.shape[2] * t.shape[3], generator=gen, device=t.device,
+                                dtype=torch.float32)
+                t[b, g].view(-1)[:] = (x / sc[g]).clamp(-448.0, 448.0).to(t.dtype)
+        return t
     flat = t.view(-1)
     n = flat.numel()
     step = chunk_rows * 256
@@ -164,7 +197,8 @@ def device_step(spec, pos, seed, device="cuda"):
     never written are NaN-poisoned per stream.  Returns a dict of tensors.
     """
     import torch
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.dtype]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "fp8": torch.float8_e4m3fn}[spec.dtype]
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
     B, H, Hkv, D, S = spec.B, spec.H, spec.Hkv, spec.D, spec.n_slots
@@ -176,12 +210,20 @@ def device_step(spec, pos, seed, device="cuda"):
     gate = torch.randn(B, H, generator=gen, device=device, dtype=torch.float32)
     kc = torch.empty(B, Hkv, S, D, device=device, dtype=tdt)
     vc = torch.empty(B, Hkv, S, D, device=device, dtype=tdt)
-    device_normal_(kc, gen)
-    device_normal_(vc, gen)
+    fp8 = spec.dtype == "fp8"
+    device_normal_(kc, gen, scale=spec.kv_scale[0] if fp8 else None)
+    device_normal_(vc, gen, scale=spec.kv_scale[1] if fp8 else None)
     for b in range(B):
         dead = torch.from_numpy(~written_rows(spec.kind, S, int(pos_t[b])))
         if bool(dead.any()):
             idx = dead.nonzero().view(-1).to(device)
-            kc[b].index_fill_(1, idx, float("nan"))
-            vc[b].index_fill_(1, idx, float("nan"))
-    return dict(pos=pos_t.to(device), q=q, k=k, v=v, gate=gate, k_cache=kc, v_cache=vc)
+            if fp8:                                   # NaN code 0x7f
+                kc[b].view(torch.uint8).index_fill_(1, idx, 0x7f)
+                vc[b].view(torch.uint8).index_fill_(1, idx, 0x7f)
+            else:
+                kc[b].index_fill_(1, idx, float("nan"))
+                vc[b].index_fill_(1, idx, float("nan"))
+    out = dict(pos=pos_t.to(device), q=q, k=k, v=v, gate=gate, k_cache=kc, v_cache=vc)
+    if fp8:
+        out["kv_scale"] = torch.as_tensor(spec.kv_scale, device=device)
+    return out

@@ -70,7 +70,12 @@
 extern "C" {
 #endif
 
-typedef enum { HSWD_F32 = 0, HSWD_F16 = 1, HSWD_BF16 = 2 } hswd_dtype;
+/* Cache element types.  HSWD_FP8_E4M3 is OCP fp8 e4m3 (4 exponent bits,
+ * bias 7, 3 fraction bits, no infinities, largest finite 448) with a scale
+ * per kv head: a cached value is scale * decode(code); an entry x is stored
+ * as the code of x / scale (the quotient rounded once to float32), rounded to
+ * nearest even and saturated to +-448. */
+typedef enum { HSWD_F32 = 0, HSWD_F16 = 1, HSWD_BF16 = 2, HSWD_FP8_E4M3 = 3 } hswd_dtype;
 
 typedef enum {
     HSWD_OK = 0,
@@ -92,7 +97,7 @@ typedef struct {
     int32_t batch;          /* B >= 1 */
     int32_t n_heads;        /* H */
     int32_t n_kv_heads;     /* Hkv, H % Hkv == 0 (the decode kernels take H == Hkv) */
-    int32_t head_dim;       /* D: 64, 128 or 256 */
+    int32_t head_dim;       /* D: 64, 128 or 256 (fp8 caches: 128 or 256) */
     int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows */
     int32_t kv_dtype;       /* hswd_dtype of the cache */
     float scale;            /* softmax scale, > 0; 1/sqrt(D) by convention */
@@ -109,6 +114,9 @@ typedef struct {
     int32_t chunks_per_workgroup; /* work split only, never the bits: how many
                                consecutive chunks one workgroup streams.  0 =
                                library choice (from B and the CU count). */
+    const float* kv_scale;  /* fp8 caches only: DEVICE pointer, float32 [2, Hkv],
+                               the K scales then the V scales of the kv heads
+                               (NULL = 1 for every head).  Ignored otherwise. */
 } hswd_attn_desc;
 
 /* Library version, (major << 16) | minor. */

@@ -6,7 +6,8 @@ imports nothing from the GPU path.
 
 The arithmetic lives in `hswd_oracle.c` (plain C, fp64); this module loads it
 with ctypes and converts numpy arrays.  Cache element types are passed as
-raw bits: float32 arrays for f32, uint16 bit patterns for f16 and bf16.
+raw bits: float32 arrays for f32, uint16 bit patterns for f16 and bf16,
+uint8 codes for fp8 e4m3.
 """
 import ctypes
 import os
@@ -15,8 +16,8 @@ import numpy as np
 
 from . import build as _build
 
-F32, F16, BF16 = 0, 1, 2
-DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
+F32, F16, BF16, FP8 = 0, 1, 2, 3
+DTYPES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8}
 
 _lib = None
 
@@ -45,22 +46,26 @@ def _bind(L):
     L.orc_f16_value.argtypes = [ctypes.c_uint16]
     L.orc_bf16_value.restype = f64
     L.orc_bf16_value.argtypes = [ctypes.c_uint16]
+    L.orc_f32_to_fp8.restype = ctypes.c_uint8
+    L.orc_f32_to_fp8.argtypes = [ctypes.c_float]
+    L.orc_fp8_value.restype = f64
+    L.orc_fp8_value.argtypes = [ctypes.c_uint8]
     L.orc_round_f32_to.argtypes = [i32, P, sz, P]
     L.orc_decode.argtypes = [i32, P, sz, P]
     L.orc_slot_mask.argtypes = [i32, i32, i32, P, P, P]
     L.orc_rope.argtypes = [P, P, i32, i32, f64, ctypes.c_int64, i32]
     L.orc_rope_batch.argtypes = [P, P, i32, i32, i32, i32, f64, P, i32]
-    L.orc_attend.argtypes = [P, P, P, P, i32, i32, i32, P, P, f64]
-    L.orc_partial.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f64]
+    L.orc_attend.argtypes = [P, P, P, P, i32, i32, i32, P, P, f64, f64, f64]
+    L.orc_partial.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f64, f64, f64]
     L.orc_merge.argtypes = [P, P, P, P, i32, i32]
-    L.orc_attend_split.argtypes = [P, P, P, P, i32, P, i32, i32, P, P, f64]
+    L.orc_attend_split.argtypes = [P, P, P, P, i32, P, i32, i32, P, P, f64, f64, f64]
     L.orc_sigmoid.restype = f64
     L.orc_sigmoid.argtypes = [f64]
     L.orc_head_gate.argtypes = [P, P, P, i32, i32, i32]
     L.orc_layer_step.restype = i32
     L.orc_layer_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f64, f64, i32,
-                                 P, P, P, P, P, P, P, i32, P, P, P, P, P, P]
-    L.orc_attend_block.argtypes = [P, P, P, P, i32, i32, i32, P, P, f64]
+                                 P, P, P, P, P, P, P, i32, P, P, P, P, P, P, P]
+    L.orc_attend_block.argtypes = [P, P, P, P, i32, i32, i32, P, P, f64, f64, f64]
     L.orc_gate_proj.argtypes = [P, P, P, i32, i32, i32]
     return L
 
@@ -75,7 +80,7 @@ def _c(a, dt):
 
 def storage_dtype(dtype):
     """numpy container for a cache element type's bits."""
-    return np.float32 if dtype == F32 else np.uint16
+    return {F32: np.float32, FP8: np.uint8}.get(dtype, np.uint16)
 
 
 # --------------------------------------------------------------------------
@@ -125,8 +130,9 @@ def rope(x, pos, rot, theta, interleaved=False, L=None):
     return out
 
 
-def attend(q, kc, vc, dtype, n, k_new, v_new, scale, L=None):
-    """One query over rows 0..n-1 of a (rows, D) cache block plus the new entry."""
+def attend(q, kc, vc, dtype, n, k_new, v_new, scale, ks=1.0, vs=1.0, L=None):
+    """One query over rows 0..n-1 of a (rows, D) cache block plus the new entry
+    (cached values are ks * decode(K), vs * decode(V))."""
     L = L or lib()
     q = _c(q, np.float64)
     D = q.size
@@ -135,11 +141,11 @@ def attend(q, kc, vc, dtype, n, k_new, v_new, scale, L=None):
     assert kc.size >= n * D and vc.size >= n * D
     o = np.empty(D, np.float64)
     L.orc_attend(_p(o), _p(q), _p(kc), _p(vc), dtype, n, D,
-                 _p(_c(k_new, np.float64)), _p(_c(v_new, np.float64)), scale)
+                 _p(_c(k_new, np.float64)), _p(_c(v_new, np.float64)), scale, ks, vs)
     return o
 
 
-def partial(q, kc, vc, dtype, j0, j1, scale, L=None):
+def partial(q, kc, vc, dtype, j0, j1, scale, ks=1.0, vs=1.0, L=None):
     L = L or lib()
     q = _c(q, np.float64)
     D = q.size
@@ -148,7 +154,7 @@ def partial(q, kc, vc, dtype, j0, j1, scale, L=None):
     m = np.zeros(1)
     l = np.zeros(1)
     o = np.empty(D)
-    L.orc_partial(_p(m), _p(l), _p(o), _p(q), _p(kc), _p(vc), dtype, j0, j1, D, scale)
+    L.orc_partial(_p(m), _p(l), _p(o), _p(q), _p(kc), _p(vc), dtype, j0, j1, D, scale, ks, vs)
     return m[0], l[0], o
 
 
@@ -164,7 +170,7 @@ def merge(m, l, o, L=None):
     return out
 
 
-def attend_split(q, kc, vc, dtype, bounds, k_new, v_new, scale, L=None):
+def attend_split(q, kc, vc, dtype, bounds, k_new, v_new, scale, ks=1.0, vs=1.0, L=None):
     L = L or lib()
     q = _c(q, np.float64)
     D = q.size
@@ -173,7 +179,7 @@ def attend_split(q, kc, vc, dtype, bounds, k_new, v_new, scale, L=None):
     L.orc_attend_split(_p(o), _p(q), _p(_c(kc, storage_dtype(dtype))),
                        _p(_c(vc, storage_dtype(dtype))), dtype, _p(bounds),
                        bounds.size - 1, D, _p(_c(k_new, np.float64)),
-                       _p(_c(v_new, np.float64)), scale)
+                       _p(_c(v_new, np.float64)), scale, ks, vs)
     return o
 
 
@@ -206,12 +212,13 @@ def gate_proj(x, w, L=None):
 
 
 def layer_step(q, k, v, gate, k_cache, v_cache, pos, dtype, ring, rot, theta,
-               scale=None, interleaved=False, write=True, L=None):
+               scale=None, interleaved=False, write=True, kv_scale=None, L=None):
     """One layer step (rotate, round, attend, gate, write) on host arrays.
 
     q [B,H,D], k/v [B,Hkv,D] float32; gate [B,H] float32 or None;
     k_cache/v_cache [B,Hkv,n_slots,D] bits of `dtype`, updated in place when
-    `write`; pos [B] int32.  Returns a dict of outputs and the status code.
+    `write`; pos [B] int32; kv_scale [2, Hkv] float32 per-head scales (K
+    then V) or None.  Returns a dict of outputs and the status code.
     """
     L = L or lib()
     q = _c(q, np.float32)
@@ -232,16 +239,17 @@ def layer_step(q, k, v, gate, k_cache, v_cache, pos, dtype, ring, rot, theta,
     k_hat = np.empty((B, Hkv, D), storage_dtype(dtype))
     v_hat = np.empty((B, Hkv, D), storage_dtype(dtype))
     g = None if gate is None else _c(gate, np.float32)
+    ksc = None if kv_scale is None else _c(kv_scale, np.float32)
     status = L.orc_layer_step(B, H, Hkv, D, n_slots, dtype, int(ring), rot, theta,
                               float(scale), int(interleaved), _p(pos), _p(q), _p(k),
-                              _p(v), _p(g), _p(k_cache), _p(v_cache), int(write),
+                              _p(v), _p(g), _p(k_cache), _p(v_cache), int(write), _p(ksc),
                               _p(out), _p(o_pre), _p(q_rot), _p(k_rot32), _p(k_hat),
                               _p(v_hat))
     return dict(out=out, o_pre=o_pre, q_rot=q_rot, k_rot32=k_rot32, k_hat=k_hat,
                 v_hat=v_hat, status=status)
 
 
-def attend_block(q_rot, kc, vc, dtype, n, k_hat, v_hat, scale, L=None):
+def attend_block(q_rot, kc, vc, dtype, n, k_hat, v_hat, scale, ks=1.0, vs=1.0, L=None):
     """One (stream, head) of a step from a cache block and the rounded entry."""
     L = L or lib()
     q_rot = _c(q_rot, np.float64)
@@ -250,5 +258,5 @@ def attend_block(q_rot, kc, vc, dtype, n, k_hat, v_hat, scale, L=None):
     L.orc_attend_block(_p(o), _p(q_rot), _p(_c(kc, storage_dtype(dtype))),
                        _p(_c(vc, storage_dtype(dtype))), dtype, n, D,
                        _p(_c(k_hat, storage_dtype(dtype))),
-                       _p(_c(v_hat, storage_dtype(dtype))), scale)
+                       _p(_c(v_hat, storage_dtype(dtype))), scale, ks, vs)
     return o

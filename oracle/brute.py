@@ -27,9 +27,15 @@ def to_f32(x):
     return struct.unpack("f", struct.pack("f", x))[0]
 
 
-def round_elt(x, dtype):
-    """float (already a float32 value) -> the value the cache type stores."""
+def round_elt(x, dtype, scale=1.0):
+    """float (already a float32 value) -> the value the cache type stores
+    (fp8: scale * e4m3 code of the float32 quotient x / scale, saturated)."""
     x = to_f32(x)
+    if dtype == "fp8":
+        import torch
+        y = torch.tensor([x], dtype=torch.float32) / torch.tensor([scale], dtype=torch.float32)
+        c = y.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).float()[0]
+        return float(c) * float(np.float32(scale))
     if dtype == "f32":
         return x
     if dtype == "f16":
@@ -50,11 +56,12 @@ def rotate(x, t, rot, theta):
     return out
 
 
-def step(history, p, window, H, Hkv, rot, theta, dtype, scale, gate=None):
+def step(history, p, window, H, Hkv, rot, theta, dtype, scale, gate=None, kv_scale=None):
     """Output of step p: history[t] = (q [H][D], k [Hkv][D], v [Hkv][D]).
 
     window = number of positions attended including the current one
-    (None for a full-attention layer).  Returns out[h][d] as floats.
+    (None for a full-attention layer); kv_scale = per-head (K, V) scales of
+    an fp8 cache, [2][Hkv].  Returns out[h][d] as floats.
     """
     q, _, _ = history[p]
     first = 0 if window is None else max(0, p - window + 1)
@@ -66,8 +73,10 @@ def step(history, p, window, H, Hkv, rot, theta, dtype, scale, gate=None):
         scores, vals = [], []
         for t in range(first, p + 1):
             _, kt, vt = history[t]
-            kr = [round_elt(to_f32(x), dtype) for x in rotate(kt[g], t, rot, theta)]
-            vr = [round_elt(x, dtype) for x in vt[g]]
+            ks = 1.0 if kv_scale is None else kv_scale[0][g]
+            vs = 1.0 if kv_scale is None else kv_scale[1][g]
+            kr = [round_elt(to_f32(x), dtype, ks) for x in rotate(kt[g], t, rot, theta)]
+            vr = [round_elt(x, dtype, vs) for x in vt[g]]
             scores.append(scale * math.fsum(a * b for a, b in zip(qr, kr)))
             vals.append(vr)
         m = max(scores)

@@ -40,9 +40,9 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_FP8 = 3 };
 
-static int elt_bytes(int dtype) { return dtype == ORC_F32 ? 4 : 2; }
+static int elt_bytes(int dtype) { return dtype == ORC_F32 ? 4 : (dtype == ORC_FP8 ? 1 : 2); }
 
 /* ------------------------------------------------------------------------ */
 /* Rounding float32 -> binary16 / bfloat16, round to nearest, ties to even. */
@@ -111,6 +111,40 @@ uint16_t orc_f32_to_bf16(float x)
     return (uint16_t)(sign | (biased << 7) | mant);
 }
 
+/* float32 -> OCP fp8 e4m3 (4 exponent bits, bias 7, 3 fraction bits; no
+ * infinities; S.1111.111 is NaN; largest finite 448), round to nearest, ties
+ * to even, saturating: finite values and infinities that would round past
+ * 448 become +-448.  NaN stays NaN (0x7f with the sign). */
+uint8_t orc_f32_to_fp8(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+    if (isnan(x)) return (uint8_t)(sign | 0x7fu);
+    double ax = fabs((double)x);
+    double r = isinf(x) ? 448.0 : round_to_grid(ax, 3, -6);
+    if (r > 448.0) r = 448.0;
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -6))                        /* subnormal: r = m * 2^-9 */
+        return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9)));
+    int e;
+    double f = frexp(r, &e);
+    uint8_t biased = (uint8_t)(e - 1 + 7);
+    uint8_t mant = (uint8_t)((f * 2.0 - 1.0) * 8.0);
+    return (uint8_t)(sign | (biased << 3) | mant);
+}
+
+/* Exact value of an OCP fp8 e4m3 code. */
+double orc_fp8_value(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 0xf, m = c & 0x7;
+    double v;
+    if (e == 0xf && m == 0x7) v = NAN;
+    else if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp((double)(8 + m), e - 10);
+    return sign ? -v : v;
+}
+
 /* Exact value of a binary16 bit pattern. */
 double orc_f16_value(uint16_t h)
 {
@@ -135,14 +169,17 @@ double orc_bf16_value(uint16_t b)
 static double load_elt(const void* base, int dtype, size_t idx)
 {
     if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+    if (dtype == ORC_FP8) return orc_fp8_value(((const uint8_t*)base)[idx]);
     uint16_t h = ((const uint16_t*)base)[idx];
     return dtype == ORC_F16 ? orc_f16_value(h) : orc_bf16_value(h);
 }
 
-/* Round a float32 to the cache element type and store it at `idx`. */
+/* Round a float32 to the cache element type and store it at `idx`
+ * (fp8: with saturation). */
 static void store_elt(void* base, int dtype, size_t idx, float x)
 {
     if (dtype == ORC_F32) ((float*)base)[idx] = x;
+    else if (dtype == ORC_FP8) ((uint8_t*)base)[idx] = orc_f32_to_fp8(x);
     else if (dtype == ORC_F16) ((uint16_t*)base)[idx] = orc_f32_to_f16(x);
     else ((uint16_t*)base)[idx] = orc_f32_to_bf16(x);
 }
@@ -218,7 +255,7 @@ void orc_rope_batch(double* out, const float* x, int n, int per_pos, int D,
 /* ------------------------------------------------------------------------ */
 void orc_attend(double* o, const double* q, const void* kc, const void* vc,
                 int dtype, int n, int D, const double* k_new,
-                const double* v_new, double scale)
+                const double* v_new, double scale, double ks, double vs)
 {
     double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
     double s_new = 0.0;
@@ -227,7 +264,7 @@ void orc_attend(double* o, const double* q, const void* kc, const void* vc,
     double m = s_new;
     for (int j = 0; j < n; ++j) {
         double acc = 0.0;
-        for (int d = 0; d < D; ++d) acc += q[d] * load_elt(kc, dtype, (size_t)j * D + d);
+        for (int d = 0; d < D; ++d) acc += q[d] * (ks * load_elt(kc, dtype, (size_t)j * D + d));
         s[j] = scale * acc;
         if (s[j] > m) m = s[j];
     }
@@ -237,7 +274,7 @@ void orc_attend(double* o, const double* q, const void* kc, const void* vc,
     for (int j = 0; j < n; ++j) {
         double w = exp(s[j] - m);
         l += w;
-        for (int d = 0; d < D; ++d) o[d] += w * load_elt(vc, dtype, (size_t)j * D + d);
+        for (int d = 0; d < D; ++d) o[d] += w * (vs * load_elt(vc, dtype, (size_t)j * D + d));
     }
     for (int d = 0; d < D; ++d) o[d] /= l;
     free(s);
@@ -252,7 +289,7 @@ void orc_attend(double* o, const double* q, const void* kc, const void* vc,
 /* ------------------------------------------------------------------------ */
 void orc_partial(double* m_out, double* l_out, double* o_out, const double* q,
                  const void* kc, const void* vc, int dtype, int j0, int j1,
-                 int D, double scale)
+                 int D, double scale, double ks, double vs)
 {
     for (int d = 0; d < D; ++d) o_out[d] = 0.0;
     if (j1 <= j0) { *m_out = -INFINITY; *l_out = 0.0; return; }
@@ -261,7 +298,7 @@ void orc_partial(double* m_out, double* l_out, double* o_out, const double* q,
     double m = -INFINITY;
     for (int j = j0; j < j1; ++j) {
         double acc = 0.0;
-        for (int d = 0; d < D; ++d) acc += q[d] * load_elt(kc, dtype, (size_t)j * D + d);
+        for (int d = 0; d < D; ++d) acc += q[d] * (ks * load_elt(kc, dtype, (size_t)j * D + d));
         s[j - j0] = scale * acc;
         if (s[j - j0] > m) m = s[j - j0];
     }
@@ -269,7 +306,7 @@ void orc_partial(double* m_out, double* l_out, double* o_out, const double* q,
     for (int j = j0; j < j1; ++j) {
         double w = exp(s[j - j0] - m);
         l += w;
-        for (int d = 0; d < D; ++d) o_out[d] += w * load_elt(vc, dtype, (size_t)j * D + d);
+        for (int d = 0; d < D; ++d) o_out[d] += w * (vs * load_elt(vc, dtype, (size_t)j * D + d));
     }
     *m_out = m;
     *l_out = l;
@@ -299,7 +336,8 @@ void orc_merge(double* out, const double* m, const double* l, const double* o,
  * of the cached rows plus the new entry as a one-key partial, then merged. */
 void orc_attend_split(double* o, const double* q, const void* kc, const void* vc,
                       int dtype, const int32_t* bounds, int n_chunks, int D,
-                      const double* k_new, const double* v_new, double scale)
+                      const double* k_new, const double* v_new, double scale, double ks,
+                      double vs)
 {
     int n = n_chunks + 1;
     double* m = (double*)malloc(sizeof(double) * (size_t)n);
@@ -307,7 +345,7 @@ void orc_attend_split(double* o, const double* q, const void* kc, const void* vc
     double* po = (double*)malloc(sizeof(double) * (size_t)n * D);
     for (int c = 0; c < n_chunks; ++c)
         orc_partial(&m[c], &l[c], po + (size_t)c * D, q, kc, vc, dtype,
-                    bounds[c], bounds[c + 1], D, scale);
+                    bounds[c], bounds[c + 1], D, scale, ks, vs);
     double s_new = 0.0;
     for (int d = 0; d < D; ++d) s_new += q[d] * k_new[d];
     m[n_chunks] = scale * s_new;
@@ -394,6 +432,7 @@ int orc_layer_step(int B, int H, int Hkv, int D, int n_slots, int dtype, int rin
                    int rot, double theta, double scale, int interleaved,
                    const int32_t* pos, const float* q, const float* k, const float* v,
                    const float* gate, void* k_cache, void* v_cache, int write,
+                   const float* kv_scale,
                    double* out, double* o_pre, double* q_rot, float* k_rot32,
                    void* k_hat, void* v_hat)
 {
@@ -412,10 +451,30 @@ int orc_layer_step(int B, int H, int Hkv, int D, int n_slots, int dtype, int rin
     orc_rope_batch(qr, q, B * H, H, D, rot, theta, pos, interleaved);
     orc_rope_batch(kr, k, B * Hkv, Hkv, D, rot, theta, pos, interleaved);
     for (size_t i = 0; i < nkv; ++i) kr32[i] = (float)kr[i];
-    orc_round_f32_to(dtype, kr32, nkv, kh);
-    orc_round_f32_to(dtype, v, nkv, vh);
+    /* With per-head scales (kv_scale [2][Hkv]: K then V; NULL = 1), a cached
+     * value is scale * decode(code) and the entry stored is the code of
+     * x / scale, the quotient rounded once to float32. */
+    float* kq = (float*)malloc(sizeof(float) * nkv);
+    float* vq = (float*)malloc(sizeof(float) * nkv);
+    for (size_t i = 0; i < nkv; ++i) {
+        int g = (int)((i / (size_t)D) % (size_t)Hkv);
+        double ks = kv_scale ? (double)kv_scale[g] : 1.0;
+        double vs = kv_scale ? (double)kv_scale[Hkv + g] : 1.0;
+        kq[i] = (float)((double)kr32[i] / ks);
+        vq[i] = (float)((double)v[i] / vs);
+    }
+    orc_round_f32_to(dtype, kq, nkv, kh);
+    orc_round_f32_to(dtype, vq, nkv, vh);
     orc_decode(dtype, kh, nkv, khd);
     orc_decode(dtype, vh, nkv, vhd);
+    for (size_t i = 0; i < nkv; ++i) {
+        int g = (int)((i / (size_t)D) % (size_t)Hkv);
+        if (kv_scale) {
+            khd[i] *= (double)kv_scale[g];
+            vhd[i] *= (double)kv_scale[Hkv + g];
+        }
+    }
+    free(kq); free(vq);
 
     int status = 0;
     /* attend: every (stream, query head) reads the cache before any write */
@@ -430,7 +489,9 @@ int orc_layer_step(int B, int H, int Hkv, int D, int n_slots, int dtype, int rin
         orc_attend(opre + (size_t)bh * D, qr + (size_t)bh * D,
                    (const char*)k_cache + blk * eb, (const char*)v_cache + blk * eb,
                    dtype, n, D, khd + ((size_t)b * Hkv + g) * D,
-                   vhd + ((size_t)b * Hkv + g) * D, scale);
+                   vhd + ((size_t)b * Hkv + g) * D, scale,
+                   kv_scale ? (double)kv_scale[g] : 1.0,
+                   kv_scale ? (double)kv_scale[Hkv + g] : 1.0);
     }
 
     if (o_pre) memcpy(o_pre, opre, sizeof(double) * (size_t)B * H * D);
@@ -454,12 +515,13 @@ int orc_layer_step(int B, int H, int Hkv, int D, int n_slots, int dtype, int rin
  * new entry already rounded to `dtype` (k_hat, v_hat as dtype arrays). */
 void orc_attend_block(double* o, const double* q_rot, const void* kc, const void* vc,
                       int dtype, int n, int D, const void* k_hat, const void* v_hat,
-                      double scale)
+                      double scale, double ks, double vs)
 {
     double* kn = (double*)malloc(sizeof(double) * (size_t)D);
     double* vn = (double*)malloc(sizeof(double) * (size_t)D);
     orc_decode(dtype, k_hat, (size_t)D, kn);
     orc_decode(dtype, v_hat, (size_t)D, vn);
-    orc_attend(o, q_rot, kc, vc, dtype, n, D, kn, vn, scale);
+    for (int d = 0; d < D; ++d) { kn[d] *= ks; vn[d] *= vs; }
+    orc_attend(o, q_rot, kc, vc, dtype, n, D, kn, vn, scale, ks, vs);
     free(kn); free(vn);
 }

@@ -17,8 +17,8 @@ import oracle
 from oracle import brute
 from hybrid_sliding_window_decode_amd import inputs
 
-F32, F16, BF16 = oracle.F32, oracle.F16, oracle.BF16
-NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
+F32, F16, BF16, FP8 = oracle.F32, oracle.F16, oracle.BF16, oracle.FP8
+NAMES = {F32: "f32", F16: "f16", BF16: "bf16", FP8: "fp8"}
 
 
 def _torch_bf16_bits(x32):
@@ -28,7 +28,8 @@ def _torch_bf16_bits(x32):
 
 
 def _nan_bits(dtype):
-    return {F32: np.float32(np.nan), F16: np.uint16(0x7e00), BF16: np.uint16(0x7fc0)}[dtype]
+    return {F32: np.float32(np.nan), F16: np.uint16(0x7e00), BF16: np.uint16(0x7fc0),
+            FP8: np.uint8(0x7f)}[dtype]
 
 
 # ----------------------------------------------------------------------------
@@ -82,6 +83,45 @@ def pin_rne_quick(L):
     rng = np.random.default_rng(11)
     u = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
     check_rne(L, np.concatenate([u.view(np.float32), rne_special_inputs()]))
+
+
+def fp8_special_inputs():
+    """float32 inputs at every tie and edge of the e4m3 grid, their float32
+    neighbours, and out-of-range values."""
+    import torch
+    codes = torch.arange(0x7f, dtype=torch.int32).to(torch.uint8)      # 0 .. 448
+    v = codes.view(torch.float8_e4m3fn).double().numpy()
+    mids = (v[:-1] + v[1:]) / 2
+    core = np.concatenate([v, mids, [464.0, 465.0, 480.0, 500.0, 1e6, 2.0 ** -10,
+                                     3 * 2.0 ** -11]]).astype(np.float32)
+    allv = np.concatenate([core, np.nextafter(core, np.float32(np.inf)),
+                           np.nextafter(core, np.float32(0)), [np.inf]])
+    return np.concatenate([allv, -allv]).astype(np.float32)
+
+
+def pin_fp8_codec(L):
+    """OCP e4m3: all 256 codes decode to torch's float8_e4m3fn values; the
+    saturating round-to-nearest-even encoder equals torch's cast of the input
+    clamped to +-448, on every tie and edge and on 2^20 random patterns."""
+    import torch
+    codes = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    d = oracle.decode(FP8, codes, L)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(d), np.isnan(ref))
+    assert np.array_equal(d[~np.isnan(d)], ref[~np.isnan(ref)])
+    rng = np.random.default_rng(33)
+    rnd = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        x = np.concatenate([fp8_special_inputs(), rnd, rnd * np.float32(1e-37)])
+    x = x.astype(np.float32)
+    got = oracle.round_to(FP8, x, L)
+    nan = np.isnan(x)
+    want = torch.from_numpy(np.clip(x, -448.0, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8)
+    want = want.numpy()
+    bad = (~nan) & (got != want)
+    assert not bad.any(), "fp8 rounding differs at %r" % x[bad][:4]
+    assert np.all((got[nan] & 0x7f) == 0x7f)
+    assert np.all((got[nan] >> 7) == (x[nan].view(np.uint32) >> 31))
 
 
 def pin_decode(L):
@@ -165,7 +205,7 @@ def pin_slot_mask(L):
 # ----------------------------------------------------------------------------
 def pin_brute_multistep(L):
     cases = [("sliding", F32, 2, 2), ("sliding", F16, 4, 2), ("sliding", BF16, 2, 2),
-             ("full", F32, 2, 2), ("full", BF16, 4, 2)]
+             ("full", F32, 2, 2), ("full", BF16, 4, 2), ("sliding", FP8, 4, 2), ("full", FP8, 2, 2)]
     D, W, steps = 8, 4, 12
     for kind, dt, H, Hkv in cases:
         rng = np.random.default_rng(100 + H + dt)
@@ -177,6 +217,7 @@ def pin_brute_multistep(L):
                  rng.standard_normal((Hkv, D)).astype(np.float32),
                  rng.standard_normal((Hkv, D)).astype(np.float32)) for _ in range(steps)]
         gate = rng.standard_normal(H).astype(np.float32)
+        ksc = inputs.default_fp8_scales(Hkv) if dt == FP8 else None
         sd = oracle.storage_dtype(dt)
         kc = np.full((1, Hkv, n_slots, D), _nan_bits(dt), sd)
         vc = np.full((1, Hkv, n_slots, D), _nan_bits(dt), sd)
@@ -184,9 +225,10 @@ def pin_brute_multistep(L):
         for p in range(steps):
             q, k, v = hist[p]
             r = oracle.layer_step(q[None], k[None], v[None], gate[None], kc, vc, [p], dt,
-                                  ring, rot, theta, scale, write=True, L=L)
+                                  ring, rot, theta, scale, write=True, kv_scale=ksc, L=L)
             ref = np.array(brute.step(hist_py, p, W if ring else None, H, Hkv, rot, theta,
-                                      NAMES[dt], scale, gate.tolist()))
+                                      NAMES[dt], scale, gate.tolist(),
+                                      None if ksc is None else ksc.tolist()))
             err = np.max(np.abs(r["out"][0] - ref)) / np.max(np.abs(ref))
             assert err < 1e-12, (kind, NAMES[dt], p, err)
 
@@ -387,7 +429,7 @@ def pin_capacity_and_poison(L):
     assert r["status"] == 0 and np.all(np.isfinite(r["out"]))
 
 
-QUICK_PINS = [pin_rne_quick, pin_decode, pin_rope, pin_slot_mask, pin_brute_multistep,
+QUICK_PINS = [pin_rne_quick, pin_fp8_codec, pin_decode, pin_rope, pin_slot_mask, pin_brute_multistep,
               pin_single_key, pin_equal_scores, pin_join_equals_concat,
               pin_split_invariance, pin_permutation, pin_ring_equals_roll, pin_merge,
               pin_gate, pin_gate_proj, pin_capacity_and_poison]

@@ -25,7 +25,7 @@ def declared():
 
 def desc(**kw):
     d = dict(batch=2, n_heads=8, n_kv_heads=8, head_dim=256, n_slots=511, kv_dtype=2,
-             scale=1 / 16, keys_per_split=0, chunks_per_workgroup=0)
+             scale=1 / 16, keys_per_split=0, chunks_per_workgroup=0, kv_scale=None)
     d.update(kw)
     return binding.AttnDesc(**d)
 
@@ -73,7 +73,9 @@ def test_workspace_and_splits():
     ("H % Hkv", dict(n_heads=6, n_kv_heads=4), -1),
     ("head_dim", dict(head_dim=96), -6),
     ("head_dim odd", dict(head_dim=7), -1),
-    ("dtype", dict(kv_dtype=3), -1),
+    ("dtype", dict(kv_dtype=4), -1),
+    ("fp8 head_dim 64", dict(kv_dtype=3, head_dim=64), -6),
+    ("fp8 kps quantum", dict(kv_dtype=3, keys_per_split=64), -1),
     ("scale", dict(scale=0.0), -1),
     ("kps", dict(keys_per_split=100), -1),
     ("kps quantum bf16", dict(keys_per_split=96), -1),

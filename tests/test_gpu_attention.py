@@ -12,8 +12,8 @@ import hybrid_sliding_window_decode_amd as hswd
 import oracle
 from oracle import brute
 from hybrid_sliding_window_decode_amd import inputs
-from gpu_util import (CODE, assert_parity, cache_to_dev, cache_to_host, f32_dev, i32_dev, say,
-                      to_dev)
+from gpu_util import (CODE, assert_parity, cache_to_dev, cache_to_host, entry_codes, f32_dev,
+                      i32_dev, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,14 +27,15 @@ def spec_for(kind, B, dtype, S=None, H=8, D=256):
 def oracle_step(x, write=False):
     kc, vc = x.k_cache.copy(), x.v_cache.copy()
     return oracle.layer_step(x.q, x.k, x.v, x.gate, kc, vc, x.pos, CODE[x.spec.dtype],
-                             x.spec.kind == "sliding", x.spec.rot, x.spec.theta, write=write)
+                             x.spec.kind == "sliding", x.spec.rot, x.spec.theta, write=write,
+                             kv_scale=x.spec.kv_scale)
 
 
 def gpu_unfused(x, kps=0, max_pos=None):
     """rope_apply -> decode_attn_* (pre-gate o) on device; returns (o, q_rot, k_rot)."""
     d = to_dev(x)
     ring = x.spec.kind == "sliding"
-    desc = hswd.make_desc(d["k_cache"], keys_per_split=kps)
+    desc = hswd.make_desc(d["k_cache"], keys_per_split=kps, kv_scale=d["kv_scale"])
     hswd.rope_apply(d["q"], d["k"], d["pos"], x.spec.rot, x.spec.theta)
     mp = int(x.pos.max()) if max_pos is None else max_pos
     ws = hswd.workspace(desc, ring, mp)
@@ -63,6 +64,10 @@ CASES = [
     ("full_8xragged_f32_kps64", "full", 8, "f32", "ragged", 700, 64),
     ("sliding_8xragged_f16_kps128", "sliding", 8, "f16", "ragged", None, 128),
     ("full_4x_f16_d128", "full", 4, "f16", [5, 300, 1000, 77], 1001, 0),
+    # fp8 e4m3 caches with per-head scales
+    ("sliding_64xragged_fp8", "sliding", 64, "fp8", "ragged", None, 0),
+    ("full_16xragged_fp8_kps128", "full", 16, "fp8", "ragged", 2049, 128),
+    ("full_4x_fp8_d128", "full", 4, "fp8", [5, 300, 1000, 77], 1001, 0),
 ]
 
 
@@ -166,6 +171,8 @@ def test_partials_and_merge_match_oracle_split_form():
     ("sliding", "f32", [600, 3], None, 128),
     ("full", "bf16", "ragged", 3000, 0),
     ("full", "f16", [1024, 1, 0, 2999], 3000, 256),
+    ("sliding", "fp8", "ragged", None, 0),
+    ("full", "fp8", [1024, 1, 0, 2999], 3000, 256),
 ])
 def test_layer_step_fused_matches_oracle_and_unfused(kind, dtype, pos, S, kps):
     """The one-launch layer step: gated output against the oracle, the stored
@@ -178,7 +185,7 @@ def test_layer_step_fused_matches_oracle_and_unfused(kind, dtype, pos, S, kps):
     ring = kind == "sliding"
     ref = oracle_step(x, write=True)
     d = to_dev(x)
-    desc = hswd.make_desc(d["k_cache"], keys_per_split=kps)
+    desc = hswd.make_desc(d["k_cache"], keys_per_split=kps, kv_scale=d["kv_scale"])
     mp = int(x.pos.max())
     ws = hswd.workspace(desc, ring, mp)
     say("layer_step fused %s %s pos=%s" % (kind, dtype, list(x.pos[:6])))
@@ -205,16 +212,16 @@ def test_layer_step_fused_matches_oracle_and_unfused(kind, dtype, pos, S, kps):
     assert hswd.check_errors(ws2) == 0
     assert np.array_equal(g.cpu().numpy(), out), "fused and unfused outputs differ"
     kc2, vc2 = cache_to_host(e["k_cache"]), cache_to_host(e["v_cache"])
-    assert np.array_equal(kc.view(np.uint16) if dtype != "f32" else kc.view(np.uint32),
-                          kc2.view(np.uint16) if dtype != "f32" else kc2.view(np.uint32))
+    assert np.array_equal(kc.view(np.uint8), kc2.view(np.uint8))
 
     # the stored entry equals the oracle's rounding of the GPU's rotated key
     k_rot = e["k"].cpu().numpy()
     for b in range(B):
         p = int(x.pos[b])
         row = p % spec.n_slots if ring else p
-        want_k = oracle.round_to(CODE[dtype], k_rot[b])
-        want_v = oracle.round_to(CODE[dtype], x.v[b])
+        sc = spec.kv_scale
+        want_k = entry_codes(k_rot[b], dtype, None if sc is None else sc[0][:, None])
+        want_v = entry_codes(x.v[b], dtype, None if sc is None else sc[1][:, None])
         if dtype == "f32":
             assert np.array_equal(kc[b, :, row].view(np.uint32), want_k.view(np.uint32))
             assert np.array_equal(vc[b, :, row].view(np.uint32), want_v.view(np.uint32))
@@ -224,13 +231,13 @@ def test_layer_step_fused_matches_oracle_and_unfused(kind, dtype, pos, S, kps):
         # every other row is untouched
         others = np.ones(spec.n_slots, bool)
         others[row] = False
-        kb = kc[b][:, others].view(np.uint16 if dtype != "f32" else np.uint32)
-        xb = x.k_cache[b][:, others].view(np.uint16 if dtype != "f32" else np.uint32)
+        kb = kc[b][:, others].view(np.uint8)
+        xb = x.k_cache[b][:, others].view(np.uint8)
         assert np.array_equal(kb, xb)
 
 
 @pytest.mark.parametrize("kind,dtype", [("sliding", "f32"), ("sliding", "bf16"),
-                                        ("full", "f16")])
+                                        ("full", "f16"), ("sliding", "fp8")])
 def test_multistep_against_brute_force(kind, dtype):
     """Several steps through the ring's wrap, driven on the GPU with the fused
     layer step (read, then write), against the brute force over the raw
@@ -246,10 +253,12 @@ def test_multistep_against_brute_force(kind, dtype):
     gate = rng.standard_normal(H).astype(np.float32)
     hist_py = [(q.tolist(), k.tolist(), v.tolist()) for q, k, v in hist]
     sd = oracle.storage_dtype(CODE[dtype])
-    nan = {"f32": np.float32(np.nan), "f16": np.uint16(0x7e00), "bf16": np.uint16(0x7fc0)}[dtype]
+    nan = inputs.nan_bits(dtype)
     kc = cache_to_dev(np.full((1, H, S, D), nan, sd), dtype)
     vc = cache_to_dev(np.full((1, H, S, D), nan, sd), dtype)
-    desc = hswd.make_desc(kc)
+    ksc = inputs.default_fp8_scales(H) if dtype == "fp8" else None
+    ksc_dev = None if ksc is None else f32_dev(ksc)
+    desc = hswd.make_desc(kc, kv_scale=ksc_dev)
     ws = hswd.workspace(desc, ring, S - 1)
     say("multistep %s %s" % (kind, dtype))
     for p in range(steps):
@@ -258,7 +267,7 @@ def test_multistep_against_brute_force(kind, dtype):
                               f32_dev(gate[None]), kc, vc, i32_dev([p]), ring, rot, theta, ws,
                               max_pos=0 if ring else S - 1, desc=desc)
         ref = np.array(brute.step(hist_py, p, W if ring else None, H, H, rot, theta, dtype,
-                                  1 / 16, gate.tolist()))
+                                  1 / 16, gate.tolist(), None if ksc is None else ksc.tolist()))
         got = out.cpu().numpy()[0]
         err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
         assert err < (1e-5 if dtype == "f32" else 2e-3 / 4), (p, err)

@@ -7,7 +7,9 @@ import torch
 import hybrid_sliding_window_decode_amd as hswd
 import oracle
 import pins
-from gpu_util import CODE, cache_to_dev, cache_to_host, f32_dev, i32_dev, say
+from gpu_util import (CODE, cache_to_dev, cache_to_host, entry_codes, f32_dev, i32_dev, say,
+                      to_dev)
+from hybrid_sliding_window_decode_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -44,14 +46,16 @@ def test_rope(rot, theta):
         assert np.array_equal(got[..., rot:], x[..., rot:])    # untouched dims
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "fp8"])
 def test_kv_slot_write_rounding_bit_exact(dtype):
     """Entry rounding on the GPU equals the oracle's, bit for bit, on 2^20
-    random float32 patterns and on every tie and edge of the target grid."""
+    random float32 patterns and on every tie and edge of the target grid
+    (fp8: of x / scale with a different scale per kv head)."""
     rng = np.random.default_rng(41)
+    special = pins.fp8_special_inputs() if dtype == "fp8" else pins.rne_special_inputs()
     vals = np.concatenate([
         rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32),
-        pins.rne_special_inputs()])
+        special])
     Hkv, D = 8, 256
     per = Hkv * D
     B = -(-vals.size // per)
@@ -65,14 +69,18 @@ def test_kv_slot_write_rounding_bit_exact(dtype):
     pos = np.arange(B, dtype=np.int32)
     ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
     slot = torch.empty(B, dtype=torch.int32, device="cuda")
-    hswd.kv_slot_write(kd, vd, f32_dev(k), f32_dev(v), i32_dev(pos), 1, ws, slot_out=slot)
+    sc = inputs.default_fp8_scales(Hkv) if dtype == "fp8" else None
+    sc_dev = None if sc is None else f32_dev(sc)
+    desc = hswd.make_desc(kd, kv_scale=sc_dev)
+    hswd.kv_slot_write(kd, vd, f32_dev(k), f32_dev(v), i32_dev(pos), 1, ws, slot_out=slot,
+                       desc=desc)
     assert hswd.check_errors(ws) == 0
     kh, vh = cache_to_host(kd), cache_to_host(vd)
     assert np.array_equal(slot.cpu().numpy(), pos % 3)
     for b in range(0, B, 97):
         assert np.all(kh[b, :, [s for s in range(3) if s != b % 3]] == 0)
-    ref_k = oracle.round_to(CODE[dtype], k)
-    ref_v = oracle.round_to(CODE[dtype], v)
+    ref_k = entry_codes(k, dtype, None if sc is None else sc[0][None, :, None])
+    ref_v = entry_codes(v, dtype, None if sc is None else sc[1][None, :, None])
     rows = pos % 3
     got_k = kh[np.arange(B), :, rows]
     got_v = vh[np.arange(B), :, rows]
@@ -82,6 +90,29 @@ def test_kv_slot_write_rounding_bit_exact(dtype):
     else:
         assert np.array_equal(got_k, ref_k)
         assert np.array_equal(got_v, ref_v)
+
+
+def test_fp8_decode_all_codes_in_attention():
+    """A one-key cache holding each of the 255 non-NaN fp8 codes in turn
+    (q = 0, new value 0): the output is the mean of the decoded cached value
+    and 0 -- the kernel's fp8 decode of every code, against the oracle's."""
+    codes = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], np.uint8)
+    B, H, D = len(codes), 8, 256
+    spec = inputs.sliding_spec(B, "fp8", n_slots=511)
+    x = inputs.make_step(spec, 1, seed=45)
+    x.q[:] = 0
+    x.v[:] = 0
+    x.k[:] = 0
+    x.v_cache[:, :, 0, :] = codes[:, None, None]
+    d = to_dev(x)
+    desc = hswd.make_desc(d["k_cache"], kv_scale=d["kv_scale"])
+    ws = hswd.workspace(desc, 1, 0)
+    say("fp8 decode of all codes")
+    hswd.rope_apply(d["q"], d["k"], d["pos"], 256, 1e4)
+    o = hswd.decode_attn_sliding(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["pos"],
+                                 ws, desc=desc).cpu().numpy()
+    val = oracle.decode(CODE["fp8"], codes)[:, None] * spec.kv_scale[1][None, :]
+    assert np.array_equal(o[:, :, 0].astype(np.float64), val / 2)
 
 
 def test_kv_slot_write_capacity_flag():

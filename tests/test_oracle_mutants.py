@@ -56,6 +56,15 @@ MUTANTS = [
     ("f16 decode subnormal scale", [("else if (e == 0) v = ldexp((double)m, -24);",
                                      "else if (e == 0) v = ldexp((double)m, -25);")]),
     ("gate weight transposed", [("(double)w[(size_t)h * hidden + i];", "(double)w[(size_t)i * H + h];")]),
+    ("fp8 without saturation", [("    if (r > 448.0) r = 448.0;\n", "")]),
+    ("fp8 decode exponent bias", [("else v = ldexp((double)(8 + m), e - 10);",
+                                   "else v = ldexp((double)(8 + m), e - 9);")]),
+    ("V scale dropped", [("o[d] += w * (vs * load_elt(vc, dtype, (size_t)j * D + d));",
+                          "o[d] += w * (1.0 * load_elt(vc, dtype, (size_t)j * D + d));")]),
+    ("K scale dropped", [("acc += q[d] * (ks * load_elt(kc, dtype, (size_t)j * D + d));\n        s[j] = scale * acc;",
+                          "acc += q[d] * (1.0 * load_elt(kc, dtype, (size_t)j * D + d));\n        s[j] = scale * acc;")]),
+    ("entry stored unscaled", [("        kq[i] = (float)((double)kr32[i] / ks);",
+                                "        kq[i] = (float)((double)kr32[i] / 1.0);")]),
     ("append capacity off by one", [("if (!ring && p >= n_slots) { status = -4; continue; }",
                                      "if (!ring && p > n_slots) { status = -4; continue; }")]),
 ]
