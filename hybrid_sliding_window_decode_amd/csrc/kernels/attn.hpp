@@ -13,15 +13,17 @@
 // workgroup streams, which the host picks from the batch and the CU count.
 //
 // Streaming.  One workgroup (4 waves) streams a contiguous range of chunks of
-// one (stream, kv head).  Each wave reads whole 16-key (bf16/f16) or 8-key
-// (f32) tiles with 128-bit non-temporal loads, lanes over head dims, and
-// keeps the next tile in flight while it scores the current one (register
-// double buffering); the prefetch runs across chunk boundaries, and chunk
-// partials wait in registers so the waves meet at a barrier only every four
-// chunks.  The first tile is requested
-// before the query prologue.  Dot products are reduced across lanes with a
-// transposed butterfly (about one exchange per key).  Softmax is in base 2
-// with log2(e) folded into the query scale.
+// one (stream, kv head).  Each wave reads whole 32-key (fp8), 16-key
+// (bf16/f16) or 8-key (f32) tiles with 128-bit non-temporal loads, lanes over
+// head dims, and keeps the next tile in flight while it scores the current
+// one (register double buffering); the prefetch runs across chunk
+// boundaries, and each wave's chunk partial goes to LDS, so the waves meet
+// at a barrier only every four chunks.  The per-stream inputs and the first
+// two tiles are requested before the prologue (RoPE of the query and the new
+// key, the new entry's score).  Dot products are reduced across lanes with a
+// transposed butterfly (about one exchange per key); every exchange is a DPP
+// move or a gfx950 permlane swap, none goes through LDS.  Softmax is in base
+// 2 with log2(e) folded into the query scale.
 //
 // Several workgroups per (stream, kv head) (long contexts, small batches):
 // each stores its chunk partials with agent-scope atomic stores, counts its
@@ -133,13 +135,31 @@ struct Fold {
 };
 
 // One exchange of the transposed butterfly: a lane whose `M` bit is set
-// keeps its upper value and sends its lower one; its partner does the
-// opposite, so each keeps the sum over both lanes of one of the two keys.
+// ends with the sum over both lanes of the pair of the upper value, its
+// partner with that of the lower one (each lane adds its own value first).
+//   M = 16, 32: one permlane swap of (lo, hi) hands each lane exactly the
+//               two addends it needs;
+//   M = 4, 8:   both pair sums in DPP, then a select;
+//   M = 1, 2:   the lane sends the value its partner keeps.
 template <int M>
 __device__ __forceinline__ float tstage(float lo, float hi, bool up) {
-    const float send = up ? lo : hi;
-    const float keep = up ? hi : lo;
-    return keep + xor_lane<M>(send);
+    if constexpr (M == 16 || M == 32) {
+        float r0, r1;
+        lane_swap<M>(lo, hi, r0, r1);
+        return up ? r1 + r0 : r0 + r1;          // own value first, as below
+    } else if constexpr (M == 8) {
+        const float a = lo + dpp::mov<dpp::kRowRor8>(lo);
+        const float b = hi + dpp::mov<dpp::kRowRor8>(hi);
+        return up ? b : a;
+    } else if constexpr (M == 4) {
+        const float a = lo + dpp::mov<dpp::kRowShl4>(lo);   // lanes with bit 2 clear
+        const float b = hi + dpp::mov<dpp::kRowShr4>(hi);   // lanes with bit 2 set
+        return up ? b : a;
+    } else {
+        const float send = up ? lo : hi;
+        const float keep = up ? hi : lo;
+        return keep + xor_lane<M>(send);
+    }
 }
 
 // Sum over the LPR lanes that share a cache row of eight per-load partials
@@ -159,7 +179,7 @@ __device__ __forceinline__ float transposed_reduce8(const float (&v)[8], int lan
     float c = tstage<M3>(b0, b1, u);
     // the remaining lane bits below M3 hold copies of the same key: plain sum
 #pragma unroll
-    for (int m = M3 / 2; m >= 1; m >>= 1) c += xor_lane_rt(c, m);
+    for (int m = M3 / 2; m >= 1; m >>= 1) c = xor_sum_rt(c, m);
     return c;
 }
 
@@ -171,7 +191,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     constexpr float kLn2 = 0.69314718055994531f;
 
     __shared__ float sm_q[D];
-    __shared__ float sm_o[2][4][kAttnWaves][D];       // stashed wave partials, by flush parity
+    __shared__ float sm_o[2][4][kAttnWaves][D];       // wave chunk partials, by flush parity
     __shared__ float sm_m[2][4][kAttnWaves], sm_l[2][4][kAttnWaves];
     __shared__ float sm_dot[kAttnWaves];
     __shared__ float sm_gl[kAttnWaves];
@@ -251,24 +271,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
 
     // Item j of this wave: tile (wid + 4 i) of chunk ch.  Rows past the
     // chunk's valid end are clamped onto its last valid row (never reading an
-    // unwritten slot) and masked out of the softmax.
+    // unwritten slot) and masked out of the softmax; an item past the last
+    // (a prefetch the loop never scores) clamps the same way, onto row 0 of
+    // the block when it has no valid row at all, so every load stays inside
+    // this (stream, kv head)'s cache block and may be issued unconditionally.
     auto item_chunk = [&](int j) { return j < n_full_items ? c_begin + j / TPW : c_full; };
     auto item_tile = [&](int j) { return j < n_full_items ? j % TPW : j - n_full_items; };
 
     auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int j) {
         const int ch = item_chunk(j);
-        const int jend = min((ch + 1) * P.K, nv);
+        const int jlast = max(min((ch + 1) * P.K, nv), 1) - 1;
         const int base = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT + r;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            int row = base + i * RPI;
-            row = row < jend ? row : jend - 1;
+            const int row = min(base + i * RPI, jlast);
             kt[i] = load_kv16(kbase + (size_t)row * D);
         }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            int row = base + i * RPI;
-            row = row < jend ? row : jend - 1;
+            const int row = min(base + i * RPI, jlast);
             vt[i] = load_kv16(vbase + (size_t)row * D);
         }
     };
@@ -295,57 +316,47 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         // tile max over the distinct keys (lane bits >= STEP)
         float mx = s;
 #pragma unroll
-        for (int m = G::STEP; m < kWave; m <<= 1) mx = fmaxf(mx, xor_lane_rt(mx, m));
+        for (int m = G::STEP; m < kWave; m <<= 1) mx = xor_max_rt(mx, m);
         if (mx == -INFINITY) return;                    // nothing valid in this tile
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
         const float pr = fast_exp2(s - m_new);
         m_run = m_new;
         l_lane = l_lane * alpha + ((lane & (G::STEP - 1)) == 0 ? pr : 0.f);
+        // every key's probability to the lanes of its row, all requests out
+        // before the first is used
+        float pk[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) pk[i] = lane_value(pr, r * LPR + i * G::STEP);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) o_acc[e] *= alpha;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const float pi = lane_value(pr, r * LPR + i * G::STEP);
             float vf[EPC];
             unpack16<DT>(vt[i], vf);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) o_acc[e] = fmaf(pi, vf[e], o_acc[e]);
+            for (int e = 0; e < EPC; ++e) o_acc[e] = fmaf(pk[i], vf[e], o_acc[e]);
         }
     };
 
     // End of a chunk (every wave, same point): the wave's partial for it is
-    // reduced across lanes and pushed on a short register stash (a shift
-    // register, so every index is a compile-time one).  Every kStash chunks,
-    // and once at the end, the stash is flushed: wave partials -> LDS, one
-    // barrier, then each thread forms the chunk partials for its dim t, in
-    // chunk order, and folds (single workgroup per pair) or stores them.
-    // Deferring the barrier keeps small chunks cheap; the arithmetic and its
-    // order are those of a barrier per chunk.
-    constexpr int kStash = EPC > 8 ? 2 : 4;    // registers: 16 dims per lane for fp8
-    float st_m[kStash], st_l[kStash], st_o[kStash][EPC];
+    // reduced across lanes and written to its LDS slot of the current flush
+    // buffer.  Every kStash chunks, and once at the end, the buffer is
+    // flushed: one barrier, then each thread forms the chunk partials for its
+    // dim t, in chunk order, and folds (single workgroup per pair) or stores
+    // them.  The two buffers alternate, so a slot is rewritten only after the
+    // barrier of the flush in between; deferring the barrier keeps small
+    // chunks cheap, and the arithmetic and its order are those of a barrier
+    // per chunk.
+    constexpr int kStash = 4;
     int n_st = 0, st_first = 0, n_flush = 0;
 
     auto flush = [&]() {
         const int buf = n_flush & 1;
         ++n_flush;
-#pragma unroll
-        for (int s = 0; s < kStash; ++s) {
-            if (s < n_st) {
-                if (r == 0) {
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) sm_o[buf][s][wid][c * EPC + e] = st_o[s][e];
-                }
-                if (lane == 0) {
-                    sm_m[buf][s][wid] = st_m[s];
-                    sm_l[buf][s][wid] = st_l[s];
-                }
-            }
-        }
         __syncthreads();
-        for (int i = 0; i < n_st; ++i) {
-            const int s = n_st - 1 - i;             // slot 0 holds the newest chunk
-            const int ch = st_first + i;
+        for (int s = 0; s < n_st; ++s) {
+            const int ch = st_first + s;
             const float Mc = lds_max<kAttnWaves>(sm_m[buf][s]);
             float Lc = 0.f, Oc = 0.f;
             if (Mc != -INFINITY) {
@@ -381,19 +392,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
 #pragma unroll
         for (int m = LPR; m < kWave; m <<= 1) {
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) o_acc[e] += xor_lane_rt(o_acc[e], m);
+            for (int e = 0; e < EPC; ++e) o_acc[e] = xor_sum_rt(o_acc[e], m);
         }
+        const int buf = n_flush & 1;
+        if (r == 0) {
 #pragma unroll
-        for (int s = kStash - 1; s > 0; --s) {
-            st_m[s] = st_m[s - 1];
-            st_l[s] = st_l[s - 1];
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) st_o[s][e] = st_o[s - 1][e];
+            for (int e = 0; e < EPC; ++e) sm_o[buf][n_st][wid][c * EPC + e] = o_acc[e];
         }
-        st_m[0] = m_run;
-        st_l[0] = l_w;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) st_o[0][e] = o_acc[e];
+        if (lane == 0) {
+            sm_m[buf][n_st][wid] = m_run;
+            sm_l[buf][n_st][wid] = l_w;
+        }
         if (n_st == 0) st_first = ch;
         ++n_st;
         m_run = -INFINITY;
@@ -403,26 +412,69 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         if (n_st == kStash) flush();
     };
 
-    // The first tile's loads do not depend on the query: issue them before
-    // the query prologue (RoPE in double precision, then a barrier), so the
-    // prologue runs under the memory latency.
-    if (n_items > 0) load_tile(kA, vA, 0);
+    // Per-stream inputs first: this thread's query dim and its RoPE partner,
+    // and for the new entry the same of the key plus the value (threads past
+    // D read dim 0 and drop it).  Vector loads retire in order, so the
+    // prologue waits for these alone; the first two tiles, requested next,
+    // stay in flight under its double-precision RoPE.  Those two requests
+    // are unconditional (clamped rows, see load_tile): a load under a branch
+    // would make the compiler's wait counts at the join assume the branch
+    // was not taken, and the prologue would wait for the tiles too.
+    const bool has_new = MODE != kModePartials;
+    const int td = t < D ? t : 0;
+    const bool rotated = MODE == kModeStep && td < P.rot;
+    const int tp = MODE == kModeStep ? rope_partner(td, P.rot) : td;
+    const float* qv = P.q + (size_t)bh * D;
+    const float* kv = P.k + (size_t)pair * D;
+    const float* vv = P.v + (size_t)pair * D;
+    const float q_t = qv[td], q_p = qv[tp];
+    float k_t = 0.f, k_p = 0.f, v_t = 0.f;
+    if (has_new) {
+        k_t = kv[td];
+        k_p = kv[tp];
+        v_t = vv[td];
+    }
+    const bool gproj = MODE == kModeStep && P.gx != nullptr;
+    const float glogit = MODE == kModeStep && !gproj && P.gate != nullptr ? P.gate[bh] : 0.f;
 
-    // Query (rotated in-kernel for the fused step), scaled by scale*log2(e)
-    // and, for an fp8 cache, by the head's K scale (cached keys are scale *
-    // code, so the scale moves onto the query once).
-    {
-        const float* qv = P.q + (size_t)bh * D;
-        const float qmul = P.qscale * kscale;
-        for (int i = tid; i < D; i += kAttnThreads) {
-            float x = MODE == kModeStep ? rope_elem(qv, i, P.rot, P.log2_theta, p) : qv[i];
-            sm_q[i] = x * qmul;
+    load_tile(kA, vA, 0);
+    load_tile(kB, vB, 1);
+
+    // Query and new key rotated in-kernel for the fused step (one angle for
+    // both); the query scaled by scale*log2(e) and, for an fp8 cache, by the
+    // head's K scale (cached keys are scale * code, so the scale moves onto
+    // the query once).
+    float q_r = q_t, k_r = k_t;
+    if (rotated) {
+        const int half = P.rot >> 1;
+        double cs, sn;
+        rope_cs(td < half ? td : td - half, P.rot, P.log2_theta, p, cs, sn);
+        q_r = rope_rotate(q_t, q_p, td < half, cs, sn);
+        k_r = rope_rotate(k_t, k_p, td < half, cs, sn);
+    }
+    const float qsc = q_r * (P.qscale * kscale);
+    if (t < D) sm_q[t] = qsc;
+
+    // The new entry, joined in score space: k_hat, v_hat are the rotated key
+    // and the value rounded to the cache element type (fp8: the code of
+    // x / scale, the quotient rounded once to float32); its score is summed
+    // now and folded last, after the cached keys.
+    S k_hat{}, v_hat{};
+    float vh = 0.f;
+    if (has_new) {
+        float prod = 0.f;
+        if (t < D) {
+            k_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(k_r, kscale) : k_r);
+            v_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(v_t, vscale) : v_t);
+            prod = qsc * elt_to_f32<DT>(k_hat);
+            vh = elt_to_f32<DT>(v_hat);
         }
+        prod = wave_sum(prod);
+        if (lane == 0) sm_dot[wid] = prod;
     }
     // Gate logit from the projection (fused step with g_proj): it needs only
-    // the layer input, so it is summed here, under the first tile's latency,
+    // the layer input, so it is summed here, under the first tiles' latency,
     // and used in the epilogue.  Same sum as hswd_gate_proj.
-    const bool gproj = MODE == kModeStep && P.gx != nullptr;
     if (gproj) {
         float gs = gate_share(P.gx + (size_t)b * P.hidden, P.gw + (size_t)h * P.hidden,
                               P.hidden, tid, kAttnThreads);
@@ -438,17 +490,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     auto after = [&](int j) {
         if (j < n_full_items && (j + 1) % TPW == 0) end_chunk(c_begin + j / TPW);
     };
+    // Entering each pass, A holds item j and B item j + 1, both requested; a
+    // buffer is refilled as soon as it has been scored.  The loop body's
+    // loads are unconditional (j + 3 < n_items), so its wait counts keep the
+    // other buffer in flight.
     int j = 0;
-    for (; j + 2 < n_items; j += 2) {
-        load_tile(kB, vB, j + 1);
+    for (; j + 3 < n_items; j += 2) {
         compute_tile(kA, vA, j);
         after(j);
         load_tile(kA, vA, j + 2);
         compute_tile(kB, vB, j + 1);
         after(j + 1);
+        load_tile(kB, vB, j + 3);
     }
-    if (j + 1 < n_items) {
-        load_tile(kB, vB, j + 1);
+    if (j + 2 < n_items) {
+        compute_tile(kA, vA, j);
+        after(j);
+        load_tile(kA, vA, j + 2);
+        compute_tile(kB, vB, j + 1);
+        after(j + 1);
+        compute_tile(kA, vA, j + 2);
+        after(j + 2);
+    } else if (j + 1 < n_items) {
         compute_tile(kA, vA, j);
         after(j);
         compute_tile(kB, vB, j + 1);
@@ -514,30 +577,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
             __hip_atomic_store(&P.counters[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Join the new entry as a one-key partial: k_hat, v_hat are the rotated
-    // key and the value rounded to the cache element type.
-    const float* kv = P.k + (size_t)pair * D;
-    const float* vv = P.v + (size_t)pair * D;
-    S k_hat{}, v_hat{};
-    float prod = 0.f, vh = 0.f;
-    if (t < D) {
-        const float kr = MODE == kModeStep ? rope_elem(kv, t, P.rot, P.log2_theta, p) : kv[t];
-        // fp8: the code of x / scale, the quotient rounded once to float32
-        k_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(kr, kscale) : kr);
-        v_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(vv[t], vscale) : vv[t]);
-        prod = sm_q[t] * elt_to_f32<DT>(k_hat);
-        vh = elt_to_f32<DT>(v_hat);
-    }
-    prod = wave_sum(prod);
-    if (lane == 0) sm_dot[wid] = prod;
-    __syncthreads();
+    // Join the new entry as a one-key partial (score summed in the prologue).
     const float s_new = lds_tree_sum<kAttnWaves>(sm_dot);
     run.add(s_new, 1.f, vh);
     if (t < D) {
         float o = run.O / run.L;
         if (DT == kFP8) o *= vscale;
         if (MODE == kModeStep && (gproj || P.gate != nullptr)) {
-            const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl) : P.gate[bh];
+            const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl) : glogit;
             o *= 1.f / (1.f + expf(-logit));
         }
         P.out[(size_t)bh * D + t] = o;
@@ -545,8 +592,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
 
     if (MODE == kModeStep) {
         // Every workgroup of this pair has finished reading (one workgroup:
-        // the barriers above; several: the arrival count), so the ring slot
-        // that still held position p - S can be overwritten now.
+        // the barrier of the last stash flush, which every wave reaches after
+        // its last tile; several: the arrival count), so the ring slot that
+        // still held position p - S can be overwritten now.
         int row = -1;
         if (p >= 0) {
             if (RING) row = p % P.S;

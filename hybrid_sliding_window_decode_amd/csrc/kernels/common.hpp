@@ -162,52 +162,127 @@ __device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave exchanges: value of lane (lane ^ mask).
-//   masks 1, 2: DPP quad permutations;  4, 8, 16: ds_swizzle bit mode
-//   (within 32-lane halves);  32: ds_bpermute.
+// Wave exchanges between lane l and lane l ^ M, all in the VALU:
+//   M = 1, 2:   DPP quad permutations;
+//   M = 4:      DPP row shifts by 4 (left for lanes with bit 2 clear, right
+//               for the others) and a select;
+//   M = 8:      DPP row rotation by 8 (rows of 16 lanes);
+//   M = 16, 32: the gfx950 permlane swaps.  v_permlane{16,32}_swap(a, b)
+//               leaves, in a lane with bit M clear, (a[l], a[l + M]) and in
+//               a lane with it set, (b[l - M], b[l]).  With a = b = v the two
+//               results are the values of both lanes of the pair, so their
+//               sum or max is the pair's (addition and max are commutative:
+//               the same bits as v + v[l ^ M]) without a select.
+// xor_sum / xor_max return v op v[l ^ M]; xor_lane the partner's value.
 // ---------------------------------------------------------------------------
+namespace dpp {
+constexpr int kQuad10 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuad23 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowShl4 = 0x104;   // lane l reads lane l + 4 of its row
+constexpr int kRowShr4 = 0x114;   // lane l reads lane l - 4 of its row
+constexpr int kRowRor8 = 0x128;   // lane l reads lane l ^ 8 of its row
+template <int CTRL>
+__device__ __forceinline__ float mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+}  // namespace dpp
+
+// The two results of a permlane swap of (a, b) over distance M (16 or 32).
+template <int M>
+__device__ __forceinline__ void lane_swap(float a, float b, float& r0, float& r1) {
+    static_assert(M == 16 || M == 32, "swap distance");
+    if constexpr (M == 16) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+        r0 = __uint_as_float(r[0]);
+        r1 = __uint_as_float(r[1]);
+    } else {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+        r0 = __uint_as_float(r[0]);
+        r1 = __uint_as_float(r[1]);
+    }
+}
+
 template <int M>
 __device__ __forceinline__ float xor_lane(float v) {
     static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "mask");
-    int x = __float_as_int(v);
-    int r;
     if constexpr (M == 1) {
-        r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false);        // quad_perm [1,0,3,2]
+        return dpp::mov<dpp::kQuad10>(v);
     } else if constexpr (M == 2) {
-        r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false);        // quad_perm [2,3,0,1]
-    } else if constexpr (M == 32) {
-        r = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2), x);
+        return dpp::mov<dpp::kQuad23>(v);
+    } else if constexpr (M == 4) {
+        const float up = dpp::mov<dpp::kRowShr4>(v), dn = dpp::mov<dpp::kRowShl4>(v);
+        return (__lane_id() & 4) ? up : dn;
+    } else if constexpr (M == 8) {
+        return dpp::mov<dpp::kRowRor8>(v);
     } else {
-        r = __builtin_amdgcn_ds_swizzle(x, 0x1f | (M << 10));          // and 0x1f, xor M
+        float r0, r1;
+        lane_swap<M>(v, v, r0, r1);
+        return (__lane_id() & M) ? r0 : r1;
     }
-    return __int_as_float(r);
 }
 
-__device__ __forceinline__ float xor_lane_rt(float v, int m) {
+template <int M>
+__device__ __forceinline__ float xor_sum(float v) {
+    if constexpr (M == 16 || M == 32) {
+        float r0, r1;
+        lane_swap<M>(v, v, r0, r1);
+        return r0 + r1;
+    } else {
+        return v + xor_lane<M>(v);
+    }
+}
+
+template <int M>
+__device__ __forceinline__ float xor_max(float v) {
+    if constexpr (M == 16 || M == 32) {
+        float r0, r1;
+        lane_swap<M>(v, v, r0, r1);
+        return fmaxf(r0, r1);
+    } else {
+        return fmaxf(v, xor_lane<M>(v));
+    }
+}
+
+// Mask known at compile time after unrolling (the loops that call these run
+// over powers of two with constant bounds).
+__device__ __forceinline__ float xor_sum_rt(float v, int m) {
     switch (m) {
-        case 1: return xor_lane<1>(v);
-        case 2: return xor_lane<2>(v);
-        case 4: return xor_lane<4>(v);
-        case 8: return xor_lane<8>(v);
-        case 16: return xor_lane<16>(v);
-        default: return xor_lane<32>(v);
+        case 1: return xor_sum<1>(v);
+        case 2: return xor_sum<2>(v);
+        case 4: return xor_sum<4>(v);
+        case 8: return xor_sum<8>(v);
+        case 16: return xor_sum<16>(v);
+        default: return xor_sum<32>(v);
     }
 }
 
-// Value of lane `src` (any lane of the wave).
+__device__ __forceinline__ float xor_max_rt(float v, int m) {
+    switch (m) {
+        case 1: return xor_max<1>(v);
+        case 2: return xor_max<2>(v);
+        case 4: return xor_max<4>(v);
+        case 8: return xor_max<8>(v);
+        case 16: return xor_max<16>(v);
+        default: return xor_max<32>(v);
+    }
+}
+
+// Value of lane `src` (any lane): ds_bpermute.
 __device__ __forceinline__ float lane_value(float v, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-    v += xor_lane<32>(v); v += xor_lane<16>(v); v += xor_lane<8>(v);
-    v += xor_lane<4>(v); v += xor_lane<2>(v); v += xor_lane<1>(v);
+    v = xor_sum<32>(v); v = xor_sum<16>(v); v = xor_sum<8>(v);
+    v = xor_sum<4>(v); v = xor_sum<2>(v); v = xor_sum<1>(v);
     return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, xor_lane<32>(v)); v = fmaxf(v, xor_lane<16>(v)); v = fmaxf(v, xor_lane<8>(v));
-    v = fmaxf(v, xor_lane<4>(v)); v = fmaxf(v, xor_lane<2>(v)); v = fmaxf(v, xor_lane<1>(v));
+    v = xor_max<32>(v); v = xor_max<16>(v); v = xor_max<8>(v);
+    v = xor_max<4>(v); v = xor_max<2>(v); v = xor_max<1>(v);
     return v;
 }
 
@@ -265,21 +340,40 @@ __device__ __forceinline__ float gate_share(const float* x, const float* w_row, 
 // RoPE of element t of one head vector x[0..D) at position p: the pair
 // (x[i], x[i + rot/2]) turns by p * theta^(-2i/rot); dims >= rot pass.  The
 // inverse frequency is 2^(-(2i/rot) * log2(theta)); angle, sine, cosine and
-// rotation are in double precision, rounded once to float.
+// rotation are in double precision, rounded once to float.  The rotation's
+// fused multiply-adds are written out, so every caller gets the same bits.
 // ---------------------------------------------------------------------------
+// Cosine and sine of pair i's angle at position p.
+__device__ __forceinline__ void rope_cs(int i, int rot, double log2_theta, int p, double& c,
+                                        double& s) {
+    const double inv = exp2(-(2.0 * (double)i / (double)rot) * log2_theta);
+    const double a = (double)p * inv;
+    sincos(a, &s, &c);
+}
+
+// Element t of the rotated pair from x[t] and its partner x[t +- rot/2]
+// (lower: t < rot/2, so x[t] is the pair's first component).
+__device__ __forceinline__ float rope_rotate(float xt, float xpart, bool lower, double c,
+                                            double s) {
+    const double x0 = lower ? (double)xt : (double)xpart;
+    const double x1 = lower ? (double)xpart : (double)xt;
+    const double r = lower ? __fma_rn(x0, c, -(x1 * s)) : __fma_rn(x1, c, x0 * s);
+    return (float)r;
+}
+
+// Partner dim of t under RoPE over the first `rot` dims (t itself past rot).
+__device__ __forceinline__ int rope_partner(int t, int rot) {
+    const int half = rot >> 1;
+    return t >= rot ? t : (t < half ? t + half : t - half);
+}
+
 __device__ __forceinline__ float rope_elem(const float* x, int t, int rot, double log2_theta,
                                            int p) {
     if (t >= rot) return x[t];
-    int half = rot >> 1;
-    int i = t < half ? t : t - half;
-    double inv = exp2(-(2.0 * (double)i / (double)rot) * log2_theta);
-    double a = (double)p * inv;
-    double sn, cs;
-    sincos(a, &sn, &cs);
-    double x0 = (double)x[i];
-    double x1 = (double)x[i + half];
-    double r = t < half ? x0 * cs - x1 * sn : x1 * cs + x0 * sn;
-    return (float)r;
+    const int half = rot >> 1;
+    double c, s;
+    rope_cs(t < half ? t : t - half, rot, log2_theta, p, c, s);
+    return rope_rotate(x[t], x[rope_partner(t, rot)], t < half, c, s);
 }
 
 }  // namespace hswd
