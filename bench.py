@@ -48,25 +48,32 @@ def is_full(l):
 KERNEL_SOURCES = ["hybrid_sliding_window_decode_amd/csrc/kernels/attn.hpp",
                   "hybrid_sliding_window_decode_amd/csrc/kernels/common.hpp",
                   "hybrid_sliding_window_decode_amd/csrc/hswd.hip"]
-COUNTERS = os.path.join(ROOT, "profiles", "attn_step28_64x4096_bf16_counters.json")
-FULL_KERNEL = "hswd::attn_kernel<256, 2, false, 1>(...)"
 
 
-def measured_traffic():
+def counters_path(kv):
+    return os.path.join(ROOT, "profiles", "attn_step28_64x4096_%s_counters.json" % kv)
+
+
+def full_kernel(kv):
+    """rocprofv3's name of the full-layer fused step kernel for a cache type."""
+    return "hswd::attn_kernel<256, %d, false, 1>(...)" % {"bf16": 2, "fp8": 3}[kv]
+
+
+def measured_traffic(kv):
     """HBM bytes per full-layer launch from the committed FETCH_SIZE /
     WRITE_SIZE counter runs (scaled by a 1 GiB copy), or None when the kernel
     sources have changed since those counters were taken."""
     import hashlib
     try:
-        rec = json.load(open(COUNTERS))
+        rec = json.load(open(counters_path(kv)))
     except (OSError, ValueError):
         return None
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, p), "rb").read())
-    if rec.get("source_sha256") != h.hexdigest() or FULL_KERNEL not in rec["kernels"]:
+    if rec.get("source_sha256") != h.hexdigest() or full_kernel(kv) not in rec["kernels"]:
         return None
-    k = rec["kernels"][FULL_KERNEL]
+    k = rec["kernels"][full_kernel(kv)]
     return int(round(k["read_bytes"] + k["write_bytes"]))
 
 
@@ -123,23 +130,21 @@ def single_layer(args, np, torch, hswd, inputs, dev):
     ws = hswd.workspace(desc, ring, mp, device=dev)
     out = torch.empty_like(sets[0]["q"])
 
-    def run(t):
-        hswd.layer_step(t["q"], t["k"], t["v"], t["gate"], t["k_cache"], t["v_cache"], t["pos"],
-                        ring, spec.rot, spec.theta, ws, max_pos=mp, out=out, desc=desc)
+    calls = [hswd.bind_layer_step(t["q"], t["k"], t["v"], t["gate"], t["k_cache"], t["v_cache"],
+                                  t["pos"], ring, spec.rot, spec.theta, ws, max_pos=mp, out=out,
+                                  desc=desc) for t in sets]
     for i in range(max(args.warmup, 1) * n_sets):
-        run(sets[i % n_sets])
+        calls[i % n_sets]()
     torch.cuda.synchronize()
     assert hswd.check_errors(ws) == 0
     reps = max(args.steps, n_sets)
     stream = torch.cuda.current_stream()
-    evs = []
-    for i in range(reps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for i, (e0, e1) in enumerate(evs):
         e0.record(stream)
-        run(sets[i % n_sets])
+        calls[i % n_sets]()
         e1.record(stream)
-        evs.append((e0, e1))
     torch.cuda.synchronize()
     us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
     med = float(np.median(us))
@@ -216,23 +221,23 @@ def main():
             t["q_rot"] = torch.empty_like(t["q"])
             t["k_rot"] = torch.empty_like(t["k"])
             t["o"] = torch.empty_like(t["q"])
+        elif args.gate == "proj":
+            t["call"] = hswd.bind_layer_step_gproj(
+                t["q"], t["k"], t["v"], t["gx"], t["gw"], t["k_cache"], t["v_cache"], t["pos"],
+                not full, spec.rot, spec.theta, t["ws"], max_pos=CTX, out=t["out"], desc=desc)
+        else:
+            t["call"] = hswd.bind_layer_step(
+                t["q"], t["k"], t["v"], t["gate"], t["k_cache"], t["v_cache"], t["pos"],
+                not full, spec.rot, spec.theta, t["ws"], max_pos=CTX, out=t["out"], desc=desc)
         layers.append(t)
     torch.cuda.synchronize()
 
     def run_layer(t):
-        if args.mode == "fused" and args.gate == "proj":
-            hswd.layer_step_gproj(t["q"], t["k"], t["v"], t["gx"], t["gw"], t["k_cache"],
-                                  t["v_cache"], t["pos"], t["ring"], t["spec"].rot,
-                                  t["spec"].theta, t["ws"], max_pos=CTX, out=t["out"],
-                                  desc=t["desc"])
+        if args.mode == "fused":            # one launch, arguments marshalled once
+            t["call"]()
             return
         if args.gate == "proj":
             hswd.gate_proj(t["gx"], t["gw"], out=t["gate"])
-        if args.mode == "fused":
-            hswd.layer_step(t["q"], t["k"], t["v"], t["gate"], t["k_cache"], t["v_cache"],
-                            t["pos"], t["ring"], t["spec"].rot, t["spec"].theta, t["ws"],
-                            max_pos=CTX, out=t["out"], desc=t["desc"])
-            return
         t["q_rot"].copy_(t["q"])
         t["k_rot"].copy_(t["k"])
         hswd.rope_apply(t["q_rot"], t["k_rot"], t["pos"], t["spec"].rot, t["spec"].theta)
@@ -264,6 +269,37 @@ def main():
         assert flags == 0, "error flags %d" % flags
     gpu_out = {l: layers[l]["out"].cpu().numpy() for l in sample}
 
+    # ---- warmup, then the timed region
+    for _ in range(args.warmup):
+        for t in layers:
+            run_layer(t)
+    torch.cuda.synchronize()
+
+    n_full = sum(1 for l in range(LAYERS) if is_full(l))
+    full_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps * n_full)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    ev = iter(full_ev)
+    for _ in range(args.steps):
+        for l, t in enumerate(layers):
+            if is_full(l):
+                e0, e1 = next(ev)
+                e0.record(stream)
+                run_layer(t)
+                e1.record(stream)
+            else:
+                run_layer(t)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    # ---- parity of the first pass (outputs kept above) and the CPU oracle
+    # baseline, after the timed region so the host's OpenMP threads cannot
+    # delay the launches being timed
     cpu = None
     parity = {}
     if not args.no_cpu_baseline:
@@ -308,33 +344,6 @@ def main():
                           "extrapolated to 21 sliding + 7 full layers; %d OpenMP threads"
                           % (t_sl, t_fu, threads))}
 
-    # ---- warmup, then the timed region
-    for _ in range(args.warmup):
-        for t in layers:
-            run_layer(t)
-    torch.cuda.synchronize()
-
-    full_ev = []
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        for l, t in enumerate(layers):
-            if is_full(l):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                run_layer(t)
-                e1.record(stream)
-                full_ev.append((e0, e1))
-            else:
-                run_layer(t)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-
     ms_step = t_start.elapsed_time(t_end) / args.steps
     full_us = float(np.mean([a.elapsed_time(b) for a, b in full_ev])) * 1e3
     step_bytes = 21 * layer_bytes("sliding", elt=elt) + 7 * layer_bytes("full", elt=elt)
@@ -367,7 +376,7 @@ def main():
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic() if kv == "bf16" else None,
+                     "traffic": measured_traffic(kv),
                      "kernel": "attn_kernel<256, %s, append, step> (full layer, one launch)" % kv,
                      "bytes_per_launch": full_bytes},
         "cpu_baseline": cpu,

@@ -286,20 +286,51 @@ def head_gate(o, gate, out=None):
     return out
 
 
-def layer_step(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, ws, max_pos=0,
-               out=None, desc=None):
-    """Whole layer step in one launch; returns the gated output [B,H,D]."""
+class BoundCall:
+    """One library entry point with its arguments marshalled once: calling it
+    launches on the stream that was current when it was bound and returns the
+    output tensor.  For loops that issue the same launch many times (a decode
+    step per layer), so each launch costs one foreign call.  The tensors it
+    was bound with must stay alive and unmoved while it is used."""
+
+    def __init__(self, name, fn, args, out):
+        self.name, self._fn, self._args, self.out = name, fn, args, out
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != 0:
+            raise HswdError(self.name, status)
+        return self.out
+
+
+def _layer_step_args(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, ws, max_pos,
+                     out, desc):
     d = _attn_args(q, k, v, k_cache, v_cache, pos, desc)
     if gate is not None:
         _need(gate, "gate", torch.float32, (q.shape[0], q.shape[1]))
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", torch.float32, q.shape)
     _need(ws, "ws")
-    _check("hswd_layer_step", lib().hswd_layer_step(
-        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(k_cache), _ptr(v_cache),
-        _ptr(pos), int(ring), int(rot_dim), float(theta), int(max_pos), ctypes.byref(d),
-        _ptr(ws), ws.numel(), _stream()))
+    return out, (_ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(k_cache),
+                 _ptr(v_cache), _ptr(pos), int(ring), int(rot_dim), float(theta), int(max_pos),
+                 ctypes.byref(d), _ptr(ws), ws.numel(), _stream())
+
+
+def layer_step(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, ws, max_pos=0,
+               out=None, desc=None):
+    """Whole layer step in one launch; returns the gated output [B,H,D]."""
+    out, args = _layer_step_args(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta,
+                                 ws, max_pos, out, desc)
+    _check("hswd_layer_step", lib().hswd_layer_step(*args))
     return out
+
+
+def bind_layer_step(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, ws, max_pos=0,
+                    out=None, desc=None):
+    """layer_step with its arguments checked and marshalled once (BoundCall)."""
+    out, args = _layer_step_args(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta,
+                                 ws, max_pos, out, desc)
+    return BoundCall("hswd_layer_step", lib().hswd_layer_step, args, out)
 
 
 def gate_proj(x, w_g, out=None):
@@ -317,9 +348,8 @@ def gate_proj(x, w_g, out=None):
     return out
 
 
-def layer_step_gproj(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim, theta, ws,
-                     max_pos=0, out=None, desc=None):
-    """Layer step with the gate logits projected from x [B, hidden] by w_g [H, hidden]."""
+def _layer_step_gproj_args(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim, theta, ws,
+                           max_pos, out, desc):
     d = _attn_args(q, k, v, k_cache, v_cache, pos, desc)
     B, H = q.shape[0], q.shape[1]
     _need(x, "x", torch.float32)
@@ -329,11 +359,26 @@ def layer_step_gproj(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim, thet
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", torch.float32, q.shape)
     _need(ws, "ws")
-    _check("hswd_layer_step_gproj", lib().hswd_layer_step_gproj(
-        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w_g), hidden, _ptr(k_cache),
-        _ptr(v_cache), _ptr(pos), int(ring), int(rot_dim), float(theta), int(max_pos),
-        ctypes.byref(d), _ptr(ws), ws.numel(), _stream()))
+    return out, (_ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w_g), hidden,
+                 _ptr(k_cache), _ptr(v_cache), _ptr(pos), int(ring), int(rot_dim), float(theta),
+                 int(max_pos), ctypes.byref(d), _ptr(ws), ws.numel(), _stream())
+
+
+def layer_step_gproj(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim, theta, ws,
+                     max_pos=0, out=None, desc=None):
+    """Layer step with the gate logits projected from x [B, hidden] by w_g [H, hidden]."""
+    out, args = _layer_step_gproj_args(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim,
+                                       theta, ws, max_pos, out, desc)
+    _check("hswd_layer_step_gproj", lib().hswd_layer_step_gproj(*args))
     return out
+
+
+def bind_layer_step_gproj(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim, theta, ws,
+                          max_pos=0, out=None, desc=None):
+    """layer_step_gproj with its arguments checked and marshalled once (BoundCall)."""
+    out, args = _layer_step_gproj_args(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim,
+                                       theta, ws, max_pos, out, desc)
+    return BoundCall("hswd_layer_step_gproj", lib().hswd_layer_step_gproj, args, out)
 
 
 def check_errors(ws):

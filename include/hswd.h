@@ -105,12 +105,14 @@ typedef struct {
                                the valid keys are cut into chunks of this many,
                                each chunk's softmax partial is formed alone and
                                the partials are folded in chunk order.  0 =
-                               library default from the cache length only:
-                               2^floor(log2(n_slots/32)) clamped to [128, 512]
-                               (and at least 4 tiles).  Else a multiple of 64
-                               (D = 256, 16-bit cache), 32 (D = 256, f32) or of
-                               4 tiles otherwise.  Results depend on it; never
-                               on the batch. */
+                               library default from the cache length and the
+                               element type only: 2^floor(log2(n_slots/32))
+                               clamped to [128, 512], and at least 4 quanta.
+                               Else a multiple of the quantum Q = 32768 /
+                               (head_dim * element bytes) keys (4 waves, one
+                               8-load tile each): 64 for D = 256 and a 16-bit
+                               cache, 32 for f32, 128 for fp8.  Results depend
+                               on it; never on the batch. */
     int32_t chunks_per_workgroup; /* work split only, never the bits: how many
                                consecutive chunks one workgroup streams.  0 =
                                library choice (from B and the CU count). */

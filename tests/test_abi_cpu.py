@@ -49,15 +49,21 @@ def test_version_and_status_strings():
 def test_workspace_and_splits():
     L = binding.lib()
     d = desc()
-    # default chunk: 128 keys up to 8191 slots, 256 below 16384, then 512
-    assert hswd.num_splits(d, 1) == 4
-    assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 32
+    # default chunk: 2^floor(log2(n_slots/32)) in [128, 512], at least four
+    # quanta (quantum = 32768 / (D * element bytes) keys): 256 keys for a
+    # bf16 ring or 4097-row cache, 512 from 16384 rows on
+    assert hswd.num_splits(d, 1) == 2
+    assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 16
     assert hswd.num_splits(desc(n_slots=8192), 0, 8191) == 32
     assert hswd.num_splits(desc(n_slots=16385), 0, 16384) == 32
     assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 256
-    assert hswd.num_splits(desc(n_slots=4097, head_dim=64), 0, 4096) == 16
+    assert hswd.num_splits(desc(n_slots=4097, head_dim=64), 0, 4096) == 4       # Q = 256
+    assert hswd.num_splits(desc(n_slots=4097, kv_dtype=0), 0, 4096) == 32       # f32: Q = 32
+    assert hswd.num_splits(desc(n_slots=4097, kv_dtype=3), 0, 4096) == 8        # fp8: Q = 128
+    assert hswd.num_splits(desc(kv_dtype=3), 1, 0) == 1
     assert hswd.num_splits(desc(n_slots=4097, keys_per_split=1024), 0, 4096) == 4
-    assert hswd.num_splits(desc(n_slots=4097, chunks_per_workgroup=3), 0, 4096) == 32
+    assert hswd.num_splits(desc(n_slots=4097, keys_per_split=128), 0, 4096) == 32
+    assert hswd.num_splits(desc(n_slots=4097, chunks_per_workgroup=3), 0, 4096) == 16
     # splits never depend on the batch
     assert hswd.num_splits(desc(batch=1, n_slots=4097), 0, 4096) == \
         hswd.num_splits(desc(batch=64, n_slots=4097), 0, 4096)

@@ -345,3 +345,35 @@ def test_work_split_never_changes_bits(kind, dtype, S, kps):
         assert np.array_equal(caches[0].view(np.uint8), caches[i].view(np.uint8)), i
     ref = oracle_step(x)
     assert_parity(outs[0], ref["o_pre"], x, "work split")
+
+
+@pytest.mark.parametrize("kind,dtype", [("sliding", "bf16"), ("full", "fp8")])
+def test_bound_layer_step_matches_plain_call(kind, dtype):
+    """bind_layer_step marshals once and launches the same entry point: the
+    output and the written entry equal those of layer_step bit for bit, on
+    each of two launches."""
+    B = 5
+    spec = spec_for(kind, B, dtype, S=1500)
+    hi = 3000 if kind == "sliding" else 1499
+    x = inputs.make_step(spec, inputs.ragged_positions(B, 1, hi, seed=19), seed=20)
+    ring = kind == "sliding"
+    mp = int(x.pos.max())
+    d1, d2 = to_dev(x), to_dev(x)
+    desc1 = hswd.make_desc(d1["k_cache"], kv_scale=d1["kv_scale"])
+    desc2 = hswd.make_desc(d2["k_cache"], kv_scale=d2["kv_scale"])
+    ws1, ws2 = hswd.workspace(desc1, ring, mp), hswd.workspace(desc2, ring, mp)
+    say("bound layer step %s %s" % (kind, dtype))
+    call = hswd.bind_layer_step(d2["q"], d2["k"], d2["v"], d2["gate"], d2["k_cache"],
+                                d2["v_cache"], d2["pos"], ring, spec.rot, spec.theta, ws2,
+                                max_pos=mp, desc=desc2)
+    # two launches each; in a ring past its capacity the first overwrites an
+    # attended slot, so both sides advance together
+    for _ in range(2):
+        ref = hswd.layer_step(d1["q"], d1["k"], d1["v"], d1["gate"], d1["k_cache"],
+                              d1["v_cache"], d1["pos"], ring, spec.rot, spec.theta, ws1,
+                              max_pos=mp, desc=desc1)
+        got = call()
+        assert np.array_equal(got.cpu().numpy(), ref.cpu().numpy())
+        assert np.array_equal(cache_to_host(d2["k_cache"]), cache_to_host(d1["k_cache"]))
+        assert np.array_equal(cache_to_host(d2["v_cache"]), cache_to_host(d1["v_cache"]))
+    assert hswd.check_errors(ws2) == 0
