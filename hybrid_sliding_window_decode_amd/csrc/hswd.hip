@@ -10,6 +10,7 @@
 #include <atomic>
 
 #include "../../include/hswd.h"
+#include "attn_launch.hpp"
 #include "kernels/attn.hpp"
 #include "kernels/small.hpp"
 
@@ -116,25 +117,15 @@ WsLayout ws_layout(const hswd_attn_desc* d, int n_chunk) {
     return L;
 }
 
-template <int D, int DT, bool RING, int MODE>
-void launch_attn(const AttnParams& P, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((attn_kernel<D, DT, RING, MODE>), dim3(grid), dim3(kAttnThreads), 0, st, P);
-}
-
+// Kernel launch for the descriptor's group size G = H / Hkv (1, 2 or 4).
 template <int MODE>
 int32_t dispatch_attn(const AttnParams& P, int D, int DT, int grid, hipStream_t st) {
-#define HSWD_CASE(DV, TV)                                                            \
-    if (D == DV && DT == TV) {                                                       \
-        if (P.ring) launch_attn<DV, TV, true, MODE>(P, grid, st);                    \
-        else launch_attn<DV, TV, false, MODE>(P, grid, st);                          \
-        return launch_status();                                                      \
+    switch (P.H / P.Hkv) {
+        case 1: return launch_attn_group<1>(P, MODE, D, DT, grid, st);
+        case 2: return launch_attn_group<2>(P, MODE, D, DT, grid, st);
+        case 4: return launch_attn_group<4>(P, MODE, D, DT, grid, st);
+        default: return HSWD_ERR_UNSUPPORTED;
     }
-    HSWD_CASE(256, kBF16) HSWD_CASE(256, kF16) HSWD_CASE(256, kF32)
-    HSWD_CASE(128, kBF16) HSWD_CASE(128, kF16) HSWD_CASE(128, kF32)
-    HSWD_CASE(64, kBF16) HSWD_CASE(64, kF16) HSWD_CASE(64, kF32)
-    HSWD_CASE(256, kFP8) HSWD_CASE(128, kFP8)
-#undef HSWD_CASE
-    return HSWD_ERR_UNSUPPORTED;
 }
 
 // Shared argument checks and parameter set-up of the attention entries.
@@ -142,7 +133,12 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
                    void* ws, size_t ws_bytes, bool need_ws) {
     int32_t st = desc_check(d);
     if (st != HSWD_OK) return st;
-    if (d->n_heads != d->n_kv_heads) return HSWD_ERR_UNSUPPORTED;
+    const int group = d->n_heads / d->n_kv_heads;       // query heads per kv head
+    if (group != 1 && group != 2 && group != 4) return HSWD_ERR_UNSUPPORTED;
+    // grouped kernels: 16-bit caches, head dim 128 or 256 (G query vectors and
+    // accumulators per lane must fit beside the tiles in 256 VGPRs)
+    if (group > 1 && ((d->kv_dtype != HSWD_BF16 && d->kv_dtype != HSWD_F16) || d->head_dim < 128))
+        return HSWD_ERR_UNSUPPORTED;
     if (!ring) {
         if (max_pos < 0) return HSWD_ERR_INVALID;
         if ((long)max_pos + 1 > d->n_slots) return HSWD_ERR_CAPACITY;

@@ -91,19 +91,23 @@ struct AttnParams {
     float qscale;            // softmax scale * log2(e)
 };
 
-template <int D, int DT>
+// Tile geometry.  G query heads per kv head keep G query vectors and G
+// accumulators per lane, so a grouped kernel halves its tile (4 loads of K
+// and of V instead of 8) to stay within 256 VGPRs (2 waves per SIMD).
+template <int D, int DT, int G = 1>
 struct AttnGeo {
     static constexpr int EB = elt_bytes<DT>();        // element bytes
     static constexpr int EPC = 16 / EB;               // elements per 16-byte chunk
     static constexpr int LPR = D / EPC;               // lanes per cache row
     static constexpr int RPI = kWave / LPR;           // rows per wave-wide load
-    static constexpr int NL = 8;                      // loads per tile (K and V each)
+    static constexpr int NL = G == 1 ? 8 : 4;         // loads per tile (K and V each)
     static constexpr int KT = NL * RPI;               // keys per wave tile
     static constexpr int STEP = LPR / NL;             // lane stride between reduced keys
     static_assert(LPR >= NL && LPR <= kWave && kWave % LPR == 0, "geometry");
 };
 
-// Keys per chunk must be a multiple of this: a whole tile for every wave.
+// Keys per chunk must be a multiple of this: a whole 8-load tile for every
+// wave (the grouped kernels' 4-load tiles divide it).
 constexpr int chunk_quantum(int D, int DT) {
     return kAttnWaves * 8 * (kWave / (D / (16 / (DT == kF32 ? 4 : (DT == kFP8 ? 1 : 2)))));
 }
@@ -183,18 +187,44 @@ __device__ __forceinline__ float transposed_reduce8(const float (&v)[8], int lan
     return c;
 }
 
-template <int D, int DT, bool RING, int MODE>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
-    using G = AttnGeo<D, DT>;
-    using S = typename Storage<DT>::type;
-    constexpr int EPC = G::EPC, LPR = G::LPR, RPI = G::RPI, NL = G::NL, KT = G::KT;
-    constexpr float kLn2 = 0.69314718055994531f;
+// The same for four per-load partials: on exit this lane holds the full sum
+// for load ((lane % LPR) / (LPR / 4)).
+template <int LPR>
+__device__ __forceinline__ float transposed_reduce4(const float (&v)[4], int lane) {
+    constexpr int M1 = LPR / 2, M2 = LPR / 4;
+    bool u = (lane & M1) != 0;
+    const float a0 = tstage<M1>(v[0], v[2], u), a1 = tstage<M1>(v[1], v[3], u);
+    u = (lane & M2) != 0;
+    float c = tstage<M2>(a0, a1, u);
+#pragma unroll
+    for (int m = M2 / 2; m >= 1; m >>= 1) c = xor_sum_rt(c, m);
+    return c;
+}
 
-    __shared__ float sm_q[D];
-    __shared__ float sm_o[2][4][kAttnWaves][D];       // wave chunk partials, by flush parity
-    __shared__ float sm_m[2][4][kAttnWaves], sm_l[2][4][kAttnWaves];
-    __shared__ float sm_dot[kAttnWaves];
-    __shared__ float sm_gl[kAttnWaves];
+// Chunk-partial slots per flush buffer: the LDS stash holds kStash chunks
+// of every query head of the group, 32 KiB in all.
+template <int G>
+constexpr int stash_slots() { return G == 1 ? 4 : (G == 2 ? 2 : 1); }
+
+// G = H / Hkv query heads share each kv head (grouped-query attention by
+// reshaping the query, the talker commit): one workgroup scores all G of
+// them against every K/V tile it loads, so the cache is read once per group.
+// Two workgroups of 4 waves per CU (2 waves per SIMD): at most 256 VGPRs.
+template <int D, int DT, bool RING, int MODE, int G>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_kernel(AttnParams P) {
+    using Geo = AttnGeo<D, DT, G>;
+    using S = typename Storage<DT>::type;
+    constexpr int EPC = Geo::EPC, LPR = Geo::LPR, RPI = Geo::RPI, NL = Geo::NL, KT = Geo::KT;
+    constexpr float kLn2 = 0.69314718055994531f;
+    constexpr int kStash = stash_slots<G>();
+    static_assert(G == 1 || G == 2 || G == 4, "query heads per kv head");
+
+    __shared__ float sm_q[G][D];
+    __shared__ float sm_o[2][kStash][G][kAttnWaves][D];   // wave chunk partials, by flush parity
+    __shared__ float sm_m[2][kStash][G][kAttnWaves], sm_l[2][kStash][G][kAttnWaves];
+    __shared__ float sm_dot[G][kAttnWaves];
+    __shared__ float sm_gl[G][kAttnWaves];
     __shared__ int sm_last;
 
     const int tid = threadIdx.x;
@@ -221,8 +251,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     }
     const int b = pair / P.Hkv;
     const int g = pair % P.Hkv;
-    const int h = g;                       // one query head per kv head
-    const int bh = b * P.H + h;
+    const int bh0 = b * P.H + g * G;       // first query head of the group
     const int p = P.pos[b];
     const float kscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[g] : 1.f;
     const float vscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[P.Hkv + g] : 1.f;
@@ -255,17 +284,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
 
     const int c = lane % LPR;       // 16-byte chunk of the row this lane reads
     const int r = lane / LPR;       // row within a wave-wide load
-    float qs[EPC];                  // this lane's query dims, set after the prologue
+    float qs[G][EPC];               // this lane's query dims, set after the prologue
 
     const S* kbase = reinterpret_cast<const S*>(P.kc) + (size_t)pair * P.S * D + c * EPC;
     const S* vbase = reinterpret_cast<const S*>(P.vc) + (size_t)pair * P.S * D + c * EPC;
 
-    float m_run = -INFINITY;
-    float l_lane = 0.f;
-    float o_acc[EPC];
+    float m_run[G], l_lane[G], o_acc[G][EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) o_acc[e] = 0.f;
-    Fold run;                       // folded chunk partials (wpp == 1)
+    for (int hh = 0; hh < G; ++hh) {
+        m_run[hh] = -INFINITY;
+        l_lane[hh] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) o_acc[hh][e] = 0.f;
+    }
+    Fold run[G];                    // folded chunk partials (wpp == 1)
 
     u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
 
@@ -275,10 +307,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     // (a prefetch the loop never scores) clamps the same way, onto row 0 of
     // the block when it has no valid row at all, so every load stays inside
     // this (stream, kv head)'s cache block and may be issued unconditionally.
-    auto item_chunk = [&](int j) { return j < n_full_items ? c_begin + j / TPW : c_full; };
-    auto item_tile = [&](int j) { return j < n_full_items ? j % TPW : j - n_full_items; };
+    auto item_chunk = [&](int j) __attribute__((always_inline)) { return j < n_full_items ? c_begin + j / TPW : c_full; };
+    auto item_tile = [&](int j) __attribute__((always_inline)) { return j < n_full_items ? j % TPW : j - n_full_items; };
 
-    auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int j) {
+    auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int j) __attribute__((always_inline)) {
         const int ch = item_chunk(j);
         const int jlast = max(min((ch + 1) * P.K, nv), 1) - 1;
         const int base = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT + r;
@@ -294,48 +326,64 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         }
     };
 
-    auto compute_tile = [&](const u32x4 (&kt)[NL], const u32x4 (&vt)[NL], int j) {
+    auto compute_tile = [&](const u32x4 (&kt)[NL], const u32x4 (&vt)[NL], int j) __attribute__((always_inline)) {
         const int ch = item_chunk(j);
         const int jend = min((ch + 1) * P.K, nv);
         const int tile0 = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT;
-        float part[NL];
+        float s[G];
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            float kf[EPC];
-            unpack16<DT>(kt[i], kf);
-            float acc = 0.f;
+        for (int hh = 0; hh < G; ++hh) {
+            float part[NL];
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) acc = fmaf(qs[e], kf[e], acc);
-            part[i] = acc;
+            for (int i = 0; i < NL; ++i) {
+                float kf[EPC];
+                unpack16<DT>(kt[i], kf);
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc = fmaf(qs[hh][e], kf[e], acc);
+                part[i] = acc;
+            }
+            if constexpr (NL == 8) s[hh] = transposed_reduce8<LPR>(part, lane);
+            else s[hh] = transposed_reduce4<LPR>(part, lane);
         }
-        static_assert(NL == 8, "tile of eight loads");
-        float s = transposed_reduce8<LPR>(part, lane);
-        const int ki = (lane % LPR) / G::STEP;          // load index of this lane's key
+        const int ki = (lane % LPR) / Geo::STEP;        // load index of this lane's key
         const int key = tile0 + ki * RPI + r;
-        s = key < jend ? s : -INFINITY;
-        // tile max over the distinct keys (lane bits >= STEP)
-        float mx = s;
+        const bool valid = key < jend;
+        // tile max over the distinct keys (lane bits >= STEP), per head
+        float mx[G];
 #pragma unroll
-        for (int m = G::STEP; m < kWave; m <<= 1) mx = xor_max_rt(mx, m);
-        if (mx == -INFINITY) return;                    // nothing valid in this tile
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
-        const float pr = fast_exp2(s - m_new);
-        m_run = m_new;
-        l_lane = l_lane * alpha + ((lane & (G::STEP - 1)) == 0 ? pr : 0.f);
-        // every key's probability to the lanes of its row, all requests out
-        // before the first is used
-        float pk[NL];
+        for (int hh = 0; hh < G; ++hh) {
+            s[hh] = valid ? s[hh] : -INFINITY;
+            mx[hh] = s[hh];
 #pragma unroll
-        for (int i = 0; i < NL; ++i) pk[i] = lane_value(pr, r * LPR + i * G::STEP);
+            for (int m = Geo::STEP; m < kWave; m <<= 1) mx[hh] = xor_max_rt(mx[hh], m);
+        }
+        if (mx[0] == -INFINITY) return;                 // nothing valid in this tile
+        float pr[G];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) o_acc[e] *= alpha;
+        for (int hh = 0; hh < G; ++hh) {
+            const float m_new = fmaxf(m_run[hh], mx[hh]);
+            const float alpha = fast_exp2(m_run[hh] - m_new);
+            pr[hh] = fast_exp2(s[hh] - m_new);
+            m_run[hh] = m_new;
+            l_lane[hh] = l_lane[hh] * alpha + ((lane & (Geo::STEP - 1)) == 0 ? pr[hh] : 0.f);
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            float vf[EPC];
-            unpack16<DT>(vt[i], vf);
+            for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= alpha;
+        }
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) o_acc[e] = fmaf(pk[i], vf[e], o_acc[e]);
+        for (int hh = 0; hh < G; ++hh) {
+            // every key's probability to the lanes of its row, all requests
+            // out before the first is used
+            float pk[NL];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) pk[i] = lane_value(pr[hh], r * LPR + i * Geo::STEP);
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                float vf[EPC];
+                unpack16<DT>(vt[i], vf);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pk[i], vf[e], o_acc[hh][e]);
+            }
         }
     };
 
@@ -348,86 +396,102 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     // barrier of the flush in between; deferring the barrier keeps small
     // chunks cheap, and the arithmetic and its order are those of a barrier
     // per chunk.
-    constexpr int kStash = 4;
     int n_st = 0, st_first = 0, n_flush = 0;
 
-    auto flush = [&]() {
+    auto flush = [&]() __attribute__((always_inline)) {
         const int buf = n_flush & 1;
         ++n_flush;
         __syncthreads();
         for (int s = 0; s < n_st; ++s) {
             const int ch = st_first + s;
-            const float Mc = lds_max<kAttnWaves>(sm_m[buf][s]);
-            float Lc = 0.f, Oc = 0.f;
-            if (Mc != -INFINITY) {
 #pragma unroll
-                for (int w = 0; w < kAttnWaves; ++w) {
-                    const float a = fast_exp2(sm_m[buf][s][w] - Mc);
-                    Lc = fmaf(sm_l[buf][s][w], a, Lc);
-                    if (t < D) Oc = fmaf(sm_o[buf][s][w][t], a, Oc);
+            for (int hh = 0; hh < G; ++hh) {
+                const float Mc = lds_max<kAttnWaves>(sm_m[buf][s][hh]);
+                float Lc = 0.f, Oc = 0.f;
+                if (Mc != -INFINITY) {
+#pragma unroll
+                    for (int w = 0; w < kAttnWaves; ++w) {
+                        const float a = fast_exp2(sm_m[buf][s][hh][w] - Mc);
+                        Lc = fmaf(sm_l[buf][s][hh][w], a, Lc);
+                        if (t < D) Oc = fmaf(sm_o[buf][s][hh][w][t], a, Oc);
+                    }
                 }
-            }
-            const size_t idx = (size_t)bh * P.n_chunk + ch;
-            if (MODE == kModePartials) {
-                if (t < D) P.part_o[idx * D + t] = Oc * vscale;
-                if (tid == 0) {
-                    P.part_ml[idx * 2 + 0] = Mc == -INFINITY ? -INFINITY : Mc * kLn2;
-                    P.part_ml[idx * 2 + 1] = Lc;
-                }
-            } else if (P.wpp == 1) {
-                run.add(Mc, Lc, Oc);
-            } else {
-                if (t < D) st_agent(P.part_o + idx * D + t, Oc);
-                if (tid == 0) {
-                    st_agent(P.part_ml + idx * 2 + 0, Mc);
-                    st_agent(P.part_ml + idx * 2 + 1, Lc);
+                const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
+                if (MODE == kModePartials) {
+                    if (t < D) P.part_o[idx * D + t] = Oc * vscale;
+                    if (tid == 0) {
+                        P.part_ml[idx * 2 + 0] = Mc == -INFINITY ? -INFINITY : Mc * kLn2;
+                        P.part_ml[idx * 2 + 1] = Lc;
+                    }
+                } else if (P.wpp == 1) {
+                    run[hh].add(Mc, Lc, Oc);
+                } else {
+                    if (t < D) st_agent(P.part_o + idx * D + t, Oc);
+                    if (tid == 0) {
+                        st_agent(P.part_ml + idx * 2 + 0, Mc);
+                        st_agent(P.part_ml + idx * 2 + 1, Lc);
+                    }
                 }
             }
         }
         n_st = 0;
     };
 
-    auto end_chunk = [&](int ch) {
-        const float l_w = wave_sum(l_lane);
+    auto end_chunk = [&](int ch) __attribute__((always_inline)) {
+        float l_w[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) l_w[hh] = wave_sum(l_lane[hh]);
 #pragma unroll
         for (int m = LPR; m < kWave; m <<= 1) {
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) o_acc[e] = xor_sum_rt(o_acc[e], m);
+            for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o_acc[hh][e] = xor_sum_rt(o_acc[hh][e], m);
+            }
         }
         const int buf = n_flush & 1;
-        if (r == 0) {
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) sm_o[buf][n_st][wid][c * EPC + e] = o_acc[e];
-        }
-        if (lane == 0) {
-            sm_m[buf][n_st][wid] = m_run;
-            sm_l[buf][n_st][wid] = l_w;
+        for (int hh = 0; hh < G; ++hh) {
+            if (r == 0) {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) sm_o[buf][n_st][hh][wid][c * EPC + e] = o_acc[hh][e];
+            }
+            if (lane == 0) {
+                sm_m[buf][n_st][hh][wid] = m_run[hh];
+                sm_l[buf][n_st][hh][wid] = l_w[hh];
+            }
+            m_run[hh] = -INFINITY;
+            l_lane[hh] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) o_acc[hh][e] = 0.f;
         }
         if (n_st == 0) st_first = ch;
         ++n_st;
-        m_run = -INFINITY;
-        l_lane = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) o_acc[e] = 0.f;
         if (n_st == kStash) flush();
     };
 
-    // Per-stream inputs first: this thread's query dim and its RoPE partner,
-    // and for the new entry the same of the key plus the value (threads past
-    // D read dim 0 and drop it).  Vector loads retire in order, so the
-    // prologue waits for these alone; the first two tiles, requested next,
-    // stay in flight under its double-precision RoPE.  Those two requests
-    // are unconditional (clamped rows, see load_tile): a load under a branch
-    // would make the compiler's wait counts at the join assume the branch
-    // was not taken, and the prologue would wait for the tiles too.
+    // Per-stream inputs first: this thread's query dim and its RoPE partner
+    // for every head of the group, and for the new entry the same of the key
+    // plus the value (threads past D read dim 0 and drop it).  Vector loads
+    // retire in order, so the prologue waits for these alone; the first two
+    // tiles, requested next, stay in flight under its double-precision RoPE.
+    // Those two requests are unconditional (clamped rows, see load_tile): a
+    // load under a branch would make the compiler's wait counts at the join
+    // assume the branch was not taken, and the prologue would wait for the
+    // tiles too.
     const bool has_new = MODE != kModePartials;
     const int td = t < D ? t : 0;
     const bool rotated = MODE == kModeStep && td < P.rot;
     const int tp = MODE == kModeStep ? rope_partner(td, P.rot) : td;
-    const float* qv = P.q + (size_t)bh * D;
+    const float* qv = P.q + (size_t)bh0 * D;
     const float* kv = P.k + (size_t)pair * D;
     const float* vv = P.v + (size_t)pair * D;
-    const float q_t = qv[td], q_p = qv[tp];
+    float q_t[G], q_p[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        q_t[hh] = qv[(size_t)hh * D + td];
+        q_p[hh] = qv[(size_t)hh * D + tp];
+    }
     float k_t = 0.f, k_p = 0.f, v_t = 0.f;
     if (has_new) {
         k_t = kv[td];
@@ -435,59 +499,79 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         v_t = vv[td];
     }
     const bool gproj = MODE == kModeStep && P.gx != nullptr;
-    const float glogit = MODE == kModeStep && !gproj && P.gate != nullptr ? P.gate[bh] : 0.f;
+    float glogit[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+        glogit[hh] = MODE == kModeStep && !gproj && P.gate != nullptr ? P.gate[bh0 + hh] : 0.f;
 
     load_tile(kA, vA, 0);
     load_tile(kB, vB, 1);
 
-    // Query and new key rotated in-kernel for the fused step (one angle for
-    // both); the query scaled by scale*log2(e) and, for an fp8 cache, by the
-    // head's K scale (cached keys are scale * code, so the scale moves onto
-    // the query once).
-    float q_r = q_t, k_r = k_t;
-    if (rotated) {
+    // Query heads and new key rotated in-kernel for the fused step (one angle
+    // for all); each query scaled by scale*log2(e) and, for an fp8 cache, by
+    // the head's K scale (cached keys are scale * code, so the scale moves
+    // onto the query once).
+    float k_r = k_t;
+    float qsc[G];
+    {
+        double cs = 1.0, sn = 0.0;
         const int half = P.rot >> 1;
-        double cs, sn;
-        rope_cs(td < half ? td : td - half, P.rot, P.log2_theta, p, cs, sn);
-        q_r = rope_rotate(q_t, q_p, td < half, cs, sn);
-        k_r = rope_rotate(k_t, k_p, td < half, cs, sn);
+        if (rotated) {
+            rope_cs(td < half ? td : td - half, P.rot, P.log2_theta, p, cs, sn);
+            k_r = rope_rotate(k_t, k_p, td < half, cs, sn);
+        }
+        const float qmul = P.qscale * kscale;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const float q_r = rotated ? rope_rotate(q_t[hh], q_p[hh], td < half, cs, sn) : q_t[hh];
+            qsc[hh] = q_r * qmul;
+            if (t < D) sm_q[hh][t] = qsc[hh];
+        }
     }
-    const float qsc = q_r * (P.qscale * kscale);
-    if (t < D) sm_q[t] = qsc;
 
     // The new entry, joined in score space: k_hat, v_hat are the rotated key
     // and the value rounded to the cache element type (fp8: the code of
-    // x / scale, the quotient rounded once to float32); its score is summed
-    // now and folded last, after the cached keys.
+    // x / scale, the quotient rounded once to float32); its score with every
+    // query head is summed now and folded last, after the cached keys.
     S k_hat{}, v_hat{};
     float vh = 0.f;
     if (has_new) {
-        float prod = 0.f;
+        float khf = 0.f;
         if (t < D) {
             k_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(k_r, kscale) : k_r);
             v_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(v_t, vscale) : v_t);
-            prod = qsc * elt_to_f32<DT>(k_hat);
+            khf = elt_to_f32<DT>(k_hat);
             vh = elt_to_f32<DT>(v_hat);
         }
-        prod = wave_sum(prod);
-        if (lane == 0) sm_dot[wid] = prod;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const float prod = wave_sum(t < D ? qsc[hh] * khf : 0.f);
+            if (lane == 0) sm_dot[hh][wid] = prod;
+        }
     }
-    // Gate logit from the projection (fused step with g_proj): it needs only
-    // the layer input, so it is summed here, under the first tiles' latency,
-    // and used in the epilogue.  Same sum as hswd_gate_proj.
+    // Gate logits from the projection (fused step with g_proj): they need
+    // only the layer input, so they are summed here, under the first tiles'
+    // latency, and used in the epilogue.  Same sum as hswd_gate_proj.
     if (gproj) {
-        float gs = gate_share(P.gx + (size_t)b * P.hidden, P.gw + (size_t)h * P.hidden,
-                              P.hidden, tid, kAttnThreads);
-        gs = wave_sum(gs);
-        if (lane == 0) sm_gl[wid] = gs;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            float gs = gate_share(P.gx + (size_t)b * P.hidden,
+                                  P.gw + (size_t)(g * G + hh) * P.hidden, P.hidden, tid,
+                                  kAttnThreads);
+            gs = wave_sum(gs);
+            if (lane == 0) sm_gl[hh][wid] = gs;
+        }
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) qs[e] = sm_q[c * EPC + e];
+    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) qs[hh][e] = sm_q[hh][c * EPC + e];
+    }
 
     // Chunk boundaries fall after the items j with (j + 1) % TPW == 0 among
     // the full chunks; every wave has the same items, so the barriers match.
-    auto after = [&](int j) {
+    auto after = [&](int j) __attribute__((always_inline)) {
         if (j < n_full_items && (j + 1) % TPW == 0) end_chunk(c_begin + j / TPW);
     };
     // Entering each pass, A holds item j and B item j + 1, both requested; a
@@ -526,11 +610,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
     if (MODE == kModePartials) {
         // chunks without a valid key are empty partials
         for (int ch = c_valid; ch < c_end; ++ch) {
-            const size_t idx = (size_t)bh * P.n_chunk + ch;
-            if (t < D) P.part_o[idx * D + t] = 0.f;
-            if (tid == 0) {
-                P.part_ml[idx * 2 + 0] = -INFINITY;
-                P.part_ml[idx * 2 + 1] = 0.f;
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
+                if (t < D) P.part_o[idx * D + t] = 0.f;
+                if (tid == 0) {
+                    P.part_ml[idx * 2 + 0] = -INFINITY;
+                    P.part_ml[idx * 2 + 1] = 0.f;
+                }
             }
         }
         return;
@@ -554,40 +641,47 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams P) {
         __syncthreads();
         if (!sm_last) return;
 
-        // Last arrival folds the valid chunks of this (stream, head) in chunk
-        // order, 32 partials' loads in flight before any is folded.
-        const float* pml = P.part_ml + (size_t)bh * P.n_chunk * 2;
-        const float* po = P.part_o + (size_t)bh * P.n_chunk * D + (t < D ? t : 0);
-        constexpr int kBatch = 32;
-        int i = 0;
-        for (; i + kBatch <= n_valid_chunks; i += kBatch) {
-            float xm[kBatch], xl[kBatch], xo[kBatch];
+        // Last arrival folds the valid chunks of each head in chunk order, 32
+        // partials' loads in flight before any is folded.
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                xm[u] = ld_agent(pml + 2 * (i + u));
-                xl[u] = ld_agent(pml + 2 * (i + u) + 1);
-                xo[u] = ld_agent(po + (size_t)(i + u) * D);
+        for (int hh = 0; hh < G; ++hh) {
+            const float* pml = P.part_ml + (size_t)(bh0 + hh) * P.n_chunk * 2;
+            const float* po = P.part_o + (size_t)(bh0 + hh) * P.n_chunk * D + (t < D ? t : 0);
+            constexpr int kBatch = 32;
+            int i = 0;
+            for (; i + kBatch <= n_valid_chunks; i += kBatch) {
+                float xm[kBatch], xl[kBatch], xo[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    xm[u] = ld_agent(pml + 2 * (i + u));
+                    xl[u] = ld_agent(pml + 2 * (i + u) + 1);
+                    xo[u] = ld_agent(po + (size_t)(i + u) * D);
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) run[hh].add(xm[u], xl[u], xo[u]);
             }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) run.add(xm[u], xl[u], xo[u]);
+            for (; i < n_valid_chunks; ++i)
+                run[hh].add(ld_agent(pml + 2 * i), ld_agent(pml + 2 * i + 1),
+                            ld_agent(po + (size_t)i * D));
         }
-        for (; i < n_valid_chunks; ++i)
-            run.add(ld_agent(pml + 2 * i), ld_agent(pml + 2 * i + 1), ld_agent(po + (size_t)i * D));
         if (tid == 0)                            // ready for the next call
             __hip_atomic_store(&P.counters[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Join the new entry as a one-key partial (score summed in the prologue).
-    const float s_new = lds_tree_sum<kAttnWaves>(sm_dot);
-    run.add(s_new, 1.f, vh);
-    if (t < D) {
-        float o = run.O / run.L;
-        if (DT == kFP8) o *= vscale;
-        if (MODE == kModeStep && (gproj || P.gate != nullptr)) {
-            const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl) : glogit;
-            o *= 1.f / (1.f + expf(-logit));
+    // Join the new entry as a one-key partial (scores summed in the prologue).
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        const float s_new = lds_tree_sum<kAttnWaves>(sm_dot[hh]);
+        run[hh].add(s_new, 1.f, vh);
+        if (t < D) {
+            float o = run[hh].O / run[hh].L;
+            if (DT == kFP8) o *= vscale;
+            if (MODE == kModeStep && (gproj || P.gate != nullptr)) {
+                const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl[hh]) : glogit[hh];
+                o *= 1.f / (1.f + expf(-logit));
+            }
+            P.out[(size_t)(bh0 + hh) * D + t] = o;
         }
-        P.out[(size_t)bh * D + t] = o;
     }
 
     if (MODE == kModeStep) {

@@ -24,21 +24,25 @@ def test_gate_proj_matches_oracle():
     assert np.all(np.abs(got2 - ref2) <= 1e-6 * (np.abs(x2) @ np.abs(w2).T))
 
 
-@pytest.mark.parametrize("kind,dtype", [("sliding", "bf16"), ("full", "f16")])
-def test_layer_step_gproj(kind, dtype):
+@pytest.mark.parametrize("kind,dtype,G", [("sliding", "bf16", 1), ("full", "f16", 1),
+                                          ("sliding", "bf16", 4), ("full", "bf16", 2)])
+def test_layer_step_gproj(kind, dtype, G):
     """Fused projection + step: the same bits as gate_proj then layer_step,
-    and the oracle's output scaled by the oracle's sigmoid(logit)."""
+    and the oracle's output scaled by the oracle's sigmoid(logit); G query
+    heads per kv head (each head keeps its own row of w_g)."""
     B = 12
     ring = kind == "sliding"
-    spec = inputs.sliding_spec(B, dtype) if ring else inputs.full_spec(B, 3000, dtype)
+    Hkv = 8 // G
+    spec = (inputs.sliding_spec(B, dtype, Hkv=Hkv) if ring
+            else inputs.full_spec(B, 3000, dtype, Hkv=Hkv))
     pos = inputs.ragged_positions(B, 0, 4096 if ring else 2999, seed=62)
     x = inputs.make_step(spec, pos, seed=63)
     gx, gw = inputs.gate_inputs(B, 2048, 8, seed=64)
     mp = int(x.pos.max())
     d = to_dev(x)
-    desc = hswd.make_desc(d["k_cache"])
+    desc = hswd.make_desc(d["k_cache"], n_heads=8)
     ws = hswd.workspace(desc, ring, mp)
-    say("layer_step_gproj %s %s" % (kind, dtype))
+    say("layer_step_gproj %s %s G=%d" % (kind, dtype, G))
     fused = hswd.layer_step_gproj(d["q"], d["k"], d["v"], f32_dev(gx), f32_dev(gw), d["k_cache"],
                                   d["v_cache"], d["pos"], ring, spec.rot, spec.theta, ws,
                                   max_pos=mp, desc=desc).cpu().numpy()

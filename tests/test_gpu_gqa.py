@@ -1,0 +1,150 @@
+"""GPU parity of grouped-query attention (H / Hkv = 2 or 4 query heads per
+kv head, the talker commit's query reshape): the fused layer step and the
+separate entries against the oracle (which maps query head h to kv head
+h // G), the stored entry bit for bit, the cross-workgroup merge, and the
+property that a group reads the same result as its kv head repeated."""
+import numpy as np
+import pytest
+
+import hybrid_sliding_window_decode_amd as hswd
+import oracle
+from hybrid_sliding_window_decode_amd import inputs
+from gpu_util import CODE, assert_parity, cache_to_host, entry_codes, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gqa_spec(kind, B, dtype, G, D=256, S=None, H=8):
+    if kind == "sliding":
+        return inputs.sliding_spec(B, dtype, H=H, Hkv=H // G, D=D)
+    return inputs.full_spec(B, S, dtype, H=H, Hkv=H // G, D=D)
+
+
+def oracle_step(x, write=False):
+    kc, vc = x.k_cache.copy(), x.v_cache.copy()
+    return oracle.layer_step(x.q, x.k, x.v, x.gate, kc, vc, x.pos, CODE[x.spec.dtype],
+                             x.spec.kind == "sliding", x.spec.rot, x.spec.theta, write=write,
+                             kv_scale=x.spec.kv_scale)
+
+
+def positions(kind, B, S, pos, seed):
+    if pos == "ragged":
+        hi = 4096 if kind == "sliding" else S - 1
+        return inputs.ragged_positions(B, 0, hi, seed=seed)
+    return pos
+
+
+@pytest.mark.parametrize("kind,dtype,G,D,B,pos,S,kps", [
+    ("sliding", "bf16", 4, 256, 12, "ragged", None, 0),
+    ("sliding", "f16", 2, 128, 9, "ragged", None, 0),
+    ("full", "bf16", 2, 256, 10, "ragged", 3000, 0),
+    ("full", "f16", 4, 128, 4, [1024, 1, 0, 2999], 3000, 256),
+    # two streams, long context: several workgroups per (stream, kv head),
+    # merged by the last to arrive
+    ("full", "bf16", 4, 256, 2, [19999, 7001], 20000, 0),
+])
+def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
+    """Fused step vs oracle; the same bits as rope -> attend -> gate -> write;
+    the stored entry equals the oracle's rounding of the rotated key."""
+    spec = gqa_spec(kind, B, dtype, G, D=D, S=S)
+    x = inputs.make_step(spec, positions(kind, B, S, pos, 21), seed=22 + G)
+    ring = kind == "sliding"
+    mp = int(x.pos.max())
+    ref = oracle_step(x, write=True)
+    d = to_dev(x)
+    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, keys_per_split=kps)
+    ws = hswd.workspace(desc, ring, mp)
+    say("gqa layer_step %s %s G=%d D=%d B=%d pos=%s" % (kind, dtype, G, D, B, list(x.pos[:6])))
+    out = hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
+                          d["pos"], ring, spec.rot, spec.theta, ws, max_pos=mp, desc=desc)
+    assert hswd.check_errors(ws) == 0
+    out = out.cpu().numpy()
+    assert_parity(out, ref["out"], x, "gqa fused step")
+
+    e = to_dev(x)
+    hswd.rope_apply(e["q"], e["k"], e["pos"], spec.rot, spec.theta)
+    ws2 = hswd.workspace(desc, ring, mp)
+    if ring:
+        o = hswd.decode_attn_sliding(e["q"], e["k"], e["v"], e["k_cache"], e["v_cache"],
+                                     e["pos"], ws2, desc=desc)
+    else:
+        o = hswd.decode_attn_full(e["q"], e["k"], e["v"], e["k_cache"], e["v_cache"], e["pos"],
+                                  mp, ws2, desc=desc)
+    assert_parity(o.cpu().numpy(), ref["o_pre"], x, "gqa attention entry")
+    g = hswd.head_gate(o, e["gate"])
+    hswd.kv_slot_write(e["k_cache"], e["v_cache"], e["k"], e["v"], e["pos"], ring, ws2,
+                       desc=desc)
+    assert hswd.check_errors(ws2) == 0
+    assert np.array_equal(g.cpu().numpy(), out), "fused and unfused outputs differ"
+    kc = cache_to_host(d["k_cache"])
+    assert np.array_equal(kc, cache_to_host(e["k_cache"]))
+    assert np.array_equal(cache_to_host(d["v_cache"]), cache_to_host(e["v_cache"]))
+    k_rot = e["k"].cpu().numpy()
+    for b in range(B):
+        p = int(x.pos[b])
+        row = p % spec.n_slots if ring else p
+        assert np.array_equal(kc[b, :, row], entry_codes(k_rot[b], dtype))
+
+
+def test_gqa_partials_merge_to_oracle():
+    """Chunk partials of a grouped full layer (cached keys only), merged by
+    hswd_lse_merge, give the oracle's attention over the same keys."""
+    B, G, S = 3, 4, 2500
+    spec = gqa_spec("full", B, "bf16", G, S=S)
+    x = inputs.make_step(spec, [2499, 700, 1], seed=31)
+    d = to_dev(x)
+    hswd.rope_apply(d["q"], d["k"], d["pos"], spec.rot, spec.theta)
+    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, keys_per_split=256)
+    say("gqa partials")
+    po, pml = hswd.decode_attn_partials(d["q"], d["k_cache"], d["v_cache"], d["pos"], 0,
+                                        max_pos=2499, desc=desc)
+    merged = hswd.lse_merge(po, pml).cpu().numpy()
+    q_rot = d["q"].cpu().numpy().astype(np.float64)
+    scale = 1.0 / np.sqrt(spec.D)
+    for b in range(B):
+        p = int(x.pos[b])
+        for h in range(spec.H):
+            gk = h // G
+            m, l, o = oracle.partial(q_rot[b, h], x.k_cache[b, gk], x.v_cache[b, gk],
+                                     CODE["bf16"], 0, p, scale)
+            vmax = np.abs(oracle.decode(CODE["bf16"], x.v_cache[b, gk, :p])).max()
+            err = np.abs(merged[b, h] - o / l).max() / vmax
+            assert err <= 2e-3, (b, h, err)
+
+
+@pytest.mark.parametrize("kind,G", [("sliding", 4), ("full", 2)])
+def test_gqa_equals_repeated_kv_heads(kind, G):
+    """A group of G query heads over one kv head gives what G separate heads
+    over G copies of that kv head give (H = Hkv): grouping only shares the
+    reads.  Within the parity bar (the tile size, and so the online-softmax
+    order, differs between the two kernels)."""
+    B, S = 6, 2000
+    spec = gqa_spec(kind, B, "bf16", G, S=S)
+    x = inputs.make_step(spec, positions(kind, B, S, "ragged", 41), seed=42)
+    rep = lambda a: np.repeat(a, G, axis=1)
+    y = inputs.StepInputs(gqa_spec(kind, B, "bf16", 1, S=S), x.pos, x.q, rep(x.k), rep(x.v),
+                          x.gate, rep(x.k_cache), rep(x.v_cache))
+    ring = kind == "sliding"
+    mp = int(x.pos.max())
+    outs = []
+    for z in (x, y):
+        d = to_dev(z)
+        desc = hswd.make_desc(d["k_cache"], n_heads=z.spec.H)
+        ws = hswd.workspace(desc, ring, mp)
+        say("gqa vs repeated kv %s G=%d Hkv=%d" % (kind, G, z.spec.Hkv))
+        outs.append(hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"],
+                                    d["v_cache"], d["pos"], ring, z.spec.rot, z.spec.theta, ws,
+                                    max_pos=mp, desc=desc).cpu().numpy())
+    assert_parity(outs[0], outs[1].astype(np.float64), x, "grouped vs repeated")
+
+
+def test_gqa_unsupported_is_refused():
+    """Groups the library has no kernel for are refused before any launch."""
+    spec = gqa_spec("sliding", 2, "fp8", 2)
+    x = inputs.make_step(spec, [3, 700], seed=51)
+    d = to_dev(x)
+    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, kv_scale=d["kv_scale"])
+    ws = hswd.workspace(desc, 1, 0)
+    with pytest.raises(hswd.HswdError):
+        hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
+                        d["pos"], 1, spec.rot, spec.theta, ws, desc=desc)
