@@ -31,13 +31,14 @@ PEAK_HBM_GBS = 8000.0                 # MI355X HBM3E, vendor figure
 B, H, HKV, D, S_RING, CTX, LAYERS = 64, 8, 8, 256, 511, 4096, 28
 
 
-def layer_bytes(kind, B=B, pos=CTX, elt=2):
+def layer_bytes(kind, B=B, pos=CTX, elt=2, heads=H):
     """Algorithmic bytes of one layer step: valid K and V rows plus the
     per-stream q in, output out, k and v in, rounded entry out, gate, pos
-    (fp8 caches: plus the 2*Hkv per-head scales)."""
+    (fp8 caches: plus the 2*Hkv per-head scales).  `heads` query heads share
+    the HKV kv heads (grouped-query attention when heads > HKV)."""
     n_keys = min(pos, S_RING) if kind == "sliding" else pos
     cache = B * HKV * n_keys * D * elt * 2
-    per_stream = H * D * 4 * 2 + HKV * D * 4 * 2 + HKV * D * elt * 2 + H * 4 + 4
+    per_stream = heads * D * 4 * 2 + HKV * D * 4 * 2 + HKV * D * elt * 2 + heads * 4 + 4
     return cache + B * per_stream + (2 * HKV * 4 if elt == 1 else 0)
 
 
@@ -56,7 +57,7 @@ def counters_path(kv):
 
 def full_kernel(kv):
     """rocprofv3's name of the full-layer fused step kernel for a cache type."""
-    return "hswd::attn_kernel<256, %d, false, 1>(...)" % {"bf16": 2, "fp8": 3}[kv]
+    return "hswd::attn_kernel<256, %d, false, 1, 1>(...)" % {"bf16": 2, "fp8": 3}[kv]
 
 
 def measured_traffic(kv):
@@ -89,6 +90,9 @@ def parse():
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="cache element type of the 28-layer step (fp8: OCP e4m3 with "
                          "per-head scales)")
+    ap.add_argument("--heads", type=int, default=H, choices=[8, 16, 32],
+                    help="query heads of the 28-layer step over its 8 kv heads (16, 32: "
+                         "grouped-query attention, 2 or 4 query heads per kv head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter scaling)")
@@ -98,33 +102,43 @@ def parse():
     return ap.parse_args()
 
 
-# Single-layer workloads: (kind, streams, cache dtype, positions, seed).  Each
-# is timed over enough independent buffer sets that no set is re-read from the
-# 256 MB Infinity Cache before it has been evicted.
+# Single-layer workloads: (kind, streams, cache dtype, positions, seed, query
+# heads).  Each is timed over enough independent buffer sets that no set is
+# re-read from the 256 MB Infinity Cache before it has been evicted.  All have
+# 8 kv heads of 256 dims; 16 or 32 query heads make them grouped.
 SINGLE_LAYER = {
-    "sliding_1x600_f32": ("sliding", 1, "f32", 600, 1),
-    "full_1x1024_f16": ("full", 1, "f16", 1024, 2),
-    "sliding_64xragged_bf16": ("sliding", 64, "bf16", "ragged", 3),
-    "long_full_8x131072_bf16": ("full", 8, "bf16", 131072, 5),
-    "long_sliding_8x131072_bf16": ("sliding", 8, "bf16", 131072, 5),
+    "sliding_1x600_f32": ("sliding", 1, "f32", 600, 1, 8),
+    "full_1x1024_f16": ("full", 1, "f16", 1024, 2, 8),
+    "sliding_64xragged_bf16": ("sliding", 64, "bf16", "ragged", 3, 8),
+    "long_full_8x131072_bf16": ("full", 8, "bf16", 131072, 5, 8),
+    "long_sliding_8x131072_bf16": ("sliding", 8, "bf16", 131072, 5, 8),
+    "gqa4_full_64x4096_bf16": ("full", 64, "bf16", 4096, 6, 32),
+    "gqa4_sliding_64x4096_bf16": ("sliding", 64, "bf16", 4096, 6, 32),
+    "gqa2_full_64x4096_bf16": ("full", 64, "bf16", 4096, 7, 16),
+    "gqa4_full_64x4096_fp8": ("full", 64, "fp8", 4096, 8, 32),
+    "gqa4_sliding_64x4096_fp8": ("sliding", 64, "fp8", 4096, 8, 32),
 }
 
 
 def single_layer(args, np, torch, hswd, inputs, dev):
-    kind, B_, dtype, pos, seed = SINGLE_LAYER[args.workload]
-    elt = 4 if dtype == "f32" else 2
+    kind, B_, dtype, pos, seed, Hq = SINGLE_LAYER[args.workload]
+    elt = {"f32": 4, "fp8": 1}.get(dtype, 2)
     if pos == "ragged":
         pos = inputs.ragged_positions(B_, 1, 4096, seed=seed)
     posv = np.broadcast_to(np.asarray(pos, np.int64), (B_,))
     cap = int(posv.max()) + 1
-    spec = inputs.sliding_spec(B_, dtype) if kind == "sliding" else inputs.full_spec(B_, cap, dtype)
+    spec = (inputs.sliding_spec(B_, dtype, H=Hq) if kind == "sliding"
+            else inputs.full_spec(B_, cap, dtype, H=Hq))
     n_keys = np.minimum(posv, S_RING) if kind == "sliding" else posv
-    per_stream = H * D * 4 * 2 + HKV * D * 4 * 2 + HKV * D * elt * 2 + H * 4 + 4
-    nbytes = int(np.sum(n_keys) * HKV * D * elt * 2 + B_ * per_stream)
+    per_stream = Hq * D * 4 * 2 + HKV * D * 4 * 2 + HKV * D * elt * 2 + Hq * 4 + 4
+    nbytes = int(np.sum(n_keys) * HKV * D * elt * 2 + B_ * per_stream
+                 + (2 * HKV * 4 if dtype == "fp8" else 0))
     set_bytes = 2 * B_ * HKV * spec.n_slots * D * elt
     n_sets = max(2, min(64, -(-(1 << 30) // set_bytes)))
     sets = [inputs.device_step(spec, pos, seed=seed * 100 + i, device=dev) for i in range(n_sets)]
-    desc = hswd.make_desc(sets[0]["k_cache"])
+    # every set holds the same per-head fp8 scales; the descriptor points at
+    # the first set's copy
+    desc = hswd.make_desc(sets[0]["k_cache"], n_heads=Hq, kv_scale=sets[0].get("kv_scale"))
     ring = kind == "sliding"
     mp = int(posv.max())
     ws = hswd.workspace(desc, ring, mp, device=dev)
@@ -156,7 +170,8 @@ def single_layer(args, np, torch, hswd, inputs, dev):
            "higher_is_better": True, "dtype": dtype, "data": "synthetic",
            "algorithmic_bytes": nbytes, "buffer_sets": n_sets,
            "frac_of_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-           "config": {"workload": args.workload, "kind": kind, "streams": B_, "heads": H,
+           "config": {"workload": args.workload, "kind": kind, "streams": B_, "heads": Hq,
+                      "kv_heads": HKV,
                       "head_dim": D, "kv_dtype": dtype,
                       "positions": "ragged U[1,4096]" if isinstance(pos, np.ndarray) else int(pos)}}
     print(json.dumps(res), flush=True)
@@ -201,22 +216,24 @@ def main():
     # ---- inputs: 28 layers, each with its own buffers, all streams at 4096
     kv = args.kv
     elt = 1 if kv == "fp8" else 2
+    hq = args.heads                          # query heads over the HKV kv heads
     log("generating 28-layer workload (%.1f GB of KV caches)" % (
         sum(2 * B * HKV * (S_RING if not is_full(l) else CTX + 1) * D * elt
             for l in range(LAYERS)) / 1e9))
     layers = []
     for l in range(LAYERS):
         full = is_full(l)
-        spec = inputs.full_spec(B, CTX + 1, kv) if full else inputs.sliding_spec(B, kv)
+        spec = (inputs.full_spec(B, CTX + 1, kv, H=hq) if full
+                else inputs.sliding_spec(B, kv, H=hq))
         t = inputs.device_step(spec, CTX, seed=4000 + l, device=dev)
-        desc = hswd.make_desc(t["k_cache"], kv_scale=t.get("kv_scale"))
+        desc = hswd.make_desc(t["k_cache"], n_heads=hq, kv_scale=t.get("kv_scale"))
         t.update(spec=spec, ring=not full, desc=desc, out=torch.empty_like(t["q"]),
                  ws=hswd.workspace(desc, not full, CTX, device=dev))
         if args.gate == "proj":
-            gx, gw = inputs.gate_inputs(B, 2048, H, seed=7000 + l)
+            gx, gw = inputs.gate_inputs(B, 2048, hq, seed=7000 + l)
             t["gx"] = torch.from_numpy(gx).to(dev)
             t["gw"] = torch.from_numpy(gw).to(dev)
-            t["gate"] = torch.empty(B, H, device=dev)
+            t["gate"] = torch.empty(B, hq, device=dev)
         if args.mode == "unfused":
             t["q_rot"] = torch.empty_like(t["q"])
             t["k_rot"] = torch.empty_like(t["k"])
@@ -336,7 +353,7 @@ def main():
         t_sl = float(np.median(times[0]))
         t_fu = float(np.median(times[3]))
         step_cpu = 21 * t_sl + 7 * t_fu
-        step_bytes = 21 * layer_bytes("sliding", elt=elt) + 7 * layer_bytes("full", elt=elt)
+        step_bytes = 21 * layer_bytes("sliding", elt=elt, heads=hq) + 7 * layer_bytes("full", elt=elt, heads=hq)
         cpu = {"value": round(step_bytes / step_cpu / 1e9, 3), "unit": "GB/s",
                "cores": threads, "kind": "oracle",
                "sample": ("fp64 oracle on layer 0 (sliding) and layer 3 (full) of the same "
@@ -346,9 +363,9 @@ def main():
 
     ms_step = t_start.elapsed_time(t_end) / args.steps
     full_us = float(np.mean([a.elapsed_time(b) for a, b in full_ev])) * 1e3
-    step_bytes = 21 * layer_bytes("sliding", elt=elt) + 7 * layer_bytes("full", elt=elt)
+    step_bytes = 21 * layer_bytes("sliding", elt=elt, heads=hq) + 7 * layer_bytes("full", elt=elt, heads=hq)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    full_bytes = layer_bytes("full", elt=elt)
+    full_bytes = layer_bytes("full", elt=elt, heads=hq)
     achieved = full_bytes / (full_us * 1e-6) / 1e9
     sl_us_est = (ms_step * 1e3 - 7 * full_us) / 21
 
@@ -365,19 +382,22 @@ def main():
         "vs_baseline": None,
         "dtype": kv,
         "data": "synthetic (seeded N(0,1) caches and projections, no model weights)",
-        "config": {"workload": "step28_64x4096_" + kv, "layers": "21 sliding (511-slot ring) "
-                   "+ 7 full (context 4096), l%4==3 full", "streams": B, "heads": H,
+        "config": {"workload": "step28_64x4096_" + kv + ("" if hq == HKV else "_h%d" % hq),
+                   "layers": "21 sliding (511-slot ring) "
+                   "+ 7 full (context 4096), l%4==3 full", "streams": B, "heads": hq,
+                   "kv_heads": HKV,
                    "head_dim": D, "kv_dtype": kv, "launch": args.mode,
                    "gate": "logits given" if args.gate == "logits" else
-                   "projected in-launch from x[64,2048] by w_g[8,2048]"},
+                   "projected in-launch from x[64,2048] by w_g[%d,2048]" % hq},
         "us_per_layer_step": round(ms_step * 1e3 / LAYERS, 2),
         "us_full_layer": round(full_us, 2),
         "us_sliding_layer_est": round(sl_us_est, 2),
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(kv),
-                     "kernel": "attn_kernel<256, %s, append, step> (full layer, one launch)" % kv,
+                     "traffic": measured_traffic(kv) if hq == HKV else None,
+                     "kernel": "attn_kernel<256, %s, append, step, %d query heads per kv head> "
+                               "(full layer, one launch)" % (kv, hq // HKV),
                      "bytes_per_launch": full_bytes},
         "cpu_baseline": cpu,
         "parity_max_err": parity,

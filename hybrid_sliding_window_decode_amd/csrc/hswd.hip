@@ -135,10 +135,9 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     if (st != HSWD_OK) return st;
     const int group = d->n_heads / d->n_kv_heads;       // query heads per kv head
     if (group != 1 && group != 2 && group != 4) return HSWD_ERR_UNSUPPORTED;
-    // grouped kernels: 16-bit caches, head dim 128 or 256 (G query vectors and
-    // accumulators per lane must fit beside the tiles in 256 VGPRs)
-    if (group > 1 && ((d->kv_dtype != HSWD_BF16 && d->kv_dtype != HSWD_F16) || d->head_dim < 128))
-        return HSWD_ERR_UNSUPPORTED;
+    // grouped kernels: 16-bit and fp8 caches, head dim 128 or 256 (G query
+    // vectors and accumulators per lane must fit beside the tiles in 256 VGPRs)
+    if (group > 1 && (d->kv_dtype == HSWD_F32 || d->head_dim < 128)) return HSWD_ERR_UNSUPPORTED;
     if (!ring) {
         if (max_pos < 0) return HSWD_ERR_INVALID;
         if ((long)max_pos + 1 > d->n_slots) return HSWD_ERR_CAPACITY;

@@ -93,11 +93,13 @@ struct AttnParams {
 
 // Tile geometry.  G query heads per kv head keep G query vectors and G
 // accumulators per lane, so a grouped kernel halves its tile (4 loads of K
-// and of V instead of 8) to stay within 256 VGPRs (2 waves per SIMD).
+// and of V instead of 8) and reads fp8 rows 8 bytes per lane (8 dims, as for
+// 16-bit rows) to stay within 256 VGPRs (2 waves per SIMD).
 template <int D, int DT, int G = 1>
 struct AttnGeo {
     static constexpr int EB = elt_bytes<DT>();        // element bytes
-    static constexpr int EPC = 16 / EB;               // elements per 16-byte chunk
+    static constexpr int CB = DT == kFP8 && G > 1 ? 8 : 16;   // bytes per lane chunk
+    static constexpr int EPC = CB / EB;               // elements per chunk
     static constexpr int LPR = D / EPC;               // lanes per cache row
     static constexpr int RPI = kWave / LPR;           // rows per wave-wide load
     static constexpr int NL = G == 1 ? 8 : 4;         // loads per tile (K and V each)
@@ -299,7 +301,8 @@ void attn_kernel(AttnParams P) {
     }
     Fold run[G];                    // folded chunk partials (wpp == 1)
 
-    u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
+    using Chunk = typename ChunkT<Geo::CB>::type;
+    Chunk kA[NL], vA[NL], kB[NL], vB[NL];
 
     // Item j of this wave: tile (wid + 4 i) of chunk ch.  Rows past the
     // chunk's valid end are clamped onto its last valid row (never reading an
@@ -310,23 +313,23 @@ void attn_kernel(AttnParams P) {
     auto item_chunk = [&](int j) __attribute__((always_inline)) { return j < n_full_items ? c_begin + j / TPW : c_full; };
     auto item_tile = [&](int j) __attribute__((always_inline)) { return j < n_full_items ? j % TPW : j - n_full_items; };
 
-    auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int j) __attribute__((always_inline)) {
+    auto load_tile = [&](Chunk (&kt)[NL], Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
         const int ch = item_chunk(j);
         const int jlast = max(min((ch + 1) * P.K, nv), 1) - 1;
         const int base = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT + r;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int row = min(base + i * RPI, jlast);
-            kt[i] = load_kv16(kbase + (size_t)row * D);
+            kt[i] = load_kv<Geo::CB>(kbase + (size_t)row * D);
         }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int row = min(base + i * RPI, jlast);
-            vt[i] = load_kv16(vbase + (size_t)row * D);
+            vt[i] = load_kv<Geo::CB>(vbase + (size_t)row * D);
         }
     };
 
-    auto compute_tile = [&](const u32x4 (&kt)[NL], const u32x4 (&vt)[NL], int j) __attribute__((always_inline)) {
+    auto compute_tile = [&](const Chunk (&kt)[NL], const Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
         const int ch = item_chunk(j);
         const int jend = min((ch + 1) * P.K, nv);
         const int tile0 = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT;
@@ -337,7 +340,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
                 float kf[EPC];
-                unpack16<DT>(kt[i], kf);
+                unpack_chunk<DT>(kt[i], kf);
                 float acc = 0.f;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) acc = fmaf(qs[hh][e], kf[e], acc);
@@ -380,7 +383,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
                 float vf[EPC];
-                unpack16<DT>(vt[i], vf);
+                unpack_chunk<DT>(vt[i], vf);
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pk[i], vf[e], o_acc[hh][e]);
             }

@@ -21,19 +21,27 @@ template <> struct Storage<kFP8> { using type = uint8_t; };
 template <int DT> constexpr int elt_bytes() { return DT == kF32 ? 4 : (DT == kFP8 ? 1 : 2); }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// K/V tile loads: 16 bytes per lane, with the non-temporal hint: the cache
-// is streamed once per step and never re-read, and on MI355X the hinted
-// loads stream from HBM about 10% faster than plain ones.
+// One lane's chunk of a cache row: 16 bytes, or 8 (fp8 rows in the grouped
+// kernels, so a lane holds 8 dims there too).
+template <int CB> struct ChunkT;
+template <> struct ChunkT<16> { using type = u32x4; };
+template <> struct ChunkT<8> { using type = u32x2; };
+
+// K/V tile loads with the non-temporal hint: the cache is streamed once per
+// step and never re-read, and on MI355X the hinted loads stream from HBM
+// about 10% faster than plain ones.
 #ifndef HSWD_KV_NT
 #define HSWD_KV_NT 1
 #endif
-template <typename T>
-__device__ __forceinline__ u32x4 load_kv16(const T* p) {
+template <int CB, typename T>
+__device__ __forceinline__ typename ChunkT<CB>::type load_kv(const T* p) {
+    using C = typename ChunkT<CB>::type;
 #if HSWD_KV_NT
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return __builtin_nontemporal_load(reinterpret_cast<const C*>(p));
 #else
-    return *reinterpret_cast<const u32x4*>(p);
+    return *reinterpret_cast<const C*>(p);
 #endif
 }
 
@@ -133,7 +141,7 @@ __device__ __forceinline__ float elt_to_f32(typename Storage<DT>::type s) {
 
 // Unpack one 16-byte chunk of cache elements into floats (EPC of them).
 template <int DT>
-__device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
+__device__ __forceinline__ void unpack_chunk(const u32x4& w, float* f) {
     if constexpr (DT == kFP8) {
         const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -158,6 +166,18 @@ __device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
             f[2 * j] = f16_bits_to_f32((uint16_t)(u[j] & 0xffffu));
             f[2 * j + 1] = f16_bits_to_f32((uint16_t)(u[j] >> 16));
         }
+    }
+}
+
+// Unpack one 8-byte chunk of fp8 codes into 8 floats, in byte order.
+template <int DT>
+__device__ __forceinline__ void unpack_chunk(const u32x2& w, float* f) {
+    static_assert(DT == kFP8, "8-byte chunks hold fp8 codes");
+    const uint32_t u[2] = {w.x, w.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const f32x2 lo = fp8x2_to_f32(u[j], false), hi = fp8x2_to_f32(u[j], true);
+        f[4 * j] = lo.x; f[4 * j + 1] = lo.y; f[4 * j + 2] = hi.x; f[4 * j + 3] = hi.y;
     }
 }
 

@@ -88,10 +88,10 @@ def test_workspace_and_splits():
     ("kps quantum d128", dict(head_dim=128, keys_per_split=64), -1),
     ("cpw", dict(chunks_per_workgroup=-1), -1),
     ("batch", dict(batch=0), -1),
-    # grouped kernels: 2 or 4 query heads per kv head, 16-bit caches, D >= 128
+    # grouped kernels: 2 or 4 query heads per kv head, 16-bit or fp8 caches,
+    # D >= 128
     ("GQA group 8", dict(n_heads=16, n_kv_heads=2), -6),
     ("GQA group 3", dict(n_heads=24, n_kv_heads=8), -6),
-    ("GQA fp8", dict(n_heads=16, n_kv_heads=8, kv_dtype=3), -6),
     ("GQA f32", dict(n_heads=16, n_kv_heads=8, kv_dtype=0), -6),
     ("GQA head_dim 64", dict(n_heads=16, n_kv_heads=8, head_dim=64), -6),
 ])

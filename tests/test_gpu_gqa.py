@@ -42,6 +42,10 @@ def positions(kind, B, S, pos, seed):
     # two streams, long context: several workgroups per (stream, kv head),
     # merged by the last to arrive
     ("full", "bf16", 4, 256, 2, [19999, 7001], 20000, 0),
+    # fp8 e4m3 caches with per-head scales (8-byte lane chunks)
+    ("sliding", "fp8", 4, 256, 12, "ragged", None, 0),
+    ("full", "fp8", 2, 128, 6, "ragged", 3000, 256),
+    ("full", "fp8", 4, 256, 2, [19999, 9000], 20000, 0),
 ])
 def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
     """Fused step vs oracle; the same bits as rope -> attend -> gate -> write;
@@ -52,7 +56,8 @@ def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
     mp = int(x.pos.max())
     ref = oracle_step(x, write=True)
     d = to_dev(x)
-    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, keys_per_split=kps)
+    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, keys_per_split=kps,
+                          kv_scale=d["kv_scale"])
     ws = hswd.workspace(desc, ring, mp)
     say("gqa layer_step %s %s G=%d D=%d B=%d pos=%s" % (kind, dtype, G, D, B, list(x.pos[:6])))
     out = hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
@@ -80,10 +85,11 @@ def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
     assert np.array_equal(kc, cache_to_host(e["k_cache"]))
     assert np.array_equal(cache_to_host(d["v_cache"]), cache_to_host(e["v_cache"]))
     k_rot = e["k"].cpu().numpy()
+    ksc = None if spec.kv_scale is None else spec.kv_scale[0][:, None]
     for b in range(B):
         p = int(x.pos[b])
         row = p % spec.n_slots if ring else p
-        assert np.array_equal(kc[b, :, row], entry_codes(k_rot[b], dtype))
+        assert np.array_equal(kc[b, :, row], entry_codes(k_rot[b], dtype, ksc))
 
 
 def test_gqa_partials_merge_to_oracle():
@@ -139,11 +145,12 @@ def test_gqa_equals_repeated_kv_heads(kind, G):
 
 
 def test_gqa_unsupported_is_refused():
-    """Groups the library has no kernel for are refused before any launch."""
-    spec = gqa_spec("sliding", 2, "fp8", 2)
+    """Groups the library has no kernel for (8 query heads per kv head) are
+    refused before any launch."""
+    spec = gqa_spec("sliding", 2, "bf16", 8, H=16)
     x = inputs.make_step(spec, [3, 700], seed=51)
     d = to_dev(x)
-    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, kv_scale=d["kv_scale"])
+    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H)
     ws = hswd.workspace(desc, 1, 0)
     with pytest.raises(hswd.HswdError):
         hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
