@@ -93,6 +93,9 @@ def parse():
     ap.add_argument("--heads", type=int, default=H, choices=[8, 16, 32],
                     help="query heads of the 28-layer step over its 8 kv heads (16, 32: "
                          "grouped-query attention, 2 or 4 query heads per kv head)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the whole step as one HIP graph and time its replays "
+                         "(reported beside the eager figures)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter scaling)")
@@ -361,6 +364,47 @@ def main():
                           "extrapolated to 21 sliding + 7 full layers; %d OpenMP threads"
                           % (t_sl, t_fu, threads))}
 
+    graph = None
+    if args.graph:
+        # One graph of the 28 launches.  Plain entry calls: they launch on
+        # torch's current stream, which is the capture stream inside
+        # torch.cuda.graph (bound calls keep the stream they were bound on).
+        def plain_layer(t):
+            if args.mode == "fused" and args.gate == "proj":
+                hswd.layer_step_gproj(t["q"], t["k"], t["v"], t["gx"], t["gw"], t["k_cache"],
+                                      t["v_cache"], t["pos"], t["ring"], t["spec"].rot,
+                                      t["spec"].theta, t["ws"], max_pos=CTX, out=t["out"],
+                                      desc=t["desc"])
+            elif args.mode == "fused":
+                hswd.layer_step(t["q"], t["k"], t["v"], t["gate"], t["k_cache"], t["v_cache"],
+                                t["pos"], t["ring"], t["spec"].rot, t["spec"].theta, t["ws"],
+                                max_pos=CTX, out=t["out"], desc=t["desc"])
+            else:
+                run_layer(t)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for t in layers:
+                plain_layer(t)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in layers:
+                plain_layer(t)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph = {"ms_per_step": round(g0.elapsed_time(g1) / args.steps, 4),
+                 "launches_per_step": LAYERS}
+
     ms_step = t_start.elapsed_time(t_end) / args.steps
     full_us = float(np.mean([a.elapsed_time(b) for a, b in full_ev])) * 1e3
     step_bytes = 21 * layer_bytes("sliding", elt=elt, heads=hq) + 7 * layer_bytes("full", elt=elt, heads=hq)
@@ -402,6 +446,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_max_err": parity,
         "wall_s_timed": round(wall, 3),
+        "graph_replay": graph,
     }
     print(json.dumps(res), flush=True)
 
