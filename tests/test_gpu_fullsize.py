@@ -9,28 +9,33 @@ import torch
 import hybrid_sliding_window_decode_amd as hswd
 import oracle
 from hybrid_sliding_window_decode_amd import inputs
-from gpu_util import TOL, cache_to_host, say
+from gpu_util import CODE, TOL, cache_to_host, entry_codes, say
 
 pytestmark = pytest.mark.gpu
 
-BF16 = oracle.BF16
-
-
 def check_layer(spec, pos, seed, samples):
+    """samples: (stream, query head) pairs; query head h reads kv head h // G."""
     dev = torch.device("cuda", 0)
     ring = spec.kind == "sliding"
+    code = CODE[spec.dtype]
+    G = spec.H // spec.Hkv
     t = inputs.device_step(spec, pos, seed=seed, device=dev)
     B = spec.B
     mp = int(t["pos"].max())
-    desc = hswd.make_desc(t["k_cache"])
+    desc = hswd.make_desc(t["k_cache"], n_heads=spec.H, kv_scale=t.get("kv_scale"))
     ws = hswd.workspace(desc, ring, mp)
+    ks = spec.kv_scale[0] if spec.kv_scale is not None else np.ones(spec.Hkv)
+    vs = spec.kv_scale[1] if spec.kv_scale is not None else np.ones(spec.Hkv)
     # host copies of the sampled blocks before the step writes its entry
     blocks = {}
     for b, h in samples:
-        blocks[(b, h)] = (cache_to_host(t["k_cache"][b, h]), cache_to_host(t["v_cache"][b, h]))
+        g = h // G
+        if (b, g) not in blocks:
+            blocks[(b, g)] = (cache_to_host(t["k_cache"][b, g]), cache_to_host(t["v_cache"][b, g]))
     q, k, v, gate = (t[x].cpu().numpy() for x in ("q", "k", "v", "gate"))
     posh = t["pos"].cpu().numpy()
-    say("full-size %s B=%d pos=%s, %d samples" % (spec.kind, B, list(posh[:4]), len(samples)))
+    say("full-size %s %s B=%d H=%d Hkv=%d pos=%s, %d samples" % (
+        spec.kind, spec.dtype, B, spec.H, spec.Hkv, list(posh[:4]), len(samples)))
     out = hswd.layer_step(t["q"], t["k"], t["v"], t["gate"], t["k_cache"], t["v_cache"], t["pos"],
                           ring, spec.rot, spec.theta, ws, max_pos=mp, desc=desc)
     assert hswd.check_errors(ws) == 0
@@ -41,26 +46,31 @@ def check_layer(spec, pos, seed, samples):
     hswd.rope_apply(torch.zeros_like(t["q"]), kr, t["pos"], spec.rot, spec.theta)
     kr = kr.cpu().numpy()
     worst = 0.0
-    for (b, h), (kc, vc) in blocks.items():
+    for b, h in samples:
+        g = h // G
+        kc, vc = blocks[(b, g)]
         p = int(posh[b])
         n = min(p, spec.n_slots)
         q_rot = oracle.rope(q[b, h][None, None], [p], spec.rot, spec.theta)[0, 0]
-        k_rot = oracle.rope(k[b, h][None, None], [p], spec.rot, spec.theta)[0, 0]
-        k_hat = oracle.round_to(BF16, k_rot.astype(np.float32))
-        v_hat = oracle.round_to(BF16, v[b, h])
-        o = oracle.attend_block(q_rot, kc, vc, BF16, n, k_hat, v_hat, 1.0 / np.sqrt(spec.D))
+        k_rot = oracle.rope(k[b, g][None, None], [p], spec.rot, spec.theta)[0, 0]
+        k_hat = entry_codes(k_rot.astype(np.float32), spec.dtype,
+                            None if spec.kv_scale is None else ks[g])
+        v_hat = entry_codes(v[b, g], spec.dtype, None if spec.kv_scale is None else vs[g])
+        o = oracle.attend_block(q_rot, kc, vc, code, n, k_hat, v_hat, 1.0 / np.sqrt(spec.D),
+                                float(ks[g]), float(vs[g]))
         ref = o * oracle.sigmoid(float(gate[b, h]))
-        vd = oracle.decode(BF16, vc[:n])
-        vmax = max(float(np.abs(vd).max()) if n else 0.0, float(np.abs(v[b, h]).max()))
+        vd = oracle.decode(code, vc[:n]) * float(vs[g])
+        vmax = max(float(np.abs(vd).max()) if n else 0.0, float(np.abs(v[b, g]).max()))
         err = float(np.max(np.abs(out[b, h] - ref)) / vmax)
         worst = max(worst, err)
-        assert err <= TOL["bf16"], (b, h, err)
+        assert err <= TOL[spec.dtype], (b, h, err)
         # the stored entry, bit for bit, given the GPU's float32 rotated key
         row = p % spec.n_slots if ring else p
-        assert np.array_equal(cache_to_host(t["k_cache"][b, h, row]),
-                              oracle.round_to(BF16, kr[b, h]))
-        assert np.array_equal(cache_to_host(t["v_cache"][b, h, row]), v_hat)
-    say("  worst normalised error %.3e over %d sampled (stream, head)" % (worst, len(blocks)))
+        assert np.array_equal(cache_to_host(t["k_cache"][b, g, row]),
+                              entry_codes(kr[b, g], spec.dtype,
+                                          None if spec.kv_scale is None else ks[g]))
+        assert np.array_equal(cache_to_host(t["v_cache"][b, g, row]), v_hat)
+    say("  worst normalised error %.3e over %d sampled (stream, head)" % (worst, len(samples)))
     del t
     torch.cuda.empty_cache()
 
@@ -92,3 +102,17 @@ def test_ragged_full_layer_64_streams():
     chunks of the short streams are empty."""
     pos = inputs.ragged_positions(64, 1, 4096, seed=6)
     check_layer(inputs.full_spec(64, 4097, "bf16"), pos, 4010, samples(64, 8, 24, 5))
+
+
+def test_step_layers_64x4096_fp8():
+    """The fp8 step's layers (per-head scales): 64 streams at 4096."""
+    check_layer(inputs.sliding_spec(64, "fp8"), 4096, 4100, samples(64, 8, 16, 7))
+    check_layer(inputs.full_spec(64, 4097, "fp8"), 4096, 4103, samples(64, 8, 16, 8))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_grouped_step_layers_64x4096(dtype):
+    """The grouped step's layers: 32 query heads over 8 kv heads (4 per kv
+    head), 64 streams at 4096."""
+    check_layer(inputs.sliding_spec(64, dtype, H=32), 4096, 4200, samples(64, 32, 16, 9))
+    check_layer(inputs.full_spec(64, 4097, dtype, H=32), 4096, 4203, samples(64, 32, 16, 10))
