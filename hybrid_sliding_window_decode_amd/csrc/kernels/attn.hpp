@@ -91,10 +91,16 @@ struct AttnParams {
     float qscale;            // softmax scale * log2(e)
 };
 
+// Scores on the matrix cores: 4 query heads per kv head over a 16-bit cache
+// (the score product is then a [4 x D] . [D x keys] contraction).
+template <int DT, int G>
+constexpr bool use_mfma() { return G == 4 && (DT == kBF16 || DT == kF16); }
+
 // Tile geometry.  G query heads per kv head keep G query vectors and G
-// accumulators per lane, so a grouped kernel halves its tile (4 loads of K
-// and of V instead of 8) and reads fp8 rows 8 bytes per lane (8 dims, as for
-// 16-bit rows) to stay within 256 VGPRs (2 waves per SIMD).
+// accumulators per lane, so a grouped VALU kernel halves its tile (4 loads
+// of K and of V instead of 8) and reads fp8 rows 8 bytes per lane (8 dims,
+// as for 16-bit rows) to stay within 256 VGPRs (2 waves per SIMD).  The
+// MFMA kernel keeps no query vectors in registers and keeps 8-load tiles.
 template <int D, int DT, int G = 1>
 struct AttnGeo {
     static constexpr int EB = elt_bytes<DT>();        // element bytes
@@ -102,7 +108,7 @@ struct AttnGeo {
     static constexpr int EPC = CB / EB;               // elements per chunk
     static constexpr int LPR = D / EPC;               // lanes per cache row
     static constexpr int RPI = kWave / LPR;           // rows per wave-wide load
-    static constexpr int NL = G == 1 ? 8 : 4;         // loads per tile (K and V each)
+    static constexpr int NL = G == 1 || use_mfma<DT, G>() ? 8 : 4;   // loads per tile
     static constexpr int KT = NL * RPI;               // keys per wave tile
     static constexpr int STEP = LPR / NL;             // lane stride between reduced keys
     static_assert(LPR >= NL && LPR <= kWave && kWave % LPR == 0, "geometry");
@@ -222,7 +228,18 @@ void attn_kernel(AttnParams P) {
     constexpr int kStash = stash_slots<G>();
     static_assert(G == 1 || G == 2 || G == 4, "query heads per kv head");
 
-    __shared__ float sm_q[G][D];
+    constexpr bool MF = use_mfma<DT, G>();
+    // MFMA kernel: each wave stages its K rows in LDS (rows padded by 16
+    // bytes so the 16 rows an operand read touches fall in distinct banks),
+    // the query heads sit there as 16-bit hi + lo parts, and the
+    // probabilities and rescale factors pass from the score layout (a key
+    // per lane group, a head per lane) to the value layout through LDS.
+    constexpr int KPAD = D * Geo::EB / 16 + 1;           // 16-byte units per staged row
+    __shared__ float sm_q[MF ? 1 : G][D];
+    __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT : 1][MF ? KPAD : 1];
+    __shared__ uint16_t sm_qh[MF ? G : 1][MF ? D : 1], sm_ql[MF ? G : 1][MF ? D : 1];
+    __shared__ float sm_p[MF ? kAttnWaves : 1][MF ? KT : 1][4];
+    __shared__ float sm_al[MF ? kAttnWaves : 1][4];
     __shared__ float sm_o[2][kStash][G][kAttnWaves][D];   // wave chunk partials, by flush parity
     __shared__ float sm_m[2][kStash][G][kAttnWaves], sm_l[2][kStash][G][kAttnWaves];
     __shared__ float sm_dot[G][kAttnWaves];
@@ -299,10 +316,16 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) o_acc[hh][e] = 0.f;
     }
+    // MFMA kernel: the running max and sum of head (lane % 16) over the keys
+    // this lane's group of 4 holds; lanes of heads >= G carry unused values
+    float m1 = -INFINITY, l1 = 0.f;
     Fold run[G];                    // folded chunk partials (wpp == 1)
 
     using Chunk = typename ChunkT<Geo::CB>::type;
     Chunk kA[NL], vA[NL], kB[NL], vB[NL];
+    // MFMA kernel: K goes to LDS as soon as it arrives, so one register tile
+    // of K suffices (LDS is its second buffer); kA, kB are then unused.
+    Chunk kR[MF ? NL : 1];
 
     // Item j of this wave: tile (wid + 4 i) of chunk ch.  Rows past the
     // chunk's valid end are clamped onto its last valid row (never reading an
@@ -313,14 +336,27 @@ void attn_kernel(AttnParams P) {
     auto item_chunk = [&](int j) __attribute__((always_inline)) { return j < n_full_items ? c_begin + j / TPW : c_full; };
     auto item_tile = [&](int j) __attribute__((always_inline)) { return j < n_full_items ? j % TPW : j - n_full_items; };
 
-    auto load_tile = [&](Chunk (&kt)[NL], Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
+    auto load_k = [&](int j) __attribute__((always_inline)) {     // MFMA kernel only
         const int ch = item_chunk(j);
         const int jlast = max(min((ch + 1) * P.K, nv), 1) - 1;
         const int base = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT + r;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
+        for (int i = 0; i < (MF ? NL : 1); ++i) {
             const int row = min(base + i * RPI, jlast);
-            kt[i] = load_kv<Geo::CB>(kbase + (size_t)row * D);
+            kR[i] = load_kv<Geo::CB>(kbase + (size_t)row * D);
+        }
+    };
+
+    auto load_tile = [&](Chunk (&kt)[NL], Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
+        const int ch = item_chunk(j);
+        const int jlast = max(min((ch + 1) * P.K, nv), 1) - 1;
+        const int base = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT + r;
+        if constexpr (!MF) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int row = min(base + i * RPI, jlast);
+                kt[i] = load_kv<Geo::CB>(kbase + (size_t)row * D);
+            }
         }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
@@ -333,59 +369,157 @@ void attn_kernel(AttnParams P) {
         const int ch = item_chunk(j);
         const int jend = min((ch + 1) * P.K, nv);
         const int tile0 = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT;
-        float s[G];
+        if constexpr (MF) {
+            // Scores on the matrix cores.  The wave's K rows go to its LDS
+            // rows (as loaded: row i * RPI + r, 16 bytes at chunk c) and come
+            // back as MFMA operands: S^T[key][head] = K . Q^T for 16 keys at
+            // a time (v_mfma_f32_16x16x32 over 32 dims per slice), with the
+            // query in hi + lo 16-bit parts (about 16 significant bits) and
+            // fp32 accumulation.  Lane l then holds keys 4 (l / 16) + i of
+            // head l % 16; heads >= G read a zero query.
+            using OpT = typename std::conditional<DT == kBF16, __bf16, _Float16>::type;
+            typedef OpT op8 __attribute__((ext_vector_type(8)));
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            constexpr int NG = KT / 16, NS = D / 32;
+            const int hq = lane & 15, kq = lane >> 4;
+            asm volatile("" ::: "memory");     // the query reads below stay in the loop
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            float part[NL];
+            for (int i = 0; i < NL; ++i) sm_k[wid][i * RPI + r][c] = kR[i];
+            // the next item's K into the freed registers, in flight under
+            // this tile's scores and values (rows clamped past the last item)
+            load_k(j + 1);
+            f32x4 acc[NG];
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                float kf[EPC];
-                unpack_chunk<DT>(kt[i], kf);
-                float acc = 0.f;
+            for (int kg = 0; kg < NG; ++kg) acc[kg] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // two slices in flight at a time: unrolled further, the
+            // operand reads of every slice would be issued up front and
+            // hold ~100 registers
+#pragma unroll 2
+            for (int sl = 0; sl < NS; ++sl) {
+                const u32x4 zero = {0u, 0u, 0u, 0u};
+                const u32x4 qh = hq < G ? *reinterpret_cast<const u32x4*>(&sm_qh[hq < G ? hq : 0][32 * sl + 8 * kq]) : zero;
+                const u32x4 ql = hq < G ? *reinterpret_cast<const u32x4*>(&sm_ql[hq < G ? hq : 0][32 * sl + 8 * kq]) : zero;
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) acc = fmaf(qs[hh][e], kf[e], acc);
-                part[i] = acc;
+                for (int kg = 0; kg < NG; ++kg) {
+                    const u32x4 a = sm_k[wid][kg * 16 + hq][4 * sl + kq];
+                    if constexpr (DT == kBF16) {
+                        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, qh), acc[kg], 0, 0, 0);
+                        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, ql), acc[kg], 0, 0, 0);
+                    } else {
+                        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, qh), acc[kg], 0, 0, 0);
+                        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, ql), acc[kg], 0, 0, 0);
+                    }
+                }
             }
-            if constexpr (NL == 8) s[hh] = transposed_reduce8<LPR>(part, lane);
-            else s[hh] = transposed_reduce4<LPR>(part, lane);
-        }
-        const int ki = (lane % LPR) / Geo::STEP;        // load index of this lane's key
-        const int key = tile0 + ki * RPI + r;
-        const bool valid = key < jend;
-        // tile max over the distinct keys (lane bits >= STEP), per head
-        float mx[G];
+            // online softmax per head over this lane's keys, the head's max
+            // across its 4 lanes (distances 16 and 32)
+            float sv[NG][4];
+            float mx = -INFINITY;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            s[hh] = valid ? s[hh] : -INFINITY;
-            mx[hh] = s[hh];
+            for (int kg = 0; kg < NG; ++kg) {
 #pragma unroll
-            for (int m = Geo::STEP; m < kWave; m <<= 1) mx[hh] = xor_max_rt(mx[hh], m);
-        }
-        if (mx[0] == -INFINITY) return;                 // nothing valid in this tile
-        float pr[G];
+                for (int i = 0; i < 4; ++i) {
+                    const int key = tile0 + kg * 16 + 4 * kq + i;
+                    sv[kg][i] = key < jend ? acc[kg][i] : -INFINITY;
+                    mx = fmaxf(mx, sv[kg][i]);
+                }
+            }
+            mx = xor_max<16>(mx);
+            mx = xor_max<32>(mx);
+            if (mx == -INFINITY) return;                // nothing valid in this tile
+            const float m_new = fmaxf(m1, mx);
+            const float alpha = fast_exp2(m1 - m_new);
+            m1 = m_new;
+            float psum = 0.f;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float m_new = fmaxf(m_run[hh], mx[hh]);
-            const float alpha = fast_exp2(m_run[hh] - m_new);
-            pr[hh] = fast_exp2(s[hh] - m_new);
-            m_run[hh] = m_new;
-            l_lane[hh] = l_lane[hh] * alpha + ((lane & (Geo::STEP - 1)) == 0 ? pr[hh] : 0.f);
+            for (int kg = 0; kg < NG; ++kg) {
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= alpha;
-        }
+                for (int i = 0; i < 4; ++i) {
+                    const float pr = fast_exp2(sv[kg][i] - m_new);
+                    psum += pr;
+                    if (hq < G) sm_p[wid][kg * 16 + 4 * kq + i][hq] = pr;
+                }
+            }
+            l1 = l1 * alpha + psum;
+            if (lane < G) sm_al[wid][lane] = alpha;
+            // P.V on the VALU, V rows in their loaded layout: the rescale
+            // factors and each row's probabilities come back from LDS
+            const f32x4 al = *reinterpret_cast<const f32x4*>(&sm_al[wid][0]);
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            // every key's probability to the lanes of its row, all requests
-            // out before the first is used
-            float pk[NL];
+            for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
-            for (int i = 0; i < NL; ++i) pk[i] = lane_value(pr[hh], r * LPR + i * Geo::STEP);
+                for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= al[hh];
+            }
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
+                const f32x4 pv = *reinterpret_cast<const f32x4*>(&sm_p[wid][i * RPI + r][0]);
                 float vf[EPC];
                 unpack_chunk<DT>(vt[i], vf);
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pk[i], vf[e], o_acc[hh][e]);
+                for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pv[hh], vf[e], o_acc[hh][e]);
+                }
+            }
+        } else {
+            float s[G];
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                float part[NL];
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    float kf[EPC];
+                    unpack_chunk<DT>(kt[i], kf);
+                    float acc = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) acc = fmaf(qs[hh][e], kf[e], acc);
+                    part[i] = acc;
+                }
+                if constexpr (NL == 8) s[hh] = transposed_reduce8<LPR>(part, lane);
+                else s[hh] = transposed_reduce4<LPR>(part, lane);
+            }
+            const int ki = (lane % LPR) / Geo::STEP;        // load index of this lane's key
+            const int key = tile0 + ki * RPI + r;
+            const bool valid = key < jend;
+            // tile max over the distinct keys (lane bits >= STEP), per head
+            float mx[G];
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                s[hh] = valid ? s[hh] : -INFINITY;
+                mx[hh] = s[hh];
+#pragma unroll
+                for (int m = Geo::STEP; m < kWave; m <<= 1) mx[hh] = xor_max_rt(mx[hh], m);
+            }
+            if (mx[0] == -INFINITY) return;                 // nothing valid in this tile
+            float pr[G];
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                const float m_new = fmaxf(m_run[hh], mx[hh]);
+                const float alpha = fast_exp2(m_run[hh] - m_new);
+                pr[hh] = fast_exp2(s[hh] - m_new);
+                m_run[hh] = m_new;
+                l_lane[hh] = l_lane[hh] * alpha + ((lane & (Geo::STEP - 1)) == 0 ? pr[hh] : 0.f);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= alpha;
+            }
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                // every key's probability to the lanes of its row, all requests
+                // out before the first is used
+                float pk[NL];
+#pragma unroll
+                for (int i = 0; i < NL; ++i) pk[i] = lane_value(pr[hh], r * LPR + i * Geo::STEP);
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    float vf[EPC];
+                    unpack_chunk<DT>(vt[i], vf);
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pk[i], vf[e], o_acc[hh][e]);
+                }
             }
         }
     };
@@ -441,9 +575,11 @@ void attn_kernel(AttnParams P) {
     };
 
     auto end_chunk = [&](int ch) __attribute__((always_inline)) {
-        float l_w[G];
+        float l_w[G] = {};
+        if constexpr (!MF) {
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) l_w[hh] = wave_sum(l_lane[hh]);
+            for (int hh = 0; hh < G; ++hh) l_w[hh] = wave_sum(l_lane[hh]);
+        }
 #pragma unroll
         for (int m = LPR; m < kWave; m <<= 1) {
 #pragma unroll
@@ -459,7 +595,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) sm_o[buf][n_st][hh][wid][c * EPC + e] = o_acc[hh][e];
             }
-            if (lane == 0) {
+            if (!MF && lane == 0) {
                 sm_m[buf][n_st][hh][wid] = m_run[hh];
                 sm_l[buf][n_st][hh][wid] = l_w[hh];
             }
@@ -467,6 +603,17 @@ void attn_kernel(AttnParams P) {
             l_lane[hh] = 0.f;
 #pragma unroll
             for (int e = 0; e < EPC; ++e) o_acc[hh][e] = 0.f;
+        }
+        if constexpr (MF) {
+            // head (lane % 16): its max is already the same in its 4 lanes;
+            // its sum adds the 4 lanes' shares
+            const float lw = xor_sum<32>(xor_sum<16>(l1));
+            if (lane < G) {
+                sm_m[buf][n_st][lane][wid] = m1;
+                sm_l[buf][n_st][lane][wid] = lw;
+            }
+            m1 = -INFINITY;
+            l1 = 0.f;
         }
         if (n_st == 0) st_first = ch;
         ++n_st;
@@ -507,6 +654,7 @@ void attn_kernel(AttnParams P) {
     for (int hh = 0; hh < G; ++hh)
         glogit[hh] = MODE == kModeStep && !gproj && P.gate != nullptr ? P.gate[bh0 + hh] : 0.f;
 
+    if constexpr (MF) load_k(0);
     load_tile(kA, vA, 0);
     load_tile(kB, vB, 1);
 
@@ -528,7 +676,15 @@ void attn_kernel(AttnParams P) {
         for (int hh = 0; hh < G; ++hh) {
             const float q_r = rotated ? rope_rotate(q_t[hh], q_p[hh], td < half, cs, sn) : q_t[hh];
             qsc[hh] = q_r * qmul;
-            if (t < D) sm_q[hh][t] = qsc[hh];
+            if (t < D) {
+                if constexpr (MF) {          // 16-bit hi + lo parts for the MFMA operand
+                    const auto hi = round_to_elt<DT>(qsc[hh]);
+                    sm_qh[hh][t] = hi;
+                    sm_ql[hh][t] = round_to_elt<DT>(qsc[hh] - elt_to_f32<DT>(hi));
+                } else {
+                    sm_q[hh][t] = qsc[hh];
+                }
+            }
         }
     }
 
@@ -566,10 +722,12 @@ void attn_kernel(AttnParams P) {
         }
     }
     __syncthreads();
+    if constexpr (!MF) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
+        for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) qs[hh][e] = sm_q[hh][c * EPC + e];
+            for (int e = 0; e < EPC; ++e) qs[hh][e] = sm_q[hh][c * EPC + e];
+        }
     }
 
     // Chunk boundaries fall after the items j with (j + 1) % TPW == 0 among
