@@ -91,10 +91,11 @@ struct AttnParams {
     float qscale;            // softmax scale * log2(e)
 };
 
-// Scores on the matrix cores: 4 query heads per kv head over a 16-bit cache
-// (the score product is then a [4 x D] . [D x keys] contraction).
+// Scores on the matrix cores: 4 query heads per kv head over a 16-bit or
+// fp8 cache (the score product is then a [4 x D] . [D x keys] contraction;
+// fp8 keys are staged as bf16, which holds every e4m3 value exactly).
 template <int DT, int G>
-constexpr bool use_mfma() { return G == 4 && (DT == kBF16 || DT == kF16); }
+constexpr bool use_mfma() { return G == 4 && (DT == kBF16 || DT == kF16 || DT == kFP8); }
 
 // Tile geometry.  G query heads per kv head keep G query vectors and G
 // accumulators per lane, so a grouped VALU kernel halves its tile (4 loads
@@ -234,7 +235,7 @@ void attn_kernel(AttnParams P) {
     // the query heads sit there as 16-bit hi + lo parts, and the
     // probabilities and rescale factors pass from the score layout (a key
     // per lane group, a head per lane) to the value layout through LDS.
-    constexpr int KPAD = D * Geo::EB / 16 + 1;           // 16-byte units per staged row
+    constexpr int KPAD = D * 2 / 16 + 1;                  // 16-byte units per staged (16-bit) row
     __shared__ float sm_q[MF ? 1 : G][D];
     __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT : 1][MF ? KPAD : 1];
     __shared__ uint16_t sm_qh[MF ? G : 1][MF ? D : 1], sm_ql[MF ? G : 1][MF ? D : 1];
@@ -377,14 +378,17 @@ void attn_kernel(AttnParams P) {
             // query in hi + lo 16-bit parts (about 16 significant bits) and
             // fp32 accumulation.  Lane l then holds keys 4 (l / 16) + i of
             // head l % 16; heads >= G read a zero query.
-            using OpT = typename std::conditional<DT == kBF16, __bf16, _Float16>::type;
+            using OpT = typename std::conditional<DT == kF16, _Float16, __bf16>::type;
             typedef OpT op8 __attribute__((ext_vector_type(8)));
             typedef float f32x4 __attribute__((ext_vector_type(4)));
             constexpr int NG = KT / 16, NS = D / 32;
             const int hq = lane & 15, kq = lane >> 4;
             asm volatile("" ::: "memory");     // the query reads below stay in the loop
 #pragma unroll
-            for (int i = 0; i < NL; ++i) sm_k[wid][i * RPI + r][c] = kR[i];
+            for (int i = 0; i < NL; ++i) {
+                if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_bf16x8(kR[i]);
+                else sm_k[wid][i * RPI + r][c] = kR[i];
+            }
             // the next item's K into the freed registers, in flight under
             // this tile's scores and values (rows clamped past the last item)
             load_k(j + 1);
@@ -402,7 +406,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
                     const u32x4 a = sm_k[wid][kg * 16 + hq][4 * sl + kq];
-                    if constexpr (DT == kBF16) {
+                    if constexpr (DT != kF16) {
                         acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, qh), acc[kg], 0, 0, 0);
                         acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -678,9 +682,10 @@ void attn_kernel(AttnParams P) {
             qsc[hh] = q_r * qmul;
             if (t < D) {
                 if constexpr (MF) {          // 16-bit hi + lo parts for the MFMA operand
-                    const auto hi = round_to_elt<DT>(qsc[hh]);
+                    constexpr int QT = DT == kF16 ? kF16 : kBF16;
+                    const uint16_t hi = round_to_elt<QT>(qsc[hh]);
                     sm_qh[hh][t] = hi;
-                    sm_ql[hh][t] = round_to_elt<DT>(qsc[hh] - elt_to_f32<DT>(hi));
+                    sm_ql[hh][t] = round_to_elt<QT>(qsc[hh] - elt_to_f32<QT>(hi));
                 } else {
                     sm_q[hh][t] = qsc[hh];
                 }

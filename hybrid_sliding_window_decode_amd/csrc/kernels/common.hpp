@@ -169,6 +169,20 @@ __device__ __forceinline__ void unpack_chunk(const u32x4& w, float* f) {
     }
 }
 
+// Eight fp8 codes (byte order) -> eight bf16 values, exactly: every e4m3
+// value is a bf16 value, so the bf16 is the upper half of the float.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(const u32x2& w) {
+    const uint32_t u[2] = {w.x, w.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const f32x2 lo = fp8x2_to_f32(u[j], false), hi = fp8x2_to_f32(u[j], true);
+        o[2 * j] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
+        o[2 * j + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
 // Unpack one 8-byte chunk of fp8 codes into 8 floats, in byte order.
 template <int DT>
 __device__ __forceinline__ void unpack_chunk(const u32x2& w, float* f) {
