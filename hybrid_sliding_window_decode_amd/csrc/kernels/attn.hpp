@@ -392,9 +392,14 @@ void attn_kernel(AttnParams P) {
             // the next item's K into the freed registers, in flight under
             // this tile's scores and values (rows clamped past the last item)
             load_k(j + 1);
-            f32x4 acc[NG];
+            // four accumulators per key group (query hi / lo part, even / odd
+            // slice) keep the matrix-core chains short; summed at the end
+            f32x4 acc[NG][4];
 #pragma unroll
-            for (int kg = 0; kg < NG; ++kg) acc[kg] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kg = 0; kg < NG; ++kg) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[kg][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
             // two slices in flight at a time: unrolled further, the
             // operand reads of every slice would be issued up front and
             // hold ~100 registers
@@ -406,16 +411,18 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
                     const u32x4 a = sm_k[wid][kg * 16 + hq][4 * sl + kq];
+                    f32x4& ah = acc[kg][2 * (sl & 1)];
+                    f32x4& al_ = acc[kg][2 * (sl & 1) + 1];
                     if constexpr (DT != kF16) {
-                        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, qh), acc[kg], 0, 0, 0);
-                        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, ql), acc[kg], 0, 0, 0);
+                        ah = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, qh), ah, 0, 0, 0);
+                        al_ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, ql), al_, 0, 0, 0);
                     } else {
-                        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, qh), acc[kg], 0, 0, 0);
-                        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, ql), acc[kg], 0, 0, 0);
+                        ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, qh), ah, 0, 0, 0);
+                        al_ = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, ql), al_, 0, 0, 0);
                     }
                 }
             }
@@ -428,7 +435,8 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = tile0 + kg * 16 + 4 * kq + i;
-                    sv[kg][i] = key < jend ? acc[kg][i] : -INFINITY;
+                    const float sc = (acc[kg][0][i] + acc[kg][1][i]) + (acc[kg][2][i] + acc[kg][3][i]);
+                    sv[kg][i] = key < jend ? sc : -INFINITY;
                     mx = fmaxf(mx, sv[kg][i]);
                 }
             }
