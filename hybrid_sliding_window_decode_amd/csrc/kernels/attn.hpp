@@ -238,7 +238,9 @@ void attn_kernel(AttnParams P) {
     constexpr int KPAD = D * 2 / 16 + 1;                  // 16-byte units per staged (16-bit) row
     __shared__ float sm_q[MF ? 1 : G][D];
     __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT : 1][MF ? KPAD : 1];
-    __shared__ uint16_t sm_qh[MF ? G : 1][MF ? D : 1], sm_ql[MF ? G : 1][MF ? D : 1];
+    // query rows padded by 16 bytes too: unpadded, the G heads' rows (512
+    // bytes apart) would share banks and the operand reads conflict 4 ways
+    __shared__ uint16_t sm_qh[MF ? G : 1][MF ? D + 8 : 1], sm_ql[MF ? G : 1][MF ? D + 8 : 1];
     __shared__ float sm_p[MF ? kAttnWaves : 1][MF ? KT : 1][4];
     __shared__ float sm_al[MF ? kAttnWaves : 1][4];
     __shared__ float sm_o[2][kStash][G][kAttnWaves][D];   // wave chunk partials, by flush parity
