@@ -18,7 +18,7 @@ namespace {
 
 using namespace hswd;
 
-constexpr int kVersion = (0 << 16) | 4;
+constexpr int kVersion = (0 << 16) | 5;
 constexpr size_t kAlign = 256;
 constexpr int kWgsPerCu = 2;          // resident attention workgroups per CU (VGPR bound)
 

@@ -96,7 +96,11 @@ typedef enum {
 typedef struct {
     int32_t batch;          /* B >= 1 */
     int32_t n_heads;        /* H */
-    int32_t n_kv_heads;     /* Hkv, H % Hkv == 0 (the decode kernels take H == Hkv) */
+    int32_t n_kv_heads;     /* Hkv, H % Hkv == 0.  Query head h reads kv head
+                               h / (H / Hkv) (grouped-query attention by reshaping
+                               the query [talker]); the attention entries take
+                               H / Hkv = 1, or 2 and 4 with a 16-bit or fp8 cache
+                               and head_dim 128 or 256, else UNSUPPORTED */
     int32_t head_dim;       /* D: 64, 128 or 256 (fp8 caches: 128 or 256) */
     int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows */
     int32_t kv_dtype;       /* hswd_dtype of the cache */
