@@ -52,20 +52,23 @@ int32_t desc_check(const hswd_attn_desc* d) {
     return HSWD_OK;
 }
 
-// Default keys per chunk, from the cache geometry and element type only
-// (never the batch): 2^floor(log2(n_slots / 32)) clamped to [128, 512], and
-// at least four quanta (a quantum, one tile per wave, is the keys of 32 KiB
-// of K rows), so each wave scores four tiles per chunk end.  Short caches get
-// small chunks, so a small batch still spreads over many workgroups; long
-// caches get 512-key chunks, so the merge folds fewer partials; the floor
-// keeps the per-chunk reduction off the streaming rate (fp8 rows are half
-// the bytes, so its chunks hold twice the keys).
+// Default keys per chunk, from the cache geometry, element type and head
+// grouping only (never the batch): 2^floor(log2(n_slots / 32)) clamped to
+// [128, 512], and at least four quanta (a quantum, one tile per wave, is the
+// keys of 32 KiB of K rows), so each wave scores four tiles per chunk end;
+// grouped layers (H > Hkv) at least eight, since their stash holds a single
+// chunk and every chunk end is a barrier.  Short caches get small chunks, so
+// a small batch still spreads over many workgroups; long caches get 512-key
+// chunks, so the merge folds fewer partials; the floor keeps the per-chunk
+// reduction off the streaming rate (fp8 rows are half the bytes, so its
+// chunks hold twice the keys).
 int chunk_keys(const hswd_attn_desc* d) {
     if (d->keys_per_split > 0) return d->keys_per_split;
     int k = 128;
     while (k < 512 && (long)k * 2 * 32 <= d->n_slots) k *= 2;
-    const int q4 = 4 * chunk_quantum(d->head_dim, d->kv_dtype);
-    return k < q4 ? q4 : k;
+    const int quanta = d->n_heads > d->n_kv_heads ? 8 : 4;
+    const int floor_keys = quanta * chunk_quantum(d->head_dim, d->kv_dtype);
+    return k < floor_keys ? floor_keys : k;
 }
 
 // Chunks over the key range: a function of the cache geometry and max_pos

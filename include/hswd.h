@@ -109,9 +109,10 @@ typedef struct {
                                the valid keys are cut into chunks of this many,
                                each chunk's softmax partial is formed alone and
                                the partials are folded in chunk order.  0 =
-                               library default from the cache length and the
-                               element type only: 2^floor(log2(n_slots/32))
-                               clamped to [128, 512], and at least 4 quanta.
+                               library default from the cache length, element
+                               type and head grouping only: 2^floor(log2(
+                               n_slots/32)) clamped to [128, 512], and at least
+                               4 quanta (8 when n_heads > n_kv_heads).
                                Else a multiple of the quantum Q = 32768 /
                                (head_dim * element bytes) keys (4 waves, one
                                8-load tile each): 64 for D = 256 and a 16-bit

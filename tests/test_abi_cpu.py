@@ -64,6 +64,10 @@ def test_workspace_and_splits():
     assert hswd.num_splits(desc(n_slots=4097, keys_per_split=1024), 0, 4096) == 4
     assert hswd.num_splits(desc(n_slots=4097, keys_per_split=128), 0, 4096) == 32
     assert hswd.num_splits(desc(n_slots=4097, chunks_per_workgroup=3), 0, 4096) == 16
+    # grouped layers: at least eight quanta (512 keys bf16, 1024 fp8)
+    assert hswd.num_splits(desc(n_slots=4097, n_heads=32), 0, 4096) == 8
+    assert hswd.num_splits(desc(n_slots=4097, n_heads=32, kv_dtype=3), 0, 4096) == 4
+    assert hswd.num_splits(desc(n_heads=16), 1, 0) == 1
     # splits never depend on the batch
     assert hswd.num_splits(desc(batch=1, n_slots=4097), 0, 4096) == \
         hswd.num_splits(desc(batch=64, n_slots=4097), 0, 4096)
