@@ -187,8 +187,9 @@ def log(*a):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
-              "(the path shards by stream with no exchange, see DESIGN.md)" % args.gpus,
+        print("bench.py measures one GPU; --gpus %d is not supported (streams are "
+              "independent: each GPU would run this same step on its share of the "
+              "streams, with no exchange)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

@@ -18,7 +18,7 @@
  *   [TensorFold#608]   TensorFold pull request 608 "Qwen3.8-27B on CUDA",
  *                      review thread on split decode attention and its merge.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - softmax scale is a parameter (1/sqrt(head_dim) by default);
  *   - RoPE pairs element i with i + rot/2 ("rotate half") unless
  *     `interleaved` asks for pairs (2i, 2i+1); inverse frequencies run over
