@@ -290,11 +290,14 @@ class BoundCall:
     """One library entry point with its arguments marshalled once: calling it
     launches on the stream that was current when it was bound and returns the
     output tensor.  For loops that issue the same launch many times (a decode
-    step per layer), so each launch costs one foreign call.  The tensors it
-    was bound with must stay alive and unmoved while it is used."""
+    step per layer), so each launch costs one foreign call.  It holds
+    references to the tensors and the descriptor it was bound with, so their
+    memory stays valid while it exists; their contents are read at each
+    launch."""
 
-    def __init__(self, name, fn, args, out):
+    def __init__(self, name, fn, args, out, keep=()):
         self.name, self._fn, self._args, self.out = name, fn, args, out
+        self._keep = tuple(keep)
 
     def __call__(self):
         status = self._fn(*self._args)
@@ -330,7 +333,8 @@ def bind_layer_step(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, 
     """layer_step with its arguments checked and marshalled once (BoundCall)."""
     out, args = _layer_step_args(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta,
                                  ws, max_pos, out, desc)
-    return BoundCall("hswd_layer_step", lib().hswd_layer_step, args, out)
+    return BoundCall("hswd_layer_step", lib().hswd_layer_step, args, out,
+                     keep=(q, k, v, gate, k_cache, v_cache, pos, ws, desc))
 
 
 def gate_proj(x, w_g, out=None):
@@ -378,7 +382,8 @@ def bind_layer_step_gproj(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim,
     """layer_step_gproj with its arguments checked and marshalled once (BoundCall)."""
     out, args = _layer_step_gproj_args(q, k, v, x, w_g, k_cache, v_cache, pos, ring, rot_dim,
                                        theta, ws, max_pos, out, desc)
-    return BoundCall("hswd_layer_step_gproj", lib().hswd_layer_step_gproj, args, out)
+    return BoundCall("hswd_layer_step_gproj", lib().hswd_layer_step_gproj, args, out,
+                     keep=(q, k, v, x, w_g, k_cache, v_cache, pos, ws, desc))
 
 
 def check_errors(ws):
