@@ -115,6 +115,7 @@ SINGLE_LAYER = {
     "sliding_64xragged_bf16": ("sliding", 64, "bf16", "ragged", 3, 8),
     "long_full_8x131072_bf16": ("full", 8, "bf16", 131072, 5, 8),
     "long_sliding_8x131072_bf16": ("sliding", 8, "bf16", 131072, 5, 8),
+    "long_full_1x1048576_bf16": ("full", 1, "bf16", 1 << 20, 9, 8),
     "gqa4_full_64x4096_bf16": ("full", 64, "bf16", 4096, 6, 32),
     "gqa4_sliding_64x4096_bf16": ("sliding", 64, "bf16", 4096, 6, 32),
     "gqa2_full_64x4096_bf16": ("full", 64, "bf16", 4096, 7, 16),

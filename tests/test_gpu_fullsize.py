@@ -116,3 +116,11 @@ def test_grouped_step_layers_64x4096(dtype):
     head), 64 streams at 4096."""
     check_layer(inputs.sliding_spec(64, dtype, H=32), 4096, 4200, samples(64, 32, 16, 9))
     check_layer(inputs.full_spec(64, 4097, dtype, H=32), 4096, 4203, samples(64, 32, 16, 10))
+
+
+def test_max_context_1x1048576():
+    """One stream at context 2^20 on a full layer (8.6 GB of cache, 2048
+    chunks of 512 keys, hundreds of workgroups per kv head merged by the
+    last to arrive): the largest context the tests exercise; the library
+    takes up to 4096 chunks."""
+    check_layer(inputs.full_spec(1, (1 << 20) + 1, "bf16"), 1 << 20, 5100, samples(1, 8, 8, 11))
