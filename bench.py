@@ -13,7 +13,8 @@ Reported `value`: algorithmic HBM bytes of the step (valid K/V rows plus
 per-token input/output) / step time, in GB/s.  `roofline` covers the
 dominant kernel, the full-layer launch, timed with HIP events on the stream
 it runs on, inside the timed region.  `cpu_baseline` is the fp64 CPU oracle
-timed on two layers of the same step on the host cores (rank 0 only).
+timed on the host cores over one period of the interleave (layers 0-3) of
+the same step, repeated for about ten seconds, after the timed region.
 
     python bench.py [--steps K] [--warmup W] [--mode fused|unfused]
 """
@@ -28,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn µs/layer-step + achieved HBM GB/s (% peak), 64 streams × 4k ctx"
 PEAK_HBM_GBS = 8000.0                 # MI355X HBM3E, vendor figure
+CPU_SECONDS = 10.0                    # host work of the oracle baseline's sample
 B, H, HKV, D, S_RING, CTX, LAYERS = 64, 8, 8, 256, 511, 4096, 28
 
 
@@ -81,8 +83,8 @@ def measured_traffic(kv):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", choices=["fused", "unfused"], default="fused")
     ap.add_argument("--gate", choices=["logits", "proj"], default="logits",
                     help="gate logits given per layer (default), or projected in the "
@@ -273,8 +275,10 @@ def main():
         hswd.kv_slot_write(t["k_cache"], t["v_cache"], t["k_rot"], t["v"], t["pos"], t["ring"],
                            t["ws"], desc=t["desc"])
 
-    # ---- parity before timing: layers 0 (sliding) and 3 (full) vs the oracle
-    sample = [0, 3]
+    # ---- parity before timing: the first period of the interleave (layers
+    # 0-2 sliding, 3 full) against the oracle; host copies of those layers'
+    # inputs are taken before the first pass writes the new entries
+    sample = [0, 1, 2, 3]
     host = {}
     for l in sample:
         t = layers[l]
@@ -283,6 +287,9 @@ def main():
                        t[k].view(torch.uint8).cpu().numpy()
                        if t[k].dtype == torch.float8_e4m3fn else t[k].cpu().numpy())
                    for k in ("q", "k", "v", "gate", "k_cache", "v_cache", "pos")}
+        if args.gate == "proj":
+            host[l]["gx"] = t["gx"].cpu().numpy()
+            host[l]["gw"] = t["gw"].cpu().numpy()
     for t in layers:
         run_layer(t)
     torch.cuda.synchronize()
@@ -300,13 +307,12 @@ def main():
     n_full = sum(1 for l in range(LAYERS) if is_full(l))
     full_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps * n_full)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    t_start.record(stream)
+    step_ev[0].record(stream)
     ev = iter(full_ev)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         for l, t in enumerate(layers):
             if is_full(l):
                 e0, e1 = next(ev)
@@ -315,7 +321,7 @@ def main():
                 e1.record(stream)
             else:
                 run_layer(t)
-    t_end.record(stream)
+        step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
 
@@ -327,44 +333,50 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        times = {}
+
+        def oracle_layer(l):
+            h = host[l]
+            spec = layers[l]["spec"]
+            gate_h = None if args.gate == "proj" else h["gate"]
+            r = oracle.layer_step(h["q"], h["k"], h["v"], gate_h, h["k_cache"], h["v_cache"],
+                                  h["pos"], oracle.DTYPES[kv], spec.kind == "sliding", spec.rot,
+                                  spec.theta, write=False, kv_scale=spec.kv_scale)
+            if args.gate == "proj":
+                lg = oracle.gate_proj(h["gx"], h["gw"])
+                r["out"] = r["o_pre"] * (1.0 / (1.0 + np.exp(-lg)))[:, :, None]
+            return r
+
+        # The sample: the period of the interleave (3 sliding layers, 1 full)
+        # run end to end, repeated until about CPU_SECONDS of work (at least
+        # 3 runs); a step is 7 periods.
+        periods = []
+        t_cpu0 = time.perf_counter()
+        while len(periods) < 3 or time.perf_counter() - t_cpu0 < CPU_SECONDS:
+            t0 = time.perf_counter()
+            res_l = {l: oracle_layer(l) for l in sample}
+            periods.append(time.perf_counter() - t0)
         for l in sample:
             h = host[l]
             spec = layers[l]["spec"]
-            best = None
-            for rep in range(3):
-                kc, vc = h["k_cache"], h["v_cache"]
-                t0 = time.perf_counter()
-                gate_h = None if args.gate == "proj" else h["gate"]
-                r = oracle.layer_step(h["q"], h["k"], h["v"], gate_h, kc, vc, h["pos"],
-                                      oracle.DTYPES[kv], spec.kind == "sliding", spec.rot,
-                                      spec.theta, write=False, kv_scale=spec.kv_scale)
-                if args.gate == "proj":
-                    lg = oracle.gate_proj(layers[l]["gx"].cpu().numpy(),
-                                          layers[l]["gw"].cpu().numpy())
-                    r["out"] = r["o_pre"] * (1.0 / (1.0 + np.exp(-lg)))[:, :, None]
-                dt = time.perf_counter() - t0
-                best = dt if best is None else min(best, dt)
-                times.setdefault(l, []).append(dt)
             vmax = np.abs(oracle.decode(oracle.DTYPES[kv], h["v_cache"]))
             if spec.kv_scale is not None:
                 vmax = vmax * spec.kv_scale[1][None, :, None, None]
             vmax = float(np.nanmax(np.where(np.isnan(vmax), 0.0, vmax)))
-            err = float(np.max(np.abs(gpu_out[l] - r["out"])) / max(vmax, 1e-30))
+            err = float(np.max(np.abs(gpu_out[l] - res_l[l]["out"])) / max(vmax, 1e-30))
             parity["layer%d_%s" % (l, spec.kind)] = err
             assert err <= 2e-3, ("parity", l, err)
-            log("oracle layer %d (%s): %s s, GPU parity %.2e" % (
-                l, spec.kind, ", ".join("%.2f" % x for x in times[l]), err))
-        t_sl = float(np.median(times[0]))
-        t_fu = float(np.median(times[3]))
-        step_cpu = 21 * t_sl + 7 * t_fu
+            log("layer %d (%s): GPU vs oracle %.2e" % (l, spec.kind, err))
+        t_period = float(np.median(periods))
+        log("oracle period (layers 0-3): %d runs, median %.3f s" % (len(periods), t_period))
+        step_cpu = (LAYERS // 4) * t_period
         step_bytes = 21 * layer_bytes("sliding", elt=elt, heads=hq) + 7 * layer_bytes("full", elt=elt, heads=hq)
         cpu = {"value": round(step_bytes / step_cpu / 1e9, 3), "unit": "GB/s",
                "cores": threads, "kind": "oracle",
-               "sample": ("fp64 oracle on layer 0 (sliding) and layer 3 (full) of the same "
-                          "step, 64 streams x 4096, median of 3 runs each (%.2f s, %.2f s), "
-                          "extrapolated to 21 sliding + 7 full layers; %d OpenMP threads"
-                          % (t_sl, t_fu, threads))}
+               "sample": ("fp64 oracle over layers 0-3 of the same step (3 sliding + 1 full, "
+                          "one period of the interleave; 64 streams x 4096, host copies of "
+                          "the same data), %d runs in %.1f s, median %.3f s per period, x7 "
+                          "periods per step; %d OpenMP threads"
+                          % (len(periods), sum(periods), t_period, threads))}
 
     graph = None
     if args.graph:
@@ -407,7 +419,8 @@ def main():
         graph = {"ms_per_step": round(g0.elapsed_time(g1) / args.steps, 4),
                  "launches_per_step": LAYERS}
 
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = step_ev[0].elapsed_time(step_ev[-1]) / args.steps
+    step_ms = np.array([a.elapsed_time(b) for a, b in zip(step_ev[:-1], step_ev[1:])])
     full_us = float(np.mean([a.elapsed_time(b) for a, b in full_ev])) * 1e3
     step_bytes = 21 * layer_bytes("sliding", elt=elt, heads=hq) + 7 * layer_bytes("full", elt=elt, heads=hq)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -435,6 +448,8 @@ def main():
                    "head_dim": D, "kv_dtype": kv, "launch": args.mode,
                    "gate": "logits given" if args.gate == "logits" else
                    "projected in-launch from x[64,2048] by w_g[%d,2048]" % hq},
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4)
+                                    for q in (10, 50, 90)],
         "us_per_layer_step": round(ms_step * 1e3 / LAYERS, 2),
         "us_full_layer": round(full_us, 2),
         "us_sliding_layer_est": round(sl_us_est, 2),
