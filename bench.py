@@ -92,13 +92,15 @@ def parse():
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="cache element type of the 28-layer step (fp8: OCP e4m3 with "
                          "per-head scales)")
-    ap.add_argument("--heads", type=int, default=H, choices=[8, 16, 32],
-                    help="query heads of the 28-layer step over its 8 kv heads (16, 32: "
-                         "grouped-query attention, 2 or 4 query heads per kv head)")
+    ap.add_argument("--heads", type=int, default=H, choices=[8, 16, 24, 32, 64],
+                    help="query heads of the 28-layer step over its 8 kv heads (16, 24, 32, "
+                         "64: grouped-query attention, 2, 3, 4 or 8 query heads per kv head)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture the whole step as one HIP graph and time its replays "
                          "(reported beside the eager figures)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--workload", default="step28_64x4096_bf16",
@@ -325,6 +327,35 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
 
+    # ---- the streaming-read ceiling: a plain read of 2 GiB (beyond the
+    # 256 MB last-level cache) with the attention kernel's loads, at a few
+    # grid sizes; the best median is the ceiling the full layer is compared with
+    ceiling = None
+    if not args.no_ceiling:
+        buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+        best = None
+        for wgs in (1024, 2048, 4096, 8192):
+            for _ in range(3):
+                hswd.stream_read(buf, wgs, sink)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+            evs[0].record(stream)
+            for i in range(20):
+                hswd.stream_read(buf, wgs, sink)
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(20)]))
+            gbs = buf.numel() / (us * 1e-6) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, wgs, us)
+        ceiling = {"value": round(best[0], 1), "unit": "GB/s", "bytes": buf.numel(),
+                   "workgroups": best[1], "us": round(best[2], 2),
+                   "kernel": "hswd_stream_read (128-bit non-temporal loads, contiguous "
+                             "range per workgroup)"}
+        log("streaming-read ceiling: %.1f GB/s (%d workgroups)" % (best[0], best[1]))
+        del buf, sink
+        torch.cuda.empty_cache()
+
     # ---- parity of the first pass (outputs kept above) and the CPU oracle
     # baseline, after the timed region so the host's OpenMP threads cannot
     # delay the launches being timed
@@ -368,10 +399,27 @@ def main():
             log("layer %d (%s): GPU vs oracle %.2e" % (l, spec.kind, err))
         t_period = float(np.median(periods))
         log("oracle period (layers 0-3): %d runs, median %.3f s" % (len(periods), t_period))
+        # the same period on one thread (OpenMP's thread count for this
+        # thread's parallel regions), once
+        t_one = None
+        try:
+            import ctypes
+            gomp = ctypes.CDLL("libgomp.so.1")
+            gomp.omp_set_num_threads(1)
+            t0 = time.perf_counter()
+            for l in sample:
+                oracle_layer(l)
+            t_one = time.perf_counter() - t0
+            gomp.omp_set_num_threads(threads)
+            log("oracle period on 1 thread: %.3f s" % t_one)
+        except OSError:
+            pass
         step_cpu = (LAYERS // 4) * t_period
         step_bytes = 21 * layer_bytes("sliding", elt=elt, heads=hq) + 7 * layer_bytes("full", elt=elt, heads=hq)
         cpu = {"value": round(step_bytes / step_cpu / 1e9, 3), "unit": "GB/s",
                "cores": threads, "kind": "oracle",
+               "value_1thread": (None if t_one is None else
+                                 round(step_bytes / ((LAYERS // 4) * t_one) / 1e9, 3)),
                "sample": ("fp64 oracle over layers 0-3 of the same step (3 sliding + 1 full, "
                           "one period of the interleave; 64 streams x 4096, host copies of "
                           "the same data), %d runs in %.1f s, median %.3f s per period, x7 "
@@ -459,7 +507,10 @@ def main():
                      "traffic": measured_traffic(kv) if hq == HKV else None,
                      "kernel": "attn_kernel<256, %s, append, step, %d query heads per kv head> "
                                "(full layer, one launch)" % (kv, hq // HKV),
-                     "bytes_per_launch": full_bytes},
+                     "bytes_per_launch": full_bytes,
+                     "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": (None if ceiling is None else
+                                              round(achieved / ceiling["value"], 4))},
         "cpu_baseline": cpu,
         "parity_max_err": parity,
         "wall_s_timed": round(wall, 3),

@@ -59,6 +59,7 @@ SIGNATURES = {
     "hswd_head_gate": ([_P, _P, _P, _I, _I, _I, _P], _I),
     "hswd_layer_step": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _D, _I, _DP, _P, _Z, _P], _I),
     "hswd_check_errors": ([_P, ctypes.POINTER(ctypes.c_int32), _P], _I),
+    "hswd_stream_read": ([_P, _Z, _P, _I, _P], _I),
     "hswd_gate_proj": ([_P, _P, _P, _I, _I, _I, _P], _I),
     "hswd_layer_step_gproj": ([_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _D, _I, _DP, _P,
                                _Z, _P], _I),
@@ -393,3 +394,18 @@ def check_errors(ws):
     if st not in (0, -4):
         raise HswdError("hswd_check_errors", st)
     return flags.value
+
+
+def stream_read(buf, workgroups=2048, sink=None):
+    """Read a device buffer once (measurement helper; see hswd_stream_read).
+    Returns the sink tensor [workgroups] int32 (never written in practice)."""
+    _need(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.zeros(workgroups, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", torch.int32)
+    if sink.numel() < workgroups:
+        raise ValueError("sink must hold at least `workgroups` int32 values")
+    _check("hswd_stream_read", lib().hswd_stream_read(_ptr(buf), nbytes, _ptr(sink),
+                                                      int(workgroups), _stream()))
+    return sink

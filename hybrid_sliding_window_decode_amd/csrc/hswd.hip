@@ -18,7 +18,7 @@ namespace {
 
 using namespace hswd;
 
-constexpr int kVersion = (0 << 16) | 5;
+constexpr int kVersion = (0 << 16) | 6;
 constexpr size_t kAlign = 256;
 constexpr int kWgsPerCu = 2;          // resident attention workgroups per CU (VGPR bound)
 
@@ -120,15 +120,26 @@ WsLayout ws_layout(const hswd_attn_desc* d, int n_chunk) {
     return L;
 }
 
-// Kernel launch for the descriptor's group size G = H / Hkv (1, 2 or 4).
+// Kernel launch for the descriptor's group size H / Hkv.  Groups of 1, 2
+// and 4 query heads per kv head have their own kernels; a group of 3 runs
+// the 4-head kernel with one head idle; a larger group runs the 4-head
+// kernel once per four of its heads (each launch reads the cache once; only
+// the last writes the new entry, which the stream orders after every
+// earlier launch's reads).
 template <int MODE>
-int32_t dispatch_attn(const AttnParams& P, int D, int DT, int grid, hipStream_t st) {
-    switch (P.H / P.Hkv) {
-        case 1: return launch_attn_group<1>(P, MODE, D, DT, grid, st);
-        case 2: return launch_attn_group<2>(P, MODE, D, DT, grid, st);
-        case 4: return launch_attn_group<4>(P, MODE, D, DT, grid, st);
-        default: return HSWD_ERR_UNSUPPORTED;
+int32_t dispatch_attn(AttnParams P, int D, int DT, int grid, hipStream_t st) {
+    const int group = P.H / P.Hkv;
+    P.Gq = group;
+    if (group == 1) return launch_attn_group<1>(P, MODE, D, DT, grid, st);
+    if (group == 2) return launch_attn_group<2>(P, MODE, D, DT, grid, st);
+    for (int h0 = 0; h0 < group; h0 += 4) {
+        P.h0 = h0;
+        P.gv = group - h0 < 4 ? group - h0 : 4;
+        P.write_entry = h0 + 4 >= group;
+        const int32_t r = launch_attn_group<4>(P, MODE, D, DT, grid, st);
+        if (r != HSWD_OK) return r;
     }
+    return HSWD_OK;
 }
 
 // Shared argument checks and parameter set-up of the attention entries.
@@ -137,7 +148,6 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     int32_t st = desc_check(d);
     if (st != HSWD_OK) return st;
     const int group = d->n_heads / d->n_kv_heads;       // query heads per kv head
-    if (group != 1 && group != 2 && group != 4) return HSWD_ERR_UNSUPPORTED;
     // grouped kernels: 16-bit and fp8 caches, head dim 128 or 256 (G query
     // vectors and accumulators per lane must fit beside the tiles in 256 VGPRs)
     if (group > 1 && (d->kv_dtype == HSWD_F32 || d->head_dim < 128)) return HSWD_ERR_UNSUPPORTED;
@@ -337,6 +347,16 @@ int32_t hswd_lse_merge(float* o, const float* part_o, const float* part_ml, int3
     if (n > 1024) return HSWD_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(lse_merge_kernel, dim3(B * H), dim3(256), 0, as_stream(stream), o, part_o,
                        part_ml, D, n);
+    return launch_status();
+}
+
+int32_t hswd_stream_read(const void* buf, size_t bytes, void* sink, int32_t workgroups,
+                         void* stream) {
+    if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > 65536)
+        return HSWD_ERR_INVALID;
+    if (!aligned16(buf) || !aligned16(sink)) return HSWD_ERR_ALIGN;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, as_stream(stream),
+                       static_cast<const u32x4*>(buf), bytes / 16, static_cast<uint32_t*>(sink));
     return launch_status();
 }
 

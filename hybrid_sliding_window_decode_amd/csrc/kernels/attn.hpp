@@ -89,6 +89,11 @@ struct AttnParams {
     int rot;
     double log2_theta;
     float qscale;            // softmax scale * log2(e)
+    // 4-head kernel only: query heads per kv head in memory (H / Hkv), the
+    // first head of the group this launch covers and how many (<= 4), and
+    // whether it writes the new entry.  A group above four heads is covered
+    // by consecutive launches of four; the last one writes the entry.
+    int Gq, h0, gv, write_entry;
 };
 
 // Scores on the matrix cores: 4 query heads per kv head over a 16-bit or
@@ -273,7 +278,10 @@ void attn_kernel(AttnParams P) {
     }
     const int b = pair / P.Hkv;
     const int g = pair % P.Hkv;
-    const int bh0 = b * P.H + g * G;       // first query head of the group
+    // query heads of this launch: bh0 .. bh0 + gv - 1 (the 4-head kernel can
+    // cover part of a larger group, or a group of three with one head idle)
+    const int gv = G == 4 ? P.gv : G;
+    const int bh0 = b * P.H + (G == 4 ? g * P.Gq + P.h0 : g * G);
     const int p = P.pos[b];
     const float kscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[g] : 1.f;
     const float vscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[P.Hkv + g] : 1.f;
@@ -568,7 +576,9 @@ void attn_kernel(AttnParams P) {
                     }
                 }
                 const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
-                if (MODE == kModePartials) {
+                if (hh >= gv) {
+                    // idle head of the 4-head kernel: nothing to keep
+                } else if (MODE == kModePartials) {
                     if (t < D) P.part_o[idx * D + t] = Oc * vscale;
                     if (tid == 0) {
                         P.part_ml[idx * 2 + 0] = Mc == -INFINITY ? -INFINITY : Mc * kLn2;
@@ -653,8 +663,8 @@ void attn_kernel(AttnParams P) {
     float q_t[G], q_p[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        q_t[hh] = qv[(size_t)hh * D + td];
-        q_p[hh] = qv[(size_t)hh * D + tp];
+        q_t[hh] = hh < gv ? qv[(size_t)hh * D + td] : 0.f;      // idle heads: zero query
+        q_p[hh] = hh < gv ? qv[(size_t)hh * D + tp] : 0.f;
     }
     float k_t = 0.f, k_p = 0.f, v_t = 0.f;
     if (has_new) {
@@ -666,7 +676,8 @@ void attn_kernel(AttnParams P) {
     float glogit[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
-        glogit[hh] = MODE == kModeStep && !gproj && P.gate != nullptr ? P.gate[bh0 + hh] : 0.f;
+        glogit[hh] = MODE == kModeStep && !gproj && P.gate != nullptr && hh < gv ? P.gate[bh0 + hh]
+                                                                                 : 0.f;
 
     if constexpr (MF) load_k(0);
     load_tile(kA, vA, 0);
@@ -729,9 +740,10 @@ void attn_kernel(AttnParams P) {
     if (gproj) {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-            float gs = gate_share(P.gx + (size_t)b * P.hidden,
-                                  P.gw + (size_t)(g * G + hh) * P.hidden, P.hidden, tid,
-                                  kAttnThreads);
+            float gs = hh < gv ? gate_share(P.gx + (size_t)b * P.hidden,
+                                            P.gw + (size_t)(bh0 - b * P.H + hh) * P.hidden,
+                                            P.hidden, tid, kAttnThreads)
+                               : 0.f;
             gs = wave_sum(gs);
             if (lane == 0) sm_gl[hh][wid] = gs;
         }
@@ -787,7 +799,7 @@ void attn_kernel(AttnParams P) {
         // chunks without a valid key are empty partials
         for (int ch = c_valid; ch < c_end; ++ch) {
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
+            for (int hh = 0; hh < gv; ++hh) {
                 const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
                 if (t < D) P.part_o[idx * D + t] = 0.f;
                 if (tid == 0) {
@@ -821,6 +833,7 @@ void attn_kernel(AttnParams P) {
         // partials' loads in flight before any is folded.
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
+            if (hh >= gv) continue;
             const float* pml = P.part_ml + (size_t)(bh0 + hh) * P.n_chunk * 2;
             const float* po = P.part_o + (size_t)(bh0 + hh) * P.n_chunk * D + (t < D ? t : 0);
             constexpr int kBatch = 32;
@@ -849,7 +862,7 @@ void attn_kernel(AttnParams P) {
     for (int hh = 0; hh < G; ++hh) {
         const float s_new = lds_tree_sum<kAttnWaves>(sm_dot[hh]);
         run[hh].add(s_new, 1.f, vh);
-        if (t < D) {
+        if (t < D && hh < gv) {
             float o = run[hh].O / run[hh].L;
             if (DT == kFP8) o *= vscale;
             if (MODE == kModeStep && (gproj || P.gate != nullptr)) {
@@ -860,7 +873,7 @@ void attn_kernel(AttnParams P) {
         }
     }
 
-    if (MODE == kModeStep) {
+    if (MODE == kModeStep && (G != 4 || P.write_entry)) {
         // Every workgroup of this pair has finished reading (one workgroup:
         // the barrier of the last stash flush, which every wave reaches after
         // its last tile; several: the arrival count), so the ring slot that

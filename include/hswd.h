@@ -99,8 +99,13 @@ typedef struct {
     int32_t n_kv_heads;     /* Hkv, H % Hkv == 0.  Query head h reads kv head
                                h / (H / Hkv) (grouped-query attention by reshaping
                                the query [talker]); the attention entries take
-                               H / Hkv = 1, or 2 and 4 with a 16-bit or fp8 cache
-                               and head_dim 128 or 256, else UNSUPPORTED */
+                               H / Hkv = 1 with any cache, and any H / Hkv > 1
+                               with a 16-bit or fp8 cache and head_dim 128 or 256
+                               (else UNSUPPORTED).  Groups of 2 and 4 read the
+                               cache once per layer; 3 runs as 4 with one head
+                               idle; a group above 4 is taken four query heads
+                               per launch, each launch reading the cache once
+                               (the last one writes the new entry). */
     int32_t head_dim;       /* D: 64, 128 or 256 (fp8 caches: 128 or 256) */
     int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows */
     int32_t kv_dtype;       /* hswd_dtype of the cache */
@@ -253,6 +258,19 @@ int32_t hswd_layer_step_gproj(float* out, const float* q, const float* k, const 
                               void* v_cache, const int32_t* pos, int32_t ring, int32_t rot_dim,
                               double theta, int32_t max_pos, const hswd_attn_desc* d, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* Measurement helper, not a step of the decode path: reads `bytes` (a
+ * multiple of 16) of device memory at `buf` once, `workgroups` workgroups
+ * of 256 threads each streaming a contiguous range with the 128-bit
+ * non-temporal loads the attention kernel uses for its K/V tiles.  Its
+ * duration over a buffer much larger than the 256 MB last-level cache gives
+ * the streaming-read ceiling the attention kernel is compared with.  `sink`
+ * (DEVICE, 16-byte aligned, at least 4 * workgroups bytes) keeps the loads
+ * from being optimised away and is in practice never written.  Errors:
+ * HSWD_ERR_INVALID (null pointer, bytes 0 or not a multiple of 16,
+ * workgroups outside [1, 65536]), HSWD_ERR_ALIGN; nothing is launched then. */
+int32_t hswd_stream_read(const void* buf, size_t bytes, void* sink, int32_t workgroups,
+                         void* stream);
 
 /* Synchronise `stream`, then read the workspace error word.  Returns
  * HSWD_OK if it is zero, HSWD_ERR_CAPACITY otherwise; *flags_out (nullable,

@@ -92,11 +92,9 @@ def test_workspace_and_splits():
     ("kps quantum d128", dict(head_dim=128, keys_per_split=64), -1),
     ("cpw", dict(chunks_per_workgroup=-1), -1),
     ("batch", dict(batch=0), -1),
-    # grouped kernels: 2 or 4 query heads per kv head, 16-bit or fp8 caches,
-    # D >= 128
-    ("GQA group 8", dict(n_heads=16, n_kv_heads=2), -6),
-    ("GQA group 3", dict(n_heads=24, n_kv_heads=8), -6),
+    # grouped layers (any H / Hkv > 1) need a 16-bit or fp8 cache and D >= 128
     ("GQA f32", dict(n_heads=16, n_kv_heads=8, kv_dtype=0), -6),
+    ("GQA f32 group 8", dict(n_heads=16, n_kv_heads=2, kv_dtype=0), -6),
     ("GQA head_dim 64", dict(n_heads=16, n_kv_heads=8, head_dim=64), -6),
 ])
 def test_sliding_rejects_bad_descriptor(case, kw, want):
@@ -157,6 +155,13 @@ def test_other_entries_host_checks():
     assert L.hswd_workspace_init(None, 64, None) == -3
     assert L.hswd_workspace_init(MIS, 64, None) == -2
     assert L.hswd_check_errors(None, None, None) == -3
+    # streaming-read helper: null, size 0 or not a multiple of 16, workgroups, alignment
+    assert L.hswd_stream_read(None, 1 << 20, A, 64, None) == -1
+    assert L.hswd_stream_read(A, 0, A, 64, None) == -1
+    assert L.hswd_stream_read(A, 1000, A, 64, None) == -1
+    assert L.hswd_stream_read(A, 1 << 20, A, 0, None) == -1
+    assert L.hswd_stream_read(A, 1 << 20, A, 65537, None) == -1
+    assert L.hswd_stream_read(MIS, 1 << 20, A, 64, None) == -2
 
 
 def test_binding_refuses_cpu_tensors():

@@ -25,7 +25,8 @@ def test_gate_proj_matches_oracle():
 
 
 @pytest.mark.parametrize("kind,dtype,G", [("sliding", "bf16", 1), ("full", "f16", 1),
-                                          ("sliding", "bf16", 4), ("full", "bf16", 2)])
+                                          ("sliding", "bf16", 4), ("full", "bf16", 2),
+                                          ("full", "bf16", 8)])
 def test_layer_step_gproj(kind, dtype, G):
     """Fused projection + step: the same bits as gate_proj then layer_step,
     and the oracle's output scaled by the oracle's sigmoid(logit); G query

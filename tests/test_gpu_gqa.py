@@ -1,5 +1,5 @@
-"""GPU parity of grouped-query attention (H / Hkv = 2 or 4 query heads per
-kv head, the talker commit's query reshape): the fused layer step and the
+"""GPU parity of grouped-query attention (H / Hkv query heads per kv head,
+the talker commit's query reshape; groups 2 and 4 and larger ones): the fused layer step and the
 separate entries against the oracle (which maps query head h to kv head
 h // G), the stored entry bit for bit, the cross-workgroup merge, and the
 property that a group reads the same result as its kv head repeated."""
@@ -48,9 +48,30 @@ def positions(kind, B, S, pos, seed):
     ("full", "fp8", 4, 256, 2, [19999, 9000], 20000, 0),
 ])
 def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
+    check_layer_step(kind, dtype, G, D, B, pos, S, kps)
+
+
+# Groups without a kernel of their own: 3 runs the 4-head kernel with one
+# head idle; 5, 6, 8 and 16 run it once per four heads (the last launch
+# writes the entry), including a cross-workgroup merge and a partial last
+# group of one and two heads.
+@pytest.mark.parametrize("kind,dtype,G,D,B,pos,S,kps,H", [
+    ("sliding", "bf16", 3, 256, 6, "ragged", None, 0, 12),
+    ("full", "f16", 3, 128, 3, [1024, 1, 2999], 3000, 256, 24),
+    ("full", "bf16", 8, 256, 5, "ragged", 3000, 0, 32),
+    ("sliding", "fp8", 8, 256, 6, "ragged", None, 0, 16),
+    ("full", "fp8", 6, 256, 3, [2999, 0, 1500], 3000, 0, 24),
+    ("full", "bf16", 5, 256, 2, [19999, 7001], 20000, 0, 10),
+    ("sliding", "f16", 16, 128, 4, "ragged", None, 0, 32),
+])
+def test_gqa_large_groups(kind, dtype, G, D, B, pos, S, kps, H):
+    check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=H)
+
+
+def check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=8):
     """Fused step vs oracle; the same bits as rope -> attend -> gate -> write;
     the stored entry equals the oracle's rounding of the rotated key."""
-    spec = gqa_spec(kind, B, dtype, G, D=D, S=S)
+    spec = gqa_spec(kind, B, dtype, G, D=D, S=S, H=H)
     x = inputs.make_step(spec, positions(kind, B, S, pos, 21), seed=22 + G)
     ring = kind == "sliding"
     mp = int(x.pos.max())
@@ -145,13 +166,14 @@ def test_gqa_equals_repeated_kv_heads(kind, G):
 
 
 def test_gqa_unsupported_is_refused():
-    """Groups the library has no kernel for (8 query heads per kv head) are
-    refused before any launch."""
-    spec = gqa_spec("sliding", 2, "bf16", 8, H=16)
-    x = inputs.make_step(spec, [3, 700], seed=51)
-    d = to_dev(x)
-    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H)
-    ws = hswd.workspace(desc, 1, 0)
-    with pytest.raises(hswd.HswdError):
-        hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
-                        d["pos"], 1, spec.rot, spec.theta, ws, desc=desc)
+    """Grouped layers over a float32 cache or with head_dim 64 have no kernel
+    and are refused before any launch."""
+    for dtype, D in (("f32", 256), ("bf16", 64)):
+        spec = gqa_spec("sliding", 2, dtype, 2, D=D, H=16)
+        x = inputs.make_step(spec, [3, 700], seed=51)
+        d = to_dev(x)
+        desc = hswd.make_desc(d["k_cache"], n_heads=spec.H)
+        ws = hswd.workspace(desc, 1, 0)
+        with pytest.raises(hswd.HswdError):
+            hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
+                            d["pos"], 1, spec.rot, spec.theta, ws, desc=desc)

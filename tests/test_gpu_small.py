@@ -169,3 +169,15 @@ def test_lse_merge(n):
             ref = oracle.merge(m[b, h], l[b, h], o[b, h])
             err = np.max(np.abs(got[b, h] - ref)) / np.max(np.abs(ref))
             assert err < 1e-5, (b, h, err)
+
+
+def test_stream_read_helper():
+    """The measurement helper reads a buffer and leaves its sink untouched."""
+    import torch
+    say("stream_read 64 MiB")
+    buf = torch.arange(1 << 24, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(512, dtype=torch.int32, device="cuda")
+    for wgs in (1, 7, 512):
+        hswd.stream_read(buf, wgs, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
