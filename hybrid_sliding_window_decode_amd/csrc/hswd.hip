@@ -37,7 +37,7 @@ struct WsLayout {
 
 int32_t desc_check(const hswd_attn_desc* d) {
     if (!d) return HSWD_ERR_INVALID;
-    if (d->batch < 1 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_slots < 1)
+    if (d->batch < 0 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_slots < 1)
         return HSWD_ERR_INVALID;
     if (d->n_heads % d->n_kv_heads != 0) return HSWD_ERR_INVALID;
     if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
@@ -50,6 +50,13 @@ int32_t desc_check(const hswd_attn_desc* d) {
         d->keys_per_split % chunk_quantum(d->head_dim, d->kv_dtype) != 0)
         return HSWD_ERR_INVALID;
     return HSWD_OK;
+}
+
+// An empty batch (B = 0, a valid descriptor otherwise) has nothing to
+// compute: the entries return HSWD_OK without launching, whatever the
+// pointers (an empty tensor may have none).
+bool empty_batch(const hswd_attn_desc* d) {
+    return d != nullptr && d->batch == 0 && desc_check(d) == HSWD_OK;
 }
 
 // Default keys per chunk, from the cache geometry, element type and head
@@ -227,7 +234,9 @@ int32_t hswd_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 
 int32_t hswd_ring_mask(uint8_t* mask, int32_t* slot, const int32_t* pos, int32_t B,
                        int32_t n_slots, int32_t ring, void* stream) {
-    if (!pos || (!mask && !slot) || B < 1 || n_slots < 1) return HSWD_ERR_INVALID;
+    if (B < 0 || n_slots < 1) return HSWD_ERR_INVALID;
+    if (B == 0) return HSWD_OK;
+    if (!pos || (!mask && !slot)) return HSWD_ERR_INVALID;
     hipLaunchKernelGGL(ring_mask_kernel, dim3(B), dim3(256), 0, as_stream(stream), mask, slot,
                        pos, n_slots, ring ? 1 : 0);
     return launch_status();
@@ -235,11 +244,13 @@ int32_t hswd_ring_mask(uint8_t* mask, int32_t* slot, const int32_t* pos, int32_t
 
 int32_t hswd_rope_apply(float* q, float* k, const int32_t* pos, int32_t B, int32_t H,
                         int32_t Hkv, int32_t D, int32_t rot_dim, double theta, void* stream) {
-    if (!q || !pos || B < 1 || H < 1 || D < 2 || (k && Hkv < 1)) return HSWD_ERR_INVALID;
+    if (B < 0 || H < 1 || D < 2 || (k && Hkv < 1)) return HSWD_ERR_INVALID;
     if (rot_dim <= 0 || rot_dim > D || (rot_dim & 1)) return HSWD_ERR_INVALID;
     if (!(theta > 0.0) || !isfinite(theta)) return HSWD_ERR_INVALID;
     const size_t lds = (size_t)(H + (k ? Hkv : 0)) * D * sizeof(float);
     if (lds > 64 * 1024) return HSWD_ERR_UNSUPPORTED;
+    if (B == 0) return HSWD_OK;
+    if (!q || !pos) return HSWD_ERR_INVALID;
     hipLaunchKernelGGL(rope_kernel, dim3(B), dim3(256), lds, as_stream(stream), q, k, pos, H,
                        k ? Hkv : 0, D, rot_dim, log2(theta));
     return launch_status();
@@ -250,6 +261,7 @@ int32_t hswd_kv_slot_write(void* k_cache, void* v_cache, const float* k_rot, con
                            int32_t* slot_out, void* ws, void* stream) {
     int32_t st = desc_check(d);
     if (st != HSWD_OK) return st;
+    if (d->batch == 0) return HSWD_OK;
     if (!k_cache || !v_cache || !k_rot || !v || !pos) return HSWD_ERR_INVALID;
     if (!ws) return HSWD_ERR_WORKSPACE;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_rot) || !aligned16(v) ||
@@ -287,6 +299,7 @@ static int32_t decode_attn(float* o, const float* q_rot, const float* k_rot, con
                            const void* kc, const void* vc, const int32_t* pos, int32_t ring,
                            int32_t max_pos, const hswd_attn_desc* d, void* ws, size_t ws_bytes,
                            void* stream) {
+    if (empty_batch(d)) return HSWD_OK;
     if (!o || !q_rot || !k_rot || !v || !kc || !vc || !pos) return HSWD_ERR_INVALID;
     if (!aligned16(o) || !aligned16(q_rot) || !aligned16(k_rot) || !aligned16(v) ||
         !aligned16(kc) || !aligned16(vc))
@@ -324,6 +337,7 @@ int32_t hswd_decode_attn_partials(float* part_o, float* part_ml, const float* q_
                                   const void* k_cache, const void* v_cache,
                                   const int32_t* pos, int32_t ring, int32_t max_pos,
                                   const hswd_attn_desc* d, void* stream) {
+    if (empty_batch(d)) return HSWD_OK;
     if (!part_o || !part_ml || !q_rot || !k_cache || !v_cache || !pos) return HSWD_ERR_INVALID;
     if (!aligned16(part_o) || !aligned16(part_ml) || !aligned16(q_rot) || !aligned16(k_cache) ||
         !aligned16(v_cache))
@@ -343,8 +357,10 @@ int32_t hswd_decode_attn_partials(float* part_o, float* part_ml, const float* q_
 
 int32_t hswd_lse_merge(float* o, const float* part_o, const float* part_ml, int32_t B,
                        int32_t H, int32_t D, int32_t n, void* stream) {
-    if (!o || !part_o || !part_ml || B < 1 || H < 1 || D < 1 || n < 1) return HSWD_ERR_INVALID;
+    if (B < 0 || H < 1 || D < 1 || n < 1) return HSWD_ERR_INVALID;
     if (n > 1024) return HSWD_ERR_UNSUPPORTED;
+    if (B == 0) return HSWD_OK;
+    if (!o || !part_o || !part_ml) return HSWD_ERR_INVALID;
     hipLaunchKernelGGL(lse_merge_kernel, dim3(B * H), dim3(256), 0, as_stream(stream), o, part_o,
                        part_ml, D, n);
     return launch_status();
@@ -362,7 +378,9 @@ int32_t hswd_stream_read(const void* buf, size_t bytes, void* sink, int32_t work
 
 int32_t hswd_head_gate(float* out, const float* o, const float* gate, int32_t B, int32_t H,
                        int32_t D, void* stream) {
-    if (!out || !o || !gate || B < 1 || H < 1 || D < 1) return HSWD_ERR_INVALID;
+    if (B < 0 || H < 1 || D < 1) return HSWD_ERR_INVALID;
+    if (B == 0) return HSWD_OK;
+    if (!out || !o || !gate) return HSWD_ERR_INVALID;
     hipLaunchKernelGGL(head_gate_kernel, dim3(B * H), dim3(256), 0, as_stream(stream), out, o,
                        gate, D);
     return launch_status();
@@ -373,12 +391,13 @@ static int32_t layer_step(float* out, const float* q, const float* k, const floa
                           void* k_cache, void* v_cache, const int32_t* pos, int32_t ring,
                           int32_t rot_dim, double theta, int32_t max_pos,
                           const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
+    if (!d || rot_dim <= 0 || rot_dim > d->head_dim || (rot_dim & 1)) return HSWD_ERR_INVALID;
+    if (!(theta > 0.0) || !isfinite(theta)) return HSWD_ERR_INVALID;
+    if (empty_batch(d)) return HSWD_OK;
     if (!out || !q || !k || !v || !k_cache || !v_cache || !pos) return HSWD_ERR_INVALID;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
         !aligned16(k_cache) || !aligned16(v_cache))
         return HSWD_ERR_ALIGN;
-    if (!d || rot_dim <= 0 || rot_dim > d->head_dim || (rot_dim & 1)) return HSWD_ERR_INVALID;
-    if (!(theta > 0.0) || !isfinite(theta)) return HSWD_ERR_INVALID;
     AttnParams P{};
     int grid = 0;
     int32_t st = attn_setup(P, grid, d, ring, max_pos, ws, ws_bytes, true);
@@ -412,14 +431,17 @@ int32_t hswd_layer_step_gproj(float* out, const float* q, const float* k, const 
                               void* v_cache, const int32_t* pos, int32_t ring, int32_t rot_dim,
                               double theta, int32_t max_pos, const hswd_attn_desc* d, void* ws,
                               size_t ws_bytes, void* stream) {
-    if (!x || !w_g || hidden < 1) return HSWD_ERR_INVALID;
+    if (hidden < 1) return HSWD_ERR_INVALID;
+    if (!(d && d->batch == 0) && (!x || !w_g)) return HSWD_ERR_INVALID;
     return layer_step(out, q, k, v, nullptr, x, w_g, hidden, k_cache, v_cache, pos, ring,
                       rot_dim, theta, max_pos, d, ws, ws_bytes, stream);
 }
 
 int32_t hswd_gate_proj(float* logits, const float* x, const float* w_g, int32_t B,
                        int32_t hidden, int32_t H, void* stream) {
-    if (!logits || !x || !w_g || B < 1 || hidden < 1 || H < 1) return HSWD_ERR_INVALID;
+    if (B < 0 || hidden < 1 || H < 1) return HSWD_ERR_INVALID;
+    if (B == 0) return HSWD_OK;
+    if (!logits || !x || !w_g) return HSWD_ERR_INVALID;
     hipLaunchKernelGGL(gate_proj_kernel, dim3(B * H), dim3(256), 0, as_stream(stream), logits, x,
                        w_g, hidden, H);
     return launch_status();

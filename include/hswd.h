@@ -56,6 +56,9 @@
  *     found on the host before anything is launched.  A stream whose device
  *     pos is out of range sets a flag in the workspace's error word; read it
  *     with hswd_check_errors.
+ *   - An empty batch (B = 0) is a no-op: once its other arguments pass, an
+ *     entry returns HSWD_OK and launches nothing, whatever its pointers
+ *     (an empty tensor may have none).  B < 0 is HSWD_ERR_INVALID.
  *   - Results are deterministic for a fixed keys_per_split and do not depend
  *     on B or on a stream's index in the batch.
  *   - Calls that share a workspace must not overlap in time.
@@ -94,7 +97,7 @@ typedef enum {
 
 /* Shape and numerics of one attention layer. */
 typedef struct {
-    int32_t batch;          /* B >= 1 */
+    int32_t batch;          /* B >= 0 (0: an empty batch, nothing to do) */
     int32_t n_heads;        /* H */
     int32_t n_kv_heads;     /* Hkv, H % Hkv == 0.  Query head h reads kv head
                                h / (H / Hkv) (grouped-query attention by reshaping

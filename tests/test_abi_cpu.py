@@ -91,7 +91,7 @@ def test_workspace_and_splits():
     ("kps quantum bf16", dict(keys_per_split=96), -1),
     ("kps quantum d128", dict(head_dim=128, keys_per_split=64), -1),
     ("cpw", dict(chunks_per_workgroup=-1), -1),
-    ("batch", dict(batch=0), -1),
+    ("batch", dict(batch=-1), -1),
     # grouped layers (any H / Hkv > 1) need a 16-bit or fp8 cache and D >= 128
     ("GQA f32", dict(n_heads=16, n_kv_heads=8, kv_dtype=0), -6),
     ("GQA f32 group 8", dict(n_heads=16, n_kv_heads=2, kv_dtype=0), -6),
@@ -169,3 +169,34 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 8, 256)
     with pytest.raises(ValueError):
         hswd.rope_apply(q, None, torch.zeros(1, dtype=torch.int32), 256, 1e4)
+
+
+def test_empty_batch_is_a_no_op():
+    """B = 0: every entry returns OK with null pointers and launches nothing
+    (there is no GPU here, so a launch would fail); its other arguments are
+    still checked."""
+    L = binding.lib()
+    d0 = desc(batch=0)
+    N = None
+    assert L.hswd_ring_mask(N, N, N, 0, 511, 1, N) == 0
+    assert L.hswd_ring_mask(N, N, N, 0, 0, 1, N) == -1
+    assert L.hswd_rope_apply(N, N, N, 0, 8, 8, 256, 256, 1e4, N) == 0
+    assert L.hswd_rope_apply(N, N, N, 0, 8, 8, 256, 255, 1e4, N) == -1
+    assert L.hswd_kv_slot_write(N, N, N, N, N, ctypes.byref(d0), 1, N, N, N) == 0
+    assert L.hswd_decode_attn_sliding(N, N, N, N, N, N, N, ctypes.byref(d0), N, 0, N) == 0
+    assert L.hswd_decode_attn_full(N, N, N, N, N, N, N, 4096, ctypes.byref(d0), N, 0, N) == 0
+    assert L.hswd_decode_attn_partials(N, N, N, N, N, N, 1, 0, ctypes.byref(d0), N) == 0
+    assert L.hswd_lse_merge(N, N, N, 0, 8, 256, 4, N) == 0
+    assert L.hswd_lse_merge(N, N, N, 0, 8, 256, 2048, N) == -6
+    assert L.hswd_head_gate(N, N, N, 0, 8, 256, N) == 0
+    assert L.hswd_gate_proj(N, N, N, 0, 2048, 8, N) == 0
+    assert L.hswd_layer_step(N, N, N, N, N, N, N, N, 1, 256, 1e4, 0, ctypes.byref(d0), N, 0,
+                             N) == 0
+    assert L.hswd_layer_step(N, N, N, N, N, N, N, N, 1, 256, -1.0, 0, ctypes.byref(d0), N, 0,
+                             N) == -1
+    assert L.hswd_layer_step_gproj(N, N, N, N, N, N, 2048, N, N, N, 1, 256, 1e4, 0,
+                                   ctypes.byref(d0), N, 0, N) == 0
+    assert L.hswd_decode_attn_sliding(N, N, N, N, N, N, N, ctypes.byref(desc(batch=0, scale=0.0)),
+                                      N, 0, N) == -1
+    assert L.hswd_workspace_bytes(ctypes.byref(d0), 1, 0) > 0
+

@@ -181,3 +181,29 @@ def test_stream_read_helper():
         hswd.stream_read(buf, wgs, sink)
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0
+
+
+def test_empty_batch_through_the_binding():
+    """Zero streams: every entry accepts the empty tensors, launches nothing
+    and returns empty outputs."""
+    say("empty batch")
+    dev = "cuda"
+    q = torch.empty(0, 8, 256, device=dev)
+    k = torch.empty(0, 8, 256, device=dev)
+    v = torch.empty(0, 8, 256, device=dev)
+    gate = torch.empty(0, 8, device=dev)
+    pos = torch.empty(0, dtype=torch.int32, device=dev)
+    kc = torch.empty(0, 8, 511, 256, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    desc = hswd.make_desc(kc)
+    ws = hswd.workspace(desc, 1, 0)
+    hswd.rope_apply(q, k, pos, 256, 1e4)
+    o = hswd.decode_attn_sliding(q, k, v, kc, vc, pos, ws, desc=desc)
+    assert tuple(o.shape) == (0, 8, 256)
+    g = hswd.head_gate(o, gate)
+    hswd.kv_slot_write(kc, vc, k, v, pos, 1, ws, desc=desc)
+    out = hswd.layer_step(q, k, v, gate, kc, vc, pos, 1, 256, 1e4, ws, desc=desc)
+    mask, slot = hswd.ring_mask(pos, 511, 1)
+    torch.cuda.synchronize()
+    assert hswd.check_errors(ws) == 0
+    assert out.numel() == 0 and g.numel() == 0 and slot.numel() == 0 and mask.numel() == 0
