@@ -245,9 +245,12 @@ void attn_kernel(AttnParams P) {
     __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT : 1][MF ? KPAD : 1];
     // query rows padded by 16 bytes too: unpadded, the G heads' rows (512
     // bytes apart) would share banks and the operand reads conflict 4 ways
-    __shared__ uint16_t sm_qh[MF ? G : 1][MF ? D + 8 : 1], sm_ql[MF ? G : 1][MF ? D + 8 : 1];
-    __shared__ float sm_p[MF ? kAttnWaves : 1][MF ? KT : 1][4];
-    __shared__ float sm_al[MF ? kAttnWaves : 1][4];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G : 1][MF ? D + 8 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_ql[MF ? G : 1][MF ? D + 8 : 1];
+    // (both read 16 bytes at a time: aligned to 16)
+    __shared__ __attribute__((aligned(16))) float sm_p[MF && DT == kBF16 ? kAttnWaves : 1][MF ? KT : 1][4];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_ph[MF && DT != kBF16 ? kAttnWaves : 1][MF ? NL / 2 : 1][RPI][4][2];
+    __shared__ __attribute__((aligned(16))) float sm_al[MF ? kAttnWaves : 1][4];
     __shared__ float sm_o[2][kStash][G][kAttnWaves][D];   // wave chunk partials, by flush parity
     __shared__ float sm_m[2][kStash][G][kAttnWaves], sm_l[2][kStash][G][kAttnWaves];
     __shared__ float sm_dot[G][kAttnWaves];
@@ -456,6 +459,11 @@ void attn_kernel(AttnParams P) {
             const float m_new = fmaxf(m1, mx);
             const float alpha = fast_exp2(m1 - m_new);
             m1 = m_new;
+            // probabilities to LDS: float per (key, head) for bf16 caches;
+            // fp8 and f16 caches: fp16, paired by load index (loads 2 j and
+            // 2 j + 1 of a lane hold the same dims of two keys), so one
+            // 16-byte read gives a lane the four heads' pairs for its row
+            constexpr bool PV16 = DT != kBF16;
             float psum = 0.f;
 #pragma unroll
             for (int kg = 0; kg < NG; ++kg) {
@@ -463,28 +471,83 @@ void attn_kernel(AttnParams P) {
                 for (int i = 0; i < 4; ++i) {
                     const float pr = fast_exp2(sv[kg][i] - m_new);
                     psum += pr;
-                    if (hq < G) sm_p[wid][kg * 16 + 4 * kq + i][hq] = pr;
+                    const int key = kg * 16 + 4 * kq + i;          // within the tile
+                    if (hq < G) {
+                        if constexpr (PV16) {
+                            const int li = key / RPI;               // load index of the key
+                            sm_ph[wid][li / 2][key % RPI][hq][li % 2] =
+                                __builtin_bit_cast(uint16_t, (_Float16)pr);
+                        } else {
+                            sm_p[wid][key][hq] = pr;
+                        }
+                    }
                 }
             }
             l1 = l1 * alpha + psum;
             if (lane < G) sm_al[wid][lane] = alpha;
             // P.V on the VALU, V rows in their loaded layout: the rescale
-            // factors and each row's probabilities come back from LDS
+            // factors and the probabilities come back from LDS; the rescale
+            // is skipped when no head's max moved (a multiply by one)
             const f32x4 al = *reinterpret_cast<const f32x4*>(&sm_al[wid][0]);
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= al[hh];
-            }
-#pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const f32x4 pv = *reinterpret_cast<const f32x4*>(&sm_p[wid][i * RPI + r][0]);
-                float vf[EPC];
-                unpack_chunk<DT>(vt[i], vf);
+            if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pv[hh], vf[e], o_acc[hh][e]);
+                    for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= al[hh];
+                }
+            }
+            if constexpr (PV16) {
+                // two keys per v_dot2_f32_f16: the values of loads 2 j and
+                // 2 j + 1 at one dim as an fp16 pair (fp8 codes converted
+                // exactly), the probabilities of the same two keys likewise
+                typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                for (int jp = 0; jp < NL / 2; ++jp) {
+                    const u32x4 pp = *reinterpret_cast<const u32x4*>(&sm_ph[wid][jp][r][0][0]);
+                    uint32_t vp[EPC];
+                    if constexpr (DT == kFP8) {
+                        const uint32_t a[2] = {vt[2 * jp].x, vt[2 * jp].y};
+                        const uint32_t bq[2] = {vt[2 * jp + 1].x, vt[2 * jp + 1].y};
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) {
+                            const uint32_t x = __builtin_amdgcn_perm(bq[w], a[w], 0x05010400u);
+                            const uint32_t y = __builtin_amdgcn_perm(bq[w], a[w], 0x07030602u);
+                            vp[4 * w + 0] = fp8x2_to_f16x2(x, false);
+                            vp[4 * w + 1] = fp8x2_to_f16x2(x, true);
+                            vp[4 * w + 2] = fp8x2_to_f16x2(y, false);
+                            vp[4 * w + 3] = fp8x2_to_f16x2(y, true);
+                        }
+                    } else {
+                        const uint32_t a[4] = {vt[2 * jp].x, vt[2 * jp].y, vt[2 * jp].z, vt[2 * jp].w};
+                        const uint32_t bq[4] = {vt[2 * jp + 1].x, vt[2 * jp + 1].y,
+                                                vt[2 * jp + 1].z, vt[2 * jp + 1].w};
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            vp[2 * w] = __builtin_amdgcn_perm(bq[w], a[w], 0x05040100u);
+                            vp[2 * w + 1] = __builtin_amdgcn_perm(bq[w], a[w], 0x07060302u);
+                        }
+                    }
+                    const uint32_t pw[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e)
+                            o_acc[hh][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, vp[e]),
+                                                                  __builtin_bit_cast(h16x2, pw[hh]),
+                                                                  o_acc[hh][e], false);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    const f32x4 pv = *reinterpret_cast<const f32x4*>(&sm_p[wid][i * RPI + r][0]);
+                    float vf[EPC];
+                    unpack_chunk<DT>(vt[i], vf);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pv[hh], vf[e], o_acc[hh][e]);
+                    }
                 }
             }
         } else {

@@ -169,18 +169,27 @@ __device__ __forceinline__ void unpack_chunk(const u32x4& w, float* f) {
     }
 }
 
-// Eight fp8 codes (byte order) -> eight bf16 values, exactly: every e4m3
-// value is a bf16 value, so the bf16 is the upper half of the float.
+// Two fp8 e4m3 codes (bytes 0-1 or 2-3 of w) to two bf16 values packed in a
+// word (the first code in the low half), by the gfx950 scaled conversion
+// with scale 1: exact, as every e4m3 value is a bf16 value.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+
+// Eight fp8 codes (byte order) -> eight bf16 values, exactly, two per
+// conversion.
 __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(const u32x2& w) {
-    const uint32_t u[2] = {w.x, w.y};
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const f32x2 lo = fp8x2_to_f32(u[j], false), hi = fp8x2_to_f32(u[j], true);
-        o[2 * j] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
-        o[2 * j + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
-    }
-    return u32x4{o[0], o[1], o[2], o[3]};
+    return u32x4{fp8x2_to_bf16x2(w.x, false), fp8x2_to_bf16x2(w.x, true),
+                 fp8x2_to_bf16x2(w.y, false), fp8x2_to_bf16x2(w.y, true)};
+}
+
+// Two fp8 e4m3 codes (bytes 0-1 or 2-3 of w) to two fp16 values packed in a
+// word (the first code in the low half), by the gfx950 scaled conversion
+// with scale 1: exact, as every e4m3 value is an fp16 value.
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w, bool hi) {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
 }
 
 // Unpack one 8-byte chunk of fp8 codes into 8 floats, in byte order.

@@ -92,27 +92,71 @@ def test_kv_slot_write_rounding_bit_exact(dtype):
         assert np.array_equal(got_v, ref_v)
 
 
-def test_fp8_decode_all_codes_in_attention():
+@pytest.mark.parametrize("H", [8, 32])
+def test_fp8_decode_all_codes_in_attention(H):
     """A one-key cache holding each of the 255 non-NaN fp8 codes in turn
     (q = 0, new value 0): the output is the mean of the decoded cached value
-    and 0 -- the kernel's fp8 decode of every code, against the oracle's."""
+    and 0 -- the kernel's fp8 decode of every code, against the oracle's
+    (H = 32: the grouped kernel's value path)."""
     codes = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], np.uint8)
-    B, H, D = len(codes), 8, 256
-    spec = inputs.sliding_spec(B, "fp8", n_slots=511)
+    B, D = len(codes), 256
+    spec = inputs.sliding_spec(B, "fp8", n_slots=511, H=H)
     x = inputs.make_step(spec, 1, seed=45)
     x.q[:] = 0
     x.v[:] = 0
     x.k[:] = 0
     x.v_cache[:, :, 0, :] = codes[:, None, None]
     d = to_dev(x)
-    desc = hswd.make_desc(d["k_cache"], kv_scale=d["kv_scale"])
+    desc = hswd.make_desc(d["k_cache"], n_heads=H, kv_scale=d["kv_scale"])
     ws = hswd.workspace(desc, 1, 0)
-    say("fp8 decode of all codes")
+    say("fp8 decode of all codes, H=%d" % H)
     hswd.rope_apply(d["q"], d["k"], d["pos"], 256, 1e4)
     o = hswd.decode_attn_sliding(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["pos"],
                                  ws, desc=desc).cpu().numpy()
     val = oracle.decode(CODE["fp8"], codes)[:, None] * spec.kv_scale[1][None, :]
-    assert np.array_equal(o[:, :, 0].astype(np.float64), val / 2)
+    G = H // 8
+    assert np.array_equal(o[:, :, 0].astype(np.float64), np.repeat(val, G, axis=1) / 2)
+
+
+@pytest.mark.parametrize("H", [8, 32])
+def test_fp8_key_decode_all_codes_in_attention(H):
+    """A one-key cache whose key holds one of the 255 non-NaN fp8 codes in
+    every dim, value 1; new key and value 0; the query a multiple t of the
+    first unit vector, t chosen so the cached score is about 1: the output's
+    first dim is sigmoid(score), so a mis-decoded key code moves it far
+    beyond the bar.  Against the oracle, all codes, both kernels."""
+    codes = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], np.uint8)
+    B, D = len(codes), 256
+    spec = inputs.sliding_spec(B, "fp8", n_slots=511, H=H)
+    x = inputs.make_step(spec, 1, seed=46)
+    dec = oracle.decode(CODE["fp8"], codes)
+    ks = spec.kv_scale[0]
+    t = np.where(dec == 0, 1.0, 16.0 / np.where(dec == 0, 1.0, np.abs(dec)))
+    x.q[:] = 0
+    x.q[:, :, 0] = (t[:, None] / ks[np.arange(H) // (H // 8)][None, :]).astype(np.float32)
+    x.k[:] = 0
+    x.v[:] = 0
+    x.k_cache[:, :, 0, :] = codes[:, None, None]
+    x.v_cache[:, :, 0, :] = 0x38                      # 1.0
+    d = to_dev(x)
+    desc = hswd.make_desc(d["k_cache"], n_heads=H, kv_scale=d["kv_scale"])
+    ws = hswd.workspace(desc, 1, 0)
+    say("fp8 key decode of all codes, H=%d" % H)
+    o = hswd.decode_attn_sliding(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"], d["pos"],
+                                 ws, desc=desc).cpu().numpy()
+    # the oracle's attention of the same rotated query (no rotation here)
+    want = np.empty((B, H))
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // 8)
+            kc = x.k_cache[b, g, :1]
+            vc = x.v_cache[b, g, :1]
+            kh = np.zeros(D, np.uint8)
+            want[b, h] = oracle.attend_block(x.q[b, h].astype(np.float64), kc, vc, CODE["fp8"],
+                                             1, kh, kh, 1 / 16.0, ks=float(ks[g]),
+                                             vs=float(spec.kv_scale[1][g]))[0]
+    vs = np.repeat(spec.kv_scale[1], H // 8)[None, :]
+    assert np.max(np.abs(o[:, :, 0] - want) / vs) <= 2e-3
 
 
 def test_kv_slot_write_capacity_flag():
