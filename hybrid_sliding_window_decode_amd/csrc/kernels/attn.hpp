@@ -341,19 +341,21 @@ void attn_kernel(AttnParams P) {
     // of K suffices (LDS is its second buffer); kA, kB are then unused.
     Chunk kR[MF ? NL : 1];
 
-    // Item j of this wave: tile (wid + 4 i) of chunk ch.  Rows past the
-    // chunk's valid end are clamped onto its last valid row (never reading an
-    // unwritten slot) and masked out of the softmax; an item past the last
-    // (a prefetch the loop never scores) clamps the same way, onto row 0 of
-    // the block when it has no valid row at all, so every load stays inside
-    // this (stream, kv head)'s cache block and may be issued unconditionally.
-    auto item_chunk = [&](int j) __attribute__((always_inline)) { return j < n_full_items ? c_begin + j / TPW : c_full; };
-    auto item_tile = [&](int j) __attribute__((always_inline)) { return j < n_full_items ? j % TPW : j - n_full_items; };
+    // Item j of this wave: tile (wid + 4 i) of chunk c_begin + j / TPW for
+    // the full chunks, tile (wid + 4 (j - n_full_items)) of the partly valid
+    // chunk after them.  A chunk is TPW * 4 tiles long, so both give the
+    // first key c_begin * K + (4 j + wid) * KT, with no division.  Rows at
+    // or past nv (only in the partly valid chunk, whose tiles end inside it,
+    // or in a prefetch the loop never scores) are clamped onto row nv - 1
+    // (row 0 when nothing is valid), so every load stays inside this
+    // (stream, kv head)'s written rows and may be issued unconditionally;
+    // the softmax masks keys >= nv.
+    const int key0 = c_begin * P.K + wid * KT;
+    const int jlast = max(nv, 1) - 1;
+    auto item_key = [&](int j) __attribute__((always_inline)) { return key0 + j * (kAttnWaves * KT); };
 
     auto load_k = [&](int j) __attribute__((always_inline)) {     // MFMA kernel only
-        const int ch = item_chunk(j);
-        const int jlast = max(min((ch + 1) * P.K, nv), 1) - 1;
-        const int base = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT + r;
+        const int base = item_key(j) + r;
 #pragma unroll
         for (int i = 0; i < (MF ? NL : 1); ++i) {
             const int row = min(base + i * RPI, jlast);
@@ -362,9 +364,7 @@ void attn_kernel(AttnParams P) {
     };
 
     auto load_tile = [&](Chunk (&kt)[NL], Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
-        const int ch = item_chunk(j);
-        const int jlast = max(min((ch + 1) * P.K, nv), 1) - 1;
-        const int base = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT + r;
+        const int base = item_key(j) + r;
         if constexpr (!MF) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
@@ -380,9 +380,8 @@ void attn_kernel(AttnParams P) {
     };
 
     auto compute_tile = [&](const Chunk (&kt)[NL], const Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
-        const int ch = item_chunk(j);
-        const int jend = min((ch + 1) * P.K, nv);
-        const int tile0 = ch * P.K + (wid + kAttnWaves * item_tile(j)) * KT;
+        const int jend = nv;
+        const int tile0 = item_key(j);
         if constexpr (MF) {
             // Scores on the matrix cores.  The wave's K rows go to its LDS
             // rows (as loaded: row i * RPI + r, 16 bytes at chunk c) and come
@@ -820,10 +819,16 @@ void attn_kernel(AttnParams P) {
         }
     }
 
-    // Chunk boundaries fall after the items j with (j + 1) % TPW == 0 among
-    // the full chunks; every wave has the same items, so the barriers match.
+    // Chunk boundaries fall after every TPW-th item among the full chunks
+    // (items are scored in order, each once); every wave has the same items,
+    // so the barriers match.
+    int left = TPW, ch_cur = c_begin;
     auto after = [&](int j) __attribute__((always_inline)) {
-        if (j < n_full_items && (j + 1) % TPW == 0) end_chunk(c_begin + j / TPW);
+        if (j < n_full_items && --left == 0) {
+            end_chunk(ch_cur);
+            ++ch_cur;
+            left = TPW;
+        }
     };
     // Entering each pass, A holds item j and B item j + 1, both requested; a
     // buffer is refilled as soon as it has been scored.  The loop body's

@@ -362,7 +362,7 @@ __device__ __forceinline__ float lds_tree_sum(const float* a) {
 // same bits.
 __device__ __forceinline__ float gate_share(const float* x, const float* w_row, int hidden,
                                             int tid, int nthreads) {
-    constexpr int kBatch = 16;
+    constexpr int kBatch = 8;
     float acc = 0.f;
     for (int i0 = tid; i0 < hidden; i0 += kBatch * nthreads) {
         float xv[kBatch], wv[kBatch];
