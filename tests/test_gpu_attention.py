@@ -103,6 +103,37 @@ def test_sliding_equals_full_on_same_history():
     assert np.max(np.abs(ring_o - full_o)) < 1e-5
 
 
+def test_wrapped_ring_equals_full_on_rolled_window():
+    """pos >= 511: the ring's 511 slots, read in position order (slot
+    (p - 511 + j) mod 511 for j = 0..510), as an append cache at pos 511,
+    with the same rotated query, key and value: the ring kernel and the
+    append kernel attend the same keys (a ring needs no reordering)."""
+    B, S = 5, 511
+    spec = inputs.sliding_spec(B, "bf16")
+    pos = np.array([511, 600, 1000, 1021, 4096], np.int32)
+    x = inputs.make_step(spec, pos, seed=8)
+    d = to_dev(x)
+    hswd.rope_apply(d["q"], d["k"], d["pos"], spec.rot, spec.theta)
+    desc = hswd.make_desc(d["k_cache"])
+    ws = hswd.workspace(desc, 1, 0)
+    ring_o = hswd.decode_attn_sliding(d["q"], d["k"], d["v"], d["k_cache"], d["v_cache"],
+                                      d["pos"], ws, desc=desc).cpu().numpy()
+    order = (pos[:, None] - S + np.arange(S)[None, :]) % S          # [B, 511] slots
+    pad = np.full((B, 8, 1, 256), 0x7fc0, np.uint16)
+    kr = np.stack([x.k_cache[b][:, order[b]] for b in range(B)])
+    vr = np.stack([x.v_cache[b][:, order[b]] for b in range(B)])
+    kf = cache_to_dev(np.concatenate([kr, pad], 2), "bf16")
+    vf = cache_to_dev(np.concatenate([vr, pad], 2), "bf16")
+    fdesc = hswd.make_desc(kf)
+    fws = hswd.workspace(fdesc, 0, S)
+    fpos = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    full_o = hswd.decode_attn_full(d["q"], d["k"], d["v"], kf, vf, fpos, S, fws,
+                                   desc=fdesc).cpu().numpy()
+    assert hswd.check_errors(ws) == 0 and hswd.check_errors(fws) == 0
+    say("wrapped ring vs rolled full max diff %.3e" % np.max(np.abs(ring_o - full_o)))
+    assert np.max(np.abs(ring_o - full_o)) < 1e-5
+
+
 def test_single_key_returns_rounded_value():
     """pos 0: nothing cached; the output is the new entry's value, bit for bit."""
     for kind, dtype in [("sliding", "bf16"), ("full", "f16"), ("sliding", "f32")]:
