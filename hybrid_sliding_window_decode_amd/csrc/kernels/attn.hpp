@@ -256,6 +256,13 @@ void attn_kernel(AttnParams P) {
     __shared__ float sm_dot[G][kAttnWaves];
     __shared__ float sm_gl[G][kAttnWaves];
     __shared__ int sm_last;
+    // MFMA kernel: the running fold of the chunk partials (single workgroup
+    // per pair) lives in LDS, not registers (it is touched once per chunk):
+    // M and L per wave (every lane of a wave computes the same values; lane
+    // 0 stores them and only that wave reads them back), O per thread.
+    __shared__ float sm_run_ml[MF ? G : 1][MF ? kAttnWaves : 1][2];
+    __shared__ float sm_run_o[MF ? G : 1][MF ? D : 1];
+    __shared__ float sm_glogit[MF ? G : 1];       // MFMA kernel: the given gate logits
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -647,7 +654,20 @@ void attn_kernel(AttnParams P) {
                         P.part_ml[idx * 2 + 1] = Lc;
                     }
                 } else if (P.wpp == 1) {
-                    run[hh].add(Mc, Lc, Oc);
+                    if constexpr (MF) {
+                        Fold f;
+                        f.M = sm_run_ml[hh][wid][0];
+                        f.L = sm_run_ml[hh][wid][1];
+                        f.O = t < D ? sm_run_o[hh][t] : 0.f;
+                        f.add(Mc, Lc, Oc);
+                        if (lane == 0) {
+                            sm_run_ml[hh][wid][0] = f.M;
+                            sm_run_ml[hh][wid][1] = f.L;
+                        }
+                        if (t < D) sm_run_o[hh][t] = f.O;
+                    } else {
+                        run[hh].add(Mc, Lc, Oc);
+                    }
                 } else {
                     if (t < D) st_agent(P.part_o + idx * D + t, Oc);
                     if (tid == 0) {
@@ -763,8 +783,16 @@ void attn_kernel(AttnParams P) {
         for (int hh = 0; hh < G; ++hh) {
             const float q_r = rotated ? rope_rotate(q_t[hh], q_p[hh], td < half, cs, sn) : q_t[hh];
             qsc[hh] = q_r * qmul;
+            if constexpr (MF) {              // empty running fold
+                if (t < D) sm_run_o[hh][t] = 0.f;
+                if (lane == 0) {
+                    sm_run_ml[hh][wid][0] = -INFINITY;
+                    sm_run_ml[hh][wid][1] = 0.f;
+                }
+            }
             if (t < D) {
                 if constexpr (MF) {          // 16-bit hi + lo parts for the MFMA operand
+                    if (t == 0) sm_glogit[hh] = glogit[hh];    // read back in the epilogue
                     constexpr int QT = DT == kF16 ? kF16 : kBF16;
                     const uint16_t hi = round_to_elt<QT>(qsc[hh]);
                     sm_qh[hh][t] = hi;
@@ -862,6 +890,16 @@ void attn_kernel(AttnParams P) {
     }
     if (c_valid > c_full) end_chunk(c_full);            // the partly valid chunk
     if (n_st > 0) flush();
+    if constexpr (MF) {
+        if (MODE != kModePartials && P.wpp == 1) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                run[hh].M = sm_run_ml[hh][wid][0];
+                run[hh].L = sm_run_ml[hh][wid][1];
+                run[hh].O = t < D ? sm_run_o[hh][t] : 0.f;
+            }
+        }
+    }
 
     if (MODE == kModePartials) {
         // chunks without a valid key are empty partials
@@ -934,7 +972,8 @@ void attn_kernel(AttnParams P) {
             float o = run[hh].O / run[hh].L;
             if (DT == kFP8) o *= vscale;
             if (MODE == kModeStep && (gproj || P.gate != nullptr)) {
-                const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl[hh]) : glogit[hh];
+                const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl[hh])
+                                          : (MF ? sm_glogit[hh] : glogit[hh]);
                 o *= 1.f / (1.f + expf(-logit));
             }
             P.out[(size_t)(bh0 + hh) * D + t] = o;
