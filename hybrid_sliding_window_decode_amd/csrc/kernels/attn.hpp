@@ -103,10 +103,12 @@ template <int DT, int G>
 constexpr bool use_mfma() { return G == 4 && (DT == kBF16 || DT == kF16 || DT == kFP8); }
 
 // Tile geometry.  G query heads per kv head keep G query vectors and G
-// accumulators per lane, so a grouped VALU kernel halves its tile (4 loads
-// of K and of V instead of 8) and reads fp8 rows 8 bytes per lane (8 dims,
-// as for 16-bit rows) to stay within 256 VGPRs (2 waves per SIMD).  The
-// MFMA kernel keeps no query vectors in registers and keeps 8-load tiles.
+// accumulators per lane, so a grouped VALU kernel reads fp8 rows 8 bytes per
+// lane (8 dims, as for 16-bit rows) and halves its 16-bit tiles (4 loads of
+// K and of V instead of 8) to stay within 256 VGPRs (2 waves per SIMD);
+// its fp8 tiles keep 8 loads, so a wave keeps as many bytes in flight as
+// with 16-bit rows.  The MFMA kernel keeps no query vectors in registers
+// and keeps 8-load tiles.
 template <int D, int DT, int G = 1>
 struct AttnGeo {
     static constexpr int EB = elt_bytes<DT>();        // element bytes
@@ -114,7 +116,7 @@ struct AttnGeo {
     static constexpr int EPC = CB / EB;               // elements per chunk
     static constexpr int LPR = D / EPC;               // lanes per cache row
     static constexpr int RPI = kWave / LPR;           // rows per wave-wide load
-    static constexpr int NL = G == 1 || use_mfma<DT, G>() ? 8 : 4;   // loads per tile
+    static constexpr int NL = G == 1 || use_mfma<DT, G>() || (G == 2 && DT == kFP8) ? 8 : 4;   // loads per tile
     static constexpr int KT = NL * RPI;               // keys per wave tile
     static constexpr int STEP = LPR / NL;             // lane stride between reduced keys
     static_assert(LPR >= NL && LPR <= kWave && kWave % LPR == 0, "geometry");
