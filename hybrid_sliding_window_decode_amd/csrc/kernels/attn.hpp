@@ -294,35 +294,11 @@ void attn_kernel(AttnParams P) {
     // cover part of a larger group, or a group of three with one head idle)
     const int gv = G == 4 ? P.gv : G;
     const int bh0 = b * P.H + (G == 4 ? g * P.Gq + P.h0 : g * G);
-    const int p = P.pos[b];
     const float kscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[g] : 1.f;
     const float vscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[P.Hkv + g] : 1.f;
-
-    // Valid cache rows: ring slots s < min(p, S); append rows < p.
-    int nv = p < 0 ? 0 : (p < P.S ? p : P.S);
-    if (!RING) {
-        const int grid_keys = P.n_chunk * P.K;
-        if (nv > grid_keys) nv = grid_keys;
-        if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p > P.max_pos)
-            atomicOr(P.err, 2);
-    }
-    if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p < 0) atomicOr(P.err, 4);
-
-    // This workgroup's chunks [c_begin, c_end): full ones [c_begin, c_full),
-    // then at most one partly valid chunk [c_full, c_valid); the rest hold no
-    // valid key.
-    const int n_valid_chunks = (nv + P.K - 1) / P.K;
     const int c_begin = wg * P.cpw;
     const int c_end = min(c_begin + P.cpw, P.n_chunk);
-    const int c_valid = max(c_begin, min(c_end, n_valid_chunks));
-    const int c_full = max(c_begin, min(c_valid, nv / P.K));
     const int TPW = P.K / (KT * kAttnWaves);          // tiles per wave in a full chunk
-    const int n_full_items = (c_full - c_begin) * TPW;
-    // tiles of the partly valid chunk, per wave (the maximum over the waves,
-    // so every wave runs the same loop; surplus tiles are fully masked)
-    const int part_tiles = c_valid > c_full ? (nv - c_full * P.K + KT - 1) / KT : 0;
-    const int part_items = (part_tiles + kAttnWaves - 1) / kAttnWaves;
-    const int n_items = n_full_items + part_items;
 
     const int c = lane % LPR;       // 16-byte chunk of the row this lane reads
     const int r = lane / LPR;       // row within a wave-wide load
@@ -355,12 +331,15 @@ void attn_kernel(AttnParams P) {
     // chunk after them.  A chunk is TPW * 4 tiles long, so both give the
     // first key c_begin * K + (4 j + wid) * KT, with no division.  Rows at
     // or past nv (only in the partly valid chunk, whose tiles end inside it,
-    // or in a prefetch the loop never scores) are clamped onto row nv - 1
-    // (row 0 when nothing is valid), so every load stays inside this
+    // or in a prefetch the loop never scores) are clamped onto row jlast =
+    // nv - 1 (row 0 when nothing is valid), so every load stays inside this
     // (stream, kv head)'s written rows and may be issued unconditionally;
-    // the softmax masks keys >= nv.
+    // the softmax masks keys >= nv.  The first two tiles go out before the
+    // position has arrived, clamped onto the block's last row S - 1 instead;
+    // a wave whose first two tiles reach past nv requests them again once nv
+    // is known (a stream with few keys), so no unwritten row is ever scored.
     const int key0 = c_begin * P.K + wid * KT;
-    const int jlast = max(nv, 1) - 1;
+    int jlast = P.S - 1;
     auto item_key = [&](int j) __attribute__((always_inline)) { return key0 + j * (kAttnWaves * KT); };
 
     auto load_k = [&](int j) __attribute__((always_inline)) {     // MFMA kernel only
@@ -387,6 +366,79 @@ void attn_kernel(AttnParams P) {
             vt[i] = load_kv<Geo::CB>(vbase + (size_t)row * D);
         }
     };
+
+    // Per-stream inputs first: this thread's query dim and its RoPE partner
+    // for every head of the group, and for the new entry the same of the key
+    // plus the value (threads past D read dim 0 and drop it).  Vector loads
+    // retire in order, so the prologue waits for these alone; the first two
+    // tiles, requested next, stay in flight under its double-precision RoPE.
+    // None of these waits for the stream's position, read only afterwards:
+    // the first tiles' rows do not depend on it (see load_tile).  Those two
+    // requests are unconditional: a load under a branch would make the
+    // compiler's wait counts at the join assume the branch was not taken, and
+    // the prologue would wait for the tiles too.
+    const bool has_new = MODE != kModePartials;
+    const int td = t < D ? t : 0;
+    const bool rotated = MODE == kModeStep && td < P.rot;
+    const int tp = MODE == kModeStep ? rope_partner(td, P.rot) : td;
+    const float* qv = P.q + (size_t)bh0 * D;
+    const float* kv = P.k + (size_t)pair * D;
+    const float* vv = P.v + (size_t)pair * D;
+    float q_t[G], q_p[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        q_t[hh] = hh < gv ? qv[(size_t)hh * D + td] : 0.f;      // idle heads: zero query
+        q_p[hh] = hh < gv ? qv[(size_t)hh * D + tp] : 0.f;
+    }
+    float k_t = 0.f, k_p = 0.f, v_t = 0.f;
+    if (has_new) {
+        k_t = kv[td];
+        k_p = kv[tp];
+        v_t = vv[td];
+    }
+    const bool gproj = MODE == kModeStep && P.gx != nullptr;
+    float glogit[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+        glogit[hh] = MODE == kModeStep && !gproj && P.gate != nullptr && hh < gv ? P.gate[bh0 + hh]
+                                                                                 : 0.f;
+
+    if constexpr (MF) load_k(0);
+    load_tile(kA, vA, 0);
+    load_tile(kB, vB, 1);
+
+    // The stream's position, requested after the first loads.
+    const int p = P.pos[b];
+
+    // Valid cache rows: ring slots s < min(p, S); append rows < p.
+    int nv = p < 0 ? 0 : (p < P.S ? p : P.S);
+    if (!RING) {
+        const int grid_keys = P.n_chunk * P.K;
+        if (nv > grid_keys) nv = grid_keys;
+        if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p > P.max_pos)
+            atomicOr(P.err, 2);
+    }
+    if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p < 0) atomicOr(P.err, 4);
+
+    // This workgroup's chunks [c_begin, c_end): full ones [c_begin, c_full),
+    // then at most one partly valid chunk [c_full, c_valid); the rest hold no
+    // valid key.
+    const int n_valid_chunks = (nv + P.K - 1) / P.K;
+    const int c_valid = max(c_begin, min(c_end, n_valid_chunks));
+    const int c_full = max(c_begin, min(c_valid, nv / P.K));
+    const int n_full_items = (c_full - c_begin) * TPW;
+    // tiles of the partly valid chunk, per wave (the maximum over the waves,
+    // so every wave runs the same loop; surplus tiles are fully masked)
+    const int part_tiles = c_valid > c_full ? (nv - c_full * P.K + KT - 1) / KT : 0;
+    const int part_items = (part_tiles + kAttnWaves - 1) / kAttnWaves;
+    const int n_items = n_full_items + part_items;
+
+    jlast = max(nv, 1) - 1;
+    if (item_key(1) + KT > nv) {        // the first two tiles reach past the valid rows
+        if constexpr (MF) load_k(0);
+        load_tile(kA, vA, 0);
+        load_tile(kB, vB, 1);
+    }
 
     auto compute_tile = [&](const Chunk (&kt)[NL], const Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
         const int jend = nv;
@@ -728,44 +780,6 @@ void attn_kernel(AttnParams P) {
         if (n_st == kStash) flush();
     };
 
-    // Per-stream inputs first: this thread's query dim and its RoPE partner
-    // for every head of the group, and for the new entry the same of the key
-    // plus the value (threads past D read dim 0 and drop it).  Vector loads
-    // retire in order, so the prologue waits for these alone; the first two
-    // tiles, requested next, stay in flight under its double-precision RoPE.
-    // Those two requests are unconditional (clamped rows, see load_tile): a
-    // load under a branch would make the compiler's wait counts at the join
-    // assume the branch was not taken, and the prologue would wait for the
-    // tiles too.
-    const bool has_new = MODE != kModePartials;
-    const int td = t < D ? t : 0;
-    const bool rotated = MODE == kModeStep && td < P.rot;
-    const int tp = MODE == kModeStep ? rope_partner(td, P.rot) : td;
-    const float* qv = P.q + (size_t)bh0 * D;
-    const float* kv = P.k + (size_t)pair * D;
-    const float* vv = P.v + (size_t)pair * D;
-    float q_t[G], q_p[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        q_t[hh] = hh < gv ? qv[(size_t)hh * D + td] : 0.f;      // idle heads: zero query
-        q_p[hh] = hh < gv ? qv[(size_t)hh * D + tp] : 0.f;
-    }
-    float k_t = 0.f, k_p = 0.f, v_t = 0.f;
-    if (has_new) {
-        k_t = kv[td];
-        k_p = kv[tp];
-        v_t = vv[td];
-    }
-    const bool gproj = MODE == kModeStep && P.gx != nullptr;
-    float glogit[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-        glogit[hh] = MODE == kModeStep && !gproj && P.gate != nullptr && hh < gv ? P.gate[bh0 + hh]
-                                                                                 : 0.f;
-
-    if constexpr (MF) load_k(0);
-    load_tile(kA, vA, 0);
-    load_tile(kB, vB, 1);
 
     // Query heads and new key rotated in-kernel for the fused step (one angle
     // for all); each query scaled by scale*log2(e) and, for an fp8 cache, by
