@@ -62,19 +62,29 @@ def full_kernel(kv):
     return "hswd::attn_kernel<256, %d, false, 1, 1>(...)" % {"bf16": 2, "fp8": 3}[kv]
 
 
+def kernel_source_digest():
+    """sha256 of the kernel sources with comments removed and whitespace
+    collapsed: it changes when the code changes, not when a comment does."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        text = open(os.path.join(ROOT, p)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(kv):
     """HBM bytes per full-layer launch from the committed FETCH_SIZE /
     WRITE_SIZE counter runs (scaled by a 1 GiB copy), or None when the kernel
-    sources have changed since those counters were taken."""
-    import hashlib
+    code has changed since those counters were taken."""
     try:
         rec = json.load(open(counters_path(kv)))
     except (OSError, ValueError):
         return None
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
-    if rec.get("source_sha256") != h.hexdigest() or full_kernel(kv) not in rec["kernels"]:
+    if rec.get("code_digest") != kernel_source_digest() or full_kernel(kv) not in rec["kernels"]:
         return None
     k = rec["kernels"][full_kernel(kv)]
     return int(round(k["read_bytes"] + k["write_bytes"]))

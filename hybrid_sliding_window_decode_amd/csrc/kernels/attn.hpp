@@ -373,10 +373,12 @@ void attn_kernel(AttnParams P) {
     // retire in order, so the prologue waits for these alone; the first two
     // tiles, requested next, stay in flight under its double-precision RoPE.
     // None of these waits for the stream's position, read only afterwards:
-    // the first tiles' rows do not depend on it (see load_tile).  Those two
+    // the first tiles' rows are clamped onto the block's last row.  Those two
     // requests are unconditional: a load under a branch would make the
     // compiler's wait counts at the join assume the branch was not taken, and
-    // the prologue would wait for the tiles too.
+    // the prologue would wait for the tiles too.  (The one branch with loads,
+    // the re-request of the first tiles of a stream with few keys, comes
+    // after them: only its own, rare path waits longer.)
     const bool has_new = MODE != kModePartials;
     const int td = t < D ? t : 0;
     const bool rotated = MODE == kModeStep && td < P.rot;
