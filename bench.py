@@ -53,13 +53,16 @@ KERNEL_SOURCES = ["hybrid_sliding_window_decode_amd/csrc/kernels/attn.hpp",
                   "hybrid_sliding_window_decode_amd/csrc/hswd.hip"]
 
 
-def counters_path(kv):
-    return os.path.join(ROOT, "profiles", "attn_step28_64x4096_%s_counters.json" % kv)
+def counters_path(kv, heads=H):
+    tag = kv if heads == HKV else "%s_h%d" % (kv, heads)
+    return os.path.join(ROOT, "profiles", "attn_step28_64x4096_%s_counters.json" % tag)
 
 
-def full_kernel(kv):
-    """rocprofv3's name of the full-layer fused step kernel for a cache type."""
-    return "hswd::attn_kernel<256, %d, false, 1, 1>(...)" % {"bf16": 2, "fp8": 3}[kv]
+def full_kernel(kv, heads=H):
+    """rocprofv3's name of the full-layer fused step kernel for a cache type
+    and a number of query heads over the HKV kv heads."""
+    return "hswd::attn_kernel<256, %d, false, 1, %d>(...)" % ({"bf16": 2, "fp8": 3}[kv],
+                                                             heads // HKV)
 
 
 def kernel_source_digest():
@@ -76,17 +79,18 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(kv):
+def measured_traffic(kv, heads=H):
     """HBM bytes per full-layer launch from the committed FETCH_SIZE /
     WRITE_SIZE counter runs (scaled by a 1 GiB copy), or None when the kernel
     code has changed since those counters were taken."""
     try:
-        rec = json.load(open(counters_path(kv)))
+        rec = json.load(open(counters_path(kv, heads)))
     except (OSError, ValueError):
         return None
-    if rec.get("code_digest") != kernel_source_digest() or full_kernel(kv) not in rec["kernels"]:
+    if (rec.get("code_digest") != kernel_source_digest()
+            or full_kernel(kv, heads) not in rec["kernels"]):
         return None
-    k = rec["kernels"][full_kernel(kv)]
+    k = rec["kernels"][full_kernel(kv, heads)]
     return int(round(k["read_bytes"] + k["write_bytes"]))
 
 
@@ -525,7 +529,7 @@ def main():
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(kv) if hq == HKV else None,
+                     "traffic": measured_traffic(kv, hq),
                      "kernel": "attn_kernel<256, %s, append, step, %d query heads per kv head> "
                                "(full layer, one launch)" % (kv, hq // HKV),
                      "bytes_per_launch": full_bytes,

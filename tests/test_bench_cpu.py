@@ -41,3 +41,16 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_committed_traffic_is_close_to_the_algorithmic_bytes():
+    """Where the committed counters match the kernel code, the measured HBM
+    bytes of the full-layer launch are within a few percent of what the
+    method must move (more would mean re-reads; less, a miscount)."""
+    for kv, elt in (("bf16", 2), ("fp8", 1)):
+        for heads in (8, 16, 32):
+            t = bench.measured_traffic(kv, heads)
+            if t is None:
+                continue
+            alg = bench.layer_bytes("full", elt=elt, heads=heads)
+            assert 0.999 * alg <= t <= 1.03 * alg, (kv, heads, t, alg)
