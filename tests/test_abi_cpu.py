@@ -200,3 +200,16 @@ def test_empty_batch_is_a_no_op():
                                       N, 0, N) == -1
     assert L.hswd_workspace_bytes(ctypes.byref(d0), 1, 0) > 0
 
+
+
+def test_binding_covers_every_declared_entry():
+    """Every hswd_* entry point the header declares has a ctypes signature and
+    a Python function of the same name (without the prefix)."""
+    import re
+    import hybrid_sliding_window_decode_amd as pkg
+    h = open(os.path.join(ROOT, "include", "hswd.h")).read()
+    declared = sorted(set(re.findall(r"\b(hswd_[a-z_0-9]+)\s*\(", h)))
+    assert len(declared) >= 18
+    for name in declared:
+        assert name in binding.SIGNATURES, name
+        assert hasattr(pkg, name[5:]) or hasattr(binding, name[5:]), name
