@@ -1,0 +1,15 @@
+// Attention kernels with 8 query heads per kv head (grouped-query attention)
+// over fp8 caches: head dims 256 and 128, scores on the matrix cores.
+#include "attn_launch.hpp"
+
+namespace hswd {
+
+template <>
+int32_t launch_attn_group<8>(const AttnParams& P, int mode, int D, int DT, int grid,
+                             hipStream_t st) {
+    constexpr int G_ = 8;
+    HSWD_ATTN_CASE(256, kFP8) HSWD_ATTN_CASE(128, kFP8)
+    return HSWD_ERR_UNSUPPORTED;
+}
+
+}  // namespace hswd

@@ -1,5 +1,5 @@
 // Launch of the attention kernel for one query-head group size G.  Each G
-// has its own translation unit (attn_g1.hip, attn_g2.hip, attn_g4.hip), so
+// has its own translation unit (attn_g1.hip, attn_g2.hip, attn_g4.hip, attn_g8.hip), so
 // the instantiations compile in parallel; hswd.hip picks one from H / Hkv.
 #pragma once
 
@@ -23,6 +23,9 @@ int32_t launch_attn_group<2>(const AttnParams& P, int mode, int D, int DT, int g
                              hipStream_t st);
 template <>
 int32_t launch_attn_group<4>(const AttnParams& P, int mode, int D, int DT, int grid,
+                             hipStream_t st);
+template <>
+int32_t launch_attn_group<8>(const AttnParams& P, int mode, int D, int DT, int grid,
                              hipStream_t st);
 
 template <int D, int DT, int G>

@@ -128,22 +128,26 @@ WsLayout ws_layout(const hswd_attn_desc* d, int n_chunk) {
 }
 
 // Kernel launch for the descriptor's group size H / Hkv.  Groups of 1, 2
-// and 4 query heads per kv head have their own kernels; a group of 3 runs
-// the 4-head kernel with one head idle; a larger group runs the 4-head
-// kernel once per four of its heads (each launch reads the cache once; only
-// the last writes the new entry, which the stream orders after every
-// earlier launch's reads).
+// and 4 query heads per kv head have their own kernels, and 8 over an fp8
+// cache; a group of 3 runs the 4-head kernel with one head idle (5 to 7
+// over fp8: the 8-head kernel); a larger group runs the 4-head (fp8: the
+// 8-head) kernel once per four (eight) of its heads (each launch reads the
+// cache once; only the last writes the new entry, which the stream orders
+// after every earlier launch's reads).
 template <int MODE>
 int32_t dispatch_attn(AttnParams P, int D, int DT, int grid, hipStream_t st) {
     const int group = P.H / P.Hkv;
     P.Gq = group;
     if (group == 1) return launch_attn_group<1>(P, MODE, D, DT, grid, st);
     if (group == 2) return launch_attn_group<2>(P, MODE, D, DT, grid, st);
-    for (int h0 = 0; h0 < group; h0 += 4) {
+    // fp8 caches: groups above 4 take eight query heads per launch
+    const int piece = DT == kFP8 && group > 4 ? 8 : 4;
+    for (int h0 = 0; h0 < group; h0 += piece) {
         P.h0 = h0;
-        P.gv = group - h0 < 4 ? group - h0 : 4;
-        P.write_entry = h0 + 4 >= group;
-        const int32_t r = launch_attn_group<4>(P, MODE, D, DT, grid, st);
+        P.gv = group - h0 < piece ? group - h0 : piece;
+        P.write_entry = h0 + piece >= group;
+        const int32_t r = piece == 8 ? launch_attn_group<8>(P, MODE, D, DT, grid, st)
+                                     : launch_attn_group<4>(P, MODE, D, DT, grid, st);
         if (r != HSWD_OK) return r;
     }
     return HSWD_OK;
@@ -247,12 +251,14 @@ int32_t hswd_rope_apply(float* q, float* k, const int32_t* pos, int32_t B, int32
     if (B < 0 || H < 1 || D < 2 || (k && Hkv < 1)) return HSWD_ERR_INVALID;
     if (rot_dim <= 0 || rot_dim > D || (rot_dim & 1)) return HSWD_ERR_INVALID;
     if (!(theta > 0.0) || !isfinite(theta)) return HSWD_ERR_INVALID;
-    const size_t lds = (size_t)(H + (k ? Hkv : 0)) * D * sizeof(float);
+    const size_t lds = (size_t)D * sizeof(float);
     if (lds > 64 * 1024) return HSWD_ERR_UNSUPPORTED;
+    const long vecs = (long)B * (H + (k ? Hkv : 0));
+    if (vecs > 0x7fffffffL) return HSWD_ERR_UNSUPPORTED;
     if (B == 0) return HSWD_OK;
     if (!q || !pos) return HSWD_ERR_INVALID;
-    hipLaunchKernelGGL(rope_kernel, dim3(B), dim3(256), lds, as_stream(stream), q, k, pos, H,
-                       k ? Hkv : 0, D, rot_dim, log2(theta));
+    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)vecs), dim3(256), lds, as_stream(stream), q, k,
+                       pos, H, k ? Hkv : 0, D, rot_dim, log2(theta));
     return launch_status();
 }
 

@@ -89,18 +89,21 @@ struct AttnParams {
     int rot;
     double log2_theta;
     float qscale;            // softmax scale * log2(e)
-    // 4-head kernel only: query heads per kv head in memory (H / Hkv), the
-    // first head of the group this launch covers and how many (<= 4), and
-    // whether it writes the new entry.  A group above four heads is covered
-    // by consecutive launches of four; the last one writes the entry.
+    // 4- and 8-head kernels only: query heads per kv head in memory (H /
+    // Hkv), the first head of the group this launch covers and how many (<=
+    // G), and whether it writes the new entry.  A larger group is covered by
+    // consecutive launches; the last one writes the entry.
     int Gq, h0, gv, write_entry;
 };
 
 // Scores on the matrix cores: 4 query heads per kv head over a 16-bit or
-// fp8 cache (the score product is then a [4 x D] . [D x keys] contraction;
-// fp8 keys are staged as bf16, which holds every e4m3 value exactly).
+// fp8 cache, or 8 over an fp8 cache (the score product is then a [G x D] .
+// [D x keys] contraction; fp8 keys become bf16, which holds every e4m3 value
+// exactly).
 template <int DT, int G>
-constexpr bool use_mfma() { return G == 4 && (DT == kBF16 || DT == kF16 || DT == kFP8); }
+constexpr bool use_mfma() {
+    return (G == 4 && (DT == kBF16 || DT == kF16 || DT == kFP8)) || (G == 8 && DT == kFP8);
+}
 
 // Tile geometry.  G query heads per kv head keep G query vectors and G
 // accumulators per lane, so a grouped VALU kernel reads fp8 rows 8 bytes per
@@ -222,6 +225,13 @@ __device__ __forceinline__ float transposed_reduce4(const float (&v)[4], int lan
 template <int G>
 constexpr int stash_slots() { return G == 1 ? 4 : (G == 2 ? 2 : 1); }
 
+// Flush buffers of the wave chunk partials: two, used alternately, so a
+// slot is rewritten only after the barrier of the flush in between; the
+// 8-head kernel keeps one (its partials take 32 KiB) and ends each flush
+// with a second barrier instead.
+template <int G>
+constexpr int flush_buffers() { return G == 8 ? 1 : 2; }
+
 // G = H / Hkv query heads share each kv head (grouped-query attention by
 // reshaping the query, the talker commit): one workgroup scores all G of
 // them against every K/V tile it loads, so the cache is read once per group.
@@ -234,7 +244,9 @@ void attn_kernel(AttnParams P) {
     constexpr int EPC = Geo::EPC, LPR = Geo::LPR, RPI = Geo::RPI, NL = Geo::NL, KT = Geo::KT;
     constexpr float kLn2 = 0.69314718055994531f;
     constexpr int kStash = stash_slots<G>();
-    static_assert(G == 1 || G == 2 || G == 4, "query heads per kv head");
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "query heads per kv head");
+    static_assert(G != 8 || use_mfma<DT, G>(), "8 query heads per kv head: fp8 caches only");
+    constexpr int NB = flush_buffers<G>();
 
     constexpr bool MF = use_mfma<DT, G>();
     // MFMA kernel: each wave stages its K rows in LDS (rows padded by 16
@@ -244,17 +256,22 @@ void attn_kernel(AttnParams P) {
     // per lane group, a head per lane) to the value layout through LDS.
     constexpr int KPAD = D * 2 / 16 + 1;                  // 16-byte units per staged (16-bit) row
     __shared__ float sm_q[MF ? 1 : G][D];
-    __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT : 1][MF ? KPAD : 1];
+    // the 8-head kernel stages fp8 keys as they are (8-byte units, rows
+    // padded by 8 bytes: the 16 rows of an operand read fall in distinct
+    // banks) and converts them when it reads them back
+    constexpr bool K8 = MF && G == 8;
+    __shared__ u32x4 sm_k[MF && !K8 ? kAttnWaves : 1][MF && !K8 ? KT : 1][MF && !K8 ? KPAD : 1];
+    __shared__ u32x2 sm_k8[K8 ? kAttnWaves : 1][K8 ? KT : 1][K8 ? D / 8 + 1 : 1];
     // query rows padded by 16 bytes too: unpadded, the G heads' rows (512
     // bytes apart) would share banks and the operand reads conflict 4 ways
     __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G : 1][MF ? D + 8 : 1];
     __shared__ __attribute__((aligned(16))) uint16_t sm_ql[MF ? G : 1][MF ? D + 8 : 1];
     // (both read 16 bytes at a time: aligned to 16)
     __shared__ __attribute__((aligned(16))) float sm_p[MF && DT == kBF16 ? kAttnWaves : 1][MF ? KT : 1][4];
-    __shared__ __attribute__((aligned(16))) uint16_t sm_ph[MF && DT != kBF16 ? kAttnWaves : 1][MF ? NL / 2 : 1][RPI][4][2];
-    __shared__ __attribute__((aligned(16))) float sm_al[MF ? kAttnWaves : 1][4];
-    __shared__ float sm_o[2][kStash][G][kAttnWaves][D];   // wave chunk partials, by flush parity
-    __shared__ float sm_m[2][kStash][G][kAttnWaves], sm_l[2][kStash][G][kAttnWaves];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_ph[MF && DT != kBF16 ? kAttnWaves : 1][MF ? NL / 2 : 1][RPI][G][2];
+    __shared__ __attribute__((aligned(16))) float sm_al[MF ? kAttnWaves : 1][G];
+    __shared__ float sm_o[NB][kStash][G][kAttnWaves][D];   // wave chunk partials, by flush parity
+    __shared__ float sm_m[NB][kStash][G][kAttnWaves], sm_l[NB][kStash][G][kAttnWaves];
     __shared__ float sm_dot[G][kAttnWaves];
     __shared__ float sm_gl[G][kAttnWaves];
     __shared__ int sm_last;
@@ -290,10 +307,11 @@ void attn_kernel(AttnParams P) {
     }
     const int b = pair / P.Hkv;
     const int g = pair % P.Hkv;
-    // query heads of this launch: bh0 .. bh0 + gv - 1 (the 4-head kernel can
-    // cover part of a larger group, or a group of three with one head idle)
-    const int gv = G == 4 ? P.gv : G;
-    const int bh0 = b * P.H + (G == 4 ? g * P.Gq + P.h0 : g * G);
+    // query heads of this launch: bh0 .. bh0 + gv - 1 (the 4- and 8-head
+    // kernels can cover part of a larger group, or a smaller group with
+    // heads idle)
+    const int gv = G >= 4 ? P.gv : G;
+    const int bh0 = b * P.H + (G >= 4 ? g * P.Gq + P.h0 : g * G);
     const float kscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[g] : 1.f;
     const float vscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[P.Hkv + g] : 1.f;
     const int c_begin = wg * P.cpw;
@@ -461,7 +479,8 @@ void attn_kernel(AttnParams P) {
             asm volatile("" ::: "memory");     // the query reads below stay in the loop
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_bf16x8(kR[i]);
+                if constexpr (K8) sm_k8[wid][i * RPI + r][c] = kR[i];
+                else if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_bf16x8(kR[i]);
                 else sm_k[wid][i * RPI + r][c] = kR[i];
             }
             // the next item's K into the freed registers, in flight under
@@ -485,7 +504,9 @@ void attn_kernel(AttnParams P) {
                 const u32x4 ql = hq < G ? *reinterpret_cast<const u32x4*>(&sm_ql[hq < G ? hq : 0][32 * sl + 8 * kq]) : zero;
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
-                    const u32x4 a = sm_k[wid][kg * 16 + hq][4 * sl + kq];
+                    u32x4 a;
+                    if constexpr (K8) a = fp8x8_to_bf16x8(sm_k8[wid][kg * 16 + hq][4 * sl + kq]);
+                    else a = sm_k[wid][kg * 16 + hq][4 * sl + kq];
                     f32x4& ah = acc[kg][2 * (sl & 1)];
                     f32x4& al_ = acc[kg][2 * (sl & 1) + 1];
                     if constexpr (DT != kF16) {
@@ -550,8 +571,18 @@ void attn_kernel(AttnParams P) {
             // P.V on the VALU, V rows in their loaded layout: the rescale
             // factors and the probabilities come back from LDS; the rescale
             // is skipped when no head's max moved (a multiply by one)
-            const f32x4 al = *reinterpret_cast<const f32x4*>(&sm_al[wid][0]);
-            if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
+            float al[G];
+            bool moved = false;
+#pragma unroll
+            for (int hh = 0; hh < G; hh += 4) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm_al[wid][hh]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    al[hh + u] = a4[u];
+                    moved = moved || a4[u] != 1.f;
+                }
+            }
+            if (moved) {
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
@@ -565,7 +596,12 @@ void attn_kernel(AttnParams P) {
                 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
                 for (int jp = 0; jp < NL / 2; ++jp) {
-                    const u32x4 pp = *reinterpret_cast<const u32x4*>(&sm_ph[wid][jp][r][0][0]);
+                    uint32_t pw[G];
+#pragma unroll
+                    for (int hh = 0; hh < G; hh += 4) {
+                        const u32x4 pp = *reinterpret_cast<const u32x4*>(&sm_ph[wid][jp][r][hh][0]);
+                        pw[hh] = pp.x; pw[hh + 1] = pp.y; pw[hh + 2] = pp.z; pw[hh + 3] = pp.w;
+                    }
                     uint32_t vp[EPC];
                     if constexpr (DT == kFP8) {
                         const uint32_t a[2] = {vt[2 * jp].x, vt[2 * jp].y};
@@ -589,7 +625,6 @@ void attn_kernel(AttnParams P) {
                             vp[2 * w + 1] = __builtin_amdgcn_perm(bq[w], a[w], 0x07060302u);
                         }
                     }
-                    const uint32_t pw[4] = {pp.x, pp.y, pp.z, pp.w};
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
@@ -683,7 +718,7 @@ void attn_kernel(AttnParams P) {
     int n_st = 0, st_first = 0, n_flush = 0;
 
     auto flush = [&]() __attribute__((always_inline)) {
-        const int buf = n_flush & 1;
+        const int buf = n_flush % NB;
         ++n_flush;
         __syncthreads();
         for (int s = 0; s < n_st; ++s) {
@@ -734,6 +769,9 @@ void attn_kernel(AttnParams P) {
             }
         }
         n_st = 0;
+        // a single flush buffer: every thread has read it before any wave
+        // writes its next chunk's partial there
+        if constexpr (NB == 1) __syncthreads();
     };
 
     auto end_chunk = [&](int ch) __attribute__((always_inline)) {
@@ -742,21 +780,21 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) l_w[hh] = wave_sum(l_lane[hh]);
         }
+        const int buf = n_flush % NB;
 #pragma unroll
-        for (int m = LPR; m < kWave; m <<= 1) {
+        for (int hh = 0; hh < G; ++hh) {
+            // head by head: sum over the lanes that share this lane's dims,
+            // then store, so only one head's exchanges are live at a time
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
+            for (int m = LPR; m < kWave; m <<= 1) {
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) o_acc[hh][e] = xor_sum_rt(o_acc[hh][e], m);
             }
-        }
-        const int buf = n_flush & 1;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
             if (r == 0) {
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) sm_o[buf][n_st][hh][wid][c * EPC + e] = o_acc[hh][e];
             }
+            if constexpr (G == 8) __builtin_amdgcn_sched_barrier(0);
             if (!MF && lane == 0) {
                 sm_m[buf][n_st][hh][wid] = m_run[hh];
                 sm_l[buf][n_st][hh][wid] = l_w[hh];
@@ -998,7 +1036,7 @@ void attn_kernel(AttnParams P) {
         }
     }
 
-    if (MODE == kModeStep && (G != 4 || P.write_entry)) {
+    if (MODE == kModeStep && (G < 4 || P.write_entry)) {
         // Every workgroup of this pair has finished reading (one workgroup:
         // the barrier of the last stash flush, which every wave reaches after
         // its last tile; several: the arrival count), so the ring slot that

@@ -6,25 +6,21 @@
 
 namespace hswd {
 
-// RoPE in place, one workgroup per stream: q [B,H,D] then k [B,Hkv,D].
-// Each thread rotates whole elements; both members of a pair are computed
-// from the unrotated vector before any store (the block barrier).
+// RoPE in place, one workgroup per (stream, head vector): q [B,H,D] heads
+// first, then k [B,Hkv,D].  Each thread rotates whole elements; both
+// members of a pair are computed from the unrotated vector before any store
+// (the block barrier), through D floats of LDS.
 __global__ __launch_bounds__(256) void rope_kernel(float* q, float* k, const int32_t* pos, int H,
                                                    int Hkv, int D, int rot, double log2_theta) {
-    extern __shared__ float sm[];                // (H + Hkv) * D rotated values
-    const int b = blockIdx.x;
+    extern __shared__ float sm[];                // D rotated values
+    const int nvec = H + Hkv;
+    const int b = blockIdx.x / nvec;
+    const int v = blockIdx.x % nvec;
     const int p = pos[b];
-    const int nq = H * D, nk = k ? Hkv * D : 0;
-    for (int i = threadIdx.x; i < nq + nk; i += blockDim.x) {
-        const float* base = i < nq ? q + ((size_t)b * H + i / D) * D
-                                   : k + ((size_t)b * Hkv + (i - nq) / D) * D;
-        sm[i] = rope_elem(base, i % D, rot, log2_theta, p);
-    }
+    float* x = v < H ? q + ((size_t)b * H + v) * D : k + ((size_t)b * Hkv + (v - H)) * D;
+    for (int i = threadIdx.x; i < D; i += blockDim.x) sm[i] = rope_elem(x, i, rot, log2_theta, p);
     __syncthreads();
-    for (int i = threadIdx.x; i < nq + nk; i += blockDim.x) {
-        float* dst = i < nq ? q + (size_t)b * nq + i : k + (size_t)b * nk + (i - nq);
-        *dst = sm[i];
-    }
+    for (int i = threadIdx.x; i < D; i += blockDim.x) x[i] = sm[i];
 }
 
 // Slot and mask of each stream.

@@ -104,11 +104,13 @@ typedef struct {
                                the query [talker]); the attention entries take
                                H / Hkv = 1 with any cache, and any H / Hkv > 1
                                with a 16-bit or fp8 cache and head_dim 128 or 256
-                               (else UNSUPPORTED).  Groups of 2 and 4 read the
-                               cache once per layer; 3 runs as 4 with one head
-                               idle; a group above 4 is taken four query heads
-                               per launch, each launch reading the cache once
-                               (the last one writes the new entry). */
+                               (else UNSUPPORTED).  Groups of 2 and 4 (and 5
+                               to 8 over an fp8 cache) read the cache once per
+                               layer, a group below a kernel's size leaving
+                               heads idle; a larger group is taken four query
+                               heads (fp8: eight) per launch, each launch
+                               reading the cache once (the last one writes the
+                               new entry). */
     int32_t head_dim;       /* D: 64, 128 or 256 (fp8 caches: 128 or 256) */
     int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows */
     int32_t kv_dtype;       /* hswd_dtype of the cache */
@@ -169,7 +171,7 @@ int32_t hswd_ring_mask(uint8_t* mask, int32_t* slot, const int32_t* pos, int32_t
  * Sliding layers: rot_dim = D, theta = 1e4; full layers: rot_dim = D/4,
  * theta = 5e6.  The angle, its sine and cosine and the rotation are computed
  * in double precision and rounded once to float32.  rot_dim even, 0 < rot_dim
- * <= D, theta > 0. */
+ * <= D, theta > 0.  D above 16384 returns HSWD_ERR_UNSUPPORTED. */
 int32_t hswd_rope_apply(float* q, float* k, const int32_t* pos, int32_t B, int32_t H,
                         int32_t Hkv, int32_t D, int32_t rot_dim, double theta,
                         void* stream);

@@ -136,7 +136,7 @@ def test_other_entries_host_checks():
     assert L.hswd_rope_apply(A, A, A, 2, 8, 8, 256, 258, 1e4, None) == -1
     assert L.hswd_rope_apply(A, A, A, 2, 8, 8, 256, 64, 0.0, None) == -1
     assert L.hswd_rope_apply(None, A, A, 2, 8, 8, 256, 64, 5e6, None) == -1
-    assert L.hswd_rope_apply(A, A, A, 2, 64, 64, 256, 64, 5e6, None) == -6   # LDS bound
+    assert L.hswd_rope_apply(A, A, A, 2, 8, 8, 16386, 64, 5e6, None) == -6   # LDS bound
     # kv write
     assert L.hswd_kv_slot_write(A, A, A, A, A, ctypes.byref(d), 1, None, None, None) == -3
     assert L.hswd_kv_slot_write(A, MIS, A, A, A, ctypes.byref(d), 1, None, A, None) == -2

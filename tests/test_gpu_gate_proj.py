@@ -26,7 +26,7 @@ def test_gate_proj_matches_oracle():
 
 @pytest.mark.parametrize("kind,dtype,G", [("sliding", "bf16", 1), ("full", "f16", 1),
                                           ("sliding", "bf16", 4), ("full", "bf16", 2),
-                                          ("full", "bf16", 8)])
+                                          ("full", "bf16", 8), ("sliding", "fp8", 8)])
 def test_layer_step_gproj(kind, dtype, G):
     """Fused projection + step: the same bits as gate_proj then layer_step,
     and the oracle's output scaled by the oracle's sigmoid(logit); G query
@@ -41,7 +41,7 @@ def test_layer_step_gproj(kind, dtype, G):
     gx, gw = inputs.gate_inputs(B, 2048, 8, seed=64)
     mp = int(x.pos.max())
     d = to_dev(x)
-    desc = hswd.make_desc(d["k_cache"], n_heads=8)
+    desc = hswd.make_desc(d["k_cache"], n_heads=8, kv_scale=d["kv_scale"])
     ws = hswd.workspace(desc, ring, mp)
     say("layer_step_gproj %s %s G=%d" % (kind, dtype, G))
     fused = hswd.layer_step_gproj(d["q"], d["k"], d["v"], f32_dev(gx), f32_dev(gw), d["k_cache"],
@@ -55,7 +55,7 @@ def test_layer_step_gproj(kind, dtype, G):
     assert np.array_equal(fused, two)
     kc, vc = x.k_cache.copy(), x.v_cache.copy()
     r = oracle.layer_step(x.q, x.k, x.v, None, kc, vc, x.pos, CODE[dtype], ring, spec.rot,
-                          spec.theta, write=False)
+                          spec.theta, write=False, kv_scale=spec.kv_scale)
     lg = oracle.gate_proj(gx, gw)
     ref = r["o_pre"] * (1.0 / (1.0 + np.exp(-lg)))[:, :, None]
     assert_parity(fused, ref, x, "gproj step")

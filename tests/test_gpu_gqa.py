@@ -63,6 +63,12 @@ def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
     ("full", "fp8", 6, 256, 3, [2999, 0, 1500], 3000, 0, 24),
     ("full", "bf16", 5, 256, 2, [19999, 7001], 20000, 0, 10),
     ("sliding", "f16", 16, 128, 4, "ragged", None, 0, 32),
+    # fp8: the 8-head kernel (one launch for 5 to 8 heads, heads idle below
+    # 8; two launches of eight for 16), cross-workgroup merge, D = 128
+    ("full", "fp8", 8, 256, 2, [19999, 7001], 20000, 0, 16),
+    ("full", "fp8", 8, 128, 4, "ragged", 3000, 0, 64),
+    ("sliding", "fp8", 16, 256, 4, "ragged", None, 0, 32),
+    ("full", "fp8", 5, 256, 3, [2999, 1, 1500], 3000, 0, 10),
 ])
 def test_gqa_large_groups(kind, dtype, G, D, B, pos, S, kps, H):
     check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=H)
@@ -130,16 +136,19 @@ def check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=8, q_mult=1.0):
         assert np.array_equal(kc[b, :, row], entry_codes(k_rot[b], dtype, ksc))
 
 
-def test_gqa_partials_merge_to_oracle():
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("fp8", 8)])
+def test_gqa_partials_merge_to_oracle(dtype, G):
     """Chunk partials of a grouped full layer (cached keys only), merged by
     hswd_lse_merge, give the oracle's attention over the same keys."""
-    B, G, S = 3, 4, 2500
-    spec = gqa_spec("full", B, "bf16", G, S=S)
+    B, S = 3, 2500
+    spec = gqa_spec("full", B, dtype, G, S=S, H=8 * G // 4 if G == 8 else 8)
     x = inputs.make_step(spec, [2499, 700, 1], seed=31)
     d = to_dev(x)
     hswd.rope_apply(d["q"], d["k"], d["pos"], spec.rot, spec.theta)
-    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, keys_per_split=256)
-    say("gqa partials")
+    kps = 256 if dtype != "fp8" else 512
+    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, keys_per_split=kps,
+                          kv_scale=d["kv_scale"])
+    say("gqa partials %s G=%d" % (dtype, G))
     po, pml = hswd.decode_attn_partials(d["q"], d["k_cache"], d["v_cache"], d["pos"], 0,
                                         max_pos=2499, desc=desc)
     merged = hswd.lse_merge(po, pml).cpu().numpy()
@@ -149,9 +158,12 @@ def test_gqa_partials_merge_to_oracle():
         p = int(x.pos[b])
         for h in range(spec.H):
             gk = h // G
+            ks = vs = 1.0
+            if spec.kv_scale is not None:
+                ks, vs = float(spec.kv_scale[0][gk]), float(spec.kv_scale[1][gk])
             m, l, o = oracle.partial(q_rot[b, h], x.k_cache[b, gk], x.v_cache[b, gk],
-                                     CODE["bf16"], 0, p, scale)
-            vmax = np.abs(oracle.decode(CODE["bf16"], x.v_cache[b, gk, :p])).max()
+                                     CODE[dtype], 0, p, scale, ks=ks, vs=vs)
+            vmax = np.abs(oracle.decode(CODE[dtype], x.v_cache[b, gk, :p])).max() * vs
             err = np.abs(merged[b, h] - o / l).max() / vmax
             assert err <= 2e-3, (b, h, err)
 

@@ -27,10 +27,11 @@ def test_ring_mask_bit_exact(ring):
     assert np.array_equal(mask.cpu().numpy(), om_mask)
 
 
-@pytest.mark.parametrize("rot,theta", [(256, 1e4), (64, 5e6), (128, 1e4)])
-def test_rope(rot, theta):
+@pytest.mark.parametrize("rot,theta,H", [(256, 1e4, 8), (64, 5e6, 8), (128, 1e4, 8),
+                                         (256, 1e4, 64)])
+def test_rope(rot, theta, H):
     rng = np.random.default_rng(40 + rot)
-    B, H, Hkv, D = len(POS), 8, 8, 256
+    B, Hkv, D = len(POS), 8, 256
     q = rng.standard_normal((B, H, D), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, D), dtype=np.float32)
     say("rope rot=%d theta=%g B=%d" % (rot, theta, B))
@@ -92,12 +93,12 @@ def test_kv_slot_write_rounding_bit_exact(dtype):
         assert np.array_equal(got_v, ref_v)
 
 
-@pytest.mark.parametrize("H", [8, 32])
+@pytest.mark.parametrize("H", [8, 32, 64])
 def test_fp8_decode_all_codes_in_attention(H):
     """A one-key cache holding each of the 255 non-NaN fp8 codes in turn
     (q = 0, new value 0): the output is the mean of the decoded cached value
     and 0 -- the kernel's fp8 decode of every code, against the oracle's
-    (H = 32: the grouped kernel's value path)."""
+    (H = 32, 64: the 4- and 8-head kernels' value paths)."""
     codes = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], np.uint8)
     B, D = len(codes), 256
     spec = inputs.sliding_spec(B, "fp8", n_slots=511, H=H)
@@ -118,7 +119,7 @@ def test_fp8_decode_all_codes_in_attention(H):
     assert np.array_equal(o[:, :, 0].astype(np.float64), np.repeat(val, G, axis=1) / 2)
 
 
-@pytest.mark.parametrize("H", [8, 32])
+@pytest.mark.parametrize("H", [8, 32, 64])
 def test_fp8_key_decode_all_codes_in_attention(H):
     """A one-key cache whose key holds one of the 255 non-NaN fp8 codes in
     every dim, value 1; new key and value 0; the query a multiple t of the
