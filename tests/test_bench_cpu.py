@@ -48,7 +48,7 @@ def test_committed_traffic_is_close_to_the_algorithmic_bytes():
     bytes of the full-layer launch are within a few percent of what the
     method must move (more would mean re-reads; less, a miscount)."""
     for kv, elt in (("bf16", 2), ("fp8", 1)):
-        for heads in (8, 16, 32):
+        for heads in (8, 16, 24, 32, 64):
             t = bench.measured_traffic(kv, heads)
             if t is None:
                 continue
