@@ -50,7 +50,8 @@ def is_full(l):
 
 KERNEL_SOURCES = ["hybrid_sliding_window_decode_amd/csrc/kernels/attn.hpp",
                   "hybrid_sliding_window_decode_amd/csrc/kernels/common.hpp",
-                  "hybrid_sliding_window_decode_amd/csrc/hswd.hip"]
+                  "hybrid_sliding_window_decode_amd/csrc/hswd.hip",
+                  "hybrid_sliding_window_decode_amd/csrc/attn_launch.hpp"]
 
 
 def counters_path(kv, heads=H):
@@ -58,11 +59,23 @@ def counters_path(kv, heads=H):
     return os.path.join(ROOT, "profiles", "attn_step28_64x4096_%s_counters.json" % tag)
 
 
+def kernel_group(kv, heads=H):
+    """(G, pieces): query heads per workgroup of the attention kernel that runs
+    `heads` query heads over the HKV kv heads, and the pieces each group is
+    split into (a group above 4, fp8: above 8, runs in pieces of 4, fp8: 8)."""
+    group = heads // HKV
+    if group <= 2:
+        return group, 1
+    piece = 8 if kv == "fp8" and group > 4 else 4
+    return piece, -(-group // piece)
+
+
 def full_kernel(kv, heads=H):
     """rocprofv3's name of the full-layer fused step kernel for a cache type
     and a number of query heads over the HKV kv heads."""
-    return "hswd::attn_kernel<256, %d, false, 1, %d>(...)" % ({"bf16": 2, "fp8": 3}[kv],
-                                                             heads // HKV)
+    g, pieces = kernel_group(kv, heads)
+    return "hswd::attn_kernel<256, %d, false, 1, %d, %s>(...)" % (
+        {"bf16": 2, "fp8": 3}[kv], g, "true" if pieces > 1 else "false")
 
 
 def kernel_source_digest():
@@ -530,8 +543,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(kv, hq),
-                     "kernel": "attn_kernel<256, %s, append, step, %d query heads per kv head> "
-                               "(full layer, one launch)" % (kv, hq // HKV),
+                     "kernel": "attn_kernel<256, %s, append, step, %d query heads per kv head%s> "
+                               "(full layer, one launch)" % (
+                                   kv, kernel_group(kv, hq)[0],
+                                   "" if kernel_group(kv, hq)[1] == 1 else
+                                   ", %d pieces per group" % kernel_group(kv, hq)[1]),
                      "bytes_per_launch": full_bytes,
                      "read_ceiling": ceiling,
                      "frac_of_read_ceiling": (None if ceiling is None else

@@ -5,9 +5,10 @@
 namespace hswd {
 
 template <>
-int32_t launch_attn_group<2>(const AttnParams& P, int mode, int D, int DT, int grid,
-                             hipStream_t st) {
+int32_t launch_attn_group<2, false>(const AttnParams& P, int mode, int D, int DT, int grid,
+                                    hipStream_t st) {
     constexpr int G_ = 2;
+    constexpr bool SH_ = false;
     HSWD_ATTN_CASE(256, kBF16) HSWD_ATTN_CASE(256, kF16) HSWD_ATTN_CASE(256, kFP8)
     HSWD_ATTN_CASE(128, kBF16) HSWD_ATTN_CASE(128, kF16) HSWD_ATTN_CASE(128, kFP8)
     return HSWD_ERR_UNSUPPORTED;

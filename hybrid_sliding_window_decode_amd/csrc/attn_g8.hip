@@ -5,9 +5,10 @@
 namespace hswd {
 
 template <>
-int32_t launch_attn_group<8>(const AttnParams& P, int mode, int D, int DT, int grid,
-                             hipStream_t st) {
+int32_t launch_attn_group<8, false>(const AttnParams& P, int mode, int D, int DT, int grid,
+                                    hipStream_t st) {
     constexpr int G_ = 8;
+    constexpr bool SH_ = false;
     HSWD_ATTN_CASE(256, kFP8) HSWD_ATTN_CASE(128, kFP8)
     return HSWD_ERR_UNSUPPORTED;
 }

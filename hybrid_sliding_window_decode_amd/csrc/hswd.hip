@@ -115,12 +115,27 @@ int chunks_per_workgroup(const hswd_attn_desc* d, int n_chunk) {
     return (int)((n_chunk + wpp - 1) / wpp);
 }
 
+// Query heads per kernel piece of a group (its kernel's G), and the pieces
+// a group is split into.
+int group_piece(int group, int DT) {
+    if (group <= 2) return group;
+    return DT == kFP8 && group > 4 ? 8 : 4;
+}
+int group_pieces(const hswd_attn_desc* d) {
+    const int group = d->n_heads / d->n_kv_heads;
+    const int piece = group_piece(group, d->kv_dtype);
+    return (group + piece - 1) / piece;
+}
+
 WsLayout ws_layout(const hswd_attn_desc* d, int n_chunk) {
     WsLayout L;
     const size_t pairs = (size_t)d->batch * d->n_kv_heads;
     const size_t bh = (size_t)d->batch * d->n_heads;
+    const int np = group_pieces(d);
+    // merge arrivals per (pair, piece), then entry arrivals per pair
+    const size_t n_counters = pairs * np + (np > 1 ? pairs : 0);
     L.counters = kAlign;
-    L.part_ml = L.counters + round_up(pairs * sizeof(int32_t), kAlign);
+    L.part_ml = L.counters + round_up(n_counters * sizeof(int32_t), kAlign);
     const size_t parts = n_chunk > 1 ? (size_t)n_chunk : 0;
     L.part_o = L.part_ml + round_up(bh * parts * 2 * sizeof(float), kAlign);
     L.total = L.part_o + round_up(bh * parts * d->head_dim * sizeof(float), kAlign);
@@ -130,27 +145,21 @@ WsLayout ws_layout(const hswd_attn_desc* d, int n_chunk) {
 // Kernel launch for the descriptor's group size H / Hkv.  Groups of 1, 2
 // and 4 query heads per kv head have their own kernels, and 8 over an fp8
 // cache; a group of 3 runs the 4-head kernel with one head idle (5 to 7
-// over fp8: the 8-head kernel); a larger group runs the 4-head (fp8: the
-// 8-head) kernel once per four (eight) of its heads (each launch reads the
-// cache once; only the last writes the new entry, which the stream orders
-// after every earlier launch's reads).
+// over fp8: the 8-head kernel); a larger group is split into pieces of four
+// (fp8: eight) heads, one workgroup per piece in the same launch (each
+// reads the cache; the last piece to finish writes the new entry).
 template <int MODE>
 int32_t dispatch_attn(AttnParams P, int D, int DT, int grid, hipStream_t st) {
     const int group = P.H / P.Hkv;
     P.Gq = group;
-    if (group == 1) return launch_attn_group<1>(P, MODE, D, DT, grid, st);
-    if (group == 2) return launch_attn_group<2>(P, MODE, D, DT, grid, st);
-    // fp8 caches: groups above 4 take eight query heads per launch
-    const int piece = DT == kFP8 && group > 4 ? 8 : 4;
-    for (int h0 = 0; h0 < group; h0 += piece) {
-        P.h0 = h0;
-        P.gv = group - h0 < piece ? group - h0 : piece;
-        P.write_entry = h0 + piece >= group;
-        const int32_t r = piece == 8 ? launch_attn_group<8>(P, MODE, D, DT, grid, st)
-                                     : launch_attn_group<4>(P, MODE, D, DT, grid, st);
-        if (r != HSWD_OK) return r;
-    }
-    return HSWD_OK;
+    if (group == 1) return launch_attn_group<1, false>(P, MODE, D, DT, grid, st);
+    if (group == 2) return launch_attn_group<2, false>(P, MODE, D, DT, grid, st);
+    const bool g8 = group_piece(group, DT) == 8;
+    if (P.npiece == 1)
+        return g8 ? launch_attn_group<8, false>(P, MODE, D, DT, grid, st)
+                  : launch_attn_group<4, false>(P, MODE, D, DT, grid, st);
+    return g8 ? launch_attn_group<8, true>(P, MODE, D, DT, grid, st)
+              : launch_attn_group<4, true>(P, MODE, D, DT, grid, st);
 }
 
 // Shared argument checks and parameter set-up of the attention entries.
@@ -192,7 +201,9 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     P.max_pos = ring ? d->n_slots : max_pos;
     P.qscale = d->scale * 1.4426950408889634f;
     P.kv_scale = d->kv_scale;
-    grid = d->batch * d->n_kv_heads * P.wpp;
+    P.Gq = d->n_heads / d->n_kv_heads;
+    P.npiece = group_pieces(d);
+    grid = d->batch * d->n_kv_heads * P.wpp * P.npiece;
     return HSWD_OK;
 }
 

@@ -77,7 +77,7 @@ struct AttnParams {
     const int32_t* pos;      // [B]
     float* part_o;           // chunk partials [B*H][n_chunk][D]
     float* part_ml;          // [B*H][n_chunk][2]
-    int32_t* counters;       // [B*Hkv]
+    int32_t* counters;       // merge arrivals [B*Hkv][npiece], then entry arrivals [B*Hkv] (npiece > 1)
     int32_t* err;            // error word
     int B, H, Hkv, S;        // S: ring slots or append capacity
     int K;                   // keys per chunk
@@ -90,10 +90,10 @@ struct AttnParams {
     double log2_theta;
     float qscale;            // softmax scale * log2(e)
     // 4- and 8-head kernels only: query heads per kv head in memory (H /
-    // Hkv), the first head of the group this launch covers and how many (<=
-    // G), and whether it writes the new entry.  A larger group is covered by
-    // consecutive launches; the last one writes the entry.
-    int Gq, h0, gv, write_entry;
+    // Hkv), and the pieces of G heads the launch splits each group into (a
+    // group larger than G; 1 otherwise).  Every piece reads the cache; the
+    // last to finish writes the new entry.
+    int Gq, npiece;
 };
 
 // Scores on the matrix cores: 4 query heads per kv head over a 16-bit or
@@ -236,7 +236,9 @@ constexpr int flush_buffers() { return G == 8 ? 1 : 2; }
 // reshaping the query, the talker commit): one workgroup scores all G of
 // them against every K/V tile it loads, so the cache is read once per group.
 // Two workgroups of 4 waves per CU (2 waves per SIMD): at most 256 VGPRs.
-template <int D, int DT, bool RING, int MODE, int G>
+// SHARED: a group larger than G is split into pieces of G heads whose
+// workgroups read the same rows at about the same time (plain loads).
+template <int D, int DT, bool RING, int MODE, int G, bool SHARED>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_kernel(AttnParams P) {
     using Geo = AttnGeo<D, DT, G>;
@@ -288,30 +290,36 @@ void attn_kernel(AttnParams P) {
     const int wid = tid / kWave;
     const int t = tid;                                 // this thread's head dim (t < D)
 
-    // Workgroup -> (stream, kv head, chunk range).  When the pair count
-    // allows, the workgroups of one pair go to the same XCD (workgroups are
-    // dealt to the 8 XCDs round robin), so the merging one finds the partials
-    // in its L2.
+    // Workgroup -> (stream, kv head, head piece, chunk range).  When the
+    // pair count allows, the workgroups of one pair go to the same XCD
+    // (workgroups are dealt to the 8 XCDs round robin) and are dealt out
+    // together: the merging one finds the partials in its L2, and the pieces
+    // of a large group, which read the same K/V rows at about the same
+    // time, share them there.
     const int n_pairs = P.B * P.Hkv;
-    int pair, wg;
+    const int npiece = G >= 4 ? P.npiece : 1;
+    const int per_pair = npiece * P.wpp;
+    int pair, sub;
     {
         const int w = blockIdx.x;
-        if ((n_pairs & 7) == 0 && P.wpp > 1) {
+        if ((n_pairs & 7) == 0 && per_pair > 1) {
             const int k = w >> 3;
-            pair = (k / P.wpp) * 8 + (w & 7);
-            wg = k % P.wpp;
+            pair = (k / per_pair) * 8 + (w & 7);
+            sub = k % per_pair;
         } else {
-            pair = w / P.wpp;
-            wg = w % P.wpp;
+            pair = w / per_pair;
+            sub = w % per_pair;
         }
     }
+    const int piece = sub / P.wpp;
+    const int wg = sub % P.wpp;
     const int b = pair / P.Hkv;
     const int g = pair % P.Hkv;
-    // query heads of this launch: bh0 .. bh0 + gv - 1 (the 4- and 8-head
-    // kernels can cover part of a larger group, or a smaller group with
+    // query heads of this workgroup: bh0 .. bh0 + gv - 1 (the 4- and 8-head
+    // kernels can cover a piece of a larger group, or a smaller group with
     // heads idle)
-    const int gv = G >= 4 ? P.gv : G;
-    const int bh0 = b * P.H + (G >= 4 ? g * P.Gq + P.h0 : g * G);
+    const int gv = G >= 4 ? min(G, P.Gq - piece * G) : G;
+    const int bh0 = b * P.H + (G >= 4 ? g * P.Gq + piece * G : g * G);
     const float kscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[g] : 1.f;
     const float vscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[P.Hkv + g] : 1.f;
     const int c_begin = wg * P.cpw;
@@ -365,7 +373,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
         for (int i = 0; i < (MF ? NL : 1); ++i) {
             const int row = min(base + i * RPI, jlast);
-            kR[i] = load_kv<Geo::CB>(kbase + (size_t)row * D);
+            kR[i] = load_kv<Geo::CB, SHARED>(kbase + (size_t)row * D);
         }
     };
 
@@ -375,13 +383,13 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
                 const int row = min(base + i * RPI, jlast);
-                kt[i] = load_kv<Geo::CB>(kbase + (size_t)row * D);
+                kt[i] = load_kv<Geo::CB, SHARED>(kbase + (size_t)row * D);
             }
         }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int row = min(base + i * RPI, jlast);
-            vt[i] = load_kv<Geo::CB>(vbase + (size_t)row * D);
+            vt[i] = load_kv<Geo::CB, SHARED>(vbase + (size_t)row * D);
         }
     };
 
@@ -984,8 +992,8 @@ void attn_kernel(AttnParams P) {
         wait_stores_complete();
         __syncthreads();
         if (tid == 0) {
-            const int prev = __hip_atomic_fetch_add(&P.counters[pair], 1, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
+            const int prev = __hip_atomic_fetch_add(&P.counters[pair * npiece + piece], 1,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             sm_last = prev == P.wpp - 1;
         }
         __syncthreads();
@@ -1016,7 +1024,8 @@ void attn_kernel(AttnParams P) {
                             ld_agent(po + (size_t)i * D));
         }
         if (tid == 0)                            // ready for the next call
-            __hip_atomic_store(&P.counters[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&P.counters[pair * npiece + piece], 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // Join the new entry as a one-key partial (scores summed in the prologue).
@@ -1036,10 +1045,26 @@ void attn_kernel(AttnParams P) {
         }
     }
 
-    if (MODE == kModeStep && (G < 4 || P.write_entry)) {
+    if (MODE == kModeStep && npiece > 1) {
+        // Several head pieces read this pair's cache: the piece that finishes
+        // last writes the entry.  Each piece arrives once (its only or its
+        // merging workgroup) after every wave's loads have returned (their
+        // values are used before the barrier).
+        __syncthreads();
+        if (tid == 0) {
+            int32_t* ec = P.counters + (size_t)n_pairs * npiece + pair;
+            const int prev = __hip_atomic_fetch_add(ec, 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            sm_last = prev == npiece - 1;
+            if (sm_last) __hip_atomic_store(ec, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!sm_last) return;
+    }
+    if (MODE == kModeStep) {
         // Every workgroup of this pair has finished reading (one workgroup:
         // the barrier of the last stash flush, which every wave reaches after
-        // its last tile; several: the arrival count), so the ring slot that
+        // its last tile; several: the arrival counts), so the ring slot that
         // still held position p - S can be overwritten now.
         int row = -1;
         if (p >= 0) {

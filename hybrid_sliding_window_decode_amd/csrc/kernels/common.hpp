@@ -29,20 +29,15 @@ template <int CB> struct ChunkT;
 template <> struct ChunkT<16> { using type = u32x4; };
 template <> struct ChunkT<8> { using type = u32x2; };
 
-// K/V tile loads with the non-temporal hint: the cache is streamed once per
-// step and never re-read, and on MI355X the hinted loads stream from HBM
-// about 10% faster than plain ones.
-#ifndef HSWD_KV_NT
-#define HSWD_KV_NT 1
-#endif
-template <int CB, typename T>
+// K/V tile loads.  A row read by one workgroup only is streamed with the
+// non-temporal hint (on MI355X the hinted loads stream from HBM about 10%
+// faster than plain ones); rows that several workgroups read close together
+// (SHARED) use plain loads, which leave them in L2 for the others.
+template <int CB, bool SHARED = false, typename T>
 __device__ __forceinline__ typename ChunkT<CB>::type load_kv(const T* p) {
     using C = typename ChunkT<CB>::type;
-#if HSWD_KV_NT
-    return __builtin_nontemporal_load(reinterpret_cast<const C*>(p));
-#else
-    return *reinterpret_cast<const C*>(p);
-#endif
+    if constexpr (SHARED) return *reinterpret_cast<const C*>(p);
+    else return __builtin_nontemporal_load(reinterpret_cast<const C*>(p));
 }
 
 // ---------------------------------------------------------------------------

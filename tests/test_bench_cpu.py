@@ -46,11 +46,23 @@ def test_more_than_one_gpu_is_refused():
 def test_committed_traffic_is_close_to_the_algorithmic_bytes():
     """Where the committed counters match the kernel code, the measured HBM
     bytes of the full-layer launch are within a few percent of what the
-    method must move (more would mean re-reads; less, a miscount)."""
+    method must move (more would mean re-reads; less, a miscount).  A group
+    split into pieces reads the cache once per piece at most."""
     for kv, elt in (("bf16", 2), ("fp8", 1)):
         for heads in (8, 16, 24, 32, 64):
             t = bench.measured_traffic(kv, heads)
             if t is None:
                 continue
             alg = bench.layer_bytes("full", elt=elt, heads=heads)
-            assert 0.999 * alg <= t <= 1.03 * alg, (kv, heads, t, alg)
+            pieces = bench.kernel_group(kv, heads)[1]
+            assert 0.999 * alg <= t <= 1.03 * pieces * alg, (kv, heads, t, alg)
+
+
+def test_kernel_group():
+    assert bench.kernel_group("bf16", 8) == (1, 1)
+    assert bench.kernel_group("bf16", 16) == (2, 1)
+    assert bench.kernel_group("bf16", 24) == (4, 1)
+    assert bench.kernel_group("bf16", 64) == (4, 2)
+    assert bench.kernel_group("fp8", 64) == (8, 1)
+    assert bench.full_kernel("bf16", 64) == "hswd::attn_kernel<256, 2, false, 1, 4, true>(...)"
+    assert bench.full_kernel("fp8", 8) == "hswd::attn_kernel<256, 3, false, 1, 1, false>(...)"
