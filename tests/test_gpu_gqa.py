@@ -9,7 +9,8 @@ import pytest
 import hybrid_sliding_window_decode_amd as hswd
 import oracle
 from hybrid_sliding_window_decode_amd import inputs
-from gpu_util import CODE, assert_parity, cache_to_host, entry_codes, say, to_dev
+from gpu_util import (CODE, assert_parity, cache_to_host, entry_codes, f32_dev, i32_dev,
+                      say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +135,51 @@ def check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=8, q_mult=1.0):
         p = int(x.pos[b])
         row = p % spec.n_slots if ring else p
         assert np.array_equal(kc[b, :, row], entry_codes(k_rot[b], dtype, ksc))
+
+
+# A group split into pieces (one workgroup per piece in one launch; the
+# last piece to finish writes the entry): consecutive steps on one
+# workspace, each against the oracle stepping the same history, so the
+# arrival counters must be back at zero after every call and each entry
+# must land before the next step reads it.  Sliding rings are full (the
+# overwritten slot is still in the window when it is read).
+@pytest.mark.parametrize("kind,dtype,G,D,B,pos,S,kps,H", [
+    ("sliding", "bf16", 8, 256, 8, "ragged", None, 0, 64),
+    ("sliding", "fp8", 16, 256, 3, [600, 511, 4000], None, 0, 32),
+    ("full", "f16", 8, 128, 3, [2500, 3, 1200], 3000, 256, 16),
+    ("full", "fp8", 16, 256, 2, [2996, 40], 3000, 512, 32),
+])
+def test_gqa_pieces_consecutive_steps(kind, dtype, G, D, B, pos, S, kps, H):
+    spec = gqa_spec(kind, B, dtype, G, D=D, S=S, H=H)
+    x = inputs.make_step(spec, positions(kind, B, S, pos, 51), seed=52)
+    if kind == "sliding":
+        x.pos = np.maximum(x.pos, spec.n_slots).astype(np.int32)
+    ring = kind == "sliding"
+    kc, vc = x.k_cache.copy(), x.v_cache.copy()
+    d = to_dev(x)
+    mp = int(x.pos.max()) + 3
+    desc = hswd.make_desc(d["k_cache"], n_heads=spec.H, keys_per_split=kps,
+                          kv_scale=d["kv_scale"])
+    ws = hswd.workspace(desc, ring, mp)
+    rng = np.random.default_rng(53)
+    for step in range(4):
+        if step > 0:
+            x.pos = (x.pos + 1).astype(np.int32)
+            for f in ("q", "k", "v", "gate"):
+                setattr(x, f, rng.standard_normal(getattr(x, f).shape).astype(np.float32))
+            # the history this step reads (the parity bar normalises by its V)
+            x.k_cache, x.v_cache = kc.copy(), vc.copy()
+        ref = oracle.layer_step(x.q, x.k, x.v, x.gate, kc, vc, x.pos, CODE[dtype], ring,
+                                spec.rot, spec.theta, write=True, kv_scale=spec.kv_scale)
+        say("gqa pieces %s %s G=%d step %d pos=%s" % (kind, dtype, G, step, list(x.pos[:4])))
+        out = hswd.layer_step(f32_dev(x.q), f32_dev(x.k), f32_dev(x.v),
+                              f32_dev(x.gate), d["k_cache"], d["v_cache"],
+                              i32_dev(x.pos), ring, spec.rot, spec.theta, ws, max_pos=mp,
+                              desc=desc)
+        assert hswd.check_errors(ws) == 0
+        assert_parity(out.cpu().numpy(), ref["out"], x, "gqa pieces step %d" % step)
+        assert np.array_equal(cache_to_host(d["k_cache"]), kc), "stored keys differ"
+        assert np.array_equal(cache_to_host(d["v_cache"]), vc), "stored values differ"
 
 
 @pytest.mark.parametrize("dtype,G", [("bf16", 4), ("fp8", 8)])
