@@ -107,10 +107,11 @@ typedef struct {
                                (else UNSUPPORTED).  Groups of 2 and 4 (and 5
                                to 8 over an fp8 cache) read the cache once per
                                layer, a group below a kernel's size leaving
-                               heads idle; a larger group is taken four query
-                               heads (fp8: eight) per launch, each launch
-                               reading the cache once (the last one writes the
-                               new entry). */
+                               heads idle; a larger group is split into pieces
+                               of four query heads (fp8: eight), one workgroup
+                               per piece in the same launch, each reading the
+                               cache (the last piece to finish writes the new
+                               entry). */
     int32_t head_dim;       /* D: 64, 128 or 256 (fp8 caches: 128 or 256) */
     int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows */
     int32_t kv_dtype;       /* hswd_dtype of the cache */
@@ -144,8 +145,9 @@ const char* hswd_status_string(int32_t status);
 
 /* Workspace bytes needed by the attention entries for this layer and the
  * largest position `max_pos` any stream will have (append caches; rings
- * ignore it).  The workspace holds the error word, per-(stream, kv head)
- * arrival counters and the chunk partials.  It must be zeroed once before
+ * ignore it).  The workspace holds the error word, the arrival counters (per
+ * (stream, kv head) and head piece, and per (stream, kv head) for the entry
+ * write of a group split into pieces) and the chunk partials.  It must be zeroed once before
  * first use (hswd_workspace_init); the library leaves the counters at zero
  * after every call, so it can be reused without clearing. */
 size_t hswd_workspace_bytes(const hswd_attn_desc* d, int32_t ring, int32_t max_pos);
