@@ -171,6 +171,9 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     // grouped kernels: 16-bit and fp8 caches, head dim 128 or 256 (G query
     // vectors and accumulators per lane must fit beside the tiles in 256 VGPRs)
     if (group > 1 && (d->kv_dtype == HSWD_F32 || d->head_dim < 128)) return HSWD_ERR_UNSUPPORTED;
+    // the kernels address a (stream, kv head) block with 32-bit offsets
+    const size_t elt = d->kv_dtype == HSWD_F32 ? 4 : (d->kv_dtype == HSWD_FP8_E4M3 ? 1 : 2);
+    if ((size_t)d->n_slots * d->head_dim * elt > 0xFFFFFFFFull) return HSWD_ERR_UNSUPPORTED;
     if (!ring) {
         if (max_pos < 0) return HSWD_ERR_INVALID;
         if ((long)max_pos + 1 > d->n_slots) return HSWD_ERR_CAPACITY;

@@ -266,11 +266,13 @@ void attn_kernel(AttnParams P) {
     __shared__ u32x2 sm_k8[K8 ? kAttnWaves : 1][K8 ? KT : 1][K8 ? D / 8 + 1 : 1];
     // query rows padded by 16 bytes too: unpadded, the G heads' rows (512
     // bytes apart) would share banks and the operand reads conflict 4 ways
-    __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G : 1][MF ? D + 8 : 1];
-    __shared__ __attribute__((aligned(16))) uint16_t sm_ql[MF ? G : 1][MF ? D + 8 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G + 1 : 1][MF ? D + 8 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_ql[MF ? G + 1 : 1][MF ? D + 8 : 1];
     // (both read 16 bytes at a time: aligned to 16)
-    __shared__ __attribute__((aligned(16))) float sm_p[MF && DT == kBF16 ? kAttnWaves : 1][MF ? KT : 1][4];
-    __shared__ __attribute__((aligned(16))) uint16_t sm_ph[MF && DT != kBF16 ? kAttnWaves : 1][MF ? NL / 2 : 1][RPI][G][2];
+    // (a column per score-product column: lanes of idle heads write unused
+    // columns rather than branch around the store)
+    __shared__ __attribute__((aligned(16))) float sm_p[MF && DT == kBF16 ? kAttnWaves : 1][MF ? KT : 1][16];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_ph[MF && DT != kBF16 ? kAttnWaves : 1][MF ? NL / 2 : 1][RPI][MF ? 16 : 1][2];
     __shared__ __attribute__((aligned(16))) float sm_al[MF ? kAttnWaves : 1][G];
     __shared__ float sm_o[NB][kStash][G][kAttnWaves][D];   // wave chunk partials, by flush parity
     __shared__ float sm_m[NB][kStash][G][kAttnWaves], sm_l[NB][kStash][G][kAttnWaves];
@@ -287,7 +289,7 @@ void attn_kernel(AttnParams P) {
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wid = tid / kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int t = tid;                                 // this thread's head dim (t < D)
 
     // Workgroup -> (stream, kv head, head piece, chunk range).  When the
@@ -330,8 +332,14 @@ void attn_kernel(AttnParams P) {
     const int r = lane / LPR;       // row within a wave-wide load
     float qs[G][EPC];               // this lane's query dims, set after the prologue
 
-    const S* kbase = reinterpret_cast<const S*>(P.kc) + (size_t)pair * P.S * D + c * EPC;
-    const S* vbase = reinterpret_cast<const S*>(P.vc) + (size_t)pair * P.S * D + c * EPC;
+    // This pair's K and V blocks (uniform), and this lane's byte offset in a
+    // row.  Offsets within a block are 32-bit (the host caps a block at
+    // 4 GiB), so a load is a scalar base plus one per-lane register.
+    constexpr int ROWB = D * Geo::EB;
+    const char* kblk = reinterpret_cast<const char*>(P.kc) + (size_t)pair * P.S * ROWB;
+    const char* vblk = reinterpret_cast<const char*>(P.vc) + (size_t)pair * P.S * ROWB;
+    const uint32_t lane_col = (uint32_t)(c * Geo::CB);
+    const uint32_t lane_row = (uint32_t)(r * ROWB) + lane_col;
 
     float m_run[G], l_lane[G], o_acc[G][EPC];
 #pragma unroll
@@ -368,29 +376,32 @@ void attn_kernel(AttnParams P) {
     int jlast = P.S - 1;
     auto item_key = [&](int j) __attribute__((always_inline)) { return key0 + j * (kAttnWaves * KT); };
 
+    // Row i * RPI + r of item j, clamped onto jlast.  When the item's last
+    // row is at or below jlast (every item but the last one or two) the
+    // clamp changes nothing and is skipped: the address is then the item's
+    // uniform base plus the lane's fixed offset.
+    auto row_load = [&](const char* blk, int j, int i) __attribute__((always_inline)) {
+        const int k0 = item_key(j);
+        if (k0 + KT - 1 <= jlast)
+            return load_kv<Geo::CB, SHARED>(
+                reinterpret_cast<const S*>(blk + (size_t)(k0 + i * RPI) * ROWB + lane_row));
+        const int row = min(k0 + r + i * RPI, jlast);
+        return load_kv<Geo::CB, SHARED>(
+            reinterpret_cast<const S*>(blk + ((uint32_t)row * ROWB + lane_col)));
+    };
+
     auto load_k = [&](int j) __attribute__((always_inline)) {     // MFMA kernel only
-        const int base = item_key(j) + r;
 #pragma unroll
-        for (int i = 0; i < (MF ? NL : 1); ++i) {
-            const int row = min(base + i * RPI, jlast);
-            kR[i] = load_kv<Geo::CB, SHARED>(kbase + (size_t)row * D);
-        }
+        for (int i = 0; i < (MF ? NL : 1); ++i) kR[i] = row_load(kblk, j, i);
     };
 
     auto load_tile = [&](Chunk (&kt)[NL], Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
-        const int base = item_key(j) + r;
         if constexpr (!MF) {
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const int row = min(base + i * RPI, jlast);
-                kt[i] = load_kv<Geo::CB, SHARED>(kbase + (size_t)row * D);
-            }
+            for (int i = 0; i < NL; ++i) kt[i] = row_load(kblk, j, i);
         }
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int row = min(base + i * RPI, jlast);
-            vt[i] = load_kv<Geo::CB, SHARED>(vbase + (size_t)row * D);
-        }
+        for (int i = 0; i < NL; ++i) vt[i] = row_load(vblk, j, i);
     };
 
     // Per-stream inputs first: this thread's query dim and its RoPE partner
@@ -484,6 +495,9 @@ void attn_kernel(AttnParams P) {
             typedef float f32x4 __attribute__((ext_vector_type(4)));
             constexpr int NG = KT / 16, NS = D / 32;
             const int hq = lane & 15, kq = lane >> 4;
+            // lanes of heads >= G read the zero row G (one address: a broadcast)
+            const uint16_t* qh_row = &sm_qh[hq < G ? hq : G][8 * kq];
+            const uint16_t* ql_row = &sm_ql[hq < G ? hq : G][8 * kq];
             asm volatile("" ::: "memory");     // the query reads below stay in the loop
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
@@ -507,9 +521,8 @@ void attn_kernel(AttnParams P) {
             // hold ~100 registers
 #pragma unroll 2
             for (int sl = 0; sl < NS; ++sl) {
-                const u32x4 zero = {0u, 0u, 0u, 0u};
-                const u32x4 qh = hq < G ? *reinterpret_cast<const u32x4*>(&sm_qh[hq < G ? hq : 0][32 * sl + 8 * kq]) : zero;
-                const u32x4 ql = hq < G ? *reinterpret_cast<const u32x4*>(&sm_ql[hq < G ? hq : 0][32 * sl + 8 * kq]) : zero;
+                const u32x4 qh = *reinterpret_cast<const u32x4*>(qh_row + 32 * sl);
+                const u32x4 ql = *reinterpret_cast<const u32x4*>(ql_row + 32 * sl);
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
                     u32x4 a;
@@ -563,7 +576,9 @@ void attn_kernel(AttnParams P) {
                     const float pr = fast_exp2(sv[kg][i] - m_new);
                     psum += pr;
                     const int key = kg * 16 + 4 * kq + i;          // within the tile
-                    if (hq < G) {
+                    // (the 8-head kernel keeps the branch: without it the
+                    // 128-dim instance needs one register more than it has)
+                    if (G < 8 || hq < G) {
                         if constexpr (PV16) {
                             const int li = key / RPI;               // load index of the key
                             sm_ph[wid][li / 2][key % RPI][hq][li % 2] =
@@ -864,6 +879,12 @@ void attn_kernel(AttnParams P) {
                 } else {
                     sm_q[hh][t] = qsc[hh];
                 }
+            }
+        }
+        if constexpr (MF) {
+            if (t < D) {                     // the zero query of idle columns
+                sm_qh[G][t] = 0;
+                sm_ql[G][t] = 0;
             }
         }
     }

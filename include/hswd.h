@@ -113,7 +113,10 @@ typedef struct {
                                cache (the last piece to finish writes the new
                                entry). */
     int32_t head_dim;       /* D: 64, 128 or 256 (fp8 caches: 128 or 256) */
-    int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows */
+    int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows.
+                               The attention entries take n_slots * head_dim *
+                               element bytes < 4 GiB (one (stream, kv head)
+                               block; else UNSUPPORTED). */
     int32_t kv_dtype;       /* hswd_dtype of the cache */
     float scale;            /* softmax scale, > 0; 1/sqrt(D) by convention */
     int32_t keys_per_split; /* keys per chunk, the unit of summation order [split]:
