@@ -96,6 +96,10 @@ def test_workspace_and_splits():
     ("GQA f32", dict(n_heads=16, n_kv_heads=8, kv_dtype=0), -6),
     ("GQA f32 group 8", dict(n_heads=16, n_kv_heads=2, kv_dtype=0), -6),
     ("GQA head_dim 64", dict(n_heads=16, n_kv_heads=8, head_dim=64), -6),
+    # a (stream, kv head) block of 4 GiB or more (32-bit offsets in the kernel)
+    ("block 4 GiB bf16", dict(n_slots=1 << 23), -6),
+    ("block 4 GiB f32", dict(n_slots=1 << 22, kv_dtype=0), -6),
+    ("block 4 GiB fp8", dict(n_slots=1 << 24, kv_dtype=3), -6),
 ])
 def test_sliding_rejects_bad_descriptor(case, kw, want):
     L = binding.lib()
