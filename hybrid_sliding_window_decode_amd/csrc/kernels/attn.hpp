@@ -289,7 +289,9 @@ void attn_kernel(AttnParams P) {
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
+    // (the matrix-core kernels take the wave index as a scalar; the VALU
+    // kernels measure 1-2% faster with it in a vector register)
+    const int wid = use_mfma<DT, G>() ? __builtin_amdgcn_readfirstlane(tid / kWave) : tid / kWave;
     const int t = tid;                                 // this thread's head dim (t < D)
 
     // Workgroup -> (stream, kv head, head piece, chunk range).  When the
@@ -332,14 +334,16 @@ void attn_kernel(AttnParams P) {
     const int r = lane / LPR;       // row within a wave-wide load
     float qs[G][EPC];               // this lane's query dims, set after the prologue
 
-    // This pair's K and V blocks (uniform), and this lane's byte offset in a
-    // row.  Offsets within a block are 32-bit (the host caps a block at
-    // 4 GiB), so a load is a scalar base plus one per-lane register.
+    // This pair's K and V blocks: as lane pointers (VALU kernels), and as
+    // the uniform block base plus a 32-bit lane offset (matrix-core kernels,
+    // 2-8% faster there; the host caps a block at 4 GiB).  Each form is the
+    // faster one for its kernels.
     constexpr int ROWB = D * Geo::EB;
+    const S* kbase = reinterpret_cast<const S*>(P.kc) + (size_t)pair * P.S * D + c * EPC;
+    const S* vbase = reinterpret_cast<const S*>(P.vc) + (size_t)pair * P.S * D + c * EPC;
     const char* kblk = reinterpret_cast<const char*>(P.kc) + (size_t)pair * P.S * ROWB;
     const char* vblk = reinterpret_cast<const char*>(P.vc) + (size_t)pair * P.S * ROWB;
     const uint32_t lane_col = (uint32_t)(c * Geo::CB);
-    const uint32_t lane_row = (uint32_t)(r * ROWB) + lane_col;
 
     float m_run[G], l_lane[G], o_acc[G][EPC];
 #pragma unroll
@@ -376,32 +380,35 @@ void attn_kernel(AttnParams P) {
     int jlast = P.S - 1;
     auto item_key = [&](int j) __attribute__((always_inline)) { return key0 + j * (kAttnWaves * KT); };
 
-    // Row i * RPI + r of item j, clamped onto jlast.  When the item's last
-    // row is at or below jlast (every item but the last one or two) the
-    // clamp changes nothing and is skipped: the address is then the item's
-    // uniform base plus the lane's fixed offset.
-    auto row_load = [&](const char* blk, int j, int i) __attribute__((always_inline)) {
-        const int k0 = item_key(j);
-        if (k0 + KT - 1 <= jlast)
-            return load_kv<Geo::CB, SHARED>(
-                reinterpret_cast<const S*>(blk + (size_t)(k0 + i * RPI) * ROWB + lane_row));
-        const int row = min(k0 + r + i * RPI, jlast);
+    // Row `row` (already clamped onto jlast) of a block, matrix-core form.
+    // (A uniform branch skipping the clamp where it changes nothing cost the
+    // VALU kernels 1-4%.)
+    auto blk_load = [&](const char* blk, int row) __attribute__((always_inline)) {
         return load_kv<Geo::CB, SHARED>(
             reinterpret_cast<const S*>(blk + ((uint32_t)row * ROWB + lane_col)));
     };
 
     auto load_k = [&](int j) __attribute__((always_inline)) {     // MFMA kernel only
+        const int base = item_key(j) + r;
 #pragma unroll
-        for (int i = 0; i < (MF ? NL : 1); ++i) kR[i] = row_load(kblk, j, i);
+        for (int i = 0; i < (MF ? NL : 1); ++i) kR[i] = blk_load(kblk, min(base + i * RPI, jlast));
     };
 
     auto load_tile = [&](Chunk (&kt)[NL], Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
+        const int base = item_key(j) + r;
         if constexpr (!MF) {
 #pragma unroll
-            for (int i = 0; i < NL; ++i) kt[i] = row_load(kblk, j, i);
+            for (int i = 0; i < NL; ++i) {
+                const int row = min(base + i * RPI, jlast);
+                kt[i] = load_kv<Geo::CB, SHARED>(kbase + (size_t)row * D);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < NL; ++i) vt[i] = row_load(vblk, j, i);
+        for (int i = 0; i < NL; ++i) {
+            const int row = min(base + i * RPI, jlast);
+            if constexpr (MF) vt[i] = blk_load(vblk, row);
+            else vt[i] = load_kv<Geo::CB, SHARED>(vbase + (size_t)row * D);
+        }
     };
 
     // Per-stream inputs first: this thread's query dim and its RoPE partner
