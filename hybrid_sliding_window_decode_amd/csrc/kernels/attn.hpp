@@ -583,9 +583,9 @@ void attn_kernel(AttnParams P) {
                     const float pr = fast_exp2(sv[kg][i] - m_new);
                     psum += pr;
                     const int key = kg * 16 + 4 * kq + i;          // within the tile
-                    // (the 8-head kernel keeps the branch: without it the
-                    // 128-dim instance needs one register more than it has)
-                    if (G < 8 || hq < G) {
+                    // (the 8-head 128-dim kernel keeps the branch: without
+                    // it that instance needs more registers than it has)
+                    if (G < 8 || D > 128 || hq < G) {
                         if constexpr (PV16) {
                             const int li = key / RPI;               // load index of the key
                             sm_ph[wid][li / 2][key % RPI][hq][li % 2] =
