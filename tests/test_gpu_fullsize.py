@@ -90,7 +90,7 @@ def test_step_layers_64x4096():
 
 
 def test_long_context_8x131072():
-    """8 streams at context 131072: full layer (256 chunks, several
+    """8 streams at context 131072: full layer (32 chunks of 4096 keys, several
     workgroups per (stream, head), last-arrival merge) and a sliding layer
     at the same positions."""
     check_layer(inputs.full_spec(8, 131073, "bf16"), 131072, 5000, samples(8, 8, 8, 3))

@@ -70,6 +70,9 @@ def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
     ("full", "fp8", 8, 128, 4, "ragged", 3000, 0, 64),
     ("sliding", "fp8", 16, 256, 4, "ragged", None, 0, 32),
     ("full", "fp8", 5, 256, 3, [2999, 1, 1500], 3000, 0, 10),
+    # long chunks, ragged last chunk: 4-head matrix-core and 8-head fp8 kernels
+    ("full", "bf16", 4, 256, 2, [9000, 4097], 9001, 4096, 32),
+    ("full", "fp8", 8, 256, 2, [9000, 2049], 9001, 4096, 64),
 ])
 def test_gqa_large_groups(kind, dtype, G, D, B, pos, S, kps, H):
     check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=H)
