@@ -97,6 +97,13 @@ def test_long_context_8x131072():
     check_layer(inputs.sliding_spec(8, "bf16"), 131072, 5001, samples(8, 8, 16, 4))
 
 
+def test_long_context_grouped_fp8_8x131072():
+    """8 streams at context 131072, 32 query heads over 8 kv heads, fp8
+    cache: the 4-head matrix-core kernel over 32 chunks of 4096 keys, merged
+    across workgroups."""
+    check_layer(inputs.full_spec(8, 131073, "fp8", H=32), 131072, 5200, samples(8, 32, 12, 12))
+
+
 def test_ragged_full_layer_64_streams():
     """64 streams with ragged positions in [1, 4096] on a full layer: most
     chunks of the short streams are empty."""
@@ -119,8 +126,7 @@ def test_grouped_step_layers_64x4096(dtype):
 
 
 def test_max_context_1x1048576():
-    """One stream at context 2^20 on a full layer (8.6 GB of cache, 2048
-    chunks of 512 keys, hundreds of workgroups per kv head merged by the
-    last to arrive): the largest context the tests exercise; the library
-    takes up to 4096 chunks."""
+    """One stream at context 2^20 on a full layer (8.6 GB of cache, 128
+    chunks of 8192 keys, 64 workgroups per kv head merged by the last to
+    arrive): the largest context the tests exercise."""
     check_layer(inputs.full_spec(1, (1 << 20) + 1, "bf16"), 1 << 20, 5100, samples(1, 8, 8, 11))
