@@ -21,7 +21,13 @@ using namespace hswd;
 constexpr int kVersion = (0 << 16) | 7;
 constexpr size_t kAlign = 256;
 constexpr int kMaxChunkKeys = 8192;  // cap of the default keys per chunk
-constexpr int kWgsPerCu = 2;          // resident attention workgroups per CU (VGPR bound)
+// Attention workgroups per CU the default split aims for: the residency of
+// the largest kernels (up to 256 VGPRs per lane).  The smaller ones could
+// hold more (the one-head bf16 kernel: 100 VGPRs, 34 KB of LDS), but more
+// workgroups per (stream, kv head) measured slower (64 x 4096 bf16 full
+// layer: 309 us at 512 workgroups, 334 us at 1024): each adds a partial to
+// merge and splits a contiguous read.
+constexpr int kWgsPerCu = 2;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
