@@ -20,7 +20,7 @@ using namespace hswd;
 
 constexpr int kVersion = (0 << 16) | 7;
 constexpr size_t kAlign = 256;
-constexpr int kMaxChunkKeys = 8192;  // cap of the default keys per chunk
+constexpr int kMaxChunkKeys = 2048;  // cap of the default keys per chunk
 // Attention workgroups per CU the default split aims for: the residency of
 // the largest kernels (up to 256 VGPRs per lane).  The smaller ones could
 // hold more (the one-head bf16 kernel: 100 VGPRs, 34 KB of LDS), but more
@@ -68,20 +68,25 @@ bool empty_batch(const hswd_attn_desc* d) {
 
 // Default keys per chunk, from the cache geometry, element type and head
 // grouping only (never the batch): 2^floor(log2(n_slots / 32)) clamped to
-// [128, kMaxChunkKeys], and at least four quanta (a quantum, one tile per
-// wave, is the keys of 32 KiB of K rows), so each wave scores four tiles
-// per chunk end; grouped layers (H > Hkv) at least eight, since their stash
-// holds a single chunk and every chunk end is a barrier.  A full cache thus
-// holds about 32 chunks at any length: short caches get small chunks, so a
-// small batch still spreads over many workgroups; long caches get long
-// chunks, so the last workgroup of a (stream, kv head) folds few partials
-// (8 x 131072 bf16 full layer: 1280 us at 512-key chunks, 1220 us at 4096);
-// the floor keeps the per-chunk reduction off the streaming rate (fp8 rows
-// are half the bytes, so its chunks hold twice the keys).
+// [128, 512]; from 131072 rows on 2^floor(log2(n_slots / 128)), at most
+// kMaxChunkKeys; and at least four quanta (a quantum, one tile per wave, is
+// the keys of 32 KiB of K rows), so each wave scores four tiles per chunk
+// end; grouped layers (H > Hkv) at least eight, since their stash holds a
+// single chunk and every chunk end is a barrier.  Short caches get small
+// chunks, so a small batch still spreads over many workgroups.  Long caches
+// get longer chunks, so the last workgroup of a (stream, kv head) folds
+// fewer partials, but not so long that a stream whose position is far below
+// the capacity (the chunk follows the capacity, not the position) is left
+// to a few workgroups: 8 x 131072 bf16 full layer 1280 us at 512-key chunks,
+// 1249 at 1024, 1220 at 4096; one stream at position 5000 of that cache
+// 19.0, 25.8 and 73.9 us.  The floor keeps the per-chunk reduction off the
+// streaming rate (fp8 rows are half the bytes, so its chunks hold twice the
+// keys).
 int chunk_keys(const hswd_attn_desc* d) {
     if (d->keys_per_split > 0) return d->keys_per_split;
     int k = 128;
-    while (k < kMaxChunkKeys && (long)k * 2 * 32 <= d->n_slots) k *= 2;
+    while (k < 512 && (long)k * 2 * 32 <= d->n_slots) k *= 2;
+    while (k < kMaxChunkKeys && (long)k * 2 * 128 <= d->n_slots) k *= 2;
     const int quanta = d->n_heads > d->n_kv_heads ? 8 : 4;
     const int floor_keys = quanta * chunk_quantum(d->head_dim, d->kv_dtype);
     return k < floor_keys ? floor_keys : k;

@@ -125,8 +125,10 @@ typedef struct {
                                the partials are folded in chunk order.  0 =
                                library default from the cache length, element
                                type and head grouping only: 2^floor(log2(
-                               n_slots/32)) clamped to [128, 8192], and at least
-                               4 quanta (8 when n_heads > n_kv_heads).
+                               n_slots/32)) clamped to [128, 512], from 131072
+                               rows on 2^floor(log2(n_slots/128)) up to 2048,
+                               and at least 4 quanta (8 when n_heads >
+                               n_kv_heads).
                                Else a multiple of the quantum Q = 32768 /
                                (head_dim * element bytes) keys (4 waves, one
                                8-load tile each): 64 for D = 256 and a 16-bit

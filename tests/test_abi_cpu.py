@@ -49,17 +49,20 @@ def test_version_and_status_strings():
 def test_workspace_and_splits():
     L = binding.lib()
     d = desc()
-    # default chunk: 2^floor(log2(n_slots/32)) in [128, 8192], at least four
-    # quanta (quantum = 32768 / (D * element bytes) keys): 256 keys for a
-    # bf16 ring or 4097-row cache, 512 from 16384 rows, 4096 at 131072
+    # default chunk: 2^floor(log2(n_slots/32)) in [128, 512], from 131072
+    # rows 2^floor(log2(n_slots/128)) up to 2048, at least four quanta
+    # (quantum = 32768 / (D * element bytes) keys): 256 keys for a bf16 ring
+    # or 4097-row cache, 512 from 16384 rows, 1024 at 131072, 2048 from 262144
     assert hswd.num_splits(d, 1) == 2
     assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 16
     assert hswd.num_splits(desc(n_slots=8192), 0, 8191) == 32
     assert hswd.num_splits(desc(n_slots=16385), 0, 16384) == 32
-    assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 32           # 4096 keys
-    assert hswd.num_splits(desc(n_slots=131073), 0, 5000) == 2
-    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1), 0, 1 << 20) == 128   # capped: 8192
-    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, kv_dtype=3), 0, 1 << 20) == 128
+    assert hswd.num_splits(desc(n_slots=65537), 0, 65536) == 128           # 512 keys
+    assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 128          # 1024 keys
+    assert hswd.num_splits(desc(n_slots=131073), 0, 5000) == 5
+    assert hswd.num_splits(desc(n_slots=262145), 0, 262144) == 128          # 2048 keys
+    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1), 0, 1 << 20) == 512   # capped: 2048
+    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, kv_dtype=3), 0, 1 << 20) == 512
     assert hswd.num_splits(desc(n_slots=4097, head_dim=64), 0, 4096) == 4       # Q = 256
     assert hswd.num_splits(desc(n_slots=4097, kv_dtype=0), 0, 4096) == 32       # f32: Q = 32
     assert hswd.num_splits(desc(n_slots=4097, kv_dtype=3), 0, 4096) == 8        # fp8: Q = 128

@@ -68,7 +68,7 @@ CASES = [
     ("sliding_64xragged_fp8", "sliding", 64, "fp8", "ragged", None, 0),
     ("full_16xragged_fp8_kps128", "full", 16, "fp8", "ragged", 2049, 128),
     ("full_4x_fp8_d128", "full", 4, "fp8", [5, 300, 1000, 77], 1001, 0),
-    # long chunks (the default from 65536 rows on), ragged last chunk
+    # long chunks, ragged last chunk
     ("full_3x_bf16_kps4096", "full", 3, "bf16", [9000, 4097, 1], 9001, 4096),
     ("full_3x_fp8_kps8192", "full", 3, "fp8", [9000, 8192, 0], 9001, 8192),
 ]

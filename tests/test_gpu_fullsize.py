@@ -90,7 +90,7 @@ def test_step_layers_64x4096():
 
 
 def test_long_context_8x131072():
-    """8 streams at context 131072: full layer (32 chunks of 4096 keys, several
+    """8 streams at context 131072: full layer (128 chunks of 1024 keys, several
     workgroups per (stream, head), last-arrival merge) and a sliding layer
     at the same positions."""
     check_layer(inputs.full_spec(8, 131073, "bf16"), 131072, 5000, samples(8, 8, 8, 3))
@@ -99,8 +99,8 @@ def test_long_context_8x131072():
 
 def test_long_context_grouped_fp8_8x131072():
     """8 streams at context 131072, 32 query heads over 8 kv heads, fp8
-    cache: the 4-head matrix-core kernel over 32 chunks of 4096 keys, merged
-    across workgroups."""
+    cache: the 4-head matrix-core kernel over 128 chunks of 1024 keys,
+    merged across workgroups."""
     check_layer(inputs.full_spec(8, 131073, "fp8", H=32), 131072, 5200, samples(8, 32, 12, 12))
 
 
@@ -126,7 +126,7 @@ def test_grouped_step_layers_64x4096(dtype):
 
 
 def test_max_context_1x1048576():
-    """One stream at context 2^20 on a full layer (8.6 GB of cache, 128
-    chunks of 8192 keys, 64 workgroups per kv head merged by the last to
+    """One stream at context 2^20 on a full layer (8.6 GB of cache, 512
+    chunks of 2048 keys, 64 workgroups per kv head merged by the last to
     arrive): the largest context the tests exercise."""
     check_layer(inputs.full_spec(1, (1 << 20) + 1, "bf16"), 1 << 20, 5100, samples(1, 8, 8, 11))
