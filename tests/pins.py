@@ -412,6 +412,40 @@ def pin_gate_proj(L):
     assert np.max(np.abs(oracle.gate_proj(x2, w2, L=L) - x2.astype(np.float64) @ w2.T)) < 1e-12
 
 
+def pin_attend_block(L):
+    """The per-(stream, head) entry the full-size checks use equals the
+    layer step's pre-gate output for the same head: it takes the rotated
+    query, the head's cache block and the stored entry's codes, and must
+    decode and scale the entry exactly as the step does (score-space join
+    commit: the new token is scored as the entry that is stored).  Every
+    cache type, per-head fp8 scales that are not powers of two, a grouped
+    head mapping, rings below and past capacity and an append cache."""
+    cases = [("sliding", F32, 8, 8, [600, 5]), ("full", F16, 8, 8, [40, 0]),
+             ("sliding", BF16, 8, 8, [511, 100]), ("sliding", FP8, 8, 8, [700, 3]),
+             ("full", FP8, 8, 4, [30, 1]), ("full", BF16, 8, 2, [17, 64])]
+    for kind, dt, H, Hkv, pos in cases:
+        ring = kind == "sliding"
+        spec = (inputs.sliding_spec(2, NAMES[dt], H=H, Hkv=Hkv, D=128) if ring
+                else inputs.full_spec(2, max(pos) + 1, NAMES[dt], H=H, Hkv=Hkv, D=128))
+        x = inputs.make_step(spec, pos, 41 + dt)
+        ksc = spec.kv_scale
+        r = oracle.layer_step(x.q, x.k, x.v, None, x.k_cache, x.v_cache, x.pos, dt, ring,
+                              spec.rot, spec.theta, write=False, kv_scale=ksc, L=L)
+        G = H // Hkv
+        for b, p in enumerate(pos):
+            n = min(p, spec.n_slots)
+            for h in range(H):
+                g = h // G
+                ks = 1.0 if ksc is None else float(ksc[0, g])
+                vs = 1.0 if ksc is None else float(ksc[1, g])
+                o = oracle.attend_block(r["q_rot"][b, h], x.k_cache[b, g], x.v_cache[b, g], dt,
+                                        n, r["k_hat"][b, g], r["v_hat"][b, g],
+                                        1.0 / math.sqrt(spec.D), ks, vs, L=L)
+                ref = r["o_pre"][b, h]
+                assert np.max(np.abs(o - ref)) <= 1e-14 * np.max(np.abs(ref)), (
+                    kind, NAMES[dt], b, h)
+
+
 def pin_capacity_and_poison(L):
     """An append position at the capacity is reported (-4) and its write is
     skipped; NaN in unwritten slots never reaches the output."""
@@ -432,4 +466,4 @@ def pin_capacity_and_poison(L):
 QUICK_PINS = [pin_rne_quick, pin_fp8_codec, pin_decode, pin_rope, pin_slot_mask, pin_brute_multistep,
               pin_single_key, pin_equal_scores, pin_join_equals_concat,
               pin_split_invariance, pin_permutation, pin_ring_equals_roll, pin_merge,
-              pin_gate, pin_gate_proj, pin_capacity_and_poison]
+              pin_gate, pin_gate_proj, pin_attend_block, pin_capacity_and_poison]

@@ -67,6 +67,14 @@ MUTANTS = [
                                 "        kq[i] = (float)((double)kr32[i] / 1.0);")]),
     ("append capacity off by one", [("if (!ring && p >= n_slots) { status = -4; continue; }",
                                      "if (!ring && p > n_slots) { status = -4; continue; }")]),
+    # the per-(stream, head) entry of the full-size checks
+    ("block entry key unscaled", [("for (int d = 0; d < D; ++d) { kn[d] *= ks; vn[d] *= vs; }",
+                                   "for (int d = 0; d < D; ++d) { vn[d] *= vs; }")]),
+    ("block entry value scaled twice", [("for (int d = 0; d < D; ++d) { kn[d] *= ks; vn[d] *= vs; }",
+                                         "for (int d = 0; d < D; ++d) { kn[d] *= ks; vn[d] *= vs * vs; }")]),
+    ("block entry decoded as the wrong type", [
+        ("    orc_decode(dtype, k_hat, (size_t)D, kn);",
+         "    orc_decode(dtype == ORC_BF16 ? ORC_F16 : dtype, k_hat, (size_t)D, kn);")]),
 ]
 
 
