@@ -48,10 +48,15 @@ def is_full(l):
     return l % 4 == 3
 
 
-KERNEL_SOURCES = ["hybrid_sliding_window_decode_amd/csrc/kernels/attn.hpp",
-                  "hybrid_sliding_window_decode_amd/csrc/kernels/common.hpp",
-                  "hybrid_sliding_window_decode_amd/csrc/hswd.hip",
-                  "hybrid_sliding_window_decode_amd/csrc/attn_launch.hpp"]
+def kernel_sources(root=ROOT):
+    """The device code: kernel headers, the launch template and the kernel
+    instantiation units (the host entry points in hswd.hip are left out, so
+    a host-only change does not void the committed counters)."""
+    import glob
+    csrc = os.path.join(root, "hybrid_sliding_window_decode_amd", "csrc")
+    return (sorted(glob.glob(os.path.join(csrc, "kernels", "*.hpp")))
+            + [os.path.join(csrc, "attn_launch.hpp")]
+            + sorted(glob.glob(os.path.join(csrc, "attn_g*.hip"))))
 
 
 def counters_path(kv, heads=H):
@@ -78,14 +83,15 @@ def full_kernel(kv, heads=H):
         {"bf16": 2, "fp8": 3}[kv], g, "true" if pieces > 1 else "false")
 
 
-def kernel_source_digest():
-    """sha256 of the kernel sources with comments removed and whitespace
-    collapsed: it changes when the code changes, not when a comment does."""
+def kernel_source_digest(root=ROOT):
+    """sha256 of the device code with comments removed and whitespace
+    collapsed: it changes when the kernels change, not when a comment does."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        text = open(os.path.join(ROOT, p)).read()
+    for p in kernel_sources(root):
+        h.update(os.path.relpath(p, root).encode())
+        text = open(p).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())

@@ -4,6 +4,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
@@ -43,19 +45,45 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
-def test_committed_traffic_is_close_to_the_algorithmic_bytes():
-    """Where the committed counters match the kernel code, the measured HBM
-    bytes of the full-layer launch are within a few percent of what the
-    method must move (more would mean re-reads; less, a miscount).  A group
-    split into pieces reads the cache once per piece at most."""
-    for kv, elt in (("bf16", 2), ("fp8", 1)):
-        for heads in (8, 16, 24, 32, 64):
-            t = bench.measured_traffic(kv, heads)
-            if t is None:
-                continue
-            alg = bench.layer_bytes("full", elt=elt, heads=heads)
-            pieces = bench.kernel_group(kv, heads)[1]
-            assert 0.999 * alg <= t <= 1.03 * pieces * alg, (kv, heads, t, alg)
+HEADLINE_COUNTERS = [("bf16", 8), ("fp8", 8)]
+OTHER_COUNTERS = [(kv, h) for kv in ("bf16", "fp8") for h in (16, 24, 32, 64)]
+
+
+def _check_traffic(kv, heads):
+    elt = 1 if kv == "fp8" else 2
+    t = bench.measured_traffic(kv, heads)
+    alg = bench.layer_bytes("full", elt=elt, heads=heads)
+    pieces = bench.kernel_group(kv, heads)[1]
+    assert 0.999 * alg <= t <= 1.03 * pieces * alg, (kv, heads, t, alg)
+
+
+@pytest.mark.parametrize("kv,heads", HEADLINE_COUNTERS)
+def test_headline_counters_match_the_kernel_code(kv, heads):
+    """The committed FETCH_SIZE / WRITE_SIZE counters of the benchmark's own
+    steps (8 query heads, bf16 and fp8 caches) must have been taken on the
+    current device code: bench.py reports roofline.traffic from them, so a
+    kernel change must come with new counters."""
+    assert os.path.exists(bench.counters_path(kv, heads)), "no committed counters"
+    assert bench.measured_traffic(kv, heads) is not None, (
+        "profiles/%s is older than the kernel code: re-take FETCH_SIZE and "
+        "WRITE_SIZE" % os.path.basename(bench.counters_path(kv, heads)))
+    # the measured HBM bytes of the full-layer launch are within a few
+    # percent of what the method must move (more would mean re-reads; less,
+    # a miscount)
+    _check_traffic(kv, heads)
+
+
+@pytest.mark.parametrize("kv,heads", OTHER_COUNTERS)
+def test_grouped_counters_close_to_the_algorithmic_bytes(kv, heads):
+    """Grouped steps: where committed counters match the kernel code, their
+    traffic is within a few percent of the algorithmic bytes (a group split
+    into pieces reads the cache once per piece at most)."""
+    if not os.path.exists(bench.counters_path(kv, heads)):
+        pytest.skip("no committed counters for %s with %d query heads" % (kv, heads))
+    if bench.measured_traffic(kv, heads) is None:
+        pytest.skip("committed counters for %s with %d query heads predate the kernel "
+                    "code" % (kv, heads))
+    _check_traffic(kv, heads)
 
 
 def test_kernel_group():
