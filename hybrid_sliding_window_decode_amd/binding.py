@@ -200,7 +200,25 @@ def _cache_pair(k_cache, v_cache):
     _need(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
 
 
+def check_desc(desc, k_cache, n_heads):
+    """A caller-supplied descriptor must describe the tensors passed with it:
+    the library addresses every cache row, query and output from the
+    descriptor alone, so a stale one (another batch, cache or head count)
+    would read and write outside the tensors."""
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, Hkv, n_slots, D], got %s" % (tuple(k_cache.shape),))
+    B, Hkv, S, D = k_cache.shape
+    code = _TORCH_CODE.get(k_cache.dtype)
+    want = dict(batch=B, n_heads=n_heads, n_kv_heads=Hkv, head_dim=D, n_slots=S, kv_dtype=code)
+    for name, value in want.items():
+        if getattr(desc, name) != value:
+            raise ValueError("desc.%s = %d does not match the tensors (%s)"
+                             % (name, getattr(desc, name), value))
+
+
 def kv_slot_write(k_cache, v_cache, k_rot, v, pos, ring, ws, slot_out=None, desc=None):
+    if desc is not None:
+        check_desc(desc, k_cache, desc.n_heads)
     _cache_pair(k_cache, v_cache)
     B, Hkv, S, D = k_cache.shape
     _need(k_rot, "k_rot", torch.float32, (B, Hkv, D))
@@ -216,6 +234,8 @@ def kv_slot_write(k_cache, v_cache, k_rot, v, pos, ring, ws, slot_out=None, desc
 
 
 def _attn_args(q, k, v, k_cache, v_cache, pos, desc):
+    if desc is not None:
+        check_desc(desc, k_cache, q.shape[1])
     _cache_pair(k_cache, v_cache)
     B, Hkv, S, D = k_cache.shape
     H = q.shape[1]
@@ -250,6 +270,8 @@ def decode_attn_full(q_rot, k_rot, v, k_cache, v_cache, pos, max_pos, ws, out=No
 
 def decode_attn_partials(q_rot, k_cache, v_cache, pos, ring, max_pos=0, desc=None):
     """(part_o [B,H,n,D], part_ml [B,H,n,2]) of the cached keys alone."""
+    if desc is not None:
+        check_desc(desc, k_cache, q_rot.shape[1])
     _cache_pair(k_cache, v_cache)
     B, Hkv, S, D = k_cache.shape
     H = q_rot.shape[1]

@@ -89,7 +89,11 @@ int chunk_keys(const hswd_attn_desc* d) {
     while (k < kMaxChunkKeys && (long)k * 2 * 128 <= d->n_slots) k *= 2;
     const int quanta = d->n_heads > d->n_kv_heads ? 8 : 4;
     const int floor_keys = quanta * chunk_quantum(d->head_dim, d->kv_dtype);
-    return k < floor_keys ? floor_keys : k;
+    if (k < floor_keys) k = floor_keys;
+    // very long caches (past 2^23 rows at the cap): longer chunks still, so
+    // the cache never needs more than kMaxChunks of them
+    while ((d->n_slots + (long)k - 1) / k > kMaxChunks) k *= 2;
+    return k;
 }
 
 // Chunks over the key range: a function of the cache geometry and max_pos
@@ -245,13 +249,16 @@ const char* hswd_status_string(int32_t s) {
 
 size_t hswd_workspace_bytes(const hswd_attn_desc* d, int32_t ring, int32_t max_pos) {
     if (desc_check(d) != HSWD_OK) return 0;
-    return ws_layout(d, num_chunks(d, ring, max_pos)).total;
+    const int n = num_chunks(d, ring, max_pos);
+    if (n > kMaxChunks) return 0;
+    return ws_layout(d, n).total;
 }
 
 int32_t hswd_num_splits(const hswd_attn_desc* d, int32_t ring, int32_t max_pos) {
     int32_t st = desc_check(d);
     if (st != HSWD_OK) return st;
-    return num_chunks(d, ring, max_pos);
+    const int n = num_chunks(d, ring, max_pos);
+    return n > kMaxChunks ? HSWD_ERR_INVALID : n;
 }
 
 int32_t hswd_workspace_init(void* ws, size_t ws_bytes, void* stream) {

@@ -3,8 +3,8 @@
 // layer step, the head gate and the entry write in the epilogue.
 //
 // Summation order.  The valid key range of each (stream, kv head) is cut into
-// chunks of K keys (K = keys_per_split; by default 128 to 512 from the cache
-// length).  A chunk's partial (max m, sum l, unnormalised o) is computed the
+// chunks of K keys (K = keys_per_split; by default 128 to 2048 from the
+// cache length, longer only past 2^23 rows).  A chunk's partial (max m, sum l, unnormalised o) is computed the
 // same way wherever it runs: the workgroup's waves take the chunk's tiles
 // round robin, keep an online
 // softmax each, and merge through LDS in wave order.  Chunk partials are then

@@ -128,12 +128,15 @@ typedef struct {
                                n_slots/32)) clamped to [128, 512], from 131072
                                rows on 2^floor(log2(n_slots/128)) up to 2048,
                                and at least 4 quanta (8 when n_heads >
-                               n_kv_heads).
+                               n_kv_heads), doubled further while the cache
+                               would need more than 4096 chunks.
                                Else a multiple of the quantum Q = 32768 /
                                (head_dim * element bytes) keys (4 waves, one
                                8-load tile each): 64 for D = 256 and a 16-bit
-                               cache, 32 for f32, 128 for fp8.  Results depend
-                               on it; never on the batch. */
+                               cache, 32 for f32, 128 for fp8, that cuts the
+                               key range into at most 4096 chunks (else
+                               HSWD_ERR_INVALID).  Results depend on it; never
+                               on the batch. */
     int32_t chunks_per_workgroup; /* work split only, never the bits: how many
                                consecutive chunks one workgroup streams.  0 =
                                library choice (from B and the CU count). */
@@ -161,7 +164,8 @@ size_t hswd_workspace_bytes(const hswd_attn_desc* d, int32_t ring, int32_t max_p
 int32_t hswd_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Number of chunks of keys_per_split keys per (stream, kv head): ceil(n_slots
- * / K) for a ring, ceil(max_pos / K) for an append cache (at least 1). */
+ * / K) for a ring, ceil(max_pos / K) for an append cache (at least 1).
+ * HSWD_ERR_INVALID (and a workspace size of 0) when that exceeds 4096. */
 int32_t hswd_num_splits(const hswd_attn_desc* d, int32_t ring, int32_t max_pos);
 
 /* Slot and mask [join].  slot[b] = pos[b] mod n_slots (ring) or pos[b]

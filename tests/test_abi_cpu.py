@@ -223,3 +223,68 @@ def test_binding_covers_every_declared_entry():
     for name in declared:
         assert name in binding.SIGNATURES, name
         assert hasattr(pkg, name[5:]) or hasattr(binding, name[5:]), name
+
+
+def test_binding_refuses_a_descriptor_that_does_not_match_the_tensors():
+    """The library addresses every row from the descriptor alone, so the
+    binding compares a caller's descriptor with the tensors before anything
+    else: a stale one (another batch, cache, head count or type) is refused
+    with ValueError.  CPU tensors: a matching descriptor gets as far as the
+    device check, which proves the descriptor check came first and passed."""
+    import torch
+    B, H, Hkv, S, D = 3, 8, 4, 40, 128
+    kc = torch.zeros(B, Hkv, S, D, dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    q = torch.zeros(B, H, D)
+    k = torch.zeros(B, Hkv, D)
+    v = torch.zeros(B, Hkv, D)
+    g = torch.zeros(B, H)
+    pos = torch.zeros(B, dtype=torch.int32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    good = binding.make_desc(kc, n_heads=H)
+    calls = [
+        lambda d: hswd.layer_step(q, k, v, g, kc, vc, pos, 0, 32, 5e6, ws, max_pos=10, desc=d),
+        lambda d: hswd.bind_layer_step(q, k, v, g, kc, vc, pos, 1, D, 1e4, ws, desc=d),
+        lambda d: hswd.decode_attn_full(q, k, v, kc, vc, pos, 10, ws, desc=d),
+        lambda d: hswd.decode_attn_sliding(q, k, v, kc, vc, pos, ws, desc=d),
+        lambda d: hswd.decode_attn_partials(q, kc, vc, pos, 1, desc=d),
+        lambda d: hswd.kv_slot_write(kc, vc, k, v, pos, 1, ws, desc=d),
+    ]
+    bad = [dict(batch=B + 1), dict(n_heads=2 * H), dict(n_kv_heads=Hkv * 2), dict(head_dim=256),
+           dict(n_slots=S + 1), dict(kv_dtype=1)]
+    for call in calls:
+        with pytest.raises(ValueError, match="CUDA"):
+            call(good)
+        for change in bad:
+            d = binding.make_desc(kc, n_heads=H)
+            for key, val in change.items():
+                setattr(d, key, val)
+            if "n_heads" in change and call is calls[-1]:
+                continue            # the entry write has no query heads to compare
+            with pytest.raises(ValueError, match="desc"):
+                call(d)
+
+
+def test_default_chunks_fit_the_chunk_limit_on_very_long_caches():
+    """Past 2^23 rows the default chunk doubles beyond its 2048-key cap, so
+    every cache the attention entries accept fits in 4096 chunks; an explicit
+    chunk size that would need more is refused by num_splits and gets no
+    workspace size."""
+    L = binding.lib()
+    for n_slots, dt, D in [((1 << 23) + 2, 3, 256), ((1 << 24) - 1, 2, 128),
+                           ((1 << 24) - 1, 3, 128), (1 << 23, 2, 256)]:
+        d = desc(n_slots=n_slots, kv_dtype=dt, head_dim=D)
+        n = hswd.num_splits(d, 0, n_slots - 1)
+        assert 1 <= n <= 4096, (n_slots, dt, D, n)
+        assert hswd.workspace_bytes(d, 0, n_slots - 1) > 0
+    # the chunk follows the capacity: 2^23 rows still take 2048-key chunks
+    # (4096 of them), one row more takes 4096-key chunks
+    assert hswd.num_splits(desc(n_slots=1 << 23), 0, (1 << 23) - 1) == 4096
+    assert hswd.num_splits(desc(n_slots=(1 << 23) + 1), 0, 1 << 23) == 2048
+    assert hswd.num_splits(desc(n_slots=(1 << 23) + 1), 0, 5000) == 2
+    # an explicit chunk that needs more than 4096 chunks
+    big = desc(n_slots=(1 << 20) + 1, keys_per_split=128)
+    assert L.hswd_num_splits(ctypes.byref(big), 0, 1 << 20) == -1
+    assert hswd.workspace_bytes(big, 0, 1 << 20) == 0
+    with pytest.raises(binding.HswdError):
+        hswd.num_splits(big, 0, 1 << 20)
