@@ -58,6 +58,8 @@ SIGNATURES = {
     "hswd_lse_merge": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "hswd_head_gate": ([_P, _P, _P, _I, _I, _I, _P], _I),
     "hswd_layer_step": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _D, _I, _DP, _P, _Z, _P], _I),
+    "hswd_layer_step_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _D, _I, _DP, _P, _P],
+                                _I),
     "hswd_check_errors": ([_P, ctypes.POINTER(ctypes.c_int32), _P], _I),
     "hswd_stream_read": ([_P, _Z, _P, _I, _P], _I),
     "hswd_gate_proj": ([_P, _P, _P, _I, _I, _I, _P], _I),
@@ -348,6 +350,30 @@ def layer_step(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, ws, m
     out, args = _layer_step_args(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta,
                                  ws, max_pos, out, desc)
     _check("hswd_layer_step", lib().hswd_layer_step(*args))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20       # HSWD_NOALLOC_SCRATCH_BYTES
+
+
+def layer_step_noalloc(q, k, v, gate, k_cache, v_cache, pos, ring, rot_dim, theta, max_pos=0,
+                       out=None, desc=None, err=None):
+    """layer_step with the library's own per-GPU workspace (no workspace
+    argument; the call allocates nothing when `out` is given).  err: an
+    optional int32 device tensor of one element into which the error flags
+    are OR-ed (read with check_errors(err)).  Calls that overlap in time on
+    one GPU share that workspace and must be serialised."""
+    d = _attn_args(q, k, v, k_cache, v_cache, pos, desc)
+    if gate is not None:
+        _need(gate, "gate", torch.float32, (q.shape[0], q.shape[1]))
+    if err is not None:
+        _need(err, "err", torch.int32)
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", torch.float32, q.shape)
+    _check("hswd_layer_step_noalloc", lib().hswd_layer_step_noalloc(
+        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(k_cache), _ptr(v_cache),
+        _ptr(pos), int(ring), int(rot_dim), float(theta), int(max_pos), ctypes.byref(d),
+        _ptr(err), _stream()))
     return out
 
 

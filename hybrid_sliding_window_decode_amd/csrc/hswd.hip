@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/hswd.h"
 #include "attn_launch.hpp"
@@ -180,9 +181,69 @@ int32_t dispatch_attn(AttnParams P, int D, int DT, int grid, hipStream_t st) {
               : launch_attn_group<4, true>(P, MODE, D, DT, grid, st);
 }
 
+// Workspace of the entry point that allocates nothing: the library's own
+// device array `scratch` (one per GPU, kept until the process ends).  Its
+// layout is fixed, whatever the descriptor: error word, then a counter
+// region of fixed size, then the chunk partials.  A call's partials never
+// land on another call's counters, which every call leaves at zero.
+constexpr size_t kScratchBytes = HSWD_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchCounterBytes = 64 * 1024;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+WsLayout noalloc_layout(const hswd_attn_desc* d, int n_chunk, bool partials) {
+    WsLayout L;
+    const size_t bh = (size_t)d->batch * d->n_heads;
+    const size_t pairs = (size_t)d->batch * d->n_kv_heads;
+    const int np = group_pieces(d);
+    const size_t n_counters = pairs * np + (np > 1 ? pairs : 0);
+    if (n_counters * sizeof(int32_t) > kScratchCounterBytes) {
+        L.counters = L.part_ml = L.part_o = 0;
+        L.total = SIZE_MAX;                       // more streams than the counters hold
+        return L;
+    }
+    L.counters = kAlign;
+    L.part_ml = L.counters + kScratchCounterBytes;
+    const size_t parts = partials && n_chunk > 1 ? (size_t)n_chunk : 0;
+    L.part_o = L.part_ml + round_up(bh * parts * 2 * sizeof(float), kAlign);
+    L.total = L.part_o + round_up(bh * parts * d->head_dim * sizeof(float), kAlign);
+    return L;
+}
+
+// Device address of `scratch` on the current device, looked up (and the
+// array cleared by a fill kernel on `stream`) by the first call on that
+// device.  In host code `scratch` names a host-side stand-in; only the
+// address returned here may reach a kernel.
+constexpr int kMaxDevices = 64;
+struct ScratchDev {
+    std::once_flag once;
+    void* ptr = nullptr;
+    int32_t status = HSWD_ERR_HIP;
+};
+ScratchDev g_scratch[kMaxDevices];
+
+int32_t scratch_ptr(void** out, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HSWD_ERR_HIP;
+    ScratchDev& sd = g_scratch[dev];
+    std::call_once(sd.once, [&] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return;
+        const size_t n = kScratchBytes / 4;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, stream,
+                           static_cast<int32_t*>(p), n);
+        if (hipGetLastError() != hipSuccess) return;
+        sd.ptr = p;
+        sd.status = HSWD_OK;
+    });
+    *out = sd.ptr;
+    return sd.status;
+}
+
 // Shared argument checks and parameter set-up of the attention entries.
+// scratch_ws: the workspace is the library's `scratch` array (ws is then
+// its device address, and ws_bytes its size), in the fixed layout above.
 int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, int max_pos,
-                   void* ws, size_t ws_bytes, bool need_ws) {
+                   void* ws, size_t ws_bytes, bool need_ws, bool scratch_ws = false) {
     int32_t st = desc_check(d);
     if (st != HSWD_OK) return st;
     const int group = d->n_heads / d->n_kv_heads;       // query heads per kv head
@@ -198,10 +259,14 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     }
     const int n_chunk = num_chunks(d, ring, max_pos);
     if (n_chunk > kMaxChunks) return HSWD_ERR_INVALID;
+    const int cpw = chunks_per_workgroup(d, n_chunk);
+    const int wpp = (n_chunk + cpw - 1) / cpw;
     if (need_ws) {
         if (!ws) return HSWD_ERR_WORKSPACE;
         if (!aligned16(ws)) return HSWD_ERR_ALIGN;
-        const WsLayout L = ws_layout(d, n_chunk);
+        // the scratch array holds chunk partials only when they cross
+        // workgroups (the fused step folds them in place otherwise)
+        const WsLayout L = scratch_ws ? noalloc_layout(d, n_chunk, wpp > 1) : ws_layout(d, n_chunk);
         if (ws_bytes < L.total) return HSWD_ERR_WORKSPACE;
         char* base = static_cast<char*>(ws);
         P.err = reinterpret_cast<int32_t*>(base);
@@ -209,7 +274,6 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
         P.part_ml = reinterpret_cast<float*>(base + L.part_ml);
         P.part_o = reinterpret_cast<float*>(base + L.part_o);
     }
-    const int cpw = chunks_per_workgroup(d, n_chunk);
     P.B = d->batch;
     P.H = d->n_heads;
     P.Hkv = d->n_kv_heads;
@@ -217,7 +281,7 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     P.K = chunk_keys(d);
     P.n_chunk = n_chunk;
     P.cpw = cpw;
-    P.wpp = (n_chunk + cpw - 1) / cpw;
+    P.wpp = wpp;
     P.ring = ring ? 1 : 0;
     P.max_pos = ring ? d->n_slots : max_pos;
     P.qscale = d->scale * 1.4426950408889634f;
@@ -431,18 +495,31 @@ static int32_t layer_step(float* out, const float* q, const float* k, const floa
                           const float* gate, const float* gx, const float* gw, int32_t hidden,
                           void* k_cache, void* v_cache, const int32_t* pos, int32_t ring,
                           int32_t rot_dim, double theta, int32_t max_pos,
-                          const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
+                          const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream,
+                          bool noalloc = false, int32_t* err = nullptr) {
     if (!d || rot_dim <= 0 || rot_dim > d->head_dim || (rot_dim & 1)) return HSWD_ERR_INVALID;
     if (!(theta > 0.0) || !isfinite(theta)) return HSWD_ERR_INVALID;
     if (empty_batch(d)) return HSWD_OK;
     if (!out || !q || !k || !v || !k_cache || !v_cache || !pos) return HSWD_ERR_INVALID;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
-        !aligned16(k_cache) || !aligned16(v_cache))
+        !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)err & 3u) != 0)
         return HSWD_ERR_ALIGN;
     AttnParams P{};
     int grid = 0;
-    int32_t st = attn_setup(P, grid, d, ring, max_pos, ws, ws_bytes, true);
+    int32_t st;
+    if (noalloc) {
+        // the size check first, on a stand-in base: a refused call touches
+        // no device state
+        st = attn_setup(P, grid, d, ring, max_pos, reinterpret_cast<void*>(kAlign), kScratchBytes,
+                        true, true);
+        if (st != HSWD_OK) return st;
+        st = scratch_ptr(&ws, as_stream(stream));
+        if (st != HSWD_OK) return st;
+        ws_bytes = kScratchBytes;
+    }
+    st = attn_setup(P, grid, d, ring, max_pos, ws, ws_bytes, true, noalloc);
     if (st != HSWD_OK) return st;
+    if (err) P.err = err;
     P.out = out;
     P.q = q;
     P.k = k;
@@ -465,6 +542,15 @@ int32_t hswd_layer_step(float* out, const float* q, const float* k, const float*
                         const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
     return layer_step(out, q, k, v, gate, nullptr, nullptr, 0, k_cache, v_cache, pos, ring,
                       rot_dim, theta, max_pos, d, ws, ws_bytes, stream);
+}
+
+int32_t hswd_layer_step_noalloc(float* out, const float* q, const float* k, const float* v,
+                                const float* gate, void* k_cache, void* v_cache,
+                                const int32_t* pos, int32_t ring, int32_t rot_dim, double theta,
+                                int32_t max_pos, const hswd_attn_desc* d, int32_t* err,
+                                void* stream) {
+    return layer_step(out, q, k, v, gate, nullptr, nullptr, 0, k_cache, v_cache, pos, ring,
+                      rot_dim, theta, max_pos, d, nullptr, 0, stream, true, err);
 }
 
 int32_t hswd_layer_step_gproj(float* out, const float* q, const float* k, const float* v,

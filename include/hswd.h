@@ -257,6 +257,32 @@ int32_t hswd_layer_step(float* out, const float* q, const float* k, const float*
                         int32_t ring, int32_t rot_dim, double theta, int32_t max_pos,
                         const hswd_attn_desc* d, void* ws, size_t ws_bytes, void* stream);
 
+/* hswd_layer_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same kernels and the same numbers as
+ * hswd_layer_step; the workspace is a device array the library owns, one
+ * per GPU, HSWD_NOALLOC_SCRATCH_BYTES (32 MiB) each, held until the process
+ * ends.  Nothing is allocated or freed: the first call on a GPU looks up the
+ * array's address and clears it with a fill kernel on `stream` (captured
+ * with the call if that first call is under capture).
+ *   err: DEVICE int32 (4-byte aligned, nullable) into which the HSWD_FLAG_*
+ *        bits are OR-ed (read them with hswd_check_errors(err, ...)); when
+ *        NULL they are recorded in the array and cannot be read.
+ * Returns HSWD_ERR_WORKSPACE, before touching the device, when the call
+ * would need more than the array holds: 64 KiB of arrival counters (B * Hkv
+ * per head piece, plus B * Hkv when a group is split into pieces) and the
+ * chunk partials B * H * n_chunk * (D + 2) * 4 bytes, needed only when the
+ * work split puts a (stream, kv head) on several workgroups (long contexts,
+ * small batches).  Every call on one GPU shares its array, whose arrival
+ * counters each call leaves at zero: calls that overlap in time on one GPU
+ * (several streams or host threads) race and must be serialised. */
+#define HSWD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int32_t hswd_layer_step_noalloc(float* out, const float* q, const float* k, const float* v,
+                                const float* gate, void* k_cache, void* v_cache,
+                                const int32_t* pos, int32_t ring, int32_t rot_dim, double theta,
+                                int32_t max_pos, const hswd_attn_desc* d, int32_t* err,
+                                void* stream);
+
 /* Gate projection g_proj [model], [export]: logits[b][h] = sum over i of
  * x[b][i] * w_g[h][i], summed in a fixed order in float32.  x float32
  * [B, hidden] is the layer's post-norm input (the same one the QKV

@@ -288,3 +288,25 @@ def test_default_chunks_fit_the_chunk_limit_on_very_long_caches():
     assert hswd.workspace_bytes(big, 0, 1 << 20) == 0
     with pytest.raises(binding.HswdError):
         hswd.num_splits(big, 0, 1 << 20)
+
+
+def test_noalloc_step_refuses_what_its_array_cannot_hold():
+    """hswd_layer_step_noalloc checks, before it touches the device, that the
+    call fits the library's 32 MiB array: a call needing more (chunk
+    partials of 64 query heads over a 2^20-row cache on a few workgroups per
+    kv head, or more arrival counters than its 64 KiB region) returns
+    HSWD_ERR_WORKSPACE (on this GPU-less host a device access would have
+    returned HSWD_ERR_HIP instead); a misaligned error word is refused."""
+    L = binding.lib()
+    f = L.hswd_layer_step_noalloc
+
+    def call(d, ring=0, max_pos=0, err=None, rot=64):
+        return f(A, A, A, A, None, A, A, A, ring, rot, 5e6, max_pos, ctypes.byref(d), err, None)
+
+    big = desc(batch=1, n_heads=64, n_slots=(1 << 20) + 1)      # 33.8 MB of partials
+    assert call(big, max_pos=1 << 20) == -3
+    many = desc(batch=2049, n_slots=511)                        # 16392 counters
+    assert call(many, ring=1, rot=256) == -3
+    assert call(desc(batch=1, n_slots=4097), max_pos=4096, err=ctypes.c_void_p(0x10002)) == -2
+    assert call(desc(batch=0, n_slots=4097), max_pos=4096) == 0  # empty batch: nothing to do
+    assert call(desc(batch=1, n_slots=4097), max_pos=4097) == -4  # capacity, as layer_step
