@@ -59,12 +59,14 @@ def short(name):
     return n[:80]
 
 
-def rocprof_cmd(kind, arg, out, prefix, bench_args):
+def rocprof_cmd(kind, arg, out, prefix, bench_args, include=None):
     base = ["rocprofv3"]
     if kind == "trace":
         base += ["--kernel-trace", "--stats"]
     else:
         base += ["--pmc"] + arg
+        if include:                  # counters of the matching kernels only
+            base += ["--kernel-include-regex", include]
     return base + ["-d", out, "-o", prefix, "--output-format", "csv", "--",
                    sys.executable, "-u", "bench.py"] + bench_args
 
@@ -76,11 +78,11 @@ def passes(out, bench_args, steps):
                                run_args + ["--steps", str(steps)]), 300)]
     short_args = run_args + ["--steps", "2", "--warmup", "1"]
     for label, ctr in [("fetch", ["FETCH_SIZE"]), ("write", ["WRITE_SIZE"])] + GROUPS:
-        p.append((label, rocprof_cmd("pmc", ctr, os.path.join(out, label), "bench", short_args),
-                  240))
+        p.append((label, rocprof_cmd("pmc", ctr, os.path.join(out, label), "bench", short_args,
+                                     "hswd"), 240))
     for label, ctr in [("copyf", ["FETCH_SIZE"]), ("copyw", ["WRITE_SIZE"])]:
         p.append((label, rocprof_cmd("pmc", ctr, os.path.join(out, label), "copy",
-                                     ["--copy-calibration"]), 120))
+                                     ["--copy-calibration"], "copy"), 120))
     return p
 
 
@@ -102,7 +104,14 @@ def run(args):
                 print("profile pass %s failed with status %d" % (label, r.returncode), flush=True)
                 return r.returncode
         print("profile pass %s done" % label, flush=True)
-    return summarize(args)
+    rc = summarize(args)
+    if rc == 0 and args.prune:
+        # the raw per-dispatch tables are large (torch's kernel names run to
+        # kilobytes); the statistics and agent tables stay
+        for f in glob.glob(os.path.join(args.out, "**", "*.csv"), recursive=True):
+            if f.endswith(("_kernel_trace.csv", "_counter_collection.csv")):
+                os.remove(f)
+    return rc
 
 
 def _csv(out, label, kind):
@@ -253,13 +262,14 @@ def summarize(args):
               "torch's seeded data generation and copies (at::native kernels, copyBuffer), which "
               "are set-up, not the decode path. Algorithmic bytes: valid K/V rows plus per-stream "
               "inputs and outputs (bench.py layer_bytes / single_layer_bytes)."]
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    md = os.path.join(ROOT, "profiles", args.name + ".md")
-    with open(md, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    with open(os.path.join(ROOT, "profiles", args.name + "_counters.json"), "w") as f:
-        json.dump(record, f, indent=1)
-    print("wrote %s" % md, flush=True)
+    for d in [os.path.join(ROOT, "profiles")] + ([args.copy_to] if args.copy_to else []):
+        os.makedirs(d, exist_ok=True)
+        md = os.path.join(d, args.name + ".md")
+        with open(md, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        with open(os.path.join(d, args.name + "_counters.json"), "w") as f:
+            json.dump(record, f, indent=1)
+        print("wrote %s" % md, flush=True)
     return 0
 
 
@@ -270,6 +280,10 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--bench-args", default="")
     ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--copy-to", default=None,
+                    help="also write the summary files into this directory")
+    ap.add_argument("--no-prune", dest="prune", action="store_false",
+                    help="keep the raw per-dispatch csv tables after summarising")
     args = ap.parse_args()
     sys.exit(run(args) if args.action == "run" else summarize(args))
 
