@@ -251,6 +251,11 @@ void attn_kernel(AttnParams P) {
     constexpr int NB = flush_buffers<G>();
 
     constexpr bool MF = use_mfma<DT, G>();
+    // fp16 probabilities of the matrix-core kernels over f16 / fp8 caches
+    // are scaled by 2^kPScale; a wave's chunk partial (sum and values) is
+    // scaled back by kPUnscale, a power of two, when the chunk ends
+    constexpr float kPScale = MF && DT != kBF16 ? 15.f : 0.f;
+    constexpr float kPUnscale = MF && DT != kBF16 ? 0x1p-15f : 1.f;
     // MFMA kernel: each wave stages its K rows in LDS (rows padded by 16
     // bytes so the 16 rows an operand read touches fall in distinct banks),
     // the query heads sit there as 16-bit hi + lo parts, and the
@@ -573,26 +578,32 @@ void attn_kernel(AttnParams P) {
             // probabilities to LDS: float per (key, head) for bf16 caches;
             // fp8 and f16 caches: fp16, paired by load index (loads 2 j and
             // 2 j + 1 of a lane hold the same dims of two keys), so one
-            // 16-byte read gives a lane the four heads' pairs for its row
+            // 16-byte read gives a lane the four heads' pairs for its row.
+            // The fp16 ones carry a factor 2^kPScale (added to the exponent,
+            // undone exactly at the chunk end), so a probability only falls
+            // into fp16's subnormal range below 2^-29, and the running sum
+            // adds the same rounded values the value product multiplies.
             constexpr bool PV16 = DT != kBF16;
             float psum = 0.f;
 #pragma unroll
             for (int kg = 0; kg < NG; ++kg) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float pr = fast_exp2(sv[kg][i] - m_new);
-                    psum += pr;
                     const int key = kg * 16 + 4 * kq + i;          // within the tile
-                    // (the 8-head 128-dim kernel keeps the branch: without
-                    // it that instance needs more registers than it has)
-                    if (G < 8 || D > 128 || hq < G) {
-                        if constexpr (PV16) {
+                    if constexpr (PV16) {
+                        const _Float16 ph = (_Float16)fast_exp2(sv[kg][i] - m_new + kPScale);
+                        psum += (float)ph;
+                        // (the 8-head 128-dim kernel keeps the branch: without
+                        // it that instance needs more registers than it has)
+                        if (G < 8 || D > 128 || hq < G) {
                             const int li = key / RPI;               // load index of the key
                             sm_ph[wid][li / 2][key % RPI][hq][li % 2] =
-                                __builtin_bit_cast(uint16_t, (_Float16)pr);
-                        } else {
-                            sm_p[wid][key][hq] = pr;
+                                __builtin_bit_cast(uint16_t, ph);
                         }
+                    } else {
+                        const float pr = fast_exp2(sv[kg][i] - m_new);
+                        psum += pr;
+                        sm_p[wid][key][hq] = pr;
                     }
                 }
             }
@@ -822,7 +833,8 @@ void attn_kernel(AttnParams P) {
             }
             if (r == 0) {
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) sm_o[buf][n_st][hh][wid][c * EPC + e] = o_acc[hh][e];
+                for (int e = 0; e < EPC; ++e)
+                    sm_o[buf][n_st][hh][wid][c * EPC + e] = o_acc[hh][e] * kPUnscale;
             }
             if constexpr (G == 8) __builtin_amdgcn_sched_barrier(0);
             if (!MF && lane == 0) {
@@ -837,7 +849,7 @@ void attn_kernel(AttnParams P) {
         if constexpr (MF) {
             // head (lane % 16): its max is already the same in its 4 lanes;
             // its sum adds the 4 lanes' shares
-            const float lw = xor_sum<32>(xor_sum<16>(l1));
+            const float lw = xor_sum<32>(xor_sum<16>(l1)) * kPUnscale;
             if (lane < G) {
                 sm_m[buf][n_st][lane][wid] = m1;
                 sm_l[buf][n_st][lane][wid] = lw;
