@@ -136,6 +136,9 @@ def parse():
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--chunks-per-workgroup", type=int, default=0,
+                    help="single-layer workloads: the work split (0 = the library's choice; "
+                         "it never changes the bits)")
     ap.add_argument("--workload", default="step28_64x4096_bf16",
                     choices=["step28_64x4096_bf16"] + sorted(SINGLE_LAYER),
                     help="the 28-layer step (default) or one single-layer workload")
@@ -199,7 +202,8 @@ def single_layer(args, np, torch, hswd, inputs, dev):
     sets = [inputs.device_step(spec, pos, seed=seed * 100 + i, device=dev) for i in range(n_sets)]
     # every set holds the same per-head fp8 scales; the descriptor points at
     # the first set's copy
-    desc = hswd.make_desc(sets[0]["k_cache"], n_heads=Hq, kv_scale=sets[0].get("kv_scale"))
+    desc = hswd.make_desc(sets[0]["k_cache"], n_heads=Hq, kv_scale=sets[0].get("kv_scale"),
+                          chunks_per_workgroup=args.chunks_per_workgroup)
     ring = kind == "sliding"
     mp = int(posv.max())
     ws = hswd.workspace(desc, ring, mp, device=dev)
@@ -243,6 +247,7 @@ def single_layer(args, np, torch, hswd, inputs, dev):
            "algorithmic_bytes": nbytes, "buffer_sets": n_sets,
            "frac_of_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
            "config": {"workload": args.workload, "kind": kind, "streams": B_, "heads": Hq,
+                      "chunks_per_workgroup": args.chunks_per_workgroup or "library",
                       "kv_heads": HKV,
                       "head_dim": D, "kv_dtype": dtype,
                       "positions": "ragged U[1,4096]" if isinstance(pos, np.ndarray) else int(pos)}}

@@ -411,3 +411,56 @@ def test_bound_layer_step_matches_plain_call(kind, dtype):
         assert np.array_equal(cache_to_host(d2["k_cache"]), cache_to_host(d1["k_cache"]))
         assert np.array_equal(cache_to_host(d2["v_cache"]), cache_to_host(d1["v_cache"]))
     assert hswd.check_errors(ws2) == 0
+
+
+@pytest.mark.parametrize("kind,B,dtype,pos,S,D", [
+    ("sliding", 1, "f32", [600], None, 256),            # one stream, f32 ring
+    ("full", 1, "f16", [1024], 1025, 256),              # one stream, f16 full layer
+    ("sliding", 8, "bf16", [131072] * 8, None, 256),    # 8 rings past capacity
+    ("full", 3, "fp8", [1099, 3, 600], 1100, 256),      # fp8, few keys, empty chunks
+    ("full", 2, "bf16", [700, 2], 1025, 128),           # D = 128, a stream with 2 keys
+    ("full", 1, "bf16", [1280], 1281, 128),             # 3 chunks: an odd count
+])
+def test_small_batch_work_split_never_changes_bits(kind, B, dtype, pos, S, D):
+    """The single-stream and few-stream shapes, where the library spreads a
+    (stream, kv head) over several workgroups and merges their chunk
+    partials: the library's split, one workgroup per chunk, and one
+    workgroup streaming every chunk give the same bits, in the fused step
+    (with the gate given, and with the gate projected in the launch) and in
+    the attention entry; and match the oracle."""
+    spec = spec_for(kind, B, dtype, S=S, D=D)
+    x = inputs.make_step(spec, pos, seed=23)
+    ring = kind == "sliding"
+    mp = int(x.pos.max())
+    gx, gw = inputs.gate_inputs(B, 2048, spec.H, seed=24)
+    results = []
+    for cpw in (0, 1, 64):
+        d = to_dev(x)
+        desc = hswd.make_desc(d["k_cache"], chunks_per_workgroup=cpw, kv_scale=d["kv_scale"])
+        n = hswd.num_splits(desc, ring, mp)
+        say("small-batch split %s %s B=%d D=%d pos=%s: %d chunks, cpw=%d" % (
+            kind, dtype, B, D, list(x.pos), n, cpw))
+        ws = hswd.workspace(desc, ring, mp)
+        out = hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
+                              d["pos"], ring, spec.rot, spec.theta, ws, max_pos=mp, desc=desc)
+        e = to_dev(x)
+        out_g = hswd.layer_step_gproj(e["q"], e["k"], e["v"], f32_dev(gx), f32_dev(gw),
+                                      e["k_cache"], e["v_cache"], e["pos"], ring, spec.rot,
+                                      spec.theta, ws, max_pos=mp, desc=desc)
+        f = to_dev(x)
+        hswd.rope_apply(f["q"], f["k"], f["pos"], spec.rot, spec.theta)
+        if ring:
+            o = hswd.decode_attn_sliding(f["q"], f["k"], f["v"], f["k_cache"], f["v_cache"],
+                                         f["pos"], ws, desc=desc)
+        else:
+            o = hswd.decode_attn_full(f["q"], f["k"], f["v"], f["k_cache"], f["v_cache"],
+                                      f["pos"], mp, ws, desc=desc)
+        assert hswd.check_errors(ws) == 0
+        results.append([out.cpu().numpy(), out_g.cpu().numpy(), o.cpu().numpy(),
+                        cache_to_host(d["k_cache"]), cache_to_host(d["v_cache"])])
+    for r in results[1:]:
+        for a, b in zip(results[0], r):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    ref = oracle_step(x)
+    assert_parity(results[0][2], ref["o_pre"], x, "small-batch split, attention entry")
+    assert_parity(results[0][0], ref["out"], x, "small-batch split, fused step")
