@@ -156,6 +156,10 @@ SINGLE_LAYER = {
     "long_full_8x131072_bf16": ("full", 8, "bf16", 131072, 5, 8),
     "long_sliding_8x131072_bf16": ("sliding", 8, "bf16", 131072, 5, 8),
     "long_full_1x1048576_bf16": ("full", 1, "bf16", 1 << 20, 9, 8),
+    # streams far below a 131072-row cache's capacity (their chunks follow
+    # their own positions): one at 5000, and 8 ragged in [1, 131072]
+    "long_full_1at5000_of_131072_bf16": ("full", 1, "bf16", 5000, 10, 8, 131073),
+    "long_full_8xragged_of_131072_bf16": ("full", 8, "bf16", "ragged:131072", 11, 8, 131073),
     "gqa4_full_64x4096_bf16": ("full", 64, "bf16", 4096, 6, 32),
     "gqa4_sliding_64x4096_bf16": ("sliding", 64, "bf16", 4096, 6, 32),
     "gqa2_full_64x4096_bf16": ("full", 64, "bf16", 4096, 7, 16),
@@ -165,20 +169,29 @@ SINGLE_LAYER = {
 
 
 def single_layer_positions(workload):
-    """Positions of a single-layer workload's streams (int64 [B])."""
+    """Positions of a single-layer workload's streams (int64 [B]): a fixed
+    position, or "ragged" (uniform in [1, 4096]) / "ragged:N" (in [1, N])."""
     import numpy as np
     from hybrid_sliding_window_decode_amd import inputs
-    kind, B_, dtype, pos, seed, Hq = SINGLE_LAYER[workload]
-    if pos == "ragged":
-        pos = inputs.ragged_positions(B_, 1, 4096, seed=seed)
+    kind, B_, dtype, pos, seed, Hq = SINGLE_LAYER[workload][:6]
+    if isinstance(pos, str):
+        hi = int(pos.split(":")[1]) if ":" in pos else 4096
+        pos = inputs.ragged_positions(B_, 1, hi, seed=seed)
     return np.broadcast_to(np.asarray(pos, np.int64), (B_,)).copy()
+
+
+def single_layer_capacity(workload):
+    """Append-cache rows of a single-layer workload (its longest position + 1
+    unless the workload names a larger cache)."""
+    w = SINGLE_LAYER[workload]
+    return w[6] if len(w) > 6 else int(single_layer_positions(workload).max()) + 1
 
 
 def single_layer_bytes(workload):
     """Algorithmic bytes of one launch of a single-layer workload: the valid
     K and V rows of every stream plus the per-stream inputs and outputs."""
     import numpy as np
-    kind, B_, dtype, pos, seed, Hq = SINGLE_LAYER[workload]
+    kind, B_, dtype, pos, seed, Hq = SINGLE_LAYER[workload][:6]
     elt = {"f32": 4, "fp8": 1}.get(dtype, 2)
     posv = single_layer_positions(workload)
     n_keys = np.minimum(posv, S_RING) if kind == "sliding" else posv
@@ -188,12 +201,12 @@ def single_layer_bytes(workload):
 
 
 def single_layer(args, np, torch, hswd, inputs, dev):
-    kind, B_, dtype, pos, seed, Hq = SINGLE_LAYER[args.workload]
+    kind, B_, dtype, pos, seed, Hq = SINGLE_LAYER[args.workload][:6]
     elt = {"f32": 4, "fp8": 1}.get(dtype, 2)
     posv = single_layer_positions(args.workload)
-    if SINGLE_LAYER[args.workload][3] == "ragged":
+    if isinstance(pos, str):
         pos = posv.astype(np.int32)
-    cap = int(posv.max()) + 1
+    cap = single_layer_capacity(args.workload)
     spec = (inputs.sliding_spec(B_, dtype, H=Hq) if kind == "sliding"
             else inputs.full_spec(B_, cap, dtype, H=Hq))
     nbytes = single_layer_bytes(args.workload)
@@ -250,7 +263,9 @@ def single_layer(args, np, torch, hswd, inputs, dev):
                       "chunks_per_workgroup": args.chunks_per_workgroup or "library",
                       "kv_heads": HKV,
                       "head_dim": D, "kv_dtype": dtype,
-                      "positions": "ragged U[1,4096]" if isinstance(pos, np.ndarray) else int(pos)}}
+                      "capacity": cap if kind == "full" else None,
+                      "positions": ("ragged U[1,%d]" % int(posv.max()) if isinstance(pos, np.ndarray)
+                                    else int(pos))}}
     print(json.dumps(res), flush=True)
 
 

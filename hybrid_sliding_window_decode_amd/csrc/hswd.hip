@@ -67,7 +67,8 @@ bool empty_batch(const hswd_attn_desc* d) {
     return d != nullptr && d->batch == 0 && desc_check(d) == HSWD_OK;
 }
 
-// Default keys per chunk, from the cache geometry, element type and head
+// Default keys per chunk of a ring (an append cache's streams take their
+// own, auto_chunk_keys), from the cache geometry, element type and head
 // grouping only (never the batch): 2^floor(log2(n_slots / 32)) clamped to
 // [128, 512]; from 131072 rows on 2^floor(log2(n_slots / 128)), at most
 // kMaxChunkKeys; and at least four quanta (a quantum, one tile per wave, is
@@ -97,11 +98,39 @@ int chunk_keys(const hswd_attn_desc* d) {
     return k;
 }
 
-// Chunks over the key range: a function of the cache geometry and max_pos
-// only, never of the batch (the chunk size is part of the summation order).
+// Append caches under the default chunking take each stream's chunk from
+// its own valid keys (auto_chunk_keys: about 32 chunks of them), so a
+// stream far below the capacity still spreads over many workgroups and a
+// long one folds few partials; the chunk depends on the stream's position
+// alone, never on the batch.  Rings and explicit chunk sizes keep one chunk
+// for every stream.
+bool auto_chunks(const hswd_attn_desc* d, int ring) { return !ring && d->keys_per_split == 0; }
+int auto_floor(const hswd_attn_desc* d) {
+    return (d->n_heads > d->n_kv_heads ? 8 : 4) * chunk_quantum(d->head_dim, d->kv_dtype);
+}
+
+// Chunks over the key range, the most any stream up to max_pos can have:
+// a function of the cache geometry and max_pos only, never of the batch
+// (the chunk size is part of the summation order).  auto_chunk_keys is
+// nondecreasing, so ceil(n / chunk(n)) peaks where a range of constant chunk
+// ends: at 32 * floor and below (32 chunks), at kAutoLongKeys - 1, at the
+// kMaxChunks threshold, or at max_pos itself.
+int auto_chunks_of(int n, int fl) {
+    const int k = auto_chunk_keys(n, fl);
+    return (int)((n + (long)k - 1) / k);
+}
 int num_chunks(const hswd_attn_desc* d, int ring, int max_pos) {
-    const long K = chunk_keys(d);
     const long keys = ring ? d->n_slots : (max_pos > 0 ? max_pos : 0);
+    if (auto_chunks(d, ring)) {
+        const int fl = auto_floor(d);
+        const long ends[] = {keys, 32l * fl, kAutoLongKeys - 1l,
+                             2l * kAutoChunkKeys * kMaxChunks};
+        int n = 1;
+        for (long e : ends)
+            if (e <= keys) n = max(n, auto_chunks_of((int)e, fl));
+        return n;
+    }
+    const long K = chunk_keys(d);
     const long n = (keys + K - 1) / K;
     return n < 1 ? 1 : (int)n;
 }
@@ -259,8 +288,17 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     }
     const int n_chunk = num_chunks(d, ring, max_pos);
     if (n_chunk > kMaxChunks) return HSWD_ERR_INVALID;
-    const int cpw = chunks_per_workgroup(d, n_chunk);
+    const bool autok = auto_chunks(d, ring);
+    int cpw = chunks_per_workgroup(d, n_chunk);
     const int wpp = (n_chunk + cpw - 1) / cpw;
+    // per-stream chunks: the launch's K and cpw are those of a stream at
+    // max_pos (its chunks spread over the pair's wpp workgroups unless the
+    // caller fixed the chunks per workgroup)
+    const int K = autok ? auto_chunk_keys(max_pos, auto_floor(d)) : chunk_keys(d);
+    if (autok && d->chunks_per_workgroup == 0) {
+        const int nb = max_pos > 0 ? (max_pos + K - 1) / K : 1;
+        cpw = (nb + wpp - 1) / wpp;
+    }
     if (need_ws) {
         if (!ws) return HSWD_ERR_WORKSPACE;
         if (!aligned16(ws)) return HSWD_ERR_ALIGN;
@@ -278,7 +316,9 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     P.H = d->n_heads;
     P.Hkv = d->n_kv_heads;
     P.S = d->n_slots;
-    P.K = chunk_keys(d);
+    P.K = K;
+    P.auto_k = autok ? (d->chunks_per_workgroup == 0 ? 1 : 2) : 0;
+    P.k_floor = auto_floor(d);
     P.n_chunk = n_chunk;
     P.cpw = cpw;
     P.wpp = wpp;

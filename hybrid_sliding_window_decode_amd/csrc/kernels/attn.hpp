@@ -54,6 +54,27 @@ constexpr int kAttnWaves = HSWD_ATTN_WAVES;          // waves per workgroup
 constexpr int kAttnThreads = kAttnWaves * kWave;
 static_assert(kAttnWaves == 4 || kAttnWaves == 8, "one thread per head dim needs >= 256 threads");
 constexpr int kMaxChunks = 4096;                     // chunks per (stream, kv head)
+constexpr int kAutoChunkKeys = 1024;                 // cap of a stream's own default chunk
+constexpr int kAutoLongKeys = 1 << 17;               // ... doubled from this many keys on
+
+// A stream's default chunk over an append cache, from its n valid keys: the
+// smallest power of two >= n / 32, at least `floor` (four quanta, eight for
+// grouped heads), at most kAutoChunkKeys below kAutoLongKeys keys and twice
+// that from there, then doubled while n would need more than kMaxChunks
+// chunks.  Nondecreasing in n.  About 32 chunks spread a stream far below its
+// cache's capacity over many workgroups; the cap keeps the chunks of long
+// streams fine enough that their workgroups get even shares (a workgroup
+// streams ceil(chunks / workgroups) of them, and one compute unit's bandwidth
+// sets how long the busiest takes).  The host sizes the launch with the same
+// function.
+__host__ __device__ inline int auto_chunk_keys(int n, int floor) {
+    const int target = (n + 31) >> 5;
+    const int cap = n < kAutoLongKeys ? kAutoChunkKeys : 2 * kAutoChunkKeys;
+    int k = floor;
+    while (k < target && k < cap) k <<= 1;
+    while ((n + (long)k - 1) / k > kMaxChunks) k <<= 1;
+    return k;
+}
 
 // What a launch of the attention kernel produces.
 enum AttnMode : int {
@@ -94,6 +115,11 @@ struct AttnParams {
     // group larger than G; 1 otherwise).  Every piece reads the cache; the
     // last to finish writes the new entry.
     int Gq, npiece;
+    // append caches under the default chunking (auto_k 1, or 2 when the
+    // caller fixed the chunks per workgroup): each stream's chunk is
+    // auto_chunk_keys(its valid keys, k_floor), and K / cpw above are the
+    // values of a stream at max_pos
+    int auto_k, k_floor;
 };
 
 // Scores on the matrix cores: 4 query heads per kv head over a 16-bit or
@@ -331,9 +357,15 @@ void attn_kernel(AttnParams P) {
     const int bh0 = b * P.H + (G >= 4 ? g * P.Gq + piece * G : g * G);
     const float kscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[g] : 1.f;
     const float vscale = DT == kFP8 && P.kv_scale != nullptr ? P.kv_scale[P.Hkv + g] : 1.f;
-    const int c_begin = wg * P.cpw;
-    const int c_end = min(c_begin + P.cpw, P.n_chunk);
-    const int TPW = P.K / (KT * kAttnWaves);          // tiles per wave in a full chunk
+    // Chunk size and chunks per workgroup: the launch's (P.K, P.cpw), or
+    // for an append cache under the default chunking the stream's own, set
+    // once its position arrives (until then the first tiles are requested
+    // on the launch's values, which the streams at the longest position
+    // share).
+    int K = P.K, cpw = P.cpw;
+    int c_begin = wg * cpw;
+    int c_end = min(c_begin + cpw, P.n_chunk);
+    int TPW = K / (KT * kAttnWaves);                  // tiles per wave in a full chunk
 
     const int c = lane % LPR;       // 16-byte chunk of the row this lane reads
     const int r = lane / LPR;       // row within a wave-wide load
@@ -381,7 +413,7 @@ void attn_kernel(AttnParams P) {
     // position has arrived, clamped onto the block's last row S - 1 instead;
     // a wave whose first two tiles reach past nv requests them again once nv
     // is known (a stream with few keys), so no unwritten row is ever scored.
-    const int key0 = c_begin * P.K + wid * KT;
+    int key0 = c_begin * K + wid * KT;
     int jlast = P.S - 1;
     auto item_key = [&](int j) __attribute__((always_inline)) { return key0 + j * (kAttnWaves * KT); };
 
@@ -463,29 +495,56 @@ void attn_kernel(AttnParams P) {
 
     // Valid cache rows: ring slots s < min(p, S); append rows < p.
     int nv = p < 0 ? 0 : (p < P.S ? p : P.S);
+    bool respread = false;
     if (!RING) {
-        const int grid_keys = P.n_chunk * P.K;
+        // keys at or past the launch's bound are not read (flagged)
+        const int grid_keys = P.auto_k ? P.max_pos : P.n_chunk * K;
         if (nv > grid_keys) nv = grid_keys;
         if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p > P.max_pos)
             atomicOr(P.err, 2);
+        if (P.auto_k) {
+            // the stream's chunk (auto_chunk_keys), a function of its
+            // position alone; its chunks spread over the pair's workgroups,
+            // each taking at least the share of a stream at max_pos (the
+            // launch's cpw): a shorter stream never needs to finish sooner
+            // than the longest, and leaves compute units whose bandwidth the
+            // longest streams' workgroups then have to themselves
+            const int k = auto_chunk_keys(nv, P.k_floor);
+            const int nb = max(1, (nv + k - 1) / k);
+            const int cw = P.auto_k == 2 ? cpw : max(cpw, (nb + P.wpp - 1) / P.wpp);   // 2: caller's split
+            if (k != K || cw != cpw) {
+                K = k;
+                cpw = cw;
+                c_begin = wg * cpw;
+                c_end = min(c_begin + cpw, P.n_chunk);
+                TPW = K / (KT * kAttnWaves);
+                key0 = c_begin * K + wid * KT;
+                respread = true;
+            }
+        }
+        // the last workgroup of a pair also covers the grid's chunks past
+        // the stream's own (empty partials for the partials entry)
+        if (MODE == kModePartials && wg == P.wpp - 1) c_end = P.n_chunk;
     }
     if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p < 0) atomicOr(P.err, 4);
 
     // This workgroup's chunks [c_begin, c_end): full ones [c_begin, c_full),
     // then at most one partly valid chunk [c_full, c_valid); the rest hold no
     // valid key.
-    const int n_valid_chunks = (nv + P.K - 1) / P.K;
+    const int n_valid_chunks = (nv + K - 1) / K;
     const int c_valid = max(c_begin, min(c_end, n_valid_chunks));
-    const int c_full = max(c_begin, min(c_valid, nv / P.K));
+    const int c_full = max(c_begin, min(c_valid, nv / K));
     const int n_full_items = (c_full - c_begin) * TPW;
     // tiles of the partly valid chunk, per wave (the maximum over the waves,
     // so every wave runs the same loop; surplus tiles are fully masked)
-    const int part_tiles = c_valid > c_full ? (nv - c_full * P.K + KT - 1) / KT : 0;
+    const int part_tiles = c_valid > c_full ? (nv - c_full * K + KT - 1) / KT : 0;
     const int part_items = (part_tiles + kAttnWaves - 1) / kAttnWaves;
     const int n_items = n_full_items + part_items;
 
     jlast = max(nv, 1) - 1;
-    if (item_key(1) + KT > nv) {        // the first two tiles reach past the valid rows
+    // the first two tiles reach past the valid rows, or the stream's chunks
+    // start elsewhere than the launch's guess
+    if (respread || item_key(1) + KT > nv) {
         if constexpr (MF) load_k(0);
         load_tile(kA, vA, 0);
         load_tile(kB, vB, 1);

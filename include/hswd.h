@@ -123,13 +123,19 @@ typedef struct {
                                the valid keys are cut into chunks of this many,
                                each chunk's softmax partial is formed alone and
                                the partials are folded in chunk order.  0 =
-                               library default from the cache length, element
-                               type and head grouping only: 2^floor(log2(
+                               library default.  Ring: from the slot count,
+                               element type and head grouping: 2^floor(log2(
                                n_slots/32)) clamped to [128, 512], from 131072
-                               rows on 2^floor(log2(n_slots/128)) up to 2048,
-                               and at least 4 quanta (8 when n_heads >
-                               n_kv_heads), doubled further while the cache
-                               would need more than 4096 chunks.
+                               slots on 2^floor(log2(n_slots/128)) up to 2048,
+                               at least the floor F = 4 quanta (8 when n_heads >
+                               n_kv_heads).  Append cache: each stream's own,
+                               from its n = min(pos, max_pos) valid keys: the
+                               smallest power of two >= max(F, ceil(n / 32)),
+                               at most 2048 (so about 32 chunks of them), then
+                               doubled while n would need more than 4096
+                               chunks.  Either way a function of the geometry
+                               and the stream's own position, never of the
+                               batch.
                                Else a multiple of the quantum Q = 32768 /
                                (head_dim * element bytes) keys (4 waves, one
                                8-load tile each): 64 for D = 256 and a 16-bit
@@ -163,9 +169,13 @@ size_t hswd_workspace_bytes(const hswd_attn_desc* d, int32_t ring, int32_t max_p
 /* Zero a workspace (error word and counters) with a fill kernel. */
 int32_t hswd_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
-/* Number of chunks of keys_per_split keys per (stream, kv head): ceil(n_slots
- * / K) for a ring, ceil(max_pos / K) for an append cache (at least 1).
- * HSWD_ERR_INVALID (and a workspace size of 0) when that exceeds 4096. */
+/* Number of chunks per (stream, kv head) a launch is sized for (partials,
+ * workspace): ceil(n_slots / K) for a ring, ceil(max_pos / K) for an append
+ * cache with an explicit keys_per_split K, and under the append default the
+ * most chunks any stream with pos <= max_pos can have: ceil(max_pos /
+ * K(max_pos)), at least 32 once max_pos reaches 32 F, 4096 from 2^23 keys
+ * (at least 1).  HSWD_ERR_INVALID (and a workspace size of 0) when that
+ * exceeds 4096. */
 int32_t hswd_num_splits(const hswd_attn_desc* d, int32_t ring, int32_t max_pos);
 
 /* Slot and mask [join].  slot[b] = pos[b] mod n_slots (ring) or pos[b]
@@ -222,7 +232,9 @@ int32_t hswd_decode_attn_full(float* o, const float* q_rot, const float* k_rot,
                               void* ws, size_t ws_bytes, void* stream);
 
 /* Chunk partials of the cached keys alone (no new entry) [split]: for chunk
- * c covering cache rows [c*K, (c+1)*K) of the valid range (K = keys_per_split),
+ * c covering cache rows [c*K, (c+1)*K) of the valid range (K the stream's
+ * chunk: keys_per_split, or the default of the descriptor's comment; chunks
+ * past the stream's valid keys are empty),
  *   part_ml[b][h][c] = (m, l): m = max scale*q.K (natural-log units, -inf if
  *                      the split is empty), l = sum exp(score - m) (0 if empty);
  *   part_o[b][h][c][:] = sum exp(score - m) * V  (not divided by l).

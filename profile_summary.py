@@ -154,7 +154,7 @@ def algorithmic_bytes(bench_args):
     a.add_argument("--heads", type=int, default=bench.H)
     ns, _ = a.parse_known_args(bench_args)
     if ns.workload != "step28_64x4096_bf16":
-        kind, B_, dtype, pos, seed, Hq = bench.SINGLE_LAYER[ns.workload]
+        kind, B_, dtype, pos, seed, Hq = bench.SINGLE_LAYER[ns.workload][:6]
         g, pieces = (bench.kernel_group("fp8" if dtype == "fp8" else "bf16", Hq)
                      if Hq > bench.HKV else (1, 1))
         code = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}[dtype]

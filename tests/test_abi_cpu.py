@@ -49,19 +49,24 @@ def test_version_and_status_strings():
 def test_workspace_and_splits():
     L = binding.lib()
     d = desc()
-    # default chunk: 2^floor(log2(n_slots/32)) in [128, 512], from 131072
-    # rows 2^floor(log2(n_slots/128)) up to 2048, at least four quanta
-    # (quantum = 32768 / (D * element bytes) keys): 256 keys for a bf16 ring
-    # or 4097-row cache, 512 from 16384 rows, 1024 at 131072, 2048 from 262144
+    # default chunk of a ring: 2^floor(log2(n_slots/32)) in [128, 512], at
+    # least four quanta (quantum = 32768 / (D * element bytes) keys): 256 keys
+    # for a bf16 ring.  An append cache's streams take their own chunk from
+    # their n valid keys: the power of two at or above n / 32, at least four
+    # quanta, at most 1024 keys below 131072 keys and 2048 from there; the
+    # launch holds the most chunks a stream up to max_pos can have (32 once
+    # max_pos reaches 32 * the floor, 128 at 131071 keys)
     assert hswd.num_splits(d, 1) == 2
-    assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 16
-    assert hswd.num_splits(desc(n_slots=8192), 0, 8191) == 32
-    assert hswd.num_splits(desc(n_slots=16385), 0, 16384) == 32
-    assert hswd.num_splits(desc(n_slots=65537), 0, 65536) == 128           # 512 keys
-    assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 128          # 1024 keys
-    assert hswd.num_splits(desc(n_slots=131073), 0, 5000) == 5
-    assert hswd.num_splits(desc(n_slots=262145), 0, 262144) == 128          # 2048 keys
-    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1), 0, 1 << 20) == 512   # capped: 2048
+    assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 16              # 256 keys
+    assert hswd.num_splits(desc(n_slots=8192), 0, 8191) == 32              # 256 keys
+    assert hswd.num_splits(desc(n_slots=16385), 0, 16384) == 32            # 512 keys
+    assert hswd.num_splits(desc(n_slots=9001), 0, 9000) == 32              # 512: 18, grid 32
+    assert hswd.num_splits(desc(n_slots=65537), 0, 65536) == 64            # 1024 keys
+    assert hswd.num_splits(desc(n_slots=131073), 0, 131071) == 128         # 1024 keys
+    assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 128         # 2048 keys, 64
+    assert hswd.num_splits(desc(n_slots=131073), 0, 5000) == 20            # 256 keys
+    assert hswd.num_splits(desc(n_slots=262145), 0, 262144) == 128         # 2048 keys
+    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1), 0, 1 << 20) == 512  # capped: 2048
     assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, kv_dtype=3), 0, 1 << 20) == 512
     assert hswd.num_splits(desc(n_slots=4097, head_dim=64), 0, 4096) == 4       # Q = 256
     assert hswd.num_splits(desc(n_slots=4097, kv_dtype=0), 0, 4096) == 32       # f32: Q = 32
@@ -277,11 +282,13 @@ def test_default_chunks_fit_the_chunk_limit_on_very_long_caches():
         n = hswd.num_splits(d, 0, n_slots - 1)
         assert 1 <= n <= 4096, (n_slots, dt, D, n)
         assert hswd.workspace_bytes(d, 0, n_slots - 1) > 0
-    # the chunk follows the capacity: 2^23 rows still take 2048-key chunks
-    # (4096 of them), one row more takes 4096-key chunks
+    # a stream's chunk follows its valid keys: 2^23 of them still take
+    # 2048-key chunks (4096 of them), one more takes 4096-key chunks; the
+    # launch is sized for 4096 chunks from 2^23 keys on
     assert hswd.num_splits(desc(n_slots=1 << 23), 0, (1 << 23) - 1) == 4096
-    assert hswd.num_splits(desc(n_slots=(1 << 23) + 1), 0, 1 << 23) == 2048
-    assert hswd.num_splits(desc(n_slots=(1 << 23) + 1), 0, 5000) == 2
+    assert hswd.num_splits(desc(n_slots=(1 << 23) + 1), 0, 1 << 23) == 4096
+    assert hswd.num_splits(desc(n_slots=(1 << 23) + 2), 0, (1 << 23) + 1) == 4096
+    assert hswd.num_splits(desc(n_slots=(1 << 23) + 1), 0, 5000) == 20
     # an explicit chunk that needs more than 4096 chunks
     big = desc(n_slots=(1 << 20) + 1, keys_per_split=128)
     assert L.hswd_num_splits(ctypes.byref(big), 0, 1 << 20) == -1

@@ -464,3 +464,76 @@ def test_small_batch_work_split_never_changes_bits(kind, B, dtype, pos, S, D):
     ref = oracle_step(x)
     assert_parity(results[0][2], ref["o_pre"], x, "small-batch split, attention entry")
     assert_parity(results[0][0], ref["out"], x, "small-batch split, fused step")
+
+
+def _stream_chunk(n, floor=256):
+    """The header's default chunk of an append-cache stream with n valid keys
+    (bf16, D = 256, one query head per kv head: floor of four 64-key quanta):
+    the smallest power of two >= max(floor, ceil(n / 32)), at most 1024 below
+    131072 keys and 2048 from there."""
+    cap = 1024 if n < 131072 else 2048
+    k = floor
+    while k < -(-n // 32) and k < cap:
+        k *= 2
+    return k
+
+
+def test_stream_chunks_follow_their_own_positions():
+    """Append caches under the default chunking cut each stream's keys into
+    chunks sized from its own position (about 32 of them): a stream far below
+    the cache's capacity still spreads over many workgroups.  A stream decoded
+    alone (its own position as the launch's bound) gives the same bits as in
+    a batch whose longest stream is at the capacity; every head matches the
+    oracle; the partials entry's chunks follow each stream's own size."""
+    S = 131073
+    pos = np.array([5000, 131072, 37, 70000], np.int32)
+    spec = inputs.full_spec(len(pos), S, "bf16")
+    t = inputs.device_step(spec, pos, seed=25, device="cuda")
+    kc_host, vc_host = cache_to_host(t["k_cache"]), cache_to_host(t["v_cache"])
+    q, k, v, gate = (t[n].cpu().numpy() for n in ("q", "k", "v", "gate"))
+    mp = int(pos.max())
+    desc = hswd.make_desc(t["k_cache"])
+    n_grid = hswd.num_splits(desc, 0, mp)
+    say("per-stream chunks: pos %s, launch sized for %d chunks" % (list(pos), n_grid))
+    ws = hswd.workspace(desc, 0, mp)
+    q_rot = t["q"].clone()
+    k_rot = t["k"].clone()
+    hswd.rope_apply(q_rot, k_rot, t["pos"], spec.rot, spec.theta)
+    o_batch = hswd.decode_attn_full(q_rot, k_rot, t["v"], t["k_cache"], t["v_cache"], t["pos"],
+                                    mp, ws, desc=desc).cpu().numpy()
+    po, pml = hswd.decode_attn_partials(q_rot, t["k_cache"], t["v_cache"], t["pos"], 0,
+                                        max_pos=mp, desc=desc)
+    assert hswd.check_errors(ws) == 0
+    po, pml = po.cpu().numpy(), pml.cpu().numpy()
+    assert po.shape[2] == n_grid
+    # each stream alone, its own position the launch's bound
+    for b, p in enumerate(pos):
+        sl = slice(b, b + 1)
+        d1 = hswd.make_desc(t["k_cache"][sl])
+        ws1 = hswd.workspace(d1, 0, int(p))
+        o1 = hswd.decode_attn_full(q_rot[sl].contiguous(), k_rot[sl].contiguous(),
+                                   t["v"][sl].contiguous(), t["k_cache"][sl], t["v_cache"][sl],
+                                   t["pos"][sl].contiguous(), int(p), ws1, desc=d1)
+        assert np.array_equal(o1.cpu().numpy()[0], o_batch[b]), b
+    # every head against the oracle
+    r = oracle.layer_step(q, k, v, gate, kc_host, vc_host, pos, CODE["bf16"], 0, spec.rot,
+                          spec.theta, write=False)
+    x = inputs.StepInputs(spec, pos, q, k, v, gate, kc_host, vc_host)
+    assert_parity(o_batch, r["o_pre"], x, "per-stream chunks")
+    # the partials' chunks: each stream's own size, empty past its keys
+    qr = q_rot.cpu().numpy().astype(np.float64)
+    for b, p in enumerate(pos):
+        K = _stream_chunk(int(p))
+        nb = -(-int(p) // K)
+        for h in (0, spec.H - 1):
+            for c in range(n_grid):
+                if c >= nb:
+                    assert pml[b, h, c, 0] == -np.inf and pml[b, h, c, 1] == 0, (b, c)
+                    assert np.all(po[b, h, c] == 0)
+                    continue
+                m, l, o = oracle.partial(qr[b, h], kc_host[b, h], vc_host[b, h], CODE["bf16"],
+                                         c * K, min((c + 1) * K, int(p)), 1 / 16)
+                assert abs(pml[b, h, c, 0] - m) < 1e-5 * (1 + abs(m)), (b, h, c)
+                sc = math.exp(pml[b, h, c, 0] - m)
+                assert abs(pml[b, h, c, 1] * sc - l) < 1e-5 * l, (b, h, c)
+                assert np.max(np.abs(po[b, h, c] * sc - o)) < 1e-5 * np.max(np.abs(o)), (b, h, c)
