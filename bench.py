@@ -67,11 +67,12 @@ def counters_path(kv, heads=H):
 def kernel_group(kv, heads=H):
     """(G, pieces): query heads per workgroup of the attention kernel that runs
     `heads` query heads over the HKV kv heads, and the pieces each group is
-    split into (a group above 4, fp8: above 8, runs in pieces of 4, fp8: 8)."""
+    split into (3 and 4 run the 4-head kernel, 5 to 8 the 8-head one, a
+    larger group pieces of 8)."""
     group = heads // HKV
     if group <= 2:
         return group, 1
-    piece = 8 if kv == "fp8" and group > 4 else 4
+    piece = 8 if group > 4 else 4
     return piece, -(-group // piece)
 
 

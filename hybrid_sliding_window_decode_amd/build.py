@@ -4,9 +4,9 @@
 
 Translation units: csrc/hswd.hip (host entry points and the small kernels)
 and csrc/attn_g{1,2,4,8}.hip (the attention kernel for 1, 2, 4 or 8 query heads
-per kv head; attn_g4s.hip and attn_g8s.hip: its form for the pieces of larger
-groups), compiled in parallel with hipcc for gfx950 only and linked into
-one shared library.  Packed fp32 instructions are turned off
+per kv head; attn_g8s.hip: its form for the pieces of larger groups),
+compiled in parallel with hipcc for gfx950 only and linked into one shared
+library.  Packed fp32 instructions are turned off
 (-packed-fp32-ops): the kernels are written for scalar fp32 VALU ops.
 """
 import glob
@@ -20,8 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in ("hswd.hip", "attn_g1.hip", "attn_g2.hip",
-                                            "attn_g4.hip", "attn_g8.hip", "attn_g4s.hip",
-                                            "attn_g8s.hip")]
+                                            "attn_g4.hip", "attn_g8.hip", "attn_g8s.hip")]
 SRC = SOURCES[0]
 LIB = os.path.join(HERE, "libhswd.so")
 DEPS = (SOURCES + sorted(glob.glob(os.path.join(CSRC, "*.hpp")))

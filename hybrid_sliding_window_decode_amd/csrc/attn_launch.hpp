@@ -1,7 +1,6 @@
 // Launch of the attention kernel for one query-head group size G.  Each G
 // has its own translation unit (attn_g1.hip, attn_g2.hip, attn_g4.hip,
-// attn_g8.hip, and attn_g4s.hip, attn_g8s.hip for the pieces of larger
-// groups), so the instantiations compile in parallel; hswd.hip picks one
+// attn_g8.hip, and attn_g8s.hip for the pieces of larger groups), so the instantiations compile in parallel; hswd.hip picks one
 // from H / Hkv.
 #pragma once
 
@@ -25,7 +24,6 @@ HSWD_DECLARE_GROUP(1, false)
 HSWD_DECLARE_GROUP(2, false)
 HSWD_DECLARE_GROUP(4, false)
 HSWD_DECLARE_GROUP(8, false)
-HSWD_DECLARE_GROUP(4, true)
 HSWD_DECLARE_GROUP(8, true)
 #undef HSWD_DECLARE_GROUP
 

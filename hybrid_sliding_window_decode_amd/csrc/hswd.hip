@@ -166,8 +166,9 @@ int chunks_per_workgroup(const hswd_attn_desc* d, int n_chunk) {
 // Query heads per kernel piece of a group (its kernel's G), and the pieces
 // a group is split into.
 int group_piece(int group, int DT) {
+    (void)DT;
     if (group <= 2) return group;
-    return DT == kFP8 && group > 4 ? 8 : 4;
+    return group > 4 ? 8 : 4;
 }
 int group_pieces(const hswd_attn_desc* d) {
     const int group = d->n_heads / d->n_kv_heads;
@@ -190,24 +191,21 @@ WsLayout ws_layout(const hswd_attn_desc* d, int n_chunk) {
     return L;
 }
 
-// Kernel launch for the descriptor's group size H / Hkv.  Groups of 1, 2
-// and 4 query heads per kv head have their own kernels, and 8 over an fp8
-// cache; a group of 3 runs the 4-head kernel with one head idle (5 to 7
-// over fp8: the 8-head kernel); a larger group is split into pieces of four
-// (fp8: eight) heads, one workgroup per piece in the same launch (each
-// reads the cache; the last piece to finish writes the new entry).
+// Kernel launch for the descriptor's group size H / Hkv.  Groups of 1, 2,
+// 4 and 8 query heads per kv head have their own kernels; a group of 3 runs
+// the 4-head kernel with one head idle, 5 to 7 the 8-head kernel; a larger
+// group is split into pieces of eight heads, one workgroup per piece in the
+// same launch (each reads the cache; the last piece to finish writes the
+// new entry).
 template <int MODE>
 int32_t dispatch_attn(AttnParams P, int D, int DT, int grid, hipStream_t st) {
     const int group = P.H / P.Hkv;
     P.Gq = group;
     if (group == 1) return launch_attn_group<1, false>(P, MODE, D, DT, grid, st);
     if (group == 2) return launch_attn_group<2, false>(P, MODE, D, DT, grid, st);
-    const bool g8 = group_piece(group, DT) == 8;
-    if (P.npiece == 1)
-        return g8 ? launch_attn_group<8, false>(P, MODE, D, DT, grid, st)
-                  : launch_attn_group<4, false>(P, MODE, D, DT, grid, st);
-    return g8 ? launch_attn_group<8, true>(P, MODE, D, DT, grid, st)
-              : launch_attn_group<4, true>(P, MODE, D, DT, grid, st);
+    if (P.npiece > 1) return launch_attn_group<8, true>(P, MODE, D, DT, grid, st);
+    return group_piece(group, DT) == 8 ? launch_attn_group<8, false>(P, MODE, D, DT, grid, st)
+                                       : launch_attn_group<4, false>(P, MODE, D, DT, grid, st);
 }
 
 // Workspace of the entry point that allocates nothing: the library's own

@@ -128,7 +128,7 @@ struct AttnParams {
 // exactly).
 template <int DT, int G>
 constexpr bool use_mfma() {
-    return (G == 4 && (DT == kBF16 || DT == kF16 || DT == kFP8)) || (G == 8 && DT == kFP8);
+    return (G == 4 || G == 8) && (DT == kBF16 || DT == kF16 || DT == kFP8);
 }
 
 // Tile geometry.  G query heads per kv head keep G query vectors and G
@@ -273,28 +273,39 @@ void attn_kernel(AttnParams P) {
     constexpr float kLn2 = 0.69314718055994531f;
     constexpr int kStash = stash_slots<G>();
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "query heads per kv head");
-    static_assert(G != 8 || use_mfma<DT, G>(), "8 query heads per kv head: fp8 caches only");
+    static_assert(G != 8 || use_mfma<DT, G>(), "8 query heads per kv head: matrix-core kernel");
     constexpr int NB = flush_buffers<G>();
 
     constexpr bool MF = use_mfma<DT, G>();
+    // The value product on the matrix cores too: V goes through the wave's
+    // LDS rows after its K, the probabilities stay in the registers the score
+    // product left them in.  Its accumulators (D / 16 x 4 per lane) cost the
+    // same for 4 and 8 heads; they fit beside two V tiles in flight for the
+    // 4-head kernel at 128 dims or over fp8 and the 8-head kernel at 128
+    // dims, and beside one (VS1: V of the next tile requested once this
+    // tile's is in LDS) for the 8-head kernel at 256 dims.  The 4-head kernel
+    // over 16-bit caches at 256 dims keeps the value product on the VALU.
+    constexpr bool MFPV = MF && ((G == 4 && (D <= 128 || DT == kFP8)) || G == 8);
+    constexpr bool VS1 = MFPV && G == 8 && D == 256;
+    // heads per flush of the wave partials: at 256 dims the 8-head kernel
+    // flushes its heads in two halves, so its partials take 16 KiB (LDS for
+    // two workgroups per CU)
+    constexpr int GO = MFPV && G == 8 && D == 256 ? 4 : G;
+    static_assert(GO == G || kStash == 1, "split flush: one chunk per flush");
     // fp16 probabilities of the matrix-core kernels over f16 / fp8 caches
     // are scaled by 2^kPScale; a wave's chunk partial (sum and values) is
     // scaled back by kPUnscale, a power of two, when the chunk ends
     constexpr float kPScale = MF && DT != kBF16 ? 15.f : 0.f;
     constexpr float kPUnscale = MF && DT != kBF16 ? 0x1p-15f : 1.f;
     // MFMA kernel: each wave stages its K rows in LDS (rows padded by 16
-    // bytes so the 16 rows an operand read touches fall in distinct banks),
-    // the query heads sit there as 16-bit hi + lo parts, and the
+    // bytes so the 16 rows an operand read touches fall in distinct banks;
+    // fp8 keys as exact bf16), the query heads sit there as 16-bit hi + lo
+    // parts, and, where the value product stays on the VALU, the
     // probabilities and rescale factors pass from the score layout (a key
     // per lane group, a head per lane) to the value layout through LDS.
     constexpr int KPAD = D * 2 / 16 + 1;                  // 16-byte units per staged (16-bit) row
     __shared__ float sm_q[MF ? 1 : G][D];
-    // the 8-head kernel stages fp8 keys as they are (8-byte units, rows
-    // padded by 8 bytes: the 16 rows of an operand read fall in distinct
-    // banks) and converts them when it reads them back
-    constexpr bool K8 = MF && G == 8;
-    __shared__ u32x4 sm_k[MF && !K8 ? kAttnWaves : 1][MF && !K8 ? KT : 1][MF && !K8 ? KPAD : 1];
-    __shared__ u32x2 sm_k8[K8 ? kAttnWaves : 1][K8 ? KT : 1][K8 ? D / 8 + 1 : 1];
+    __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT : 1][MF ? KPAD : 1];
     // query rows padded by 16 bytes too: unpadded, the G heads' rows (512
     // bytes apart) would share banks and the operand reads conflict 4 ways
     __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G + 1 : 1][MF ? D + 8 : 1];
@@ -302,10 +313,11 @@ void attn_kernel(AttnParams P) {
     // (both read 16 bytes at a time: aligned to 16)
     // (a column per score-product column: lanes of idle heads write unused
     // columns rather than branch around the store)
-    __shared__ __attribute__((aligned(16))) float sm_p[MF && DT == kBF16 ? kAttnWaves : 1][MF ? KT : 1][16];
-    __shared__ __attribute__((aligned(16))) uint16_t sm_ph[MF && DT != kBF16 ? kAttnWaves : 1][MF ? NL / 2 : 1][RPI][MF ? 16 : 1][2];
-    __shared__ __attribute__((aligned(16))) float sm_al[MF ? kAttnWaves : 1][G];
-    __shared__ float sm_o[NB][kStash][G][kAttnWaves][D];   // wave chunk partials, by flush parity
+    constexpr bool PLDS = MF && !MFPV;                    // probabilities through LDS
+    __shared__ __attribute__((aligned(16))) float sm_p[PLDS && DT == kBF16 ? kAttnWaves : 1][PLDS ? KT : 1][16];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_ph[PLDS && DT != kBF16 ? kAttnWaves : 1][PLDS ? NL / 2 : 1][RPI][PLDS ? 16 : 1][2];
+    __shared__ __attribute__((aligned(16))) float sm_al[PLDS ? kAttnWaves : 1][G];
+    __shared__ __attribute__((aligned(16))) float sm_o[NB][kStash][GO][kAttnWaves][D];   // wave chunk partials, by flush parity
     __shared__ float sm_m[NB][kStash][G][kAttnWaves], sm_l[NB][kStash][G][kAttnWaves];
     __shared__ float sm_dot[G][kAttnWaves];
     __shared__ float sm_gl[G][kAttnWaves];
@@ -393,6 +405,12 @@ void attn_kernel(AttnParams P) {
     // MFMA kernel: the running max and sum of head (lane % 16) over the keys
     // this lane's group of 4 holds; lanes of heads >= G carry unused values
     float m1 = -INFINITY, l1 = 0.f;
+    // value product on the matrix cores: O^T (16 dims x 16 heads) per group
+    // of 16 dims; lane l holds dims 4 (l / 16) + i of the group, head l % 16
+    typedef float pv4 __attribute__((ext_vector_type(4)));
+    pv4 pv_acc[MFPV ? D / 16 : 1];
+#pragma unroll
+    for (int m = 0; m < (MFPV ? D / 16 : 1); ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
     Fold run[G];                    // folded chunk partials (wpp == 1)
 
     using Chunk = typename ChunkT<Geo::CB>::type;
@@ -488,7 +506,7 @@ void attn_kernel(AttnParams P) {
 
     if constexpr (MF) load_k(0);
     load_tile(kA, vA, 0);
-    load_tile(kB, vB, 1);
+    if constexpr (!VS1) load_tile(kB, vB, 1);
 
     // The stream's position, requested after the first loads.
     const int p = P.pos[b];
@@ -547,7 +565,7 @@ void attn_kernel(AttnParams P) {
     if (respread || item_key(1) + KT > nv) {
         if constexpr (MF) load_k(0);
         load_tile(kA, vA, 0);
-        load_tile(kB, vB, 1);
+        if constexpr (!VS1) load_tile(kB, vB, 1);
     }
 
     auto compute_tile = [&](const Chunk (&kt)[NL], const Chunk (&vt)[NL], int j) __attribute__((always_inline)) {
@@ -572,8 +590,7 @@ void attn_kernel(AttnParams P) {
             asm volatile("" ::: "memory");     // the query reads below stay in the loop
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                if constexpr (K8) sm_k8[wid][i * RPI + r][c] = kR[i];
-                else if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_bf16x8(kR[i]);
+                if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_bf16x8(kR[i]);
                 else sm_k[wid][i * RPI + r][c] = kR[i];
             }
             // the next item's K into the freed registers, in flight under
@@ -597,8 +614,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
                     u32x4 a;
-                    if constexpr (K8) a = fp8x8_to_bf16x8(sm_k8[wid][kg * 16 + hq][4 * sl + kq]);
-                    else a = sm_k[wid][kg * 16 + hq][4 * sl + kq];
+                    a = sm_k[wid][kg * 16 + hq][4 * sl + kq];
                     f32x4& ah = acc[kg][2 * (sl & 1)];
                     f32x4& al_ = acc[kg][2 * (sl & 1) + 1];
                     if constexpr (DT != kF16) {
@@ -630,120 +646,195 @@ void attn_kernel(AttnParams P) {
             }
             mx = xor_max<16>(mx);
             mx = xor_max<32>(mx);
-            if (mx == -INFINITY) return;                // nothing valid in this tile
+            if (mx == -INFINITY) {                      // nothing valid in this tile
+                if constexpr (VS1) load_tile(kA, vA, j + 1);
+                return;
+            }
             const float m_new = fmaxf(m1, mx);
             const float alpha = fast_exp2(m1 - m_new);
             m1 = m_new;
-            // probabilities to LDS: float per (key, head) for bf16 caches;
-            // fp8 and f16 caches: fp16, paired by load index (loads 2 j and
-            // 2 j + 1 of a lane hold the same dims of two keys), so one
-            // 16-byte read gives a lane the four heads' pairs for its row.
-            // The fp16 ones carry a factor 2^kPScale (added to the exponent,
-            // undone exactly at the chunk end), so a probability only falls
-            // into fp16's subnormal range below 2^-29, and the running sum
-            // adds the same rounded values the value product multiplies.
-            constexpr bool PV16 = DT != kBF16;
-            float psum = 0.f;
+            if constexpr (MFPV) {
+                // The probabilities are the B operand of P.V as they stand:
+                // lane l holds keys 4 (l / 16) + i of head l % 16, the
+                // operand's k and column.  f16 / fp8 caches: fp16 weights
+                // (times 2^kPScale, undone at the chunk end), the running sum
+                // over the same rounded values; bf16 caches: the weight as a
+                // bf16 hi part plus a bf16 lo part (about 16 significant
+                // bits), the running sum over the float weights.
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+                s16x4 pb[NG], pbl[NG];
+                float psum = 0.f;
 #pragma unroll
-            for (int kg = 0; kg < NG; ++kg) {
+                for (int kg = 0; kg < NG; ++kg) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kg * 16 + 4 * kq + i;          // within the tile
-                    if constexpr (PV16) {
-                        const _Float16 ph = (_Float16)fast_exp2(sv[kg][i] - m_new + kPScale);
-                        psum += (float)ph;
-                        // (the 8-head 128-dim kernel keeps the branch: without
-                        // it that instance needs more registers than it has)
-                        if (G < 8 || D > 128 || hq < G) {
-                            const int li = key / RPI;               // load index of the key
-                            sm_ph[wid][li / 2][key % RPI][hq][li % 2] =
-                                __builtin_bit_cast(uint16_t, ph);
-                        }
-                    } else {
-                        const float pr = fast_exp2(sv[kg][i] - m_new);
-                        psum += pr;
-                        sm_p[wid][key][hq] = pr;
-                    }
-                }
-            }
-            l1 = l1 * alpha + psum;
-            if (lane < G) sm_al[wid][lane] = alpha;
-            // P.V on the VALU, V rows in their loaded layout: the rescale
-            // factors and the probabilities come back from LDS; the rescale
-            // is skipped when no head's max moved (a multiply by one)
-            float al[G];
-            bool moved = false;
-#pragma unroll
-            for (int hh = 0; hh < G; hh += 4) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm_al[wid][hh]);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    al[hh + u] = a4[u];
-                    moved = moved || a4[u] != 1.f;
-                }
-            }
-            if (moved) {
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= al[hh];
-                }
-            }
-            if constexpr (PV16) {
-                // two keys per v_dot2_f32_f16: the values of loads 2 j and
-                // 2 j + 1 at one dim as an fp16 pair (fp8 codes converted
-                // exactly), the probabilities of the same two keys likewise
-                typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-                for (int jp = 0; jp < NL / 2; ++jp) {
-                    uint32_t pw[G];
-#pragma unroll
-                    for (int hh = 0; hh < G; hh += 4) {
-                        const u32x4 pp = *reinterpret_cast<const u32x4*>(&sm_ph[wid][jp][r][hh][0]);
-                        pw[hh] = pp.x; pw[hh + 1] = pp.y; pw[hh + 2] = pp.z; pw[hh + 3] = pp.w;
-                    }
-                    uint32_t vp[EPC];
-                    if constexpr (DT == kFP8) {
-                        const uint32_t a[2] = {vt[2 * jp].x, vt[2 * jp].y};
-                        const uint32_t bq[2] = {vt[2 * jp + 1].x, vt[2 * jp + 1].y};
-#pragma unroll
-                        for (int w = 0; w < 2; ++w) {
-                            const uint32_t x = __builtin_amdgcn_perm(bq[w], a[w], 0x05010400u);
-                            const uint32_t y = __builtin_amdgcn_perm(bq[w], a[w], 0x07030602u);
-                            vp[4 * w + 0] = fp8x2_to_f16x2(x, false);
-                            vp[4 * w + 1] = fp8x2_to_f16x2(x, true);
-                            vp[4 * w + 2] = fp8x2_to_f16x2(y, false);
-                            vp[4 * w + 3] = fp8x2_to_f16x2(y, true);
-                        }
-                    } else {
-                        const uint32_t a[4] = {vt[2 * jp].x, vt[2 * jp].y, vt[2 * jp].z, vt[2 * jp].w};
-                        const uint32_t bq[4] = {vt[2 * jp + 1].x, vt[2 * jp + 1].y,
-                                                vt[2 * jp + 1].z, vt[2 * jp + 1].w};
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            vp[2 * w] = __builtin_amdgcn_perm(bq[w], a[w], 0x05040100u);
-                            vp[2 * w + 1] = __builtin_amdgcn_perm(bq[w], a[w], 0x07060302u);
+                    for (int i = 0; i < 4; ++i) {
+                        if constexpr (DT != kBF16) {
+                            const _Float16 ph = (_Float16)fast_exp2(sv[kg][i] - m_new + kPScale);
+                            psum += (float)ph;
+                            pb[kg][i] = __builtin_bit_cast(short, ph);
+                        } else {
+                            const float pr = fast_exp2(sv[kg][i] - m_new);
+                            psum += pr;
+                            const uint16_t hi = round_to_elt<kBF16>(pr);
+                            pb[kg][i] = (short)hi;
+                            pbl[kg][i] = (short)round_to_elt<kBF16>(pr - elt_to_f32<kBF16>(hi));
                         }
                     }
+                }
+                l1 = l1 * alpha + psum;
+                // rescale this lane's head (skipped when no head's max moved)
+                if (__any(alpha != 1.f)) {
 #pragma unroll
-                    for (int hh = 0; hh < G; ++hh) {
+                    for (int m = 0; m < D / 16; ++m) pv_acc[m] *= alpha;
+                }
+                // V to the wave's LDS rows, where its K was (this wave has
+                // read them; its LDS accesses complete in order), fp8 codes
+                // as exact fp16
 #pragma unroll
-                        for (int e = 0; e < EPC; ++e)
-                            o_acc[hh][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, vp[e]),
-                                                                  __builtin_bit_cast(h16x2, pw[hh]),
-                                                                  o_acc[hh][e], false);
+                for (int i = 0; i < NL; ++i) {
+                    if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_f16x8(vt[i]);
+                    else sm_k[wid][i * RPI + r][c] = vt[i];
+                }
+                // one V tile in flight: the next one into the registers just
+                // staged (rows clamped past the last item, as for K)
+                if constexpr (VS1) load_tile(kA, vA, j + 1);
+                // A operand V^T (16 dims x 16 keys): lane l needs keys
+                // 4 (l / 16) + j of dim l % 16; the transposing LDS read hands
+                // lane i of each 16-lane group element i of the four rows its
+                // lanes 4 j .. 4 j + 3 point at (16 consecutive dims of key
+                // 4 (l / 16) + j)
+                const uint16_t* vrow0 = reinterpret_cast<const uint16_t*>(
+                    &sm_k[wid][4 * kq + ((lane & 15) >> 2)][0]) + 4 * (lane & 3);
+#pragma unroll
+                for (int kg = 0; kg < NG; ++kg) {
+                    const uint16_t* vrow = vrow0 + kg * 16 * (KPAD * 8);
+#pragma unroll
+                    for (int m = 0; m < D / 16; ++m) {
+                        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4*)(vrow + 16 * m));
+                        if constexpr (DT == kBF16) {
+                            pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kg], pv_acc[m], 0, 0, 0);
+                            pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbl[kg], pv_acc[m], 0, 0, 0);
+                        } else {
+                            pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                                __builtin_bit_cast(h16x4, va), __builtin_bit_cast(h16x4, pb[kg]),
+                                pv_acc[m], 0, 0, 0);
+                        }
                     }
                 }
             } else {
-#pragma unroll
-                for (int i = 0; i < NL; ++i) {
-                    const f32x4 pv = *reinterpret_cast<const f32x4*>(&sm_p[wid][i * RPI + r][0]);
-                    float vf[EPC];
-                    unpack_chunk<DT>(vt[i], vf);
-#pragma unroll
+                // probabilities to LDS: float per (key, head) for bf16 caches;
+                // fp8 and f16 caches: fp16, paired by load index (loads 2 j and
+                // 2 j + 1 of a lane hold the same dims of two keys), so one
+                // 16-byte read gives a lane the four heads' pairs for its row.
+                // The fp16 ones carry a factor 2^kPScale (added to the exponent,
+                // undone exactly at the chunk end), so a probability only falls
+                // into fp16's subnormal range below 2^-29, and the running sum
+                // adds the same rounded values the value product multiplies.
+                constexpr bool PV16 = DT != kBF16;
+                float psum = 0.f;
+    #pragma unroll
+                for (int kg = 0; kg < NG; ++kg) {
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = kg * 16 + 4 * kq + i;          // within the tile
+                        if constexpr (PV16) {
+                            const _Float16 ph = (_Float16)fast_exp2(sv[kg][i] - m_new + kPScale);
+                            psum += (float)ph;
+                            // (the 8-head 128-dim kernel keeps the branch: without
+                            // it that instance needs more registers than it has)
+                            if (G < 8 || D > 128 || hq < G) {
+                                const int li = key / RPI;               // load index of the key
+                                sm_ph[wid][li / 2][key % RPI][hq][li % 2] =
+                                    __builtin_bit_cast(uint16_t, ph);
+                            }
+                        } else {
+                            const float pr = fast_exp2(sv[kg][i] - m_new);
+                            psum += pr;
+                            sm_p[wid][key][hq] = pr;
+                        }
+                    }
+                }
+                l1 = l1 * alpha + psum;
+                if (lane < G) sm_al[wid][lane] = alpha;
+                // P.V on the VALU, V rows in their loaded layout: the rescale
+                // factors and the probabilities come back from LDS; the rescale
+                // is skipped when no head's max moved (a multiply by one)
+                float al[G];
+                bool moved = false;
+    #pragma unroll
+                for (int hh = 0; hh < G; hh += 4) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm_al[wid][hh]);
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        al[hh + u] = a4[u];
+                        moved = moved || a4[u] != 1.f;
+                    }
+                }
+                if (moved) {
+    #pragma unroll
                     for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-                        for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pv[hh], vf[e], o_acc[hh][e]);
+    #pragma unroll
+                        for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= al[hh];
+                    }
+                }
+                if constexpr (PV16) {
+                    // two keys per v_dot2_f32_f16: the values of loads 2 j and
+                    // 2 j + 1 at one dim as an fp16 pair (fp8 codes converted
+                    // exactly), the probabilities of the same two keys likewise
+                    typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+    #pragma unroll
+                    for (int jp = 0; jp < NL / 2; ++jp) {
+                        uint32_t pw[G];
+    #pragma unroll
+                        for (int hh = 0; hh < G; hh += 4) {
+                            const u32x4 pp = *reinterpret_cast<const u32x4*>(&sm_ph[wid][jp][r][hh][0]);
+                            pw[hh] = pp.x; pw[hh + 1] = pp.y; pw[hh + 2] = pp.z; pw[hh + 3] = pp.w;
+                        }
+                        uint32_t vp[EPC];
+                        if constexpr (DT == kFP8) {
+                            const uint32_t a[2] = {vt[2 * jp].x, vt[2 * jp].y};
+                            const uint32_t bq[2] = {vt[2 * jp + 1].x, vt[2 * jp + 1].y};
+    #pragma unroll
+                            for (int w = 0; w < 2; ++w) {
+                                const uint32_t x = __builtin_amdgcn_perm(bq[w], a[w], 0x05010400u);
+                                const uint32_t y = __builtin_amdgcn_perm(bq[w], a[w], 0x07030602u);
+                                vp[4 * w + 0] = fp8x2_to_f16x2(x, false);
+                                vp[4 * w + 1] = fp8x2_to_f16x2(x, true);
+                                vp[4 * w + 2] = fp8x2_to_f16x2(y, false);
+                                vp[4 * w + 3] = fp8x2_to_f16x2(y, true);
+                            }
+                        } else {
+                            const uint32_t a[4] = {vt[2 * jp].x, vt[2 * jp].y, vt[2 * jp].z, vt[2 * jp].w};
+                            const uint32_t bq[4] = {vt[2 * jp + 1].x, vt[2 * jp + 1].y,
+                                                    vt[2 * jp + 1].z, vt[2 * jp + 1].w};
+    #pragma unroll
+                            for (int w = 0; w < 4; ++w) {
+                                vp[2 * w] = __builtin_amdgcn_perm(bq[w], a[w], 0x05040100u);
+                                vp[2 * w + 1] = __builtin_amdgcn_perm(bq[w], a[w], 0x07060302u);
+                            }
+                        }
+    #pragma unroll
+                        for (int hh = 0; hh < G; ++hh) {
+    #pragma unroll
+                            for (int e = 0; e < EPC; ++e)
+                                o_acc[hh][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, vp[e]),
+                                                                      __builtin_bit_cast(h16x2, pw[hh]),
+                                                                      o_acc[hh][e], false);
+                        }
+                    }
+                } else {
+    #pragma unroll
+                    for (int i = 0; i < NL; ++i) {
+                        const f32x4 pv = *reinterpret_cast<const f32x4*>(&sm_p[wid][i * RPI + r][0]);
+                        float vf[EPC];
+                        unpack_chunk<DT>(vt[i], vf);
+    #pragma unroll
+                        for (int hh = 0; hh < G; ++hh) {
+    #pragma unroll
+                            for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pv[hh], vf[e], o_acc[hh][e]);
+                        }
                     }
                 }
             }
@@ -817,14 +908,15 @@ void attn_kernel(AttnParams P) {
     // per chunk.
     int n_st = 0, st_first = 0, n_flush = 0;
 
-    auto flush = [&]() __attribute__((always_inline)) {
-        const int buf = n_flush % NB;
-        ++n_flush;
+    // Heads h0 .. h0 + GO - 1 of the stashed chunks (every head, but for the
+    // 8-head kernel over 16-bit caches, which flushes two halves per chunk).
+    auto flush_heads = [&](int buf, int h0) __attribute__((always_inline)) {
         __syncthreads();
         for (int s = 0; s < n_st; ++s) {
             const int ch = st_first + s;
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
+            for (int ho = 0; ho < GO; ++ho) {
+                const int hh = h0 + ho;
                 const float Mc = lds_max<kAttnWaves>(sm_m[buf][s][hh]);
                 float Lc = 0.f, Oc = 0.f;
                 if (Mc != -INFINITY) {
@@ -832,7 +924,7 @@ void attn_kernel(AttnParams P) {
                     for (int w = 0; w < kAttnWaves; ++w) {
                         const float a = fast_exp2(sm_m[buf][s][hh][w] - Mc);
                         Lc = fmaf(sm_l[buf][s][hh][w], a, Lc);
-                        if (t < D) Oc = fmaf(sm_o[buf][s][hh][w][t], a, Oc);
+                        if (t < D) Oc = fmaf(sm_o[buf][s][ho][w][t], a, Oc);
                     }
                 }
                 const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
@@ -868,10 +960,15 @@ void attn_kernel(AttnParams P) {
                 }
             }
         }
-        n_st = 0;
         // a single flush buffer: every thread has read it before any wave
-        // writes its next chunk's partial there
+        // writes its next chunk's partial (or next heads) there
         if constexpr (NB == 1) __syncthreads();
+    };
+    auto flush = [&]() __attribute__((always_inline)) {
+        const int buf = n_flush % NB;
+        ++n_flush;
+        flush_heads(buf, G - GO);
+        n_st = 0;
     };
 
     auto end_chunk = [&](int ch) __attribute__((always_inline)) {
@@ -881,8 +978,42 @@ void attn_kernel(AttnParams P) {
             for (int hh = 0; hh < G; ++hh) l_w[hh] = wave_sum(l_lane[hh]);
         }
         const int buf = n_flush % NB;
+        if constexpr (MFPV) {
+            // the running max and sum first (the flushes below read them);
+            // head (lane % 16): its max is already the same in its 4 lanes,
+            // its sum adds the 4 lanes' shares
+            const float lw = xor_sum<32>(xor_sum<16>(l1)) * kPUnscale;
+            if (lane < G) {
+                sm_m[buf][n_st][lane][wid] = m1;
+                sm_l[buf][n_st][lane][wid] = lw;
+            }
+            m1 = -INFINITY;
+            l1 = 0.f;
+            if (n_st == 0) st_first = ch;
+            // O^T from the matrix cores: the lanes of the group's heads write
+            // their dims 16 m + 4 (l / 16) + 0..3 (already summed over this
+            // wave's keys), GO heads at a time; all but the last GO heads are
+            // flushed here
+            const int hq = lane & 15, kq = lane >> 4;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
+            for (int h0 = 0; h0 < G; h0 += GO) {
+                if (hq >= h0 && hq < h0 + GO) {
+#pragma unroll
+                    for (int m = 0; m < D / 16; ++m)
+                        *reinterpret_cast<pv4*>(&sm_o[buf][n_st][hq - h0][wid][16 * m + 4 * kq]) =
+                            pv_acc[m] * kPUnscale;
+                }
+                if (h0 + GO < G) {
+                    ++n_st;
+                    flush_heads(buf, h0);
+                    --n_st;
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int hh = 0; hh < (MFPV ? 0 : G); ++hh) {
             // head by head: sum over the lanes that share this lane's dims,
             // then store, so only one head's exchanges are live at a time
 #pragma unroll
@@ -905,7 +1036,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) o_acc[hh][e] = 0.f;
         }
-        if constexpr (MF) {
+        if constexpr (MF && !MFPV) {
             // head (lane % 16): its max is already the same in its 4 lanes;
             // its sum adds the 4 lanes' shares
             const float lw = xor_sum<32>(xor_sum<16>(l1)) * kPUnscale;
@@ -916,7 +1047,7 @@ void attn_kernel(AttnParams P) {
             m1 = -INFINITY;
             l1 = 0.f;
         }
-        if (n_st == 0) st_first = ch;
+        if (!MFPV && n_st == 0) st_first = ch;
         ++n_st;
         if (n_st == kStash) flush();
     };
@@ -1025,31 +1156,39 @@ void attn_kernel(AttnParams P) {
     // buffer is refilled as soon as it has been scored.  The loop body's
     // loads are unconditional (j + 3 < n_items), so its wait counts keep the
     // other buffer in flight.
-    int j = 0;
-    for (; j + 3 < n_items; j += 2) {
-        compute_tile(kA, vA, j);
-        after(j);
-        load_tile(kA, vA, j + 2);
-        compute_tile(kB, vB, j + 1);
-        after(j + 1);
-        load_tile(kB, vB, j + 3);
-    }
-    if (j + 2 < n_items) {
-        compute_tile(kA, vA, j);
-        after(j);
-        load_tile(kA, vA, j + 2);
-        compute_tile(kB, vB, j + 1);
-        after(j + 1);
-        compute_tile(kA, vA, j + 2);
-        after(j + 2);
-    } else if (j + 1 < n_items) {
-        compute_tile(kA, vA, j);
-        after(j);
-        compute_tile(kB, vB, j + 1);
-        after(j + 1);
-    } else if (j < n_items) {
-        compute_tile(kA, vA, j);
-        after(j);
+    if constexpr (VS1) {
+        // one buffer: each tile requests the next one's K and V itself
+        for (int j = 0; j < n_items; ++j) {
+            compute_tile(kA, vA, j);
+            after(j);
+        }
+    } else {
+        int j = 0;
+        for (; j + 3 < n_items; j += 2) {
+            compute_tile(kA, vA, j);
+            after(j);
+            load_tile(kA, vA, j + 2);
+            compute_tile(kB, vB, j + 1);
+            after(j + 1);
+            load_tile(kB, vB, j + 3);
+        }
+        if (j + 2 < n_items) {
+            compute_tile(kA, vA, j);
+            after(j);
+            load_tile(kA, vA, j + 2);
+            compute_tile(kB, vB, j + 1);
+            after(j + 1);
+            compute_tile(kA, vA, j + 2);
+            after(j + 2);
+        } else if (j + 1 < n_items) {
+            compute_tile(kA, vA, j);
+            after(j);
+            compute_tile(kB, vB, j + 1);
+            after(j + 1);
+        } else if (j < n_items) {
+            compute_tile(kA, vA, j);
+            after(j);
+        }
     }
     if (c_valid > c_full) end_chunk(c_full);            // the partly valid chunk
     if (n_st > 0) flush();

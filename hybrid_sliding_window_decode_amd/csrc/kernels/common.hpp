@@ -187,6 +187,13 @@ __device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w, bool hi) {
               : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
 }
 
+// Eight fp8 codes (a lane's chunk of a grouped kernel's row) as eight fp16
+// values, in element order; exact, since every e4m3 value is an fp16 value.
+__device__ __forceinline__ u32x4 fp8x8_to_f16x8(const u32x2& w) {
+    return u32x4{fp8x2_to_f16x2(w.x, false), fp8x2_to_f16x2(w.x, true),
+                 fp8x2_to_f16x2(w.y, false), fp8x2_to_f16x2(w.y, true)};
+}
+
 // Unpack one 8-byte chunk of fp8 codes into 8 floats, in byte order.
 template <int DT>
 __device__ __forceinline__ void unpack_chunk(const u32x2& w, float* f) {

@@ -104,14 +104,13 @@ typedef struct {
                                the query [talker]); the attention entries take
                                H / Hkv = 1 with any cache, and any H / Hkv > 1
                                with a 16-bit or fp8 cache and head_dim 128 or 256
-                               (else UNSUPPORTED).  Groups of 2 and 4 (and 5
-                               to 8 over an fp8 cache) read the cache once per
-                               layer, a group below a kernel's size leaving
-                               heads idle; a larger group is split into pieces
-                               of four query heads (fp8: eight), one workgroup
-                               per piece in the same launch, each reading the
-                               cache (the last piece to finish writes the new
-                               entry). */
+                               (else UNSUPPORTED).  Groups of 2 to 8 read the
+                               cache once per layer (kernels for 2, 4 and 8
+                               heads, a group below a kernel's size leaving
+                               heads idle); a larger group is split into pieces
+                               of eight query heads, one workgroup per piece in
+                               the same launch, each reading the cache (the
+                               last piece to finish writes the new entry). */
     int32_t head_dim;       /* D: 64, 128 or 256 (fp8 caches: 128 or 256) */
     int32_t n_slots;        /* ring: slots (window - 1, 511 [join]); append: capacity rows.
                                The attention entries take n_slots * head_dim *

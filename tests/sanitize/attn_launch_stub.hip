@@ -15,7 +15,6 @@ HSWD_STUB_GROUP(1, false)
 HSWD_STUB_GROUP(2, false)
 HSWD_STUB_GROUP(4, false)
 HSWD_STUB_GROUP(8, false)
-HSWD_STUB_GROUP(4, true)
 HSWD_STUB_GROUP(8, true)
 #undef HSWD_STUB_GROUP
 }  // namespace hswd

@@ -89,6 +89,6 @@ def _case(dtype, H, values):
 
 
 @pytest.mark.parametrize("values", ["constant", "alternating"])
-@pytest.mark.parametrize("dtype,H", [("f16", 32), ("fp8", 32), ("fp8", 64)])
+@pytest.mark.parametrize("dtype,H", [("f16", 32), ("f16", 64), ("fp8", 32), ("fp8", 64)])
 def test_dominant_keys_with_tiny_probabilities_131072(dtype, H, values):
     _case(dtype, H, values)

@@ -161,8 +161,8 @@ def test_grouped_step_layers_64x4096(dtype):
 
 
 def test_grouped_step_layers_64x4096_h64():
-    """64 query heads over 8 kv heads: bf16 in two 4-head pieces per group,
-    fp8 in one 8-head kernel."""
+    """64 query heads over 8 kv heads: the 8-head kernel (one workgroup
+    per group, the value product on the matrix cores), bf16 and fp8."""
     check_layer(inputs.full_spec(64, 4097, "bf16", H=64), 4096, 4300)
     check_layer(inputs.full_spec(64, 4097, "fp8", H=64), 4096, 4301)
 

@@ -47,15 +47,19 @@ def positions(kind, B, S, pos, seed):
     ("sliding", "fp8", 4, 256, 12, "ragged", None, 0),
     ("full", "fp8", 2, 128, 6, "ragged", 3000, 256),
     ("full", "fp8", 4, 256, 2, [19999, 9000], 20000, 0),
+    # bf16 at D = 128: the 4-head kernel's value product on the matrix cores
+    # with each probability split into two bf16 parts
+    ("full", "bf16", 4, 128, 3, [4000, 17, 2048], 4001, 0),
+    ("sliding", "bf16", 4, 128, 5, "ragged", None, 0),
 ])
 def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
     check_layer_step(kind, dtype, G, D, B, pos, S, kps)
 
 
 # Groups without a kernel of their own: 3 runs the 4-head kernel with one
-# head idle; 5, 6, 8 and 16 run it once per four heads (the last launch
-# writes the entry), including a cross-workgroup merge and a partial last
-# group of one and two heads.
+# head idle, 5 to 7 the 8-head kernel with heads idle; 16 runs the 8-head
+# kernel in two pieces (one workgroup each, the last to finish writes the
+# entry); with cross-workgroup merges, 128 and 256 dims, every cache type.
 @pytest.mark.parametrize("kind,dtype,G,D,B,pos,S,kps,H", [
     ("sliding", "bf16", 3, 256, 6, "ragged", None, 0, 12),
     ("full", "f16", 3, 128, 3, [1024, 1, 2999], 3000, 256, 24),
@@ -64,15 +68,21 @@ def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
     ("full", "fp8", 6, 256, 3, [2999, 0, 1500], 3000, 0, 24),
     ("full", "bf16", 5, 256, 2, [19999, 7001], 20000, 0, 10),
     ("sliding", "f16", 16, 128, 4, "ragged", None, 0, 32),
-    # fp8: the 8-head kernel (one launch for 5 to 8 heads, heads idle below
-    # 8; two launches of eight for 16), cross-workgroup merge, D = 128
     ("full", "fp8", 8, 256, 2, [19999, 7001], 20000, 0, 16),
     ("full", "fp8", 8, 128, 4, "ragged", 3000, 0, 64),
     ("sliding", "fp8", 16, 256, 4, "ragged", None, 0, 32),
     ("full", "fp8", 5, 256, 3, [2999, 1, 1500], 3000, 0, 10),
-    # long chunks, ragged last chunk: 4-head matrix-core and 8-head fp8 kernels
+    # the 8-head kernel over 16-bit caches: 128 dims (two V tiles in
+    # flight), 256 dims (one), merges across workgroups, pieces of 16
+    ("full", "f16", 8, 128, 3, [4000, 17, 2048], 4001, 0, 64),
+    ("sliding", "bf16", 7, 128, 5, "ragged", None, 0, 56),
+    ("full", "bf16", 8, 256, 2, [19999, 7001], 20000, 0, 64),
+    ("full", "f16", 16, 256, 2, [6000, 4097], 6001, 0, 32),
+    ("sliding", "bf16", 16, 256, 3, "ragged", None, 0, 64),
+    # long chunks, ragged last chunk: the 4- and 8-head kernels
     ("full", "bf16", 4, 256, 2, [9000, 4097], 9001, 4096, 32),
     ("full", "fp8", 8, 256, 2, [9000, 2049], 9001, 4096, 64),
+    ("full", "bf16", 8, 256, 2, [9000, 2049], 9001, 4096, 64),
 ])
 def test_gqa_large_groups(kind, dtype, G, D, B, pos, S, kps, H):
     check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=H)
@@ -88,7 +98,11 @@ def test_gqa_large_groups(kind, dtype, G, D, B, pos, S, kps, H):
     ("full", "bf16", 1, 256, 2, [19999, 7001], 20000, 0),
     ("sliding", "fp8", 4, 256, 8, "ragged", None, 0),
     ("full", "bf16", 4, 256, 4, "ragged", 3000, 0),
+    ("full", "bf16", 8, 256, 3, "ragged", 3000, 0),
+    ("sliding", "fp8", 8, 256, 4, "ragged", None, 0),
     ("full", "f16", 2, 128, 4, "ragged", 3000, 256),
+    ("full", "bf16", 4, 128, 3, "ragged", 3000, 0),
+    ("full", "f16", 4, 128, 3, "ragged", 3000, 0),
 ])
 def test_sharp_softmax(kind, dtype, G, D, B, pos, S, kps):
     check_layer_step(kind, dtype, G, D, B, pos, S, kps, q_mult=20.0)
@@ -147,9 +161,9 @@ def check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=8, q_mult=1.0):
 # must land before the next step reads it.  Sliding rings are full (the
 # overwritten slot is still in the window when it is read).
 @pytest.mark.parametrize("kind,dtype,G,D,B,pos,S,kps,H", [
-    ("sliding", "bf16", 8, 256, 8, "ragged", None, 0, 64),
+    ("sliding", "bf16", 16, 256, 8, "ragged", None, 0, 64),
     ("sliding", "fp8", 16, 256, 3, [600, 511, 4000], None, 0, 32),
-    ("full", "f16", 8, 128, 3, [2500, 3, 1200], 3000, 256, 16),
+    ("full", "f16", 16, 128, 3, [2500, 3, 1200], 3000, 256, 32),
     ("full", "fp8", 16, 256, 2, [2996, 40], 3000, 512, 32),
 ])
 def test_gqa_pieces_consecutive_steps(kind, dtype, G, D, B, pos, S, kps, H):

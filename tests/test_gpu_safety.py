@@ -94,7 +94,9 @@ def test_canaries_around_every_buffer(noalloc):
     # cross-workgroup merges: few streams, long append caches
     _guarded_step(inputs.full_spec(3, 9001, "f16"), [9000, 4097, 1], 82, noalloc)
     # a group split into head pieces (entry arrival counters)
-    _guarded_step(inputs.full_spec(2, 4097, "bf16", H=64), [4096, 3000], 83, noalloc)
+    _guarded_step(inputs.full_spec(2, 4097, "bf16", H=128), [4096, 3000], 83, noalloc)
+    # the 8-head kernel over a 16-bit cache (partials flushed in two halves)
+    _guarded_step(inputs.full_spec(2, 9001, "bf16", H=64), [9000, 4097], 86, noalloc)
     # fp8 with per-head scales, 4-head matrix-core kernel, ring
     _guarded_step(inputs.sliding_spec(2, "fp8", H=32), [600, 7], 84, noalloc)
     # f32 ring, one stream

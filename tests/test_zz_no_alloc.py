@@ -54,9 +54,9 @@ def test_noalloc_equals_layer_step_on_calls_in_a_row():
     assert _compare(big, [20000, 19000, 7777, 20000], 71) == 0
     # 2: smaller, 2 streams near 9000: other chunks, other partial offsets
     assert _compare(inputs.full_spec(2, 9001, "bf16"), [9000, 8191], 72) == 0
-    # 3: smaller again, 64 query heads over 8 kv heads in two pieces per
-    #    group (entry-write arrival counters)
-    assert _compare(inputs.full_spec(1, 4097, "bf16", H=64), [4096], 73) == 0
+    # 3: smaller again, 128 query heads over 8 kv heads in two pieces of
+    #    eight per group (entry-write arrival counters)
+    assert _compare(inputs.full_spec(1, 4097, "bf16", H=128), [4096], 73) == 0
     # 4: a ring, f32, one stream
     assert _compare(inputs.sliding_spec(1, "f32"), [600], 74) == 0
     # 5: error flags through the caller's word: a stream past the grid's
