@@ -122,10 +122,10 @@ struct AttnParams {
     int auto_k, k_floor;
 };
 
-// Scores on the matrix cores: 4 query heads per kv head over a 16-bit or
-// fp8 cache, or 8 over an fp8 cache (the score product is then a [G x D] .
-// [D x keys] contraction; fp8 keys become bf16, which holds every e4m3 value
-// exactly).
+// Matrix-core kernels: 4 or 8 query heads per kv head over a 16-bit or fp8
+// cache.  The score product is then a [G x D] . [D x keys] contraction (fp8
+// keys become bf16, which holds every e4m3 value exactly) and the value
+// product a [D x keys] . [keys x G] one (fp8 values become fp16, exact too).
 template <int DT, int G>
 constexpr bool use_mfma() {
     return (G == 4 || G == 8) && (DT == kBF16 || DT == kF16 || DT == kFP8);
@@ -277,32 +277,28 @@ void attn_kernel(AttnParams P) {
     constexpr int NB = flush_buffers<G>();
 
     constexpr bool MF = use_mfma<DT, G>();
-    // The value product on the matrix cores too: V goes through the wave's
-    // LDS rows after its K, the probabilities stay in the registers the score
-    // product left them in.  Its accumulators (D / 16 x 4 per lane) cost the
-    // same for 4 and 8 heads; they fit beside two V tiles in flight for the
-    // 4-head kernel at 128 dims or over fp8 and the 8-head kernel at 128
-    // dims, and beside one (VS1: V of the next tile requested once this
-    // tile's is in LDS) for the 8-head kernel at 256 dims.  The 4-head kernel
-    // over 16-bit caches at 256 dims keeps the value product on the VALU.
-    constexpr bool MFPV = MF && ((G == 4 && (D <= 128 || DT == kFP8)) || G == 8);
-    constexpr bool VS1 = MFPV && G == 8 && D == 256;
+    // The matrix-core kernels take the value product on the matrix cores
+    // too: V goes through the wave's LDS rows after its K, the probabilities
+    // stay in the registers the score product left them in.  Its
+    // accumulators (D / 16 x 4 per lane) cost the same for 4 and 8 heads;
+    // they fit beside two V tiles in flight at 128 dims and for the 4-head
+    // kernel over fp8, and beside one (VS1: V of the next tile requested
+    // once this tile's is in LDS) otherwise.
+    constexpr bool VS1 = MF && D == 256 && (G == 8 || DT != kFP8);
     // heads per flush of the wave partials: at 256 dims the 8-head kernel
     // flushes its heads in two halves, so its partials take 16 KiB (LDS for
     // two workgroups per CU)
-    constexpr int GO = MFPV && G == 8 && D == 256 ? 4 : G;
+    constexpr int GO = MF && G == 8 && D == 256 ? 4 : G;
     static_assert(GO == G || kStash == 1, "split flush: one chunk per flush");
     // fp16 probabilities of the matrix-core kernels over f16 / fp8 caches
     // are scaled by 2^kPScale; a wave's chunk partial (sum and values) is
     // scaled back by kPUnscale, a power of two, when the chunk ends
     constexpr float kPScale = MF && DT != kBF16 ? 15.f : 0.f;
     constexpr float kPUnscale = MF && DT != kBF16 ? 0x1p-15f : 1.f;
-    // MFMA kernel: each wave stages its K rows in LDS (rows padded by 16
-    // bytes so the 16 rows an operand read touches fall in distinct banks;
-    // fp8 keys as exact bf16), the query heads sit there as 16-bit hi + lo
-    // parts, and, where the value product stays on the VALU, the
-    // probabilities and rescale factors pass from the score layout (a key
-    // per lane group, a head per lane) to the value layout through LDS.
+    // MFMA kernel: each wave stages its K rows (then its V rows) in LDS
+    // (rows padded by 16 bytes so the 16 rows an operand read touches fall
+    // in distinct banks; fp8 keys as exact bf16, fp8 values as exact fp16),
+    // and the query heads sit there as 16-bit hi + lo parts.
     constexpr int KPAD = D * 2 / 16 + 1;                  // 16-byte units per staged (16-bit) row
     __shared__ float sm_q[MF ? 1 : G][D];
     __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT : 1][MF ? KPAD : 1];
@@ -311,12 +307,6 @@ void attn_kernel(AttnParams P) {
     __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G + 1 : 1][MF ? D + 8 : 1];
     __shared__ __attribute__((aligned(16))) uint16_t sm_ql[MF ? G + 1 : 1][MF ? D + 8 : 1];
     // (both read 16 bytes at a time: aligned to 16)
-    // (a column per score-product column: lanes of idle heads write unused
-    // columns rather than branch around the store)
-    constexpr bool PLDS = MF && !MFPV;                    // probabilities through LDS
-    __shared__ __attribute__((aligned(16))) float sm_p[PLDS && DT == kBF16 ? kAttnWaves : 1][PLDS ? KT : 1][16];
-    __shared__ __attribute__((aligned(16))) uint16_t sm_ph[PLDS && DT != kBF16 ? kAttnWaves : 1][PLDS ? NL / 2 : 1][RPI][PLDS ? 16 : 1][2];
-    __shared__ __attribute__((aligned(16))) float sm_al[PLDS ? kAttnWaves : 1][G];
     __shared__ __attribute__((aligned(16))) float sm_o[NB][kStash][GO][kAttnWaves][D];   // wave chunk partials, by flush parity
     __shared__ float sm_m[NB][kStash][G][kAttnWaves], sm_l[NB][kStash][G][kAttnWaves];
     __shared__ float sm_dot[G][kAttnWaves];
@@ -408,9 +398,9 @@ void attn_kernel(AttnParams P) {
     // value product on the matrix cores: O^T (16 dims x 16 heads) per group
     // of 16 dims; lane l holds dims 4 (l / 16) + i of the group, head l % 16
     typedef float pv4 __attribute__((ext_vector_type(4)));
-    pv4 pv_acc[MFPV ? D / 16 : 1];
+    pv4 pv_acc[MF ? D / 16 : 1];
 #pragma unroll
-    for (int m = 0; m < (MFPV ? D / 16 : 1); ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < (MF ? D / 16 : 1); ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
     Fold run[G];                    // folded chunk partials (wpp == 1)
 
     using Chunk = typename ChunkT<Geo::CB>::type;
@@ -653,188 +643,72 @@ void attn_kernel(AttnParams P) {
             const float m_new = fmaxf(m1, mx);
             const float alpha = fast_exp2(m1 - m_new);
             m1 = m_new;
-            if constexpr (MFPV) {
-                // The probabilities are the B operand of P.V as they stand:
-                // lane l holds keys 4 (l / 16) + i of head l % 16, the
-                // operand's k and column.  f16 / fp8 caches: fp16 weights
-                // (times 2^kPScale, undone at the chunk end), the running sum
-                // over the same rounded values; bf16 caches: the weight as a
-                // bf16 hi part plus a bf16 lo part (about 16 significant
-                // bits), the running sum over the float weights.
-                typedef short s16x4 __attribute__((ext_vector_type(4)));
-                typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
-                s16x4 pb[NG], pbl[NG];
-                float psum = 0.f;
+            // The probabilities are the B operand of P.V as they stand:
+            // lane l holds keys 4 (l / 16) + i of head l % 16, the
+            // operand's k and column.  f16 / fp8 caches: fp16 weights
+            // (times 2^kPScale, undone at the chunk end), the running sum
+            // over the same rounded values; bf16 caches: the weight as a
+            // bf16 hi part plus a bf16 lo part (about 16 significant
+            // bits), the running sum over the float weights.
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+            s16x4 pb[NG], pbl[NG];
+            float psum = 0.f;
 #pragma unroll
-                for (int kg = 0; kg < NG; ++kg) {
+            for (int kg = 0; kg < NG; ++kg) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if constexpr (DT != kBF16) {
-                            const _Float16 ph = (_Float16)fast_exp2(sv[kg][i] - m_new + kPScale);
-                            psum += (float)ph;
-                            pb[kg][i] = __builtin_bit_cast(short, ph);
-                        } else {
-                            const float pr = fast_exp2(sv[kg][i] - m_new);
-                            psum += pr;
-                            const uint16_t hi = round_to_elt<kBF16>(pr);
-                            pb[kg][i] = (short)hi;
-                            pbl[kg][i] = (short)round_to_elt<kBF16>(pr - elt_to_f32<kBF16>(hi));
-                        }
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (DT != kBF16) {
+                        const _Float16 ph = (_Float16)fast_exp2(sv[kg][i] - m_new + kPScale);
+                        psum += (float)ph;
+                        pb[kg][i] = __builtin_bit_cast(short, ph);
+                    } else {
+                        const float pr = fast_exp2(sv[kg][i] - m_new);
+                        psum += pr;
+                        const uint16_t hi = round_to_elt<kBF16>(pr);
+                        pb[kg][i] = (short)hi;
+                        pbl[kg][i] = (short)round_to_elt<kBF16>(pr - elt_to_f32<kBF16>(hi));
                     }
                 }
-                l1 = l1 * alpha + psum;
-                // rescale this lane's head (skipped when no head's max moved)
-                if (__any(alpha != 1.f)) {
+            }
+            l1 = l1 * alpha + psum;
+            // rescale this lane's head (skipped when no head's max moved)
+            if (__any(alpha != 1.f)) {
 #pragma unroll
-                    for (int m = 0; m < D / 16; ++m) pv_acc[m] *= alpha;
-                }
-                // V to the wave's LDS rows, where its K was (this wave has
-                // read them; its LDS accesses complete in order), fp8 codes
-                // as exact fp16
+                for (int m = 0; m < D / 16; ++m) pv_acc[m] *= alpha;
+            }
+            // V to the wave's LDS rows, where its K was (this wave has
+            // read them; its LDS accesses complete in order), fp8 codes
+            // as exact fp16
 #pragma unroll
-                for (int i = 0; i < NL; ++i) {
-                    if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_f16x8(vt[i]);
-                    else sm_k[wid][i * RPI + r][c] = vt[i];
-                }
-                // one V tile in flight: the next one into the registers just
-                // staged (rows clamped past the last item, as for K)
-                if constexpr (VS1) load_tile(kA, vA, j + 1);
-                // A operand V^T (16 dims x 16 keys): lane l needs keys
-                // 4 (l / 16) + j of dim l % 16; the transposing LDS read hands
-                // lane i of each 16-lane group element i of the four rows its
-                // lanes 4 j .. 4 j + 3 point at (16 consecutive dims of key
-                // 4 (l / 16) + j)
-                const uint16_t* vrow0 = reinterpret_cast<const uint16_t*>(
-                    &sm_k[wid][4 * kq + ((lane & 15) >> 2)][0]) + 4 * (lane & 3);
+            for (int i = 0; i < NL; ++i) {
+                if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_f16x8(vt[i]);
+                else sm_k[wid][i * RPI + r][c] = vt[i];
+            }
+            // one V tile in flight: the next one into the registers just
+            // staged (rows clamped past the last item, as for K)
+            if constexpr (VS1) load_tile(kA, vA, j + 1);
+            // A operand V^T (16 dims x 16 keys): lane l needs keys
+            // 4 (l / 16) + j of dim l % 16; the transposing LDS read hands
+            // lane i of each 16-lane group element i of the four rows its
+            // lanes 4 j .. 4 j + 3 point at (16 consecutive dims of key
+            // 4 (l / 16) + j)
+            const uint16_t* vrow0 = reinterpret_cast<const uint16_t*>(
+                &sm_k[wid][4 * kq + ((lane & 15) >> 2)][0]) + 4 * (lane & 3);
 #pragma unroll
-                for (int kg = 0; kg < NG; ++kg) {
-                    const uint16_t* vrow = vrow0 + kg * 16 * (KPAD * 8);
+            for (int kg = 0; kg < NG; ++kg) {
+                const uint16_t* vrow = vrow0 + kg * 16 * (KPAD * 8);
 #pragma unroll
-                    for (int m = 0; m < D / 16; ++m) {
-                        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4*)(vrow + 16 * m));
-                        if constexpr (DT == kBF16) {
-                            pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kg], pv_acc[m], 0, 0, 0);
-                            pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbl[kg], pv_acc[m], 0, 0, 0);
-                        } else {
-                            pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                                __builtin_bit_cast(h16x4, va), __builtin_bit_cast(h16x4, pb[kg]),
-                                pv_acc[m], 0, 0, 0);
-                        }
-                    }
-                }
-            } else {
-                // probabilities to LDS: float per (key, head) for bf16 caches;
-                // fp8 and f16 caches: fp16, paired by load index (loads 2 j and
-                // 2 j + 1 of a lane hold the same dims of two keys), so one
-                // 16-byte read gives a lane the four heads' pairs for its row.
-                // The fp16 ones carry a factor 2^kPScale (added to the exponent,
-                // undone exactly at the chunk end), so a probability only falls
-                // into fp16's subnormal range below 2^-29, and the running sum
-                // adds the same rounded values the value product multiplies.
-                constexpr bool PV16 = DT != kBF16;
-                float psum = 0.f;
-    #pragma unroll
-                for (int kg = 0; kg < NG; ++kg) {
-    #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = kg * 16 + 4 * kq + i;          // within the tile
-                        if constexpr (PV16) {
-                            const _Float16 ph = (_Float16)fast_exp2(sv[kg][i] - m_new + kPScale);
-                            psum += (float)ph;
-                            // (the 8-head 128-dim kernel keeps the branch: without
-                            // it that instance needs more registers than it has)
-                            if (G < 8 || D > 128 || hq < G) {
-                                const int li = key / RPI;               // load index of the key
-                                sm_ph[wid][li / 2][key % RPI][hq][li % 2] =
-                                    __builtin_bit_cast(uint16_t, ph);
-                            }
-                        } else {
-                            const float pr = fast_exp2(sv[kg][i] - m_new);
-                            psum += pr;
-                            sm_p[wid][key][hq] = pr;
-                        }
-                    }
-                }
-                l1 = l1 * alpha + psum;
-                if (lane < G) sm_al[wid][lane] = alpha;
-                // P.V on the VALU, V rows in their loaded layout: the rescale
-                // factors and the probabilities come back from LDS; the rescale
-                // is skipped when no head's max moved (a multiply by one)
-                float al[G];
-                bool moved = false;
-    #pragma unroll
-                for (int hh = 0; hh < G; hh += 4) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm_al[wid][hh]);
-    #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        al[hh + u] = a4[u];
-                        moved = moved || a4[u] != 1.f;
-                    }
-                }
-                if (moved) {
-    #pragma unroll
-                    for (int hh = 0; hh < G; ++hh) {
-    #pragma unroll
-                        for (int e = 0; e < EPC; ++e) o_acc[hh][e] *= al[hh];
-                    }
-                }
-                if constexpr (PV16) {
-                    // two keys per v_dot2_f32_f16: the values of loads 2 j and
-                    // 2 j + 1 at one dim as an fp16 pair (fp8 codes converted
-                    // exactly), the probabilities of the same two keys likewise
-                    typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
-    #pragma unroll
-                    for (int jp = 0; jp < NL / 2; ++jp) {
-                        uint32_t pw[G];
-    #pragma unroll
-                        for (int hh = 0; hh < G; hh += 4) {
-                            const u32x4 pp = *reinterpret_cast<const u32x4*>(&sm_ph[wid][jp][r][hh][0]);
-                            pw[hh] = pp.x; pw[hh + 1] = pp.y; pw[hh + 2] = pp.z; pw[hh + 3] = pp.w;
-                        }
-                        uint32_t vp[EPC];
-                        if constexpr (DT == kFP8) {
-                            const uint32_t a[2] = {vt[2 * jp].x, vt[2 * jp].y};
-                            const uint32_t bq[2] = {vt[2 * jp + 1].x, vt[2 * jp + 1].y};
-    #pragma unroll
-                            for (int w = 0; w < 2; ++w) {
-                                const uint32_t x = __builtin_amdgcn_perm(bq[w], a[w], 0x05010400u);
-                                const uint32_t y = __builtin_amdgcn_perm(bq[w], a[w], 0x07030602u);
-                                vp[4 * w + 0] = fp8x2_to_f16x2(x, false);
-                                vp[4 * w + 1] = fp8x2_to_f16x2(x, true);
-                                vp[4 * w + 2] = fp8x2_to_f16x2(y, false);
-                                vp[4 * w + 3] = fp8x2_to_f16x2(y, true);
-                            }
-                        } else {
-                            const uint32_t a[4] = {vt[2 * jp].x, vt[2 * jp].y, vt[2 * jp].z, vt[2 * jp].w};
-                            const uint32_t bq[4] = {vt[2 * jp + 1].x, vt[2 * jp + 1].y,
-                                                    vt[2 * jp + 1].z, vt[2 * jp + 1].w};
-    #pragma unroll
-                            for (int w = 0; w < 4; ++w) {
-                                vp[2 * w] = __builtin_amdgcn_perm(bq[w], a[w], 0x05040100u);
-                                vp[2 * w + 1] = __builtin_amdgcn_perm(bq[w], a[w], 0x07060302u);
-                            }
-                        }
-    #pragma unroll
-                        for (int hh = 0; hh < G; ++hh) {
-    #pragma unroll
-                            for (int e = 0; e < EPC; ++e)
-                                o_acc[hh][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, vp[e]),
-                                                                      __builtin_bit_cast(h16x2, pw[hh]),
-                                                                      o_acc[hh][e], false);
-                        }
-                    }
-                } else {
-    #pragma unroll
-                    for (int i = 0; i < NL; ++i) {
-                        const f32x4 pv = *reinterpret_cast<const f32x4*>(&sm_p[wid][i * RPI + r][0]);
-                        float vf[EPC];
-                        unpack_chunk<DT>(vt[i], vf);
-    #pragma unroll
-                        for (int hh = 0; hh < G; ++hh) {
-    #pragma unroll
-                            for (int e = 0; e < EPC; ++e) o_acc[hh][e] = fmaf(pv[hh], vf[e], o_acc[hh][e]);
-                        }
+                for (int m = 0; m < D / 16; ++m) {
+                    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(vrow + 16 * m));
+                    if constexpr (DT == kBF16) {
+                        pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kg], pv_acc[m], 0, 0, 0);
+                        pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbl[kg], pv_acc[m], 0, 0, 0);
+                    } else {
+                        pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                            __builtin_bit_cast(h16x4, va), __builtin_bit_cast(h16x4, pb[kg]),
+                            pv_acc[m], 0, 0, 0);
                     }
                 }
             }
@@ -978,7 +852,7 @@ void attn_kernel(AttnParams P) {
             for (int hh = 0; hh < G; ++hh) l_w[hh] = wave_sum(l_lane[hh]);
         }
         const int buf = n_flush % NB;
-        if constexpr (MFPV) {
+        if constexpr (MF) {
             // the running max and sum first (the flushes below read them);
             // head (lane % 16): its max is already the same in its 4 lanes,
             // its sum adds the 4 lanes' shares
@@ -1013,7 +887,7 @@ void attn_kernel(AttnParams P) {
             for (int m = 0; m < D / 16; ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int hh = 0; hh < (MFPV ? 0 : G); ++hh) {
+        for (int hh = 0; hh < (MF ? 0 : G); ++hh) {
             // head by head: sum over the lanes that share this lane's dims,
             // then store, so only one head's exchanges are live at a time
 #pragma unroll
@@ -1026,8 +900,7 @@ void attn_kernel(AttnParams P) {
                 for (int e = 0; e < EPC; ++e)
                     sm_o[buf][n_st][hh][wid][c * EPC + e] = o_acc[hh][e] * kPUnscale;
             }
-            if constexpr (G == 8) __builtin_amdgcn_sched_barrier(0);
-            if (!MF && lane == 0) {
+            if (lane == 0) {
                 sm_m[buf][n_st][hh][wid] = m_run[hh];
                 sm_l[buf][n_st][hh][wid] = l_w[hh];
             }
@@ -1036,18 +909,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) o_acc[hh][e] = 0.f;
         }
-        if constexpr (MF && !MFPV) {
-            // head (lane % 16): its max is already the same in its 4 lanes;
-            // its sum adds the 4 lanes' shares
-            const float lw = xor_sum<32>(xor_sum<16>(l1)) * kPUnscale;
-            if (lane < G) {
-                sm_m[buf][n_st][lane][wid] = m1;
-                sm_l[buf][n_st][lane][wid] = lw;
-            }
-            m1 = -INFINITY;
-            l1 = 0.f;
-        }
-        if (!MFPV && n_st == 0) st_first = ch;
+        if (!MF && n_st == 0) st_first = ch;
         ++n_st;
         if (n_st == kStash) flush();
     };
