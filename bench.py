@@ -149,7 +149,7 @@ def parse():
 # Single-layer workloads: (kind, streams, cache dtype, positions, seed, query
 # heads).  Each is timed over enough independent buffer sets that no set is
 # re-read from the 256 MB Infinity Cache before it has been evicted.  All have
-# 8 kv heads of 256 dims; 16 or 32 query heads make them grouped.
+# 8 kv heads of 256 dims; 16, 32 or 64 query heads make them grouped.
 SINGLE_LAYER = {
     "sliding_1x600_f32": ("sliding", 1, "f32", 600, 1, 8),
     "full_1x1024_f16": ("full", 1, "f16", 1024, 2, 8),
@@ -166,6 +166,9 @@ SINGLE_LAYER = {
     "gqa2_full_64x4096_bf16": ("full", 64, "bf16", 4096, 7, 16),
     "gqa4_full_64x4096_fp8": ("full", 64, "fp8", 4096, 8, 32),
     "gqa4_sliding_64x4096_fp8": ("sliding", 64, "fp8", 4096, 8, 32),
+    "gqa8_full_64x4096_bf16": ("full", 64, "bf16", 4096, 12, 64),
+    "gqa8_sliding_64x4096_bf16": ("sliding", 64, "bf16", 4096, 12, 64),
+    "gqa8_full_64x4096_fp8": ("full", 64, "fp8", 4096, 13, 64),
 }
 
 
@@ -439,8 +442,8 @@ def main():
                 best = (gbs, wgs, us)
         ceiling = {"value": round(best[0], 1), "unit": "GB/s", "bytes": buf.numel(),
                    "workgroups": best[1], "us": round(best[2], 2),
-                   "kernel": "hswd_stream_read (128-bit non-temporal loads, contiguous "
-                             "range per workgroup)"}
+                   "kernel": "hswd_measure_stream_read (libhswd_measure.so; 128-bit "
+                             "non-temporal loads, contiguous range per workgroup)"}
         log("streaming-read ceiling: %.1f GB/s (%d workgroups)" % (best[0], best[1]))
         del buf, sink
         torch.cuda.empty_cache()

@@ -61,17 +61,28 @@ SIGNATURES = {
     "hswd_layer_step_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _D, _I, _DP, _P, _P],
                                 _I),
     "hswd_check_errors": ([_P, ctypes.POINTER(ctypes.c_int32), _P], _I),
-    "hswd_stream_read": ([_P, _Z, _P, _I, _P], _I),
     "hswd_gate_proj": ([_P, _P, _P, _I, _I, _I, _P], _I),
     "hswd_layer_step_gproj": ([_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _D, _I, _DP, _P,
                                _Z, _P], _I),
 }
 
+# include/hswd_measure.h, the measurement library beside libhswd.so
+MEASURE_SIGNATURES = {
+    "hswd_measure_stream_read": ([_P, _Z, _P, _I, _P], _I),
+}
+
 _lib = None
+_measure_lib = None
 
 
 def library_path():
     return os.environ.get("HSWD_LIBRARY", _build.LIB)
+
+
+def measure_library_path():
+    """libhswd_measure.so beside the loaded libhswd.so."""
+    return os.path.join(os.path.dirname(os.path.abspath(library_path())),
+                        os.path.basename(_build.MEASURE_LIB))
 
 
 def lib():
@@ -89,6 +100,23 @@ def lib():
             fn.restype = res
         _lib = L
     return _lib
+
+
+def measure_lib():
+    """The loaded libhswd_measure.so (loaded once)."""
+    global _measure_lib
+    if _measure_lib is None:
+        path = measure_library_path()
+        if not os.path.exists(path):
+            raise HswdUnavailable("libhswd_measure.so is not built (%s); run "
+                                  "python -m hybrid_sliding_window_decode_amd.build" % path)
+        L = ctypes.CDLL(path)
+        for name, (args, res) in MEASURE_SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _measure_lib = L
+    return _measure_lib
 
 
 def _check(fn, status):
@@ -445,8 +473,9 @@ def check_errors(ws):
 
 
 def stream_read(buf, workgroups=2048, sink=None):
-    """Read a device buffer once (measurement helper; see hswd_stream_read).
-    Returns the sink tensor [workgroups] int32 (never written in practice)."""
+    """Read a device buffer once (the measurement library's
+    hswd_measure_stream_read).  Returns the sink tensor [workgroups] int32
+    (never written in practice)."""
     _need(buf, "buf")
     nbytes = buf.numel() * buf.element_size()
     if sink is None:
@@ -454,6 +483,7 @@ def stream_read(buf, workgroups=2048, sink=None):
     _need(sink, "sink", torch.int32)
     if sink.numel() < workgroups:
         raise ValueError("sink must hold at least `workgroups` int32 values")
-    _check("hswd_stream_read", lib().hswd_stream_read(_ptr(buf), nbytes, _ptr(sink),
-                                                      int(workgroups), _stream()))
+    _check("hswd_measure_stream_read",
+           measure_lib().hswd_measure_stream_read(_ptr(buf), nbytes, _ptr(sink),
+                                                  int(workgroups), _stream()))
     return sink

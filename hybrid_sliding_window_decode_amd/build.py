@@ -6,7 +6,8 @@ Translation units: csrc/hswd.hip (host entry points and the small kernels)
 and csrc/attn_g{1,2,4,8}.hip (the attention kernel for 1, 2, 4 or 8 query heads
 per kv head; attn_g8s.hip: its form for the pieces of larger groups),
 compiled in parallel with hipcc for gfx950 only and linked into one shared
-library.  Packed fp32 instructions are turned off
+library; csrc/measure.hip (the streaming-read probe the benchmark compares
+the kernels with) into libhswd_measure.so beside it.  Packed fp32 instructions are turned off
 (-packed-fp32-ops): the kernels are written for scalar fp32 VALU ops.
 """
 import glob
@@ -23,9 +24,11 @@ SOURCES = [os.path.join(CSRC, f) for f in ("hswd.hip", "attn_g1.hip", "attn_g2.h
                                             "attn_g4.hip", "attn_g8.hip", "attn_g8s.hip")]
 SRC = SOURCES[0]
 LIB = os.path.join(HERE, "libhswd.so")
-DEPS = (SOURCES + sorted(glob.glob(os.path.join(CSRC, "*.hpp")))
+MEASURE_SRC = os.path.join(CSRC, "measure.hip")
+MEASURE_LIB = os.path.join(HERE, "libhswd_measure.so")
+DEPS = (SOURCES + [MEASURE_SRC] + sorted(glob.glob(os.path.join(CSRC, "*.hpp")))
         + sorted(glob.glob(os.path.join(CSRC, "kernels", "*.hpp")))
-        + [os.path.join(ROOT, "include", "hswd.h")])
+        + [os.path.join(ROOT, "include", "hswd.h"), os.path.join(ROOT, "include", "hswd_measure.h")])
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -34,31 +37,37 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 
 def build(out=LIB, extra=(), verbose=False, jobs=7):
+    """Compile and link libhswd.so at `out` and libhswd_measure.so beside it."""
+    measure_out = os.path.join(os.path.dirname(os.path.abspath(out)), os.path.basename(MEASURE_LIB))
+    srcs = SOURCES + [MEASURE_SRC]
     with tempfile.TemporaryDirectory(prefix="hswd_build_") as tmpdir:
-        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in srcs]
 
-        def compile_one(pair):
-            src, obj = pair
-            cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+        def run(cmd):
             if verbose:
                 print(" ".join(cmd), file=sys.stderr)
             subprocess.run(cmd, check=True)
 
+        def compile_one(pair):
+            src, obj = pair
+            run([HIPCC, *FLAGS, *extra, "-c", src, "-o", obj])
+
         with ThreadPoolExecutor(max_workers=jobs) as ex:
-            list(ex.map(compile_one, zip(SOURCES, objs)))
-        tmp = out + ".tmp%d" % os.getpid()
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-        if verbose:
-            print(" ".join(cmd), file=sys.stderr)
-        subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
+            list(ex.map(compile_one, zip(srcs, objs)))
+        tmps = []
+        for target, parts in ((out, objs[:-1]), (measure_out, objs[-1:])):
+            tmp = target + ".tmp%d" % os.getpid()
+            run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *parts, "-o", tmp])
+            tmps.append((tmp, target))
+    for tmp, target in tmps:
+        os.replace(tmp, target)
     return out
 
 
 def stale():
-    if not os.path.exists(LIB):
+    if not (os.path.exists(LIB) and os.path.exists(MEASURE_LIB)):
         return True
-    t = os.path.getmtime(LIB)
+    t = min(os.path.getmtime(LIB), os.path.getmtime(MEASURE_LIB))
     return any(os.path.getmtime(p) > t for p in DEPS)
 
 

@@ -509,16 +509,6 @@ int32_t hswd_lse_merge(float* o, const float* part_o, const float* part_ml, int3
     return launch_status();
 }
 
-int32_t hswd_stream_read(const void* buf, size_t bytes, void* sink, int32_t workgroups,
-                         void* stream) {
-    if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > 65536)
-        return HSWD_ERR_INVALID;
-    if (!aligned16(buf) || !aligned16(sink)) return HSWD_ERR_ALIGN;
-    hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, as_stream(stream),
-                       static_cast<const u32x4*>(buf), bytes / 16, static_cast<uint32_t*>(sink));
-    return launch_status();
-}
-
 int32_t hswd_head_gate(float* out, const float* o, const float* gate, int32_t B, int32_t H,
                        int32_t D, void* stream) {
     if (B < 0 || H < 1 || D < 1) return HSWD_ERR_INVALID;

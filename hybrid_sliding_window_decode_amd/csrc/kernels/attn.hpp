@@ -300,8 +300,12 @@ void attn_kernel(AttnParams P) {
     // in distinct banks; fp8 keys as exact bf16, fp8 values as exact fp16),
     // and the query heads sit there as 16-bit hi + lo parts.
     constexpr int KPAD = D * 2 / 16 + 1;                  // 16-byte units per staged (16-bit) row
+    // V rows are staged 32 bytes apart instead (VPAD): the transposing read
+    // takes 32 contiguous bytes from each of 4 (8) rows per 128 (256) bytes
+    // of a pass, so 16-byte offsets would make neighbouring rows share banks
+    constexpr int VPAD = D * 2 / 16 + 2;
     __shared__ float sm_q[MF ? 1 : G][D];
-    __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT : 1][MF ? KPAD : 1];
+    __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT * VPAD : 1];   // K rows at KPAD, then V rows at VPAD
     // query rows padded by 16 bytes too: unpadded, the G heads' rows (512
     // bytes apart) would share banks and the operand reads conflict 4 ways
     __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G + 1 : 1][MF ? D + 8 : 1];
@@ -580,8 +584,8 @@ void attn_kernel(AttnParams P) {
             asm volatile("" ::: "memory");     // the query reads below stay in the loop
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_bf16x8(kR[i]);
-                else sm_k[wid][i * RPI + r][c] = kR[i];
+                if constexpr (DT == kFP8) sm_k[wid][(i * RPI + r) * KPAD + c] = fp8x8_to_bf16x8(kR[i]);
+                else sm_k[wid][(i * RPI + r) * KPAD + c] = kR[i];
             }
             // the next item's K into the freed registers, in flight under
             // this tile's scores and values (rows clamped past the last item)
@@ -604,7 +608,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
                     u32x4 a;
-                    a = sm_k[wid][kg * 16 + hq][4 * sl + kq];
+                    a = sm_k[wid][(kg * 16 + hq) * KPAD + 4 * sl + kq];
                     f32x4& ah = acc[kg][2 * (sl & 1)];
                     f32x4& al_ = acc[kg][2 * (sl & 1) + 1];
                     if constexpr (DT != kF16) {
@@ -682,8 +686,8 @@ void attn_kernel(AttnParams P) {
             // as exact fp16
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                if constexpr (DT == kFP8) sm_k[wid][i * RPI + r][c] = fp8x8_to_f16x8(vt[i]);
-                else sm_k[wid][i * RPI + r][c] = vt[i];
+                if constexpr (DT == kFP8) sm_k[wid][(i * RPI + r) * VPAD + c] = fp8x8_to_f16x8(vt[i]);
+                else sm_k[wid][(i * RPI + r) * VPAD + c] = vt[i];
             }
             // one V tile in flight: the next one into the registers just
             // staged (rows clamped past the last item, as for K)
@@ -694,10 +698,10 @@ void attn_kernel(AttnParams P) {
             // lanes 4 j .. 4 j + 3 point at (16 consecutive dims of key
             // 4 (l / 16) + j)
             const uint16_t* vrow0 = reinterpret_cast<const uint16_t*>(
-                &sm_k[wid][4 * kq + ((lane & 15) >> 2)][0]) + 4 * (lane & 3);
+                &sm_k[wid][(4 * kq + ((lane & 15) >> 2)) * VPAD]) + 4 * (lane & 3);
 #pragma unroll
             for (int kg = 0; kg < NG; ++kg) {
-                const uint16_t* vrow = vrow0 + kg * 16 * (KPAD * 8);
+                const uint16_t* vrow = vrow0 + kg * 16 * (VPAD * 8);
 #pragma unroll
                 for (int m = 0; m < D / 16; ++m) {
                     const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

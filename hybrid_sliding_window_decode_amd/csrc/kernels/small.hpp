@@ -143,33 +143,6 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(float* out, const float*
     }
 }
 
-// Measurement helper (not part of the decode path): read n16 16-byte words
-// once, each workgroup a contiguous range, with the 128-bit non-temporal
-// loads the attention kernel streams its tiles with, eight in flight per
-// thread.  The loaded words are folded into a value that is stored only in
-// the (practically impossible) case that it equals a fixed pattern, so the
-// loads cannot be dropped and nothing else reaches memory.
-__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* p, size_t n16,
-                                                          uint32_t* sink) {
-    const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
-    const size_t beg = per * blockIdx.x;
-    const size_t end = beg + per < n16 ? beg + per : n16;
-    uint32_t acc = 0;
-    size_t i = beg + threadIdx.x;
-    for (; i + 7 * 256 < end; i += 8 * 256) {
-        u32x4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = load_kv<16>(p + i + u * 256);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    }
-    for (; i < end; i += 256) {
-        const u32x4 v = load_kv<16>(p + i);
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
-    }
-    if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
-}
-
 // Zero n 32-bit words.
 __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;

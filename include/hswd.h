@@ -312,19 +312,6 @@ int32_t hswd_layer_step_gproj(float* out, const float* q, const float* k, const 
                               double theta, int32_t max_pos, const hswd_attn_desc* d, void* ws,
                               size_t ws_bytes, void* stream);
 
-/* Measurement helper, not a step of the decode path: reads `bytes` (a
- * multiple of 16) of device memory at `buf` once, `workgroups` workgroups
- * of 256 threads each streaming a contiguous range with the 128-bit
- * non-temporal loads the attention kernel uses for its K/V tiles.  Its
- * duration over a buffer much larger than the 256 MB last-level cache gives
- * the streaming-read ceiling the attention kernel is compared with.  `sink`
- * (DEVICE, 16-byte aligned, at least 4 * workgroups bytes) keeps the loads
- * from being optimised away and is in practice never written.  Errors:
- * HSWD_ERR_INVALID (null pointer, bytes 0 or not a multiple of 16,
- * workgroups outside [1, 65536]), HSWD_ERR_ALIGN; nothing is launched then. */
-int32_t hswd_stream_read(const void* buf, size_t bytes, void* sink, int32_t workgroups,
-                         void* stream);
-
 /* Synchronise `stream`, then read the workspace error word.  Returns
  * HSWD_OK if it is zero, HSWD_ERR_CAPACITY otherwise; *flags_out (nullable,
  * host) receives the HSWD_FLAG_* bits.  Flags stay set until

@@ -11,6 +11,7 @@
 #include <stdlib.h>
 
 #include "../../include/hswd.h"
+#include "../../include/hswd_measure.h"
 
 static int fails = 0;
 #define EXPECT(call, want) do { int32_t got_ = (int32_t)(call); if (got_ != (want)) { \
@@ -89,7 +90,9 @@ int main(void)
     EXPECT(hswd_lse_merge(A, A, A, 2, 8, 256, 2000, NULL), HSWD_ERR_UNSUPPORTED);
     EXPECT(hswd_head_gate(NULL, A, A, 2, 8, 256, NULL), HSWD_ERR_INVALID);
     EXPECT(hswd_gate_proj(A, A, A, 2, 0, 8, NULL), HSWD_ERR_INVALID);
-    EXPECT(hswd_stream_read(A, 17, A, 8, NULL), HSWD_ERR_INVALID);
+    EXPECT(hswd_measure_stream_read(A, 17, A, 8, NULL), HSWD_ERR_INVALID);
+    EXPECT(hswd_measure_stream_read(A, 1 << 20, A, 0, NULL), HSWD_ERR_INVALID);
+    EXPECT(hswd_measure_stream_read((void*)0x10008, 1 << 20, A, 8, NULL), HSWD_ERR_ALIGN);
     EXPECT(hswd_workspace_init(NULL, 64, NULL), HSWD_ERR_WORKSPACE);
     EXPECT(hswd_check_errors(NULL, NULL, NULL), HSWD_ERR_WORKSPACE);
     hswd_attn_desc g = desc(2, 16, 8, 256, 4097, HSWD_F32);       /* grouped f32: not built */

@@ -12,13 +12,14 @@ from hybrid_sliding_window_decode_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hswd.h")
+MEASURE_HEADER = os.path.join(ROOT, "include", "hswd_measure.h")
 
 A = ctypes.c_void_p(0x10000)       # aligned stand-in pointer (never dereferenced)
 MIS = ctypes.c_void_p(0x10004)     # misaligned stand-in pointer
 
 
-def declared():
-    text = open(HEADER).read()
+def declared(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:const char\*|int32_t|size_t)\s+(hswd_\w+)\s*\(",
                                  text, re.M)))
 
@@ -37,6 +38,30 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding.SIGNATURES), set(names) ^ set(binding.SIGNATURES)
+
+
+def test_measurement_library_exports_its_header_and_nothing_leaks_into_libhswd():
+    M = binding.measure_lib()
+    names = declared(MEASURE_HEADER)
+    assert names == ["hswd_measure_stream_read"]
+    for n in names:
+        assert hasattr(M, n), n
+    assert set(names) == set(binding.MEASURE_SIGNATURES)
+    # the decode library exports no measurement entry
+    assert not hasattr(binding.lib(), "hswd_measure_stream_read")
+    assert not hasattr(binding.lib(), "hswd_stream_read")
+
+
+def test_measurement_host_checks():
+    M = binding.measure_lib()
+    # null, size 0 or not a multiple of 16, workgroups, alignment
+    assert M.hswd_measure_stream_read(None, 1 << 20, A, 64, None) == -1
+    assert M.hswd_measure_stream_read(A, 0, A, 64, None) == -1
+    assert M.hswd_measure_stream_read(A, 1000, A, 64, None) == -1
+    assert M.hswd_measure_stream_read(A, 1 << 20, A, 0, None) == -1
+    assert M.hswd_measure_stream_read(A, 1 << 20, A, 65537, None) == -1
+    assert M.hswd_measure_stream_read(MIS, 1 << 20, A, 64, None) == -2
+    assert M.hswd_measure_stream_read(A, 1 << 20, MIS, 64, None) == -2
 
 
 def test_version_and_status_strings():
@@ -170,13 +195,6 @@ def test_other_entries_host_checks():
     assert L.hswd_workspace_init(None, 64, None) == -3
     assert L.hswd_workspace_init(MIS, 64, None) == -2
     assert L.hswd_check_errors(None, None, None) == -3
-    # streaming-read helper: null, size 0 or not a multiple of 16, workgroups, alignment
-    assert L.hswd_stream_read(None, 1 << 20, A, 64, None) == -1
-    assert L.hswd_stream_read(A, 0, A, 64, None) == -1
-    assert L.hswd_stream_read(A, 1000, A, 64, None) == -1
-    assert L.hswd_stream_read(A, 1 << 20, A, 0, None) == -1
-    assert L.hswd_stream_read(A, 1 << 20, A, 65537, None) == -1
-    assert L.hswd_stream_read(MIS, 1 << 20, A, 64, None) == -2
 
 
 def test_binding_refuses_cpu_tensors():
@@ -224,10 +242,15 @@ def test_binding_covers_every_declared_entry():
     import hybrid_sliding_window_decode_amd as pkg
     h = open(os.path.join(ROOT, "include", "hswd.h")).read()
     declared = sorted(set(re.findall(r"\b(hswd_[a-z_0-9]+)\s*\(", h)))
-    assert len(declared) >= 18
+    assert len(declared) >= 17
     for name in declared:
         assert name in binding.SIGNATURES, name
         assert hasattr(pkg, name[5:]) or hasattr(binding, name[5:]), name
+    # the measurement library: hswd_measure_stream_read -> stream_read
+    m = open(os.path.join(ROOT, "include", "hswd_measure.h")).read()
+    for name in sorted(set(re.findall(r"\b(hswd_measure_[a-z_0-9]+)\s*\(", m))):
+        assert name in binding.MEASURE_SIGNATURES, name
+        assert hasattr(pkg, name[len("hswd_measure_"):]), name
 
 
 def test_binding_refuses_a_descriptor_that_does_not_match_the_tensors():

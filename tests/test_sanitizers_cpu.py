@@ -4,7 +4,8 @@
   with gcc's sanitizers (leak checking on) and calls every public function
   on small cases that reach its edges.
 * The host side of libhswd: hswd.hip (argument checks, chunking, workspace
-  layout, dispatch) built with the sanitizers on its host code only, linked
+  layout, dispatch) and the measurement library's measure.hip, built with
+  the sanitizers on their host code only, linked
   with stub attention launchers (tests/sanitize/attn_launch_stub.hip) so the
   attention kernels need not be compiled, and driven through every entry
   point's host checks by tests/sanitize/abi_driver.c.  Without a GPU, valid
@@ -58,6 +59,7 @@ def test_library_host_side_under_address_and_undefined_behaviour_sanitizers(tmp_
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + HOST_SAN
     objs = []
     for src, obj in [(os.path.join(CSRC, "hswd.hip"), "hswd.o"),
+                     (os.path.join(CSRC, "measure.hip"), "measure.o"),
                      (os.path.join(SAN, "attn_launch_stub.hip"), "stub.o")]:
         _run([HIPCC] + flags + ["-c", src, "-o", os.path.join(t, obj)])
         objs.append(os.path.join(t, obj))
