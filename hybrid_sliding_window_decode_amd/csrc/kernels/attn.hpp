@@ -3,11 +3,13 @@
 // layer step, the head gate and the entry write in the epilogue.
 //
 // Summation order.  The valid key range of each (stream, kv head) is cut into
-// chunks of K keys (K = keys_per_split; by default 128 to 2048 from the
-// cache length, longer only past 2^23 rows).  A chunk's partial (max m, sum l, unnormalised o) is computed the
+// chunks of K keys (K = keys_per_split; by default a ring's from its slot
+// count, 128 to 512, and an append cache stream's from its own position, at
+// most 1024 keys below 131072 and 2048 from there, longer only past 4096
+// chunks).  A chunk's partial (max m, sum l, unnormalised o) is computed the
 // same way wherever it runs: the workgroup's waves take the chunk's tiles
-// round robin, keep an online
-// softmax each, and merge through LDS in wave order.  Chunk partials are then
+// round robin, keep an online softmax each, and merge through LDS in wave
+// order.  Chunk partials are then
 // folded in chunk order, and the new entry last.  The bits therefore depend
 // on K and the positions only -- not on the batch, nor on how many chunks a
 // workgroup streams, which the host picks from the batch and the CU count.
@@ -141,7 +143,7 @@ constexpr bool use_mfma() {
 template <int D, int DT, int G = 1>
 struct AttnGeo {
     static constexpr int EB = elt_bytes<DT>();        // element bytes
-    static constexpr int CB = DT == kFP8 && G > 1 ? 8 : 16;   // bytes per lane chunk
+    static constexpr int CB = DT == kFP8 && G > 1 && !use_mfma<DT, G>() ? 8 : 16;   // bytes per lane chunk
     static constexpr int EPC = CB / EB;               // elements per chunk
     static constexpr int LPR = D / EPC;               // lanes per cache row
     static constexpr int RPI = kWave / LPR;           // rows per wave-wide load
@@ -155,6 +157,15 @@ struct AttnGeo {
 // wave (the grouped kernels' 4-load tiles divide it).
 constexpr int chunk_quantum(int D, int DT) {
     return kAttnWaves * 8 * (kWave / (D / (16 / (DT == kF32 ? 4 : (DT == kFP8 ? 1 : 2)))));
+}
+
+// Row of key k of a tile in the fp8 matrix-core kernels' staged V: the two
+// 16-key halves of every 32 keys are laid out so that the 16 rows one pass
+// of the transposing read touches (keys 4 q .. 4 q + 3 and 16 + 4 q .. 16 +
+// 4 q + 3 for two neighbouring q) are distinct modulo 16, hence in distinct
+// banks at a row pitch of 16 bytes modulo 256.
+__host__ __device__ constexpr int f8_vrow(int k) {
+    return (k & 16) ? ((k & ~15) | ((k & 15) ^ 8)) : k;
 }
 
 // Max of N values in LDS.
@@ -281,10 +292,13 @@ void attn_kernel(AttnParams P) {
     // too: V goes through the wave's LDS rows after its K, the probabilities
     // stay in the registers the score product left them in.  Its
     // accumulators (D / 16 x 4 per lane) cost the same for 4 and 8 heads;
-    // they fit beside two V tiles in flight at 128 dims and for the 4-head
-    // kernel over fp8, and beside one (VS1: V of the next tile requested
-    // once this tile's is in LDS) otherwise.
-    constexpr bool VS1 = MF && D == 256 && (G == 8 || DT != kFP8);
+    // they fit beside two V tiles in flight for 16-bit caches at 128 dims,
+    // and beside one (VS1: V of the next tile requested once this tile's is
+    // in LDS) otherwise.
+    // fp8 caches (F8): 32-key tiles at 256 dims (64 at 128), K and V staged
+    // in LDS as the fp8 codes they are and converted as they are read back
+    constexpr bool F8 = MF && DT == kFP8;
+    constexpr bool VS1 = MF && (D == 256 || F8);
     // heads per flush of the wave partials: at 256 dims the 8-head kernel
     // flushes its heads in two halves, so its partials take 16 KiB (LDS for
     // two workgroups per CU)
@@ -304,8 +318,12 @@ void attn_kernel(AttnParams P) {
     // takes 32 contiguous bytes from each of 4 (8) rows per 128 (256) bytes
     // of a pass, so 16-byte offsets would make neighbouring rows share banks
     constexpr int VPAD = D * 2 / 16 + 2;
+    // F8 rows: D code bytes plus 16, so the 16 rows of a score-operand read
+    // and the 16 rows of a pass of the transposing read (placed by
+    // f8_vrow) fall in distinct banks
+    constexpr int P8 = D / 16 + 1;                        // 16-byte units per staged fp8 row
     __shared__ float sm_q[MF ? 1 : G][D];
-    __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT * VPAD : 1];   // K rows at KPAD, then V rows at VPAD
+    __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT * (F8 ? P8 : VPAD) : 1];   // K rows, then V rows
     // query rows padded by 16 bytes too: unpadded, the G heads' rows (512
     // bytes apart) would share banks and the operand reads conflict 4 ways
     __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G + 1 : 1][MF ? D + 8 : 1];
@@ -584,7 +602,7 @@ void attn_kernel(AttnParams P) {
             asm volatile("" ::: "memory");     // the query reads below stay in the loop
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                if constexpr (DT == kFP8) sm_k[wid][(i * RPI + r) * KPAD + c] = fp8x8_to_bf16x8(kR[i]);
+                if constexpr (F8) sm_k[wid][(i * RPI + r) * P8 + c] = kR[i];
                 else sm_k[wid][(i * RPI + r) * KPAD + c] = kR[i];
             }
             // the next item's K into the freed registers, in flight under
@@ -608,7 +626,13 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
                     u32x4 a;
-                    a = sm_k[wid][(kg * 16 + hq) * KPAD + 4 * sl + kq];
+                    if constexpr (F8) {
+                        // the 8 codes of dims 32 sl + 8 kq .. + 7, as exact bf16
+                        const uint8_t* k8 = reinterpret_cast<const uint8_t*>(&sm_k[wid][(kg * 16 + hq) * P8]);
+                        a = fp8x8_to_bf16x8(*reinterpret_cast<const u32x2*>(k8 + 32 * sl + 8 * kq));
+                    } else {
+                        a = sm_k[wid][(kg * 16 + hq) * KPAD + 4 * sl + kq];
+                    }
                     f32x4& ah = acc[kg][2 * (sl & 1)];
                     f32x4& al_ = acc[kg][2 * (sl & 1) + 1];
                     if constexpr (DT != kF16) {
@@ -656,6 +680,8 @@ void attn_kernel(AttnParams P) {
             // bits), the running sum over the float weights.
             typedef short s16x4 __attribute__((ext_vector_type(4)));
             typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+            typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+            typedef int i32x2 __attribute__((ext_vector_type(2)));
             s16x4 pb[NG], pbl[NG];
             float psum = 0.f;
 #pragma unroll
@@ -682,16 +708,46 @@ void attn_kernel(AttnParams P) {
                 for (int m = 0; m < D / 16; ++m) pv_acc[m] *= alpha;
             }
             // V to the wave's LDS rows, where its K was (this wave has
-            // read them; its LDS accesses complete in order), fp8 codes
-            // as exact fp16
+            // read them; its LDS accesses complete in order); fp8 codes as
+            // they are, each key at its row f8_vrow
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                if constexpr (DT == kFP8) sm_k[wid][(i * RPI + r) * VPAD + c] = fp8x8_to_f16x8(vt[i]);
+                if constexpr (F8) sm_k[wid][f8_vrow(i * RPI + r) * P8 + c] = vt[i];
                 else sm_k[wid][(i * RPI + r) * VPAD + c] = vt[i];
             }
             // one V tile in flight: the next one into the registers just
             // staged (rows clamped past the last item, as for K)
             if constexpr (VS1) load_tile(kA, vA, j + 1);
+            if constexpr (F8) {
+                // fp8: one v_mfma_f32_16x16x32_f16 per 16 dims and 32 keys
+                // (key groups 2 p and 2 p + 1).  Its B operand is the two
+                // groups' probabilities side by side: lane l holds keys
+                // 32 p + 4 (l / 16) + i and 32 p + 16 + 4 (l / 16) + i, i =
+                // 0..3, of head l % 16, as its k = 8 (l / 16) + 0..7.  Its A
+                // operand (V^T, 16 dims x those keys in that order) comes
+                // from the 8-bit transposing read: within each 16-lane
+                // group, lanes 2 j and 2 j + 1 point at 8 codes each of row
+                // j, and lane i receives code i of rows 0..7; row j here is
+                // the j-th key of the lane's list, dims 16 m .. 16 m + 15.
+                // The codes become fp16 (exact) in registers.
+                const int jr = (lane & 15) >> 1;
+                const int key0 = 4 * kq + (jr < 4 ? jr : 12 + jr);    // 16 + 4 kq + (jr - 4)
+                const uint8_t* vb = reinterpret_cast<const uint8_t*>(&sm_k[wid][0]) + 8 * (lane & 1);
+#pragma unroll
+                for (int pp = 0; pp < NG / 2; ++pp) {
+                    const uint8_t* vrow = vb + f8_vrow(32 * pp + key0) * (P8 * 16);
+                    const h16x8 pbw = __builtin_shufflevector(
+                        __builtin_bit_cast(h16x4, pb[2 * pp]), __builtin_bit_cast(h16x4, pb[2 * pp + 1]),
+                        0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int m = 0; m < D / 16; ++m) {
+                        const u32x2 v8 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (__attribute__((address_space(3))) i32x2*)(vrow + 16 * m)));
+                        pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(h16x8, fp8x8_to_f16x8(v8)), pbw, pv_acc[m], 0, 0, 0);
+                    }
+                }
+            } else {
             // A operand V^T (16 dims x 16 keys): lane l needs keys
             // 4 (l / 16) + j of dim l % 16; the transposing LDS read hands
             // lane i of each 16-lane group element i of the four rows its
@@ -715,6 +771,7 @@ void attn_kernel(AttnParams P) {
                             pv_acc[m], 0, 0, 0);
                     }
                 }
+            }
             }
         } else {
             float s[G];
