@@ -51,6 +51,9 @@ def positions(kind, B, S, pos, seed):
     # with each probability split into two bf16 parts
     ("full", "bf16", 4, 128, 3, [4000, 17, 2048], 4001, 0),
     ("sliding", "bf16", 4, 128, 5, "ragged", None, 0),
+    # fp8 at D = 128: 64-key tiles, two 32-key value products per tile
+    ("full", "fp8", 4, 128, 3, [4000, 17, 2048], 4001, 0),
+    ("sliding", "fp8", 4, 128, 5, "ragged", None, 0),
 ])
 def test_gqa_layer_step(kind, dtype, G, D, B, pos, S, kps):
     check_layer_step(kind, dtype, G, D, B, pos, S, kps)
@@ -100,6 +103,8 @@ def test_gqa_large_groups(kind, dtype, G, D, B, pos, S, kps, H):
     ("full", "bf16", 4, 256, 4, "ragged", 3000, 0),
     ("full", "bf16", 8, 256, 3, "ragged", 3000, 0),
     ("sliding", "fp8", 8, 256, 4, "ragged", None, 0),
+    ("full", "fp8", 4, 128, 3, "ragged", 3000, 0),
+    ("full", "fp8", 8, 128, 3, "ragged", 3000, 0),
     ("full", "f16", 2, 128, 4, "ragged", 3000, 256),
     ("full", "bf16", 4, 128, 3, "ragged", 3000, 0),
     ("full", "f16", 4, 128, 3, "ragged", 3000, 0),
