@@ -115,6 +115,24 @@ def test_workspace_and_splits():
     assert L.hswd_num_splits(ctypes.byref(desc(keys_per_split=100)), 1, 0) == -1
 
 
+def test_groups_up_to_eight_heads_run_in_one_piece():
+    """A ring layer with one chunk holds no partials, so its workspace is the
+    error word (256 bytes) plus the arrival counters rounded up to 256 bytes:
+    one per (stream, kv head) and piece, plus one per (stream, kv head) for
+    the entry write when a group runs in pieces.  Groups of 2 to 8 query
+    heads per kv head run in one piece; larger ones in pieces of eight."""
+    def counters(H, Hkv=8, B=64, dt=2):
+        d = desc(batch=B, n_heads=H, n_kv_heads=Hkv, kv_dtype=dt)
+        assert hswd.num_splits(d, 1) == 1
+        return (hswd.workspace_bytes(d, 1) - 256) // 4
+    for dt in (1, 2, 3):
+        for H in (16, 24, 32, 40, 48, 56, 64):
+            assert counters(H, dt=dt) == 64 * 8, (dt, H)
+        assert counters(128, dt=dt) == 64 * 8 * 2 + 64 * 8          # two pieces of 8
+        assert counters(96, dt=dt) == 64 * 8 * 2 + 64 * 8           # 12: pieces of 8 and 4
+        assert counters(256, Hkv=8, dt=dt) == 64 * 8 * 4 + 64 * 8   # 32: four pieces
+
+
 @pytest.mark.parametrize("case,kw,want", [
     ("H % Hkv", dict(n_heads=6, n_kv_heads=4), -1),
     ("head_dim", dict(head_dim=96), -6),
