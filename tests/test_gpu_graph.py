@@ -22,7 +22,8 @@ def make_layers(seed):
     layers = []
     for i, (kind, dtype, H) in enumerate([("sliding", "bf16", 8), ("full", "bf16", 8),
                                           ("full", "fp8", 8), ("sliding", "bf16", 32),
-                                          ("full", "f16", 16)]):
+                                          ("full", "f16", 16), ("full", "fp8", 32),
+                                          ("sliding", "fp8", 64), ("full", "bf16", 64)]):
         B = 6
         if kind == "sliding":
             spec = inputs.sliding_spec(B, dtype, H=H)
