@@ -16,11 +16,13 @@
 //
 // Streaming.  One workgroup (4 waves) streams a contiguous range of chunks of
 // one (stream, kv head).  Each wave reads whole 32-key (fp8), 16-key
-// (bf16/f16) or 8-key (f32) tiles with 128-bit non-temporal loads, lanes over
-// head dims, and keeps the next tile in flight while it scores the current
-// one (register double buffering); the prefetch runs across chunk
-// boundaries, and each wave's chunk partial goes to LDS, so the waves meet
-// at a barrier only every four chunks.  The per-stream inputs and the first
+// (bf16/f16) or 8-key (f32) tiles (at 256 dims) with 128-bit non-temporal
+// loads, lanes over head dims, and keeps the next tile in flight while it
+// scores the current one (register double buffering); the prefetch runs
+// across chunk boundaries, and each wave's chunk partial goes to LDS, so the
+// waves of the one-head kernel meet at a barrier only every four chunks.
+// The grouped kernels for 4 and 8 query heads per kv head run both products
+// on the matrix cores, staging K and then V through the wave's LDS rows.  The per-stream inputs and the first
 // two tiles are requested before the prologue (RoPE of the query and the new
 // key, the new entry's score).  Dot products are reduced across lanes with a
 // transposed butterfly (about one exchange per key); every exchange is a DPP
@@ -138,8 +140,8 @@ constexpr bool use_mfma() {
 // lane (8 dims, as for 16-bit rows) and halves its 16-bit tiles (4 loads of
 // K and of V instead of 8) to stay within 256 VGPRs (2 waves per SIMD);
 // its fp8 tiles keep 8 loads, so a wave keeps as many bytes in flight as
-// with 16-bit rows.  The MFMA kernel keeps no query vectors in registers
-// and keeps 8-load tiles.
+// with 16-bit rows.  The MFMA kernels keep no query vectors in registers
+// and keep 8-load tiles of 16 bytes per lane (fp8: 32 keys at 256 dims).
 template <int D, int DT, int G = 1>
 struct AttnGeo {
     static constexpr int EB = elt_bytes<DT>();        // element bytes
