@@ -93,5 +93,7 @@ def test_kernel_group():
     assert bench.kernel_group("bf16", 64) == (8, 1)
     assert bench.kernel_group("bf16", 40) == (8, 1)
     assert bench.kernel_group("fp8", 64) == (8, 1)
+    assert bench.kernel_group("fp8", 16) == (4, 1)
+    assert bench.kernel_group("bf16", 16) == (2, 1)
     assert bench.full_kernel("bf16", 64) == "hswd::attn_kernel<256, 2, false, 1, 8, false>(...)"
     assert bench.full_kernel("fp8", 8) == "hswd::attn_kernel<256, 3, false, 1, 1, false>(...)"
