@@ -153,8 +153,11 @@ def check_layer_step(kind, dtype, G, D, B, pos, S, kps, H=8, q_mult=1.0):
     assert hswd.check_errors(ws2) == 0
     assert np.array_equal(g.cpu().numpy(), out), "fused and unfused outputs differ"
     kc = cache_to_host(d["k_cache"])
-    assert np.array_equal(kc, cache_to_host(e["k_cache"]))
-    assert np.array_equal(cache_to_host(d["v_cache"]), cache_to_host(e["v_cache"]))
+    # bit patterns (an f32 cache's unwritten rows hold NaN)
+    same = lambda a, b: np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                                       np.ascontiguousarray(b).view(np.uint8))
+    assert same(kc, cache_to_host(e["k_cache"]))
+    assert same(cache_to_host(d["v_cache"]), cache_to_host(e["v_cache"]))
     k_rot = e["k"].cpu().numpy()
     ksc = None if spec.kv_scale is None else spec.kv_scale[0][:, None]
     for b in range(B):
