@@ -358,3 +358,19 @@ def test_noalloc_step_refuses_what_its_array_cannot_hold():
     assert call(desc(batch=1, n_slots=4097), max_pos=4096, err=ctypes.c_void_p(0x10002)) == -2
     assert call(desc(batch=0, n_slots=4097), max_pos=4096) == 0  # empty batch: nothing to do
     assert call(desc(batch=1, n_slots=4097), max_pos=4097) == -4  # capacity, as layer_step
+
+
+def test_c_abi_caller_links_and_checks_its_arguments():
+    """tests/c_abi/layer_step (the C-ABI caller of the GPU tests) loads the
+    library and refuses a wrong argument count before any GPU call."""
+    import subprocess
+    exe = os.path.join(ROOT, "tests", "c_abi", "layer_step")
+    if not os.path.exists(exe):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "hswd_c_abi_build", os.path.join(ROOT, "tests", "c_abi", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
