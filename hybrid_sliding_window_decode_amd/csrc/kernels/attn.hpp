@@ -49,6 +49,8 @@
 
 #include "common.hpp"
 
+#include <utility>
+
 namespace hswd {
 
 #ifndef HSWD_ATTN_WAVES
@@ -161,13 +163,33 @@ constexpr int chunk_quantum(int D, int DT) {
     return kAttnWaves * 8 * (kWave / (D / (16 / (DT == kF32 ? 4 : (DT == kFP8 ? 1 : 2)))));
 }
 
-// Row of key k of a tile in the fp8 matrix-core kernels' staged V: the two
-// 16-key halves of every 32 keys are laid out so that the 16 rows one pass
-// of the transposing read touches (keys 4 q .. 4 q + 3 and 16 + 4 q .. 16 +
-// 4 q + 3 for two neighbouring q) are distinct modulo 16, hence in distinct
-// banks at a row pitch of 16 bytes modulo 256.
-__host__ __device__ constexpr int f8_vrow(int k) {
-    return (k & 16) ? ((k & ~15) | ((k & 15) ^ 8)) : k;
+// Calls f(integral_constant<int, I>) for I = 0 .. N - 1, so each call can
+// pass I on as an immediate operand.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The 16-block 4x4x4 matrix product with block AB's A operand broadcast to
+// all 16 blocks (cbsz 4, abid AB): D[b][v][c] += sum_k A_AB[v][k] B_b[k][c],
+// where lane 4 b + i holds A_b[i][0..3] and B_b[0..3][i], and register v of
+// lane 4 b + c holds D[b][v][c] (layouts checked on the GPU with a probe
+// before use).  BF: bf16 operands, else fp16.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+template <int AB, bool BF>
+__device__ __forceinline__ f32x4v mfma4_bcast(const u32x2& a, const u32x2& b, const f32x4v& c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 4, AB, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h16x4, a),
+                                                 __builtin_bit_cast(h16x4, b), c, 4, AB, 0);
 }
 
 // Max of N values in LDS.
@@ -292,14 +314,17 @@ void attn_kernel(AttnParams P) {
     constexpr bool MF = use_mfma<DT, G>();
     // The matrix-core kernels take the value product on the matrix cores
     // too: V goes through the wave's LDS rows after its K, the probabilities
-    // stay in the registers the score product left them in.  Its
-    // accumulators (D / 16 x 4 per lane) cost the same for 4 and 8 heads;
-    // they fit beside two V tiles in flight for 16-bit caches at 128 dims,
-    // and beside one (VS1: V of the next tile requested once this tile's is
-    // in LDS) otherwise.
+    // stay in the registers the score product left them in, and the product
+    // is a series of 16-block 4x4x4 products, each with the probabilities of
+    // 4 keys for 4 heads broadcast to all 16 blocks (4 dims each): a lane
+    // accumulates 4 heads of one dim per 64 dims, D / 16 registers per set of
+    // 4 heads.  Two V tiles in flight for 16-bit caches at 128 dims, one
+    // otherwise (VS1: V of the next tile requested once this tile's is in
+    // LDS).
     // fp8 caches (F8): 32-key tiles at 256 dims (64 at 128), K and V staged
     // in LDS as the fp8 codes they are and converted as they are read back
     constexpr bool F8 = MF && DT == kFP8;
+    constexpr int NQ = G / 4;                 // sets of 4 heads (matrix-core kernels)
     constexpr bool VS1 = MF && (D == 256 || F8);
     // heads per flush of the wave partials: at 256 dims the 8-head kernel
     // flushes its heads in two halves, so its partials take 16 KiB (LDS for
@@ -316,13 +341,10 @@ void attn_kernel(AttnParams P) {
     // in distinct banks; fp8 keys as exact bf16, fp8 values as exact fp16),
     // and the query heads sit there as 16-bit hi + lo parts.
     constexpr int KPAD = D * 2 / 16 + 1;                  // 16-byte units per staged (16-bit) row
-    // V rows are staged 32 bytes apart instead (VPAD): the transposing read
-    // takes 32 contiguous bytes from each of 4 (8) rows per 128 (256) bytes
-    // of a pass, so 16-byte offsets would make neighbouring rows share banks
+    // V rows are staged 32 bytes apart instead (VPAD)
     constexpr int VPAD = D * 2 / 16 + 2;
     // F8 rows: D code bytes plus 16, so the 16 rows of a score-operand read
-    // and the 16 rows of a pass of the transposing read (placed by
-    // f8_vrow) fall in distinct banks
+    // fall in distinct banks
     constexpr int P8 = D / 16 + 1;                        // 16-byte units per staged fp8 row
     __shared__ float sm_q[MF ? 1 : G][D];
     __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT * (F8 ? P8 : VPAD) : 1];   // K rows, then V rows
@@ -419,12 +441,14 @@ void attn_kernel(AttnParams P) {
     // MFMA kernel: the running max and sum of head (lane % 16) over the keys
     // this lane's group of 4 holds; lanes of heads >= G carry unused values
     float m1 = -INFINITY, l1 = 0.f;
-    // value product on the matrix cores: O^T (16 dims x 16 heads) per group
-    // of 16 dims; lane l holds dims 4 (l / 16) + i of the group, head l % 16
+    // value product on the matrix cores: O (4 heads x 64 dims) per set z of
+    // 4 heads and group m of 64 dims, pv_acc[z * D / 64 + m]; lane l holds
+    // dim 64 m + l of heads 4 z + i, i = 0..3
     typedef float pv4 __attribute__((ext_vector_type(4)));
-    pv4 pv_acc[MF ? D / 16 : 1];
+    constexpr int NACC = MF ? NQ * (D / 64) : 1;
+    pv4 pv_acc[NACC];
 #pragma unroll
-    for (int m = 0; m < (MF ? D / 16 : 1); ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < NACC; ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
     Fold run[G];                    // folded chunk partials (wpp == 1)
 
     using Chunk = typename ChunkT<Geo::CB>::type;
@@ -673,16 +697,15 @@ void attn_kernel(AttnParams P) {
             const float m_new = fmaxf(m1, mx);
             const float alpha = fast_exp2(m1 - m_new);
             m1 = m_new;
-            // The probabilities are the B operand of P.V as they stand:
-            // lane l holds keys 4 (l / 16) + i of head l % 16, the
-            // operand's k and column.  f16 / fp8 caches: fp16 weights
+            // The probabilities are the A operand of P.V as they stand:
+            // lane l holds keys 4 (l / 16) + i of head l % 16, so lanes
+            // 16 s + 4 z .. + 3 hold the operand of block 4 s + z (rows:
+            // heads 4 z .. 4 z + 3, k: keys 4 s + i).  f16 / fp8 caches: fp16 weights
             // (times 2^kPScale, undone at the chunk end), the running sum
             // over the same rounded values; bf16 caches: the weight as a
             // bf16 hi part plus a bf16 lo part (about 16 significant
             // bits), the running sum over the float weights.
             typedef short s16x4 __attribute__((ext_vector_type(4)));
-            typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
-            typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
             typedef int i32x2 __attribute__((ext_vector_type(2)));
             s16x4 pb[NG], pbl[NG];
             float psum = 0.f;
@@ -704,76 +727,93 @@ void attn_kernel(AttnParams P) {
                 }
             }
             l1 = l1 * alpha + psum;
-            // rescale this lane's head (skipped when no head's max moved)
+            // rescale the accumulators (skipped when no head's max moved):
+            // every lane holds heads 4 z .. 4 z + 3 of set z, whose factors
+            // lanes 4 z .. 4 z + 3 hold
             if (__any(alpha != 1.f)) {
+                const int ab = __builtin_bit_cast(int, alpha);
 #pragma unroll
-                for (int m = 0; m < D / 16; ++m) pv_acc[m] *= alpha;
+                for (int z = 0; z < NQ; ++z) {
+                    const pv4 al4{__builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, 4 * z)),
+                                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, 4 * z + 1)),
+                                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, 4 * z + 2)),
+                                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, 4 * z + 3))};
+#pragma unroll
+                    for (int m = 0; m < D / 64; ++m) pv_acc[z * (D / 64) + m] *= al4;
+                }
             }
             // V to the wave's LDS rows, where its K was (this wave has
             // read them; its LDS accesses complete in order); fp8 codes as
-            // they are, each key at its row f8_vrow
+            // they are
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                if constexpr (F8) sm_k[wid][f8_vrow(i * RPI + r) * P8 + c] = vt[i];
+                if constexpr (F8) sm_k[wid][(i * RPI + r) * P8 + c] = vt[i];
                 else sm_k[wid][(i * RPI + r) * VPAD + c] = vt[i];
             }
             // one V tile in flight: the next one into the registers just
             // staged (rows clamped past the last item, as for K)
             if constexpr (VS1) load_tile(kA, vA, j + 1);
-            if constexpr (F8) {
-                // fp8: one v_mfma_f32_16x16x32_f16 per 16 dims and 32 keys
-                // (key groups 2 p and 2 p + 1).  Its B operand is the two
-                // groups' probabilities side by side: lane l holds keys
-                // 32 p + 4 (l / 16) + i and 32 p + 16 + 4 (l / 16) + i, i =
-                // 0..3, of head l % 16, as its k = 8 (l / 16) + 0..7.  Its A
-                // operand (V^T, 16 dims x those keys in that order) comes
-                // from the 8-bit transposing read: within each 16-lane
-                // group, lanes 2 j and 2 j + 1 point at 8 codes each of row
-                // j, and lane i receives code i of rows 0..7; row j here is
-                // the j-th key of the lane's list, dims 16 m .. 16 m + 15.
-                // The codes become fp16 (exact) in registers.
-                const int jr = (lane & 15) >> 1;
-                const int key0 = 4 * kq + (jr < 4 ? jr : 12 + jr);    // 16 + 4 kq + (jr - 4)
-                const uint8_t* vb = reinterpret_cast<const uint8_t*>(&sm_k[wid][0]) + 8 * (lane & 1);
+            {
+                // per 4 keys, 64 dims and 4 heads one 16-block 4x4x4
+                // product, O[head][dim] += P[head][key] V[key][dim], its A
+                // operand (P: 4 heads x 4 keys) broadcast from the block
+                // whose lanes hold those keys (lanes 16 s + 4 z .. + 3 hold
+                // keys 4 s + i of heads 4 z .. 4 z + 3: block 4 s + z) and
+                // its B operand V (4 keys x 4 dims per block), lane l
+                // holding dim 64 m + l of the 4 keys.  The transposing LDS
+                // reads give exactly that when every 16-lane group points at
+                // the same keys, group q at dims 64 m + 16 q .. + 15.
+                if constexpr (F8) {
+                    // 8-bit read: lanes 2 j, 2 j + 1 of a group point at 8
+                    // codes each of key 8 e + j; lane i receives code i of
+                    // the 8 keys, in key order (fp16 in registers, exact)
+                    const uint8_t* vb = reinterpret_cast<const uint8_t*>(&sm_k[wid][0]) +
+                                        ((lane & 15) >> 1) * (P8 * 16) + 16 * kq + 8 * (lane & 1);
+                    static_for<KT / 8>([&](auto ec) {
+                        constexpr int e = decltype(ec)::value;
+                        constexpr int n = e / 2, s0 = (2 * e) % 4;   // 16-key group, first 4-key block
+                        const u32x2 pa = __builtin_bit_cast(u32x2, pb[n]);
 #pragma unroll
-                for (int pp = 0; pp < NG / 2; ++pp) {
-                    const uint8_t* vrow = vb + f8_vrow(32 * pp + key0) * (P8 * 16);
-                    const h16x8 pbw = __builtin_shufflevector(
-                        __builtin_bit_cast(h16x4, pb[2 * pp]), __builtin_bit_cast(h16x4, pb[2 * pp + 1]),
-                        0, 1, 2, 3, 4, 5, 6, 7);
+                        for (int m = 0; m < D / 64; ++m) {
+                            const u32x2 v8 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                (__attribute__((address_space(3))) i32x2*)(vb + 8 * e * (P8 * 16) + 64 * m)));
+                            const u32x4 vh = fp8x8_to_f16x8(v8);
+                            static_for<NQ>([&](auto zc) {
+                                constexpr int z = decltype(zc)::value;
+                                pv4& acc4 = pv_acc[z * (D / 64) + m];
+                                acc4 = mfma4_bcast<4 * s0 + z, false>(pa, u32x2{vh.x, vh.y}, acc4);
+                                acc4 = mfma4_bcast<4 * s0 + 4 + z, false>(pa, u32x2{vh.z, vh.w}, acc4);
+                            });
+                        }
+                    });
+                } else {
+                    // 16-bit read: lanes 4 j .. 4 j + 3 of a group point at
+                    // 4 dims each of key 4 s + j; lane i receives element i
+                    // of the 4 keys
+                    const uint16_t* vb = reinterpret_cast<const uint16_t*>(&sm_k[wid][0]) +
+                                         ((lane & 15) >> 2) * (VPAD * 8) + 16 * kq + 4 * (lane & 3);
 #pragma unroll
-                    for (int m = 0; m < D / 16; ++m) {
-                        const u32x2 v8 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                            (__attribute__((address_space(3))) i32x2*)(vrow + 16 * m)));
-                        pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(h16x8, fp8x8_to_f16x8(v8)), pbw, pv_acc[m], 0, 0, 0);
+                    for (int kg = 0; kg < NG; ++kg) {
+                        const u32x2 ph = __builtin_bit_cast(u32x2, pb[kg]);
+                        static_for<4>([&](auto sc) {
+                            constexpr int s4 = decltype(sc)::value;
+                            const uint16_t* vrow = vb + (16 * kg + 4 * s4) * (VPAD * 8);
+#pragma unroll
+                            for (int m = 0; m < D / 64; ++m) {
+                                const u32x2 va = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (__attribute__((address_space(3))) s16x4*)(vrow + 64 * m)));
+                                static_for<NQ>([&](auto zc) {
+                                    constexpr int z = decltype(zc)::value;
+                                    pv4& acc4 = pv_acc[z * (D / 64) + m];
+                                    acc4 = mfma4_bcast<4 * s4 + z, DT == kBF16>(ph, va, acc4);
+                                    if constexpr (DT == kBF16)
+                                        acc4 = mfma4_bcast<4 * s4 + z, true>(
+                                            __builtin_bit_cast(u32x2, pbl[kg]), va, acc4);
+                                });
+                            }
+                        });
                     }
                 }
-            } else {
-            // A operand V^T (16 dims x 16 keys): lane l needs keys
-            // 4 (l / 16) + j of dim l % 16; the transposing LDS read hands
-            // lane i of each 16-lane group element i of the four rows its
-            // lanes 4 j .. 4 j + 3 point at (16 consecutive dims of key
-            // 4 (l / 16) + j)
-            const uint16_t* vrow0 = reinterpret_cast<const uint16_t*>(
-                &sm_k[wid][(4 * kq + ((lane & 15) >> 2)) * VPAD]) + 4 * (lane & 3);
-#pragma unroll
-            for (int kg = 0; kg < NG; ++kg) {
-                const uint16_t* vrow = vrow0 + kg * 16 * (VPAD * 8);
-#pragma unroll
-                for (int m = 0; m < D / 16; ++m) {
-                    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(vrow + 16 * m));
-                    if constexpr (DT == kBF16) {
-                        pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kg], pv_acc[m], 0, 0, 0);
-                        pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbl[kg], pv_acc[m], 0, 0, 0);
-                    } else {
-                        pv_acc[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                            __builtin_bit_cast(h16x4, va), __builtin_bit_cast(h16x4, pb[kg]),
-                            pv_acc[m], 0, 0, 0);
-                    }
-                }
-            }
             }
         } else {
             float s[G];
@@ -927,18 +967,18 @@ void attn_kernel(AttnParams P) {
             m1 = -INFINITY;
             l1 = 0.f;
             if (n_st == 0) st_first = ch;
-            // O^T from the matrix cores: the lanes of the group's heads write
-            // their dims 16 m + 4 (l / 16) + 0..3 (already summed over this
-            // wave's keys), GO heads at a time; all but the last GO heads are
-            // flushed here
-            const int hq = lane & 15, kq = lane >> 4;
+            // O from the matrix cores (already summed over this wave's
+            // keys): every lane writes dim 64 m + l of every head, GO heads
+            // at a time; all but the last GO heads are flushed here
 #pragma unroll
             for (int h0 = 0; h0 < G; h0 += GO) {
-                if (hq >= h0 && hq < h0 + GO) {
 #pragma unroll
-                    for (int m = 0; m < D / 16; ++m)
-                        *reinterpret_cast<pv4*>(&sm_o[buf][n_st][hq - h0][wid][16 * m + 4 * kq]) =
-                            pv_acc[m] * kPUnscale;
+                for (int ho = 0; ho < GO; ++ho) {
+                    const int hh = h0 + ho;
+#pragma unroll
+                    for (int m = 0; m < D / 64; ++m)
+                        sm_o[buf][n_st][ho][wid][64 * m + lane] =
+                            pv_acc[hh / 4 * (D / 64) + m][hh % 4] * kPUnscale;
                 }
                 if (h0 + GO < G) {
                     ++n_st;
@@ -947,7 +987,7 @@ void attn_kernel(AttnParams P) {
                 }
             }
 #pragma unroll
-            for (int m = 0; m < D / 16; ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < NACC; ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int hh = 0; hh < (MF ? 0 : G); ++hh) {
