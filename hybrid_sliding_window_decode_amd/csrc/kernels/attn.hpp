@@ -326,6 +326,10 @@ void attn_kernel(AttnParams P) {
     constexpr bool F8 = MF && DT == kFP8;
     constexpr int NQ = G / 4;                 // sets of 4 heads (matrix-core kernels)
     constexpr bool VS1 = MF && (D == 256 || F8);
+    // 4-head kernel: the query's MFMA operands (hi and lo, D / 32 slices)
+    // stay in registers for the whole launch instead of being read from LDS
+    // for every tile
+    constexpr bool QR = MF && G == 4;
     // heads per flush of the wave partials: at 256 dims the 8-head kernel
     // flushes its heads in two halves, so its partials take 16 KiB (LDS for
     // two workgroups per CU)
@@ -418,6 +422,7 @@ void attn_kernel(AttnParams P) {
     const int c = lane % LPR;       // 16-byte chunk of the row this lane reads
     const int r = lane / LPR;       // row within a wave-wide load
     float qs[G][EPC];               // this lane's query dims, set after the prologue
+    u32x4 qhr[QR ? D / 32 : 1], qlr[QR ? D / 32 : 1];    // 4-head kernel: query operands
 
     // This pair's K and V blocks: as lane pointers (VALU kernels), and as
     // the uniform block base plus a 32-bit lane offset (matrix-core kernels,
@@ -642,13 +647,7 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[kg][u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            // two slices in flight at a time: unrolled further, the
-            // operand reads of every slice would be issued up front and
-            // hold ~100 registers
-#pragma unroll 2
-            for (int sl = 0; sl < NS; ++sl) {
-                const u32x4 qh = *reinterpret_cast<const u32x4*>(qh_row + 32 * sl);
-                const u32x4 ql = *reinterpret_cast<const u32x4*>(ql_row + 32 * sl);
+            auto slice = [&](int sl, const u32x4& qh, const u32x4& ql) __attribute__((always_inline)) {
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
                     u32x4 a;
@@ -673,6 +672,19 @@ void attn_kernel(AttnParams P) {
                             __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, ql), al_, 0, 0, 0);
                     }
                 }
+            };
+            if constexpr (QR) {
+                // the query operands live in registers (read once per launch)
+#pragma unroll
+                for (int sl = 0; sl < NS; ++sl) slice(sl, qhr[sl], qlr[sl]);
+            } else {
+                // two slices in flight at a time: unrolled further, the
+                // operand reads of every slice would be issued up front and
+                // hold ~100 registers
+#pragma unroll 2
+                for (int sl = 0; sl < NS; ++sl)
+                    slice(sl, *reinterpret_cast<const u32x4*>(qh_row + 32 * sl),
+                          *reinterpret_cast<const u32x4*>(ql_row + 32 * sl));
             }
             // online softmax per head over this lane's keys, the head's max
             // across its 4 lanes (distances 16 and 32)
@@ -1103,6 +1115,14 @@ void attn_kernel(AttnParams P) {
         for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) qs[hh][e] = sm_q[hh][c * EPC + e];
+        }
+    }
+    if constexpr (QR) {
+        const int hq = lane & 15, kq = lane >> 4;
+#pragma unroll
+        for (int sl = 0; sl < D / 32; ++sl) {
+            qhr[sl] = *reinterpret_cast<const u32x4*>(&sm_qh[hq < G ? hq : G][8 * kq + 32 * sl]);
+            qlr[sl] = *reinterpret_cast<const u32x4*>(&sm_ql[hq < G ? hq : G][8 * kq + 32 * sl]);
         }
     }
 
