@@ -288,8 +288,8 @@ constexpr int stash_slots() { return G == 1 ? 4 : (G == 2 ? 2 : 1); }
 
 // Flush buffers of the wave chunk partials: two, used alternately, so a
 // slot is rewritten only after the barrier of the flush in between; the
-// 8-head kernel keeps one (its partials take 32 KiB) and ends each flush
-// with a second barrier instead.
+// 8-head kernel keeps one (its partials sit over the waves' K / V rows)
+// and ends each flush with a second barrier instead.
 template <int G>
 constexpr int flush_buffers() { return G == 8 ? 1 : 2; }
 
@@ -330,11 +330,12 @@ void attn_kernel(AttnParams P) {
     // stay in registers for the whole launch instead of being read from LDS
     // for every tile
     constexpr bool QR = MF && G == 4;
-    // heads per flush of the wave partials: at 256 dims the 8-head kernel
-    // flushes its heads in two halves, so its partials take 16 KiB (LDS for
-    // two workgroups per CU)
-    constexpr int GO = MF && G == 8 && D == 256 ? 4 : G;
-    static_assert(GO == G || kStash == 1, "split flush: one chunk per flush");
+    // 8-head kernel (OA): each wave writes its chunk partial (8 heads x D
+    // floats) over its own K / V rows, free at a chunk end, so the partials
+    // take no LDS of their own (two workgroups per CU); every flush ends
+    // with a barrier before any wave stages its next tile there
+    constexpr bool OA = MF && G == 8;
+    static_assert(!OA || NB == 1, "partials over the K / V rows: one flush buffer");
     // fp16 probabilities of the matrix-core kernels over f16 / fp8 caches
     // are scaled by 2^kPScale; a wave's chunk partial (sum and values) is
     // scaled back by kPUnscale, a power of two, when the chunk ends
@@ -352,12 +353,14 @@ void attn_kernel(AttnParams P) {
     constexpr int P8 = D / 16 + 1;                        // 16-byte units per staged fp8 row
     __shared__ float sm_q[MF ? 1 : G][D];
     __shared__ u32x4 sm_k[MF ? kAttnWaves : 1][MF ? KT * (F8 ? P8 : VPAD) : 1];   // K rows, then V rows
+    static_assert(!OA || G * D * 4 <= KT * (F8 ? P8 : VPAD) * 16, "a wave's partial fits its K / V rows");
     // query rows padded by 16 bytes too: unpadded, the G heads' rows (512
     // bytes apart) would share banks and the operand reads conflict 4 ways
     __shared__ __attribute__((aligned(16))) uint16_t sm_qh[MF ? G + 1 : 1][MF ? D + 8 : 1];
     __shared__ __attribute__((aligned(16))) uint16_t sm_ql[MF ? G + 1 : 1][MF ? D + 8 : 1];
     // (both read 16 bytes at a time: aligned to 16)
-    __shared__ __attribute__((aligned(16))) float sm_o[NB][kStash][GO][kAttnWaves][D];   // wave chunk partials, by flush parity
+    // wave chunk partials, by flush parity (8-head kernel: over the K / V rows)
+    __shared__ __attribute__((aligned(16))) float sm_o[OA ? 1 : NB][OA ? 1 : kStash][OA ? 1 : G][OA ? 1 : kAttnWaves][OA ? 1 : D];
     __shared__ float sm_m[NB][kStash][G][kAttnWaves], sm_l[NB][kStash][G][kAttnWaves];
     __shared__ float sm_dot[G][kAttnWaves];
     __shared__ float sm_gl[G][kAttnWaves];
@@ -897,15 +900,21 @@ void attn_kernel(AttnParams P) {
     // per chunk.
     int n_st = 0, st_first = 0, n_flush = 0;
 
-    // Heads h0 .. h0 + GO - 1 of the stashed chunks (every head, but for the
-    // 8-head kernel over 16-bit caches, which flushes two halves per chunk).
-    auto flush_heads = [&](int buf, int h0) __attribute__((always_inline)) {
+    // Wave w's partial of head hh for stash slot s of flush buffer buf
+    // (8-head kernel: over the wave's K / V rows).
+    auto part = [&](int buf, int s, int hh, int w) __attribute__((always_inline)) -> float* {
+        if constexpr (OA) return reinterpret_cast<float*>(&sm_k[w][0]) + hh * D;
+        else return &sm_o[buf][s][hh][w][0];
+    };
+
+    auto flush = [&]() __attribute__((always_inline)) {
+        const int buf = n_flush % NB;
+        ++n_flush;
         __syncthreads();
         for (int s = 0; s < n_st; ++s) {
             const int ch = st_first + s;
 #pragma unroll
-            for (int ho = 0; ho < GO; ++ho) {
-                const int hh = h0 + ho;
+            for (int hh = 0; hh < G; ++hh) {
                 const float Mc = lds_max<kAttnWaves>(sm_m[buf][s][hh]);
                 float Lc = 0.f, Oc = 0.f;
                 if (Mc != -INFINITY) {
@@ -913,7 +922,7 @@ void attn_kernel(AttnParams P) {
                     for (int w = 0; w < kAttnWaves; ++w) {
                         const float a = fast_exp2(sm_m[buf][s][hh][w] - Mc);
                         Lc = fmaf(sm_l[buf][s][hh][w], a, Lc);
-                        if (t < D) Oc = fmaf(sm_o[buf][s][ho][w][t], a, Oc);
+                        if (t < D) Oc = fmaf(part(buf, s, hh, w)[t], a, Oc);
                     }
                 }
                 const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
@@ -950,13 +959,8 @@ void attn_kernel(AttnParams P) {
             }
         }
         // a single flush buffer: every thread has read it before any wave
-        // writes its next chunk's partial (or next heads) there
+        // writes its next chunk's partial (or stages a tile) there
         if constexpr (NB == 1) __syncthreads();
-    };
-    auto flush = [&]() __attribute__((always_inline)) {
-        const int buf = n_flush % NB;
-        ++n_flush;
-        flush_heads(buf, G - GO);
         n_st = 0;
     };
 
@@ -980,23 +984,15 @@ void attn_kernel(AttnParams P) {
             l1 = 0.f;
             if (n_st == 0) st_first = ch;
             // O from the matrix cores (already summed over this wave's
-            // keys): every lane writes dim 64 m + l of every head, GO heads
-            // at a time; all but the last GO heads are flushed here
+            // keys): every lane writes dim 64 m + l of every head (the
+            // 8-head kernel over its own K / V rows: it has read them, and
+            // its LDS accesses complete in order)
 #pragma unroll
-            for (int h0 = 0; h0 < G; h0 += GO) {
+            for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
-                for (int ho = 0; ho < GO; ++ho) {
-                    const int hh = h0 + ho;
-#pragma unroll
-                    for (int m = 0; m < D / 64; ++m)
-                        sm_o[buf][n_st][ho][wid][64 * m + lane] =
-                            pv_acc[hh / 4 * (D / 64) + m][hh % 4] * kPUnscale;
-                }
-                if (h0 + GO < G) {
-                    ++n_st;
-                    flush_heads(buf, h0);
-                    --n_st;
-                }
+                for (int m = 0; m < D / 64; ++m)
+                    part(buf, n_st, hh, wid)[64 * m + lane] =
+                        pv_acc[hh / 4 * (D / 64) + m][hh % 4] * kPUnscale;
             }
 #pragma unroll
             for (int m = 0; m < NACC; ++m) pv_acc[m] = pv4{0.f, 0.f, 0.f, 0.f};
