@@ -326,10 +326,6 @@ void attn_kernel(AttnParams P) {
     constexpr bool F8 = MF && DT == kFP8;
     constexpr int NQ = G / 4;                 // sets of 4 heads (matrix-core kernels)
     constexpr bool VS1 = MF && (D == 256 || F8);
-    // 4-head kernel: the query's MFMA operands (hi and lo, D / 32 slices)
-    // stay in registers for the whole launch instead of being read from LDS
-    // for every tile
-    constexpr bool QR = MF && G == 4;
     // 8-head kernel (OA): each wave writes its chunk partial (8 heads x D
     // floats) over its own K / V rows, free at a chunk end, so the partials
     // take no LDS of their own (two workgroups per CU); every flush ends
@@ -425,7 +421,9 @@ void attn_kernel(AttnParams P) {
     const int c = lane % LPR;       // 16-byte chunk of the row this lane reads
     const int r = lane / LPR;       // row within a wave-wide load
     float qs[G][EPC];               // this lane's query dims, set after the prologue
-    u32x4 qhr[QR ? D / 32 : 1], qlr[QR ? D / 32 : 1];    // 4-head kernel: query operands
+    // matrix-core kernels: the query's MFMA operands (hi and lo, D / 32
+    // slices), in registers for the whole launch (set after the prologue)
+    u32x4 qhr[MF ? D / 32 : 1], qlr[MF ? D / 32 : 1];
 
     // This pair's K and V blocks: as lane pointers (VALU kernels), and as
     // the uniform block base plus a 32-bit lane offset (matrix-core kernels,
@@ -630,10 +628,6 @@ void attn_kernel(AttnParams P) {
             typedef float f32x4 __attribute__((ext_vector_type(4)));
             constexpr int NG = KT / 16, NS = D / 32;
             const int hq = lane & 15, kq = lane >> 4;
-            // lanes of heads >= G read the zero row G (one address: a broadcast)
-            const uint16_t* qh_row = &sm_qh[hq < G ? hq : G][8 * kq];
-            const uint16_t* ql_row = &sm_ql[hq < G ? hq : G][8 * kq];
-            asm volatile("" ::: "memory");     // the query reads below stay in the loop
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
                 if constexpr (F8) sm_k[wid][(i * RPI + r) * P8 + c] = kR[i];
@@ -650,7 +644,11 @@ void attn_kernel(AttnParams P) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[kg][u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            auto slice = [&](int sl, const u32x4& qh, const u32x4& ql) __attribute__((always_inline)) {
+            // the query operands are in registers (qhr, qlr: read once per launch)
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                const u32x4& qh = qhr[sl];
+                const u32x4& ql = qlr[sl];
 #pragma unroll
                 for (int kg = 0; kg < NG; ++kg) {
                     u32x4 a;
@@ -675,19 +673,6 @@ void attn_kernel(AttnParams P) {
                             __builtin_bit_cast(op8, a), __builtin_bit_cast(op8, ql), al_, 0, 0, 0);
                     }
                 }
-            };
-            if constexpr (QR) {
-                // the query operands live in registers (read once per launch)
-#pragma unroll
-                for (int sl = 0; sl < NS; ++sl) slice(sl, qhr[sl], qlr[sl]);
-            } else {
-                // two slices in flight at a time: unrolled further, the
-                // operand reads of every slice would be issued up front and
-                // hold ~100 registers
-#pragma unroll 2
-                for (int sl = 0; sl < NS; ++sl)
-                    slice(sl, *reinterpret_cast<const u32x4*>(qh_row + 32 * sl),
-                          *reinterpret_cast<const u32x4*>(ql_row + 32 * sl));
             }
             // online softmax per head over this lane's keys, the head's max
             // across its 4 lanes (distances 16 and 32)
@@ -1113,7 +1098,8 @@ void attn_kernel(AttnParams P) {
             for (int e = 0; e < EPC; ++e) qs[hh][e] = sm_q[hh][c * EPC + e];
         }
     }
-    if constexpr (QR) {
+    if constexpr (MF) {
+        // lanes of heads >= G read the zero row G
         const int hq = lane & 15, kq = lane >> 4;
 #pragma unroll
         for (int sl = 0; sl < D / 32; ++sl) {
