@@ -216,6 +216,19 @@ struct Fold {
         O = fmaf(O, a, o * b);
         M = Mn;
     }
+    // The same as add, with selects instead of branches (so a caller's
+    // loads for several folds need not wait for one another).
+    __device__ __forceinline__ void add_sel(float m, float l, float o) {
+        const bool take = l > 0.f, have = L > 0.f;
+        const float Mn = fmaxf(M, m);
+        const float a = fast_exp2(M - Mn);
+        const float b = fast_exp2(m - Mn);
+        const float Lm = fmaf(L, a, l * b);
+        const float Om = fmaf(O, a, o * b);
+        M = take ? (have ? Mn : m) : M;
+        L = take ? (have ? Lm : l) : L;
+        O = take ? (have ? Om : o) : O;
+    }
 };
 
 // One exchange of the transposed butterfly: a lane whose `M` bit is set
@@ -282,7 +295,8 @@ __device__ __forceinline__ float transposed_reduce4(const float (&v)[4], int lan
 }
 
 // Chunk-partial slots per flush buffer: the LDS stash holds kStash chunks
-// of every query head of the group, 32 KiB in all.
+// of every query head of the group, 32 KiB in all at 256 dims (the 8-head
+// kernel's one slot sits over its waves' K / V rows instead).
 template <int G>
 constexpr int stash_slots() { return G == 1 ? 4 : (G == 2 ? 2 : 1); }
 
@@ -898,47 +912,83 @@ void attn_kernel(AttnParams P) {
         __syncthreads();
         for (int s = 0; s < n_st; ++s) {
             const int ch = st_first + s;
+            // every head's wave maxima, sums and partials are read first and
+            // merged with selects, not branches (a branch per head would make
+            // each head wait for its own LDS reads in turn)
+            float Mc[G], Lc[G], Oc[G];
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
-                const float Mc = lds_max<kAttnWaves>(sm_m[buf][s][hh]);
-                float Lc = 0.f, Oc = 0.f;
-                if (Mc != -INFINITY) {
+                float mw[kAttnWaves], lw[kAttnWaves], ow[kAttnWaves];
 #pragma unroll
-                    for (int w = 0; w < kAttnWaves; ++w) {
-                        const float a = fast_exp2(sm_m[buf][s][hh][w] - Mc);
-                        Lc = fmaf(sm_l[buf][s][hh][w], a, Lc);
-                        if (t < D) Oc = fmaf(part(buf, s, hh, w)[t], a, Oc);
+                for (int w = 0; w < kAttnWaves; ++w) {
+                    mw[w] = sm_m[buf][s][hh][w];
+                    lw[w] = sm_l[buf][s][hh][w];
+                    ow[w] = t < D ? part(buf, s, hh, w)[t] : 0.f;
+                }
+                float M = mw[0];
+#pragma unroll
+                for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, mw[w]);
+                // no valid key in the chunk: sum and partial stay zero
+                const bool any = M != -INFINITY;
+                float L = 0.f, O = 0.f;
+#pragma unroll
+                for (int w = 0; w < kAttnWaves; ++w) {
+                    const float a = any ? fast_exp2(mw[w] - M) : 0.f;
+                    L = fmaf(lw[w], a, L);
+                    O = fmaf(ow[w], a, O);
+                }
+                Mc[hh] = M;
+                Lc[hh] = L;
+                Oc[hh] = O;
+            }
+            // then each head's chunk partial is kept (idle heads of the 4- and
+            // 8-head kernels: nothing to keep)
+            if (MODE == kModePartials) {
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    if (hh >= gv) continue;
+                    const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
+                    if (t < D) P.part_o[idx * D + t] = Oc[hh] * vscale;
+                    if (tid == 0) {
+                        P.part_ml[idx * 2 + 0] = Mc[hh] == -INFINITY ? -INFINITY : Mc[hh] * kLn2;
+                        P.part_ml[idx * 2 + 1] = Lc[hh];
                     }
                 }
-                const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
-                if (hh >= gv) {
-                    // idle head of the 4-head kernel: nothing to keep
-                } else if (MODE == kModePartials) {
-                    if (t < D) P.part_o[idx * D + t] = Oc * vscale;
-                    if (tid == 0) {
-                        P.part_ml[idx * 2 + 0] = Mc == -INFINITY ? -INFINITY : Mc * kLn2;
-                        P.part_ml[idx * 2 + 1] = Lc;
+            } else if (P.wpp == 1) {
+                if constexpr (MF) {
+                    // the running folds wait in LDS: all read, folded, written
+                    Fold f[G];
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+                        f[hh].M = sm_run_ml[hh][wid][0];
+                        f[hh].L = sm_run_ml[hh][wid][1];
+                        f[hh].O = t < D ? sm_run_o[hh][t] : 0.f;
                     }
-                } else if (P.wpp == 1) {
-                    if constexpr (MF) {
-                        Fold f;
-                        f.M = sm_run_ml[hh][wid][0];
-                        f.L = sm_run_ml[hh][wid][1];
-                        f.O = t < D ? sm_run_o[hh][t] : 0.f;
-                        f.add(Mc, Lc, Oc);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) f[hh].add_sel(Mc[hh], Lc[hh], Oc[hh]);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+                        if (hh >= gv) continue;
                         if (lane == 0) {
-                            sm_run_ml[hh][wid][0] = f.M;
-                            sm_run_ml[hh][wid][1] = f.L;
+                            sm_run_ml[hh][wid][0] = f[hh].M;
+                            sm_run_ml[hh][wid][1] = f[hh].L;
                         }
-                        if (t < D) sm_run_o[hh][t] = f.O;
-                    } else {
-                        run[hh].add(Mc, Lc, Oc);
+                        if (t < D) sm_run_o[hh][t] = f[hh].O;
                     }
                 } else {
-                    if (t < D) st_agent(P.part_o + idx * D + t, Oc);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh)
+                        if (hh < gv) run[hh].add(Mc[hh], Lc[hh], Oc[hh]);
+                }
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    if (hh >= gv) continue;
+                    const size_t idx = (size_t)(bh0 + hh) * P.n_chunk + ch;
+                    if (t < D) st_agent(P.part_o + idx * D + t, Oc[hh]);
                     if (tid == 0) {
-                        st_agent(P.part_ml + idx * 2 + 0, Mc);
-                        st_agent(P.part_ml + idx * 2 + 1, Lc);
+                        st_agent(P.part_ml + idx * 2 + 0, Mc[hh]);
+                        st_agent(P.part_ml + idx * 2 + 1, Lc[hh]);
                     }
                 }
             }
@@ -1233,19 +1283,25 @@ void attn_kernel(AttnParams P) {
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Join the new entry as a one-key partial (scores summed in the prologue).
+    // Join the new entry as a one-key partial (scores summed in the prologue),
+    // every head's LDS reads first.
+    float s_new[G], logit[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        const float s_new = lds_tree_sum<kAttnWaves>(sm_dot[hh]);
-        run[hh].add(s_new, 1.f, vh);
+        s_new[hh] = lds_tree_sum<kAttnWaves>(sm_dot[hh]);
+        if (gproj) logit[hh] = lds_tree_sum<kAttnWaves>(sm_gl[hh]);
+        else if constexpr (MF) logit[hh] = sm_glogit[hh];
+        else logit[hh] = glogit[hh];
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        if constexpr (MF) run[hh].add_sel(s_new[hh], 1.f, vh);
+        else run[hh].add(s_new[hh], 1.f, vh);
         if (t < D && hh < gv) {
             float o = run[hh].O / run[hh].L;
             if (DT == kFP8) o *= vscale;
-            if (MODE == kModeStep && (gproj || P.gate != nullptr)) {
-                const float logit = gproj ? lds_tree_sum<kAttnWaves>(sm_gl[hh])
-                                          : (MF ? sm_glogit[hh] : glogit[hh]);
-                o *= 1.f / (1.f + expf(-logit));
-            }
+            if (MODE == kModeStep && (gproj || P.gate != nullptr))
+                o *= 1.f / (1.f + expf(-logit[hh]));
             P.out[(size_t)(bh0 + hh) * D + t] = o;
         }
     }
