@@ -888,9 +888,9 @@ void attn_kernel(AttnParams P) {
         }
     };
 
-    // End of a chunk (every wave, same point): the wave's partial for it is
-    // reduced across lanes and written to its LDS slot of the current flush
-    // buffer.  Every kStash chunks, and once at the end, the buffer is
+    // End of a chunk (every wave, same point): the wave's partial for it
+    // (reduced across lanes first in the one- and two-head kernels) is
+    // written to its LDS slot of the current flush buffer.  Every kStash chunks, and once at the end, the buffer is
     // flushed: one barrier, then each thread forms the chunk partials for its
     // dim t, in chunk order, and folds (single workgroup per pair) or stores
     // them.  The two buffers alternate, so a slot is rewritten only after the
