@@ -906,10 +906,88 @@ void attn_kernel(AttnParams P) {
         else return &sm_o[buf][s][hh][w][0];
     };
 
+    // Matrix-core kernels: the flush runs head-major, thread tid merging
+    // head tid / TPH at its EH consecutive dims, so each thread takes the
+    // exponentials of one head's wave maxima (not of every head's) and reads
+    // its partials as vectors; each (head, dim) gets the same arithmetic.
+    constexpr int TPH = MF ? kAttnThreads / G : 1;       // threads per head
+    constexpr int EH = MF ? D / TPH : 1;                  // dims per thread
+    static_assert(!MF || EH * TPH == D, "head-major flush: whole dims per thread");
+    const int fh = MF ? tid / TPH : 0;                    // this thread's head
+    const int fd = MF ? (tid % TPH) * EH : 0;             // its first dim
+
     auto flush = [&]() __attribute__((always_inline)) {
         const int buf = n_flush % NB;
         ++n_flush;
         __syncthreads();
+        if constexpr (MF) {
+            for (int s = 0; s < n_st; ++s) {
+                const int ch = st_first + s;
+                float mw[kAttnWaves], lw[kAttnWaves], ow[kAttnWaves][EH];
+#pragma unroll
+                for (int w = 0; w < kAttnWaves; ++w) {
+                    mw[w] = sm_m[buf][s][fh][w];
+                    lw[w] = sm_l[buf][s][fh][w];
+                    const float* pw = part(buf, s, fh, w) + fd;
+#pragma unroll
+                    for (int e = 0; e < EH; ++e) ow[w][e] = pw[e];
+                }
+                float M = mw[0];
+#pragma unroll
+                for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, mw[w]);
+                // no valid key in the chunk: sum and partial stay zero
+                const bool any = M != -INFINITY;
+                float L = 0.f, O[EH];
+#pragma unroll
+                for (int e = 0; e < EH; ++e) O[e] = 0.f;
+#pragma unroll
+                for (int w = 0; w < kAttnWaves; ++w) {
+                    const float a = any ? fast_exp2(mw[w] - M) : 0.f;
+                    L = fmaf(lw[w], a, L);
+#pragma unroll
+                    for (int e = 0; e < EH; ++e) O[e] = fmaf(ow[w][e], a, O[e]);
+                }
+                if (fh >= gv) {
+                    // idle head: nothing to keep
+                } else if (MODE == kModePartials) {
+                    const size_t idx = (size_t)(bh0 + fh) * P.n_chunk + ch;
+#pragma unroll
+                    for (int e = 0; e < EH; ++e) P.part_o[idx * D + fd + e] = O[e] * vscale;
+                    if (fd == 0) {
+                        P.part_ml[idx * 2 + 0] = M == -INFINITY ? -INFINITY : M * kLn2;
+                        P.part_ml[idx * 2 + 1] = L;
+                    }
+                } else if (P.wpp == 1) {
+                    // the running fold waits in LDS, each (head, dim) with the
+                    // threads that merge it (M and L: the head's first one)
+                    float fo[EH];
+#pragma unroll
+                    for (int e = 0; e < EH; ++e) fo[e] = sm_run_o[fh][fd + e];
+                    const float fM = sm_run_ml[fh][0][0], fL = sm_run_ml[fh][0][1];
+#pragma unroll
+                    for (int e = 0; e < EH; ++e) {
+                        Fold f;
+                        f.M = fM;
+                        f.L = fL;
+                        f.O = fo[e];
+                        f.add_sel(M, L, O[e]);
+                        sm_run_o[fh][fd + e] = f.O;
+                        if (e == 0 && fd == 0) {
+                            sm_run_ml[fh][0][0] = f.M;
+                            sm_run_ml[fh][0][1] = f.L;
+                        }
+                    }
+                } else {
+                    const size_t idx = (size_t)(bh0 + fh) * P.n_chunk + ch;
+#pragma unroll
+                    for (int e = 0; e < EH; ++e) st_agent(P.part_o + idx * D + fd + e, O[e]);
+                    if (fd == 0) {
+                        st_agent(P.part_ml + idx * 2 + 0, M);
+                        st_agent(P.part_ml + idx * 2 + 1, L);
+                    }
+                }
+            }
+        } else
         for (int s = 0; s < n_st; ++s) {
             const int ch = st_first + s;
             // every head's wave maxima, sums and partials are read first and
@@ -955,31 +1033,9 @@ void attn_kernel(AttnParams P) {
                     }
                 }
             } else if (P.wpp == 1) {
-                if constexpr (MF) {
-                    // the running folds wait in LDS: all read, folded, written
-                    Fold f[G];
 #pragma unroll
-                    for (int hh = 0; hh < G; ++hh) {
-                        f[hh].M = sm_run_ml[hh][wid][0];
-                        f[hh].L = sm_run_ml[hh][wid][1];
-                        f[hh].O = t < D ? sm_run_o[hh][t] : 0.f;
-                    }
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) f[hh].add_sel(Mc[hh], Lc[hh], Oc[hh]);
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) {
-                        if (hh >= gv) continue;
-                        if (lane == 0) {
-                            sm_run_ml[hh][wid][0] = f[hh].M;
-                            sm_run_ml[hh][wid][1] = f[hh].L;
-                        }
-                        if (t < D) sm_run_o[hh][t] = f[hh].O;
-                    }
-                } else {
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh)
-                        if (hh < gv) run[hh].add(Mc[hh], Lc[hh], Oc[hh]);
-                }
+                for (int hh = 0; hh < G; ++hh)
+                    if (hh < gv) run[hh].add(Mc[hh], Lc[hh], Oc[hh]);
             } else {
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
@@ -1211,10 +1267,11 @@ void attn_kernel(AttnParams P) {
     if (n_st > 0) flush();
     if constexpr (MF) {
         if (MODE != kModePartials && P.wpp == 1) {
+            __syncthreads();            // the folds were written head-major
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
-                run[hh].M = sm_run_ml[hh][wid][0];
-                run[hh].L = sm_run_ml[hh][wid][1];
+                run[hh].M = sm_run_ml[hh][0][0];
+                run[hh].L = sm_run_ml[hh][0][1];
                 run[hh].O = t < D ? sm_run_o[hh][t] : 0.f;
             }
         }
