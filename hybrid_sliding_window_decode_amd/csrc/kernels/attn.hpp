@@ -231,6 +231,26 @@ struct Fold {
     }
 };
 
+// Fold::add for E values sharing one (M, L): a partial (m, l, o[0..E)) into
+// the running (M, L, O[0..E)), each O[e] exactly as Fold::add would fold
+// it (M and L do not depend on O).
+template <int E>
+__device__ __forceinline__ void fold_row(float& M, float& L, float (&O)[E], float m, float l,
+                                         const float (&o)[E]) {
+    const bool take = l > 0.f, have = L > 0.f;
+    const float Mn = fmaxf(M, m);
+    const float a = fast_exp2(M - Mn);
+    const float b = fast_exp2(m - Mn);
+    const float Lm = fmaf(L, a, l * b);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float Om = fmaf(O[e], a, o[e] * b);
+        O[e] = take ? (have ? Om : o[e]) : O[e];
+    }
+    M = take ? (have ? Mn : m) : M;
+    L = take ? (have ? Lm : l) : L;
+}
+
 // One exchange of the transposed butterfly: a lane whose `M` bit is set
 // ends with the sum over both lanes of the pair of the upper value, its
 // partner with that of the lower one (each lane adds its own value first).
@@ -382,6 +402,7 @@ void attn_kernel(AttnParams P) {
     __shared__ float sm_run_ml[MF ? G : 1][MF ? kAttnWaves : 1][2];
     __shared__ float sm_run_o[MF ? G : 1][MF ? D : 1];
     __shared__ float sm_glogit[MF ? G : 1];       // MFMA kernel: the given gate logits
+    __shared__ float sm_vh[MF ? D : 1];           // MFMA kernel: the new entry's value
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -1175,6 +1196,7 @@ void attn_kernel(AttnParams P) {
             v_hat = round_to_elt<DT>(DT == kFP8 ? __fdiv_rn(v_t, vscale) : v_t);
             khf = elt_to_f32<DT>(k_hat);
             vh = elt_to_f32<DT>(v_hat);
+            if constexpr (MF) sm_vh[t] = vh;        // joined head-major in the epilogue
         }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
@@ -1265,15 +1287,18 @@ void attn_kernel(AttnParams P) {
     }
     if (c_valid > c_full) end_chunk(c_full);            // the partly valid chunk
     if (n_st > 0) flush();
+    // Matrix-core kernels finish head-major too: thread (fh, fd) holds the
+    // running fold of head fh at dims fd .. fd + EH - 1 (M and L per head)
+    float hM = -INFINITY, hL = 0.f, hO[EH];
+#pragma unroll
+    for (int e = 0; e < EH; ++e) hO[e] = 0.f;
     if constexpr (MF) {
         if (MODE != kModePartials && P.wpp == 1) {
-            __syncthreads();            // the folds were written head-major
+            // folded in LDS by this thread's own flushes
+            hM = sm_run_ml[fh][0][0];
+            hL = sm_run_ml[fh][0][1];
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                run[hh].M = sm_run_ml[hh][0][0];
-                run[hh].L = sm_run_ml[hh][0][1];
-                run[hh].O = t < D ? sm_run_o[hh][t] : 0.f;
-            }
+            for (int e = 0; e < EH; ++e) hO[e] = sm_run_o[fh][fd + e];
         }
     }
 
@@ -1312,7 +1337,34 @@ void attn_kernel(AttnParams P) {
         if (!sm_last) return;
 
         // Last arrival folds the valid chunks of each head in chunk order, 32
-        // partials' loads in flight before any is folded.
+        // partials' loads in flight before any is folded (matrix-core
+        // kernels: head-major, 64 partial values in flight per thread).
+        if constexpr (MF) {
+            if (fh < gv) {
+                const float* pml = P.part_ml + (size_t)(bh0 + fh) * P.n_chunk * 2;
+                const float* po = P.part_o + (size_t)(bh0 + fh) * P.n_chunk * D + fd;
+                constexpr int kB = EH >= 8 ? 8 : 32 / EH;
+                int i = 0;
+                for (; i + kB <= n_valid_chunks; i += kB) {
+                    float xm[kB], xl[kB], xo[kB][EH];
+#pragma unroll
+                    for (int u = 0; u < kB; ++u) {
+                        xm[u] = ld_agent(pml + 2 * (i + u));
+                        xl[u] = ld_agent(pml + 2 * (i + u) + 1);
+#pragma unroll
+                        for (int e = 0; e < EH; ++e) xo[u][e] = ld_agent(po + (size_t)(i + u) * D + e);
+                    }
+#pragma unroll
+                    for (int u = 0; u < kB; ++u) fold_row<EH>(hM, hL, hO, xm[u], xl[u], xo[u]);
+                }
+                for (; i < n_valid_chunks; ++i) {
+                    float xo[EH];
+#pragma unroll
+                    for (int e = 0; e < EH; ++e) xo[e] = ld_agent(po + (size_t)i * D + e);
+                    fold_row<EH>(hM, hL, hO, ld_agent(pml + 2 * i), ld_agent(pml + 2 * i + 1), xo);
+                }
+            }
+        } else
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
             if (hh >= gv) continue;
@@ -1340,26 +1392,44 @@ void attn_kernel(AttnParams P) {
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Join the new entry as a one-key partial (scores summed in the prologue),
-    // every head's LDS reads first.
-    float s_new[G], logit[G];
+    // Join the new entry as a one-key partial (scores summed in the prologue).
+    // Matrix-core kernels: head-major, the head's gate computed once.
+    if constexpr (MF) {
+        const float sn = lds_tree_sum<kAttnWaves>(sm_dot[fh]);
+        const float lg = gproj ? lds_tree_sum<kAttnWaves>(sm_gl[fh]) : sm_glogit[fh];
+        float vv[EH];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        s_new[hh] = lds_tree_sum<kAttnWaves>(sm_dot[hh]);
-        if (gproj) logit[hh] = lds_tree_sum<kAttnWaves>(sm_gl[hh]);
-        else if constexpr (MF) logit[hh] = sm_glogit[hh];
-        else logit[hh] = glogit[hh];
-    }
+        for (int e = 0; e < EH; ++e) vv[e] = sm_vh[fd + e];
+        fold_row<EH>(hM, hL, hO, sn, 1.f, vv);
+        if (fh < gv) {
+            const bool gated = MODE == kModeStep && (gproj || P.gate != nullptr);
+            const float gs = gated ? 1.f / (1.f + expf(-lg)) : 1.f;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        if constexpr (MF) run[hh].add_sel(s_new[hh], 1.f, vh);
-        else run[hh].add(s_new[hh], 1.f, vh);
-        if (t < D && hh < gv) {
-            float o = run[hh].O / run[hh].L;
-            if (DT == kFP8) o *= vscale;
-            if (MODE == kModeStep && (gproj || P.gate != nullptr))
-                o *= 1.f / (1.f + expf(-logit[hh]));
-            P.out[(size_t)(bh0 + hh) * D + t] = o;
+            for (int e = 0; e < EH; ++e) {
+                float o = hO[e] / hL;
+                if (DT == kFP8) o *= vscale;
+                if (gated) o *= gs;
+                P.out[(size_t)(bh0 + fh) * D + fd + e] = o;
+            }
+        }
+    } else {
+        // every head's LDS reads first
+        float s_new[G], logit[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            s_new[hh] = lds_tree_sum<kAttnWaves>(sm_dot[hh]);
+            logit[hh] = gproj ? lds_tree_sum<kAttnWaves>(sm_gl[hh]) : glogit[hh];
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            run[hh].add(s_new[hh], 1.f, vh);
+            if (t < D && hh < gv) {
+                float o = run[hh].O / run[hh].L;
+                if (DT == kFP8) o *= vscale;
+                if (MODE == kModeStep && (gproj || P.gate != nullptr))
+                    o *= 1.f / (1.f + expf(-logit[hh]));
+                P.out[(size_t)(bh0 + hh) * D + t] = o;
+            }
         }
     }
 
