@@ -68,11 +68,10 @@ def kernel_group(kv, heads=H):
     """(G, pieces): query heads per workgroup of the attention kernel that runs
     `heads` query heads over the HKV kv heads, and the pieces each group is
     split into (3 and 4 run the 4-head kernel, 5 to 8 the 8-head one, a
-    larger group pieces of 8; over fp8 a group of 2 runs the 4-head kernel
-    on append caches)."""
+    larger group pieces of 8; over fp8 a group of 2 runs the 4-head kernel)."""
     group = heads // HKV
     if group == 2 and kv == "fp8":
-        return 4, 1             # the full layer's kernel (rings keep the 2-head one)
+        return 4, 1
     if group <= 2:
         return group, 1
     piece = 8 if group > 4 else 4

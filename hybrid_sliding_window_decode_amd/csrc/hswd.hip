@@ -202,11 +202,10 @@ int32_t dispatch_attn(AttnParams P, int D, int DT, int grid, hipStream_t st) {
     const int group = P.H / P.Hkv;
     P.Gq = group;
     if (group == 1) return launch_attn_group<1, false>(P, MODE, D, DT, grid, st);
-    // A group of 2 over an fp8 append cache runs the 4-head matrix-core
-    // kernel with two heads idle: at 64 x 4096 its full layer takes 164.6 us
-    // against 170.0 us for the 2-head kernel; over rings the 2-head kernel
-    // is the faster one.
-    if (group == 2 && !(DT == kFP8 && !P.ring))
+    // A group of 2 over an fp8 cache runs the 4-head matrix-core kernel with
+    // two heads idle: at 64 x 4096 its full layer takes 164.6 us against
+    // 170.0 us for the 2-head kernel, its sliding layer ~27 us against 28.5.
+    if (group == 2 && DT != kFP8)
         return launch_attn_group<2, false>(P, MODE, D, DT, grid, st);
     if (P.npiece > 1) return launch_attn_group<8, true>(P, MODE, D, DT, grid, st);
     return group_piece(group, DT) == 8 ? launch_attn_group<8, false>(P, MODE, D, DT, grid, st)

@@ -107,8 +107,8 @@ typedef struct {
                                (else UNSUPPORTED).  Groups of 2 to 8 read the
                                cache once per layer (kernels for 2, 4 and 8
                                heads, a group below a kernel's size leaving
-                               heads idle; 2 over an fp8 append cache run the
-                               4-head kernel); a larger group is split into pieces
+                               heads idle; 2 over an fp8 cache run the 4-head
+                               kernel); a larger group is split into pieces
                                of eight query heads, one workgroup per piece in
                                the same launch, each reading the cache (the
                                last piece to finish writes the new entry). */
