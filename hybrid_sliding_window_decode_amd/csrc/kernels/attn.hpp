@@ -396,10 +396,11 @@ void attn_kernel(AttnParams P) {
     __shared__ float sm_gl[G][kAttnWaves];
     __shared__ int sm_last;
     // MFMA kernel: the running fold of the chunk partials (single workgroup
-    // per pair) lives in LDS, not registers (it is touched once per chunk):
-    // M and L per wave (every lane of a wave computes the same values; lane
-    // 0 stores them and only that wave reads them back), O per thread.
-    __shared__ float sm_run_ml[MF ? G : 1][MF ? kAttnWaves : 1][2];
+    // per pair) lives in LDS, not registers (it is touched once per chunk),
+    // head-major like the flush: M and L per head (the head's first flush
+    // thread stores them; the head's threads, all in one wave, read them
+    // back), O per (head, dim).
+    __shared__ float sm_run_ml[MF ? G : 1][2];
     __shared__ float sm_run_o[MF ? G : 1][MF ? D : 1];
     __shared__ float sm_glogit[MF ? G : 1];       // MFMA kernel: the given gate logits
     __shared__ float sm_vh[MF ? D : 1];           // MFMA kernel: the new entry's value
@@ -984,7 +985,7 @@ void attn_kernel(AttnParams P) {
                     float fo[EH];
 #pragma unroll
                     for (int e = 0; e < EH; ++e) fo[e] = sm_run_o[fh][fd + e];
-                    const float fM = sm_run_ml[fh][0][0], fL = sm_run_ml[fh][0][1];
+                    const float fM = sm_run_ml[fh][0], fL = sm_run_ml[fh][1];
 #pragma unroll
                     for (int e = 0; e < EH; ++e) {
                         Fold f;
@@ -994,8 +995,8 @@ void attn_kernel(AttnParams P) {
                         f.add_sel(M, L, O[e]);
                         sm_run_o[fh][fd + e] = f.O;
                         if (e == 0 && fd == 0) {
-                            sm_run_ml[fh][0][0] = f.M;
-                            sm_run_ml[fh][0][1] = f.L;
+                            sm_run_ml[fh][0] = f.M;
+                            sm_run_ml[fh][1] = f.L;
                         }
                     }
                 } else {
@@ -1158,9 +1159,9 @@ void attn_kernel(AttnParams P) {
             qsc[hh] = q_r * qmul;
             if constexpr (MF) {              // empty running fold
                 if (t < D) sm_run_o[hh][t] = 0.f;
-                if (lane == 0) {
-                    sm_run_ml[hh][wid][0] = -INFINITY;
-                    sm_run_ml[hh][wid][1] = 0.f;
+                if (tid == 0) {
+                    sm_run_ml[hh][0] = -INFINITY;
+                    sm_run_ml[hh][1] = 0.f;
                 }
             }
             if (t < D) {
@@ -1295,8 +1296,8 @@ void attn_kernel(AttnParams P) {
     if constexpr (MF) {
         if (MODE != kModePartials && P.wpp == 1) {
             // folded in LDS by this thread's own flushes
-            hM = sm_run_ml[fh][0][0];
-            hL = sm_run_ml[fh][0][1];
+            hM = sm_run_ml[fh][0];
+            hL = sm_run_ml[fh][1];
 #pragma unroll
             for (int e = 0; e < EH; ++e) hO[e] = sm_run_o[fh][fd + e];
         }
