@@ -51,8 +51,8 @@ def positions(kind, B, S, pos, seed):
     # with each probability split into two bf16 parts
     ("full", "bf16", 4, 128, 3, [4000, 17, 2048], 4001, 0),
     ("sliding", "bf16", 4, 128, 5, "ragged", None, 0),
-    # fp8, 2 heads per kv head: the 2-head kernel over rings, the 4-head
-    # matrix-core kernel (two heads idle) over append caches
+    # fp8, 2 heads per kv head: the 4-head matrix-core kernel with two heads
+    # idle, over rings and append caches
     ("sliding", "fp8", 2, 256, 6, "ragged", None, 0),
     ("full", "fp8", 2, 256, 3, [4000, 17, 2048], 4001, 0),
     # fp8 at D = 128: 64-key tiles, two 32-key value products per tile

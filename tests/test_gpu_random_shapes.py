@@ -1,10 +1,12 @@
-"""GPU parity over a fixed, seeded draw of layer shapes: cache type, head
+"""GPU parity over fixed, seeded draws of layer shapes: cache type, head
 dim, query heads per kv head (every kernel and piece route: 1, 2, 3, 4, 5,
-8, 16), streams, capacity, chunk size (library default or a multiple of the
-quantum) and ragged positions from 0 to the capacity, each a fused layer
-step against the oracle, the same bits as the separate entries, and the
-stored entry (the checks of test_gpu_gqa.check_layer_step).  The draw is
-fixed, so each case is reproducible by its id."""
+8, 16 in the first draw; 2, 3, 6, 7, 8, 12 in the second, mostly groups
+that leave heads idle; fp8 groups of 2 in a third), streams, capacity, chunk size (library default or a
+multiple of the quantum) and ragged positions from 0 to the capacity, each
+a fused layer step against the oracle, the same bits as the separate
+entries, and the stored entry (the checks of
+test_gpu_gqa.check_layer_step).  The draws are fixed, so each case is
+reproducible by its id."""
 import numpy as np
 import pytest
 
@@ -15,13 +17,13 @@ pytestmark = pytest.mark.gpu
 ELT = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 
-def draw(n, seed=2024):
+def draw(n, seed=2024, groups=(1, 2, 3, 4, 5, 8, 16)):
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
         kind = ["sliding", "full"][rng.integers(2)]
         dtype = ["f32", "f16", "bf16", "fp8"][rng.integers(4)]
-        G = int([1, 2, 3, 4, 5, 8, 16][rng.integers(7)])
+        G = int(groups[rng.integers(len(groups))])
         D = int([64, 128, 256][rng.integers(3)])
         if dtype == "f32" and G > 1:
             continue                      # grouped f32 caches are refused
@@ -36,7 +38,8 @@ def draw(n, seed=2024):
     return cases
 
 
-CASES = draw(24)
+CASES = (draw(24) + draw(16, seed=7, groups=(2, 3, 6, 7, 8, 12))
+         + [c for c in draw(40, seed=11, groups=(2,)) if c[1] == "fp8"][:4])
 
 
 @pytest.mark.parametrize("kind,dtype,G,D,B,pos,S,kps,H", CASES,
