@@ -29,6 +29,10 @@ constexpr int kMaxChunkKeys = 2048;  // cap of the default keys per chunk
 // layer: 309 us at 512 workgroups, 334 us at 1024): each adds a partial to
 // merge and splits a contiguous read.
 constexpr int kWgsPerCu = 2;
+// Longest position from which an append cache's launch takes the packed
+// split (below it a launch is short, and the deal's extra round trip for the
+// positions would show).
+constexpr int kPackMinKeys = 32768;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -330,7 +334,18 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     P.kv_scale = d->kv_scale;
     P.Gq = d->n_heads / d->n_kv_heads;
     P.npiece = group_pieces(d);
-    grid = d->batch * d->n_kv_heads * P.wpp * P.npiece;
+    // The packed split: long append caches under the default chunking (one
+    // piece per group, at most one stream per thread of the deal) take their
+    // workgroups from the positions on the device, in proportion to each
+    // stream's valid keys, instead of the same count for every stream: with
+    // ragged positions a short stream's pair no longer holds workgroups
+    // idle while the long ones stream.  Only the work split changes.
+    P.pack = 0;
+    if (autok && d->chunks_per_workgroup == 0 && wpp > 1 && P.npiece == 1 &&
+        max_pos >= kPackMinKeys && d->batch <= kAttnThreads)
+        P.pack = device_cus() * kWgsPerCu;
+    grid = P.pack > 0 ? P.pack + d->batch * d->n_kv_heads
+                      : d->batch * d->n_kv_heads * P.wpp * P.npiece;
     return HSWD_OK;
 }
 
@@ -493,6 +508,9 @@ int32_t hswd_decode_attn_partials(float* part_o, float* part_ml, const float* q_
     int grid = 0;
     int32_t st = attn_setup(P, grid, d, ring, max_pos, nullptr, 0, false);
     if (st != HSWD_OK) return st;
+    // every chunk's partial is written, by the pairs' own workgroups
+    P.pack = 0;
+    grid = d->batch * d->n_kv_heads * P.wpp * P.npiece;
     P.q = q_rot;
     P.kc = const_cast<void*>(k_cache);
     P.vc = const_cast<void*>(v_cache);

@@ -126,6 +126,10 @@ struct AttnParams {
     // auto_chunk_keys(its valid keys, k_floor), and K / cpw above are the
     // values of a stream at max_pos
     int auto_k, k_floor;
+    // packed split (long append caches, default chunking, one piece per
+    // group): the workgroups the launch deals out to the streams in
+    // proportion to their valid keys, or 0 (the grid is pack + B * Hkv)
+    int pack;
 };
 
 // Matrix-core kernels: 4 or 8 query heads per kv head over a 16-bit or fp8
@@ -327,6 +331,65 @@ constexpr int stash_slots() { return G == 1 ? 4 : (G == 2 ? 2 : 1); }
 template <int G>
 constexpr int flush_buffers() { return G == 8 ? 1 : 2; }
 
+// The packed split's deal (see the kernel): every thread takes stream tid
+// (tid < B), the workgroup sums the valid keys and the dealt workgroup
+// counts in a fixed order, and the thread whose stream owns workgroup w
+// writes its role to role[0..4] (pair, workgroup of the pair, workgroups of
+// the pair, chunks per workgroup, keys per chunk); role[0] stays -1 past the
+// last stream's workgroups.  scan: 2 * kAttnThreads ints of LDS, then
+// kAttnThreads 64-bit sums.  Not inlined: it runs once per launch, and its
+// temporaries stay out of the kernel's register budget.
+__device__ __attribute__((noinline)) void pack_deal(const int32_t* pos, int B, int Hkv, int S,
+                                                    int max_pos, int k_floor, int pack, int w,
+                                                    int tid, int* scan, int* role) {
+    long long* scan64 = reinterpret_cast<long long*>(scan + 2 * kAttnThreads);
+    const int i = tid;                              // this thread's stream
+    int nv_i = 0;
+    if (i < B) {
+        const int p_i = pos[i];
+        nv_i = p_i < 0 ? 0 : (p_i < S ? p_i : S);
+        if (nv_i > max_pos) nv_i = max_pos;
+    }
+    const int K_i = auto_chunk_keys(nv_i, k_floor);
+    const int nb_i = (nv_i + K_i - 1) / K_i;
+    // total valid keys: inclusive scan in a fixed order (64-bit)
+    scan64[tid] = nv_i;
+    __syncthreads();
+    for (int off = 1; off < kAttnThreads; off <<= 1) {
+        const long long v = tid >= off ? scan64[tid - off] : 0;
+        __syncthreads();
+        scan64[tid] += v;
+        __syncthreads();
+    }
+    const long long T = scan64[kAttnThreads - 1];
+    int w_i = 1, cw_i = 1;
+    if (nb_i > 0 && T > 0) {
+        const double share = (double)pack / Hkv * (double)nv_i / (double)T;
+        w_i = min(nb_i, max(1, (int)ceil(share)));
+        cw_i = (nb_i + w_i - 1) / w_i;
+        w_i = (nb_i + cw_i - 1) / cw_i;
+    }
+    const int c_i = i < B ? w_i * Hkv : 0;
+    scan[tid] = c_i;
+    if (tid == 0) role[0] = -1;
+    __syncthreads();
+    for (int off = 1; off < kAttnThreads; off <<= 1) {
+        const int v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const int incl = scan[tid], excl = incl - c_i;
+    if (i < B && w >= excl && w < incl) {
+        const int li = w - excl;
+        role[0] = i * Hkv + li % Hkv;
+        role[1] = li / Hkv;
+        role[2] = w_i;
+        role[3] = cw_i;
+        role[4] = K_i;
+    }
+}
+
 // G = H / Hkv query heads share each kv head (grouped-query attention by
 // reshaping the query, the talker commit): one workgroup scores all G of
 // them against every K/V tile it loads, so the cache is read once per group.
@@ -422,7 +485,32 @@ void attn_kernel(AttnParams P) {
     const int npiece = G >= 4 ? P.npiece : 1;
     const int per_pair = npiece * P.wpp;
     int pair, sub;
-    {
+    // Packed split: every workgroup reads all positions and deals P.pack
+    // workgroups out to the streams in proportion to their valid keys (at
+    // least one each, at most one per chunk of the stream's own size), in
+    // stream order, Hkv consecutive workgroups (one per kv head) per round
+    // of a stream; workgroups past the last stream's exit at once.  Only
+    // the work split follows from it, never a stream's chunks or their
+    // order.  The same integer and double arithmetic in every workgroup
+    // gives every workgroup the same deal.
+    const bool packed = !RING && MODE != kModePartials && P.pack > 0 && npiece == 1;
+    int pack_parts = 0, pack_cw = 0, pack_K = 0;
+    if (packed) {
+        // scratch for the scans: LDS no other code touches before the tiles
+        int* scan = MF ? reinterpret_cast<int*>(&sm_k[0][0]) : reinterpret_cast<int*>(&sm_o[0][0][0][0][0]);
+        int* role = scan + 4 * kAttnThreads + 8;
+        pack_deal(P.pos, P.B, P.Hkv, P.S, P.max_pos, P.k_floor, P.pack, (int)blockIdx.x, tid,
+                  scan, role);
+        __syncthreads();
+        // (uniform values: held in scalar registers)
+        pair = __builtin_amdgcn_readfirstlane(role[0]);
+        if (pair < 0) return;                           // past the last stream's workgroups
+        sub = __builtin_amdgcn_readfirstlane(role[1]);
+        pack_parts = __builtin_amdgcn_readfirstlane(role[2]);
+        pack_cw = __builtin_amdgcn_readfirstlane(role[3]);
+        pack_K = __builtin_amdgcn_readfirstlane(role[4]);
+        __syncthreads();                                // the scratch is free again
+    } else {
         const int w = blockIdx.x;
         if ((n_pairs & 7) == 0 && per_pair > 1) {
             const int k = w >> 3;
@@ -433,8 +521,8 @@ void attn_kernel(AttnParams P) {
             sub = w % per_pair;
         }
     }
-    const int piece = sub / P.wpp;
-    const int wg = sub % P.wpp;
+    const int piece = packed ? 0 : sub / P.wpp;
+    const int wg = packed ? sub : sub % P.wpp;
     const int b = pair / P.Hkv;
     const int g = pair % P.Hkv;
     // query heads of this workgroup: bh0 .. bh0 + gv - 1 (the 4- and 8-head
@@ -449,7 +537,7 @@ void attn_kernel(AttnParams P) {
     // once its position arrives (until then the first tiles are requested
     // on the launch's values, which the streams at the longest position
     // share).
-    int K = P.K, cpw = P.cpw;
+    int K = packed ? pack_K : P.K, cpw = packed ? pack_cw : P.cpw;
     int c_begin = wg * cpw;
     int c_end = min(c_begin + cpw, P.n_chunk);
     int TPW = K / (KT * kAttnWaves);                  // tiles per wave in a full chunk
@@ -600,7 +688,8 @@ void attn_kernel(AttnParams P) {
         if (nv > grid_keys) nv = grid_keys;
         if (MODE != kModePartials && wg == 0 && g == 0 && tid == 0 && p > P.max_pos)
             atomicOr(P.err, 2);
-        if (P.auto_k) {
+        if (P.auto_k && !packed) {
+            // (packed split: already the stream's own, from the deal)
             // the stream's chunk (auto_chunk_keys), a function of its
             // position alone; its chunks spread over the pair's workgroups,
             // each taking at least the share of a stream at max_pos (the
@@ -1332,7 +1421,7 @@ void attn_kernel(AttnParams P) {
         if (tid == 0) {
             const int prev = __hip_atomic_fetch_add(&P.counters[pair * npiece + piece], 1,
                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sm_last = prev == P.wpp - 1;
+            sm_last = prev == (packed ? pack_parts : P.wpp) - 1;
         }
         __syncthreads();
         if (!sm_last) return;
