@@ -132,6 +132,17 @@ def test_long_context_grouped_fp8_8x131072():
     check_layer(inputs.full_spec(8, 131073, "fp8", H=32), 131072, 5200)
 
 
+def test_ragged_long_context_packed_split():
+    """8 streams of a 131073-row cache at ragged positions (from empty to the
+    capacity, a stream far below it, one past 32768 keys only): the packed
+    split deals the launch's workgroups out by valid keys, so the streams
+    get different workgroup counts and chunk sizes; all 64 (stream, head),
+    bf16, and again over fp8 with 32 query heads (the 4-head kernel)."""
+    pos = np.array([131072, 0, 5000, 40000, 33000, 90000, 1, 70001], np.int64)
+    check_layer(inputs.full_spec(8, 131073, "bf16"), pos, 5300)
+    check_layer(inputs.full_spec(8, 131073, "fp8", H=32), pos[::-1].copy(), 5301)
+
+
 def test_ragged_full_layer_64_streams():
     """64 streams with ragged positions in [1, 4096] on a full layer: most
     chunks of the short streams are empty."""
