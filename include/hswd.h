@@ -146,7 +146,11 @@ typedef struct {
                                on the batch. */
     int32_t chunks_per_workgroup; /* work split only, never the bits: how many
                                consecutive chunks one workgroup streams.  0 =
-                               library choice (from B and the CU count). */
+                               library choice (from B and the CU count; for
+                               append caches with max_pos >= 32768, at most 256
+                               streams and at most 8 query heads per kv head,
+                               dealt on the device in proportion to each
+                               stream's valid keys). */
     const float* kv_scale;  /* fp8 caches only: DEVICE pointer, float32 [2, Hkv],
                                the K scales then the V scales of the kv heads
                                (NULL = 1 for every head).  Ignored otherwise. */
