@@ -331,18 +331,71 @@ constexpr int stash_slots() { return G == 1 ? 4 : (G == 2 ? 2 : 1); }
 template <int G>
 constexpr int flush_buffers() { return G == 8 ? 1 : 2; }
 
+// Totals over the workgroup's threads in one exchange: the 64-bit sum of
+// w, and the maxima of a, b and c, floats that hold integers exactly (wave
+// butterflies, then the waves' results meet in red: two sets of kAttnWaves
+// x 4 slots, used alternately by successive calls, so one barrier per call
+// suffices).  Exact, so every order gives the same totals.
+__device__ __forceinline__ void deal_totals(long long (*red)[kAttnWaves][4], int& parity, int tid,
+                                            long long& w, float& a, float& b, float& c) {
+    for (int m = 1; m < kWave; m <<= 1) w += __shfl_xor(w, m, kWave);
+    a = wave_max(a);
+    b = wave_max(b);
+    c = wave_max(c);
+    long long(*r)[4] = red[parity];
+    parity ^= 1;
+    if (tid % kWave == 0) {
+        r[tid / kWave][0] = w;
+        r[tid / kWave][1] = __float_as_int(a);
+        r[tid / kWave][2] = __float_as_int(b);
+        r[tid / kWave][3] = __float_as_int(c);
+    }
+    __syncthreads();
+    w = r[0][0];
+    a = __int_as_float((int)r[0][1]), b = __int_as_float((int)r[0][2]),
+    c = __int_as_float((int)r[0][3]);
+    for (int v = 1; v < kAttnWaves; ++v) {
+        w += r[v][0];
+        a = fmaxf(a, __int_as_float((int)r[v][1]));
+        b = fmaxf(b, __int_as_float((int)r[v][2]));
+        c = fmaxf(c, __int_as_float((int)r[v][3]));
+    }
+}
+
+// The sum alone, of integers below 2^24 held as floats (exact in any
+// order), through the same exchange.
+__device__ __forceinline__ float deal_sum(long long (*red)[kAttnWaves][4], int& parity, int tid,
+                                          float v) {
+    v = wave_sum(v);
+    float* r = reinterpret_cast<float*>(red[parity]);
+    parity ^= 1;
+    if (tid % kWave == 0) r[tid / kWave] = v;
+    __syncthreads();
+    v = r[0];
+    for (int w = 1; w < kAttnWaves; ++w) v += r[w];
+    return v;
+}
+
 // The packed split's deal (see the kernel): every thread takes stream tid
-// (tid < B), the workgroup sums the valid keys and the dealt workgroup
-// counts in a fixed order, and the thread whose stream owns workgroup w
-// writes its role to role[0..4] (pair, workgroup of the pair, workgroups of
-// the pair, chunks per workgroup, keys per chunk); role[0] stays -1 past the
-// last stream's workgroups.  scan: 2 * kAttnThreads ints of LDS, then
-// kAttnThreads 64-bit sums.  Not inlined: it runs once per launch, and its
-// temporaries stay out of the kernel's register budget.
+// (tid < B).  A stream of nb chunks of K keys that gets c chunks per
+// workgroup takes ceil(nb / c) workgroups, each streaming at most c * K
+// keys; the deal is the smallest such bound M (a multiple of the smallest
+// chunk, c = M / K for every stream) whose workgroups, Hkv per stream and
+// workgroup slot, fit in the pack (every stream takes at least one; past
+// pack / Hkv streams, in the launch's pack + B * Hkv), found by bisection
+// between the balanced share of all chunks and the largest stream; then c
+// is evened out over the stream's workgroups.  The thread whose stream owns
+// workgroup w writes its role to role[0..4] (pair, workgroup of the pair,
+// workgroups of the pair, chunks per workgroup, keys per chunk); role[0]
+// stays -1 past the last stream's workgroups.  scan: 4 * kAttnThreads ints
+// of LDS.  Not inlined: it runs once per launch, and its temporaries stay
+// out of the kernel's register budget.
 __device__ __attribute__((noinline)) void pack_deal(const int32_t* pos, int B, int Hkv, int S,
                                                     int max_pos, int k_floor, int pack, int w,
                                                     int tid, int* scan, int* role) {
-    long long* scan64 = reinterpret_cast<long long*>(scan + 2 * kAttnThreads);
+    auto red = reinterpret_cast<long long(*)[kAttnWaves][4]>(scan);
+    int* wsum = scan + 2 * kAttnWaves * 4 * 2;      // kAttnWaves ints past red
+    int parity = 0;
     const int i = tid;                              // this thread's stream
     int nv_i = 0;
     if (i < B) {
@@ -352,34 +405,78 @@ __device__ __attribute__((noinline)) void pack_deal(const int32_t* pos, int B, i
     }
     const int K_i = auto_chunk_keys(nv_i, k_floor);
     const int nb_i = (nv_i + K_i - 1) / K_i;
-    // total valid keys: inclusive scan in a fixed order (64-bit)
-    scan64[tid] = nv_i;
-    __syncthreads();
-    for (int off = 1; off < kAttnThreads; off <<= 1) {
-        const long long v = tid >= off ? scan64[tid - off] : 0;
-        __syncthreads();
-        scan64[tid] += v;
-        __syncthreads();
+    const long long keys_i = (long long)nb_i * K_i;  // keys of its chunks
+    if (tid == 0) role[0] = -1;
+    // all chunks' keys; the largest chunk, the smallest (as the largest
+    // -K), the largest stream: powers of two and nb * K (nb < 2^24), exact
+    // as floats
+    long long W = keys_i;
+    float fKmax = nb_i > 0 ? (float)K_i : 0.f, fKmin = nb_i > 0 ? -(float)K_i : -0x1p31f,
+          fHi = (float)keys_i;
+    deal_totals(red, parity, tid, W, fKmax, fKmin, fHi);
+    // workgroups per kv head: the pack's, or with more streams than that
+    // (no deal then fits the GPU at once) the launch's pack + B
+    const int budget = B <= pack / Hkv ? pack / Hkv : pack / Hkv + B;
+    int c_i = nb_i;                                 // chunks per workgroup (one workgroup)
+    if (W > 0) {
+        const unsigned Kmax = (unsigned)fKmax, Kmin = (unsigned)-fKmin, Hi = (unsigned)fHi;
+        // bound M = m * Kmin, from lo: the balanced share (or the largest
+        // chunk); at hi one workgroup per stream (B of them) fits.  32-bit
+        // from here: Hi < 2^32, chunk sizes are powers of two, so c = m *
+        // Kmin / K is a shift of m, and the counts stay below 2^24
+        // (B * kMaxChunks).  W / (budget * Kmin) is exact enough in double
+        // (W < 2^41) for its ceiling.
+        const unsigned lo = max((unsigned)ceil((double)W / ((double)budget * Kmin)),
+                                (Kmax + Kmin - 1) / Kmin);
+        const unsigned hi = max(lo, (unsigned)(((unsigned long long)Hi + Kmin - 1) / Kmin));
+        const int sh = nb_i > 0 ? __builtin_ctz((unsigned)K_i / Kmin) : 0;
+        auto fits = [&](unsigned m) {
+            unsigned n = 0;
+            if (i < B) {
+                const unsigned c = m >> sh;
+                n = nb_i > 0 ? ((unsigned)nb_i + c - 1) / c : 1;
+            }
+            return deal_sum(red, parity, tid, (float)n) <= (float)budget;
+        };
+        // the smallest m that fits: lo itself (balanced streams), else
+        // steps of 1, 2, 4, ... above it, then bisection of the last step
+        unsigned good = hi, bad = lo;
+        if (fits(lo)) {
+            good = lo;
+        } else {
+            for (unsigned step = 1; bad + step < good; step *= 2) {
+                if (fits(bad + step)) {
+                    good = bad + step;
+                    break;
+                }
+                bad += step;
+            }
+            while (good - bad > 1) {
+                const unsigned mid = bad + (good - bad) / 2;
+                if (fits(mid)) good = mid;
+                else bad = mid;
+            }
+        }
+        if (nb_i > 0) c_i = (int)min((unsigned)nb_i, good >> sh);
     }
-    const long long T = scan64[kAttnThreads - 1];
     int w_i = 1, cw_i = 1;
-    if (nb_i > 0 && T > 0) {
-        const double share = (double)pack / Hkv * (double)nv_i / (double)T;
-        w_i = min(nb_i, max(1, (int)ceil(share)));
-        cw_i = (nb_i + w_i - 1) / w_i;
+    if (nb_i > 0) {
+        w_i = (nb_i + c_i - 1) / c_i;
+        cw_i = (nb_i + w_i - 1) / w_i;              // even shares, same count
         w_i = (nb_i + cw_i - 1) / cw_i;
     }
-    const int c_i = i < B ? w_i * Hkv : 0;
-    scan[tid] = c_i;
-    if (tid == 0) role[0] = -1;
-    __syncthreads();
-    for (int off = 1; off < kAttnThreads; off <<= 1) {
-        const int v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+    // this stream's first workgroup: exclusive prefix of Hkv * w over the
+    // streams (wave scans, then the waves' totals)
+    const int c_own = i < B ? w_i * Hkv : 0;
+    int incl = c_own;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off, kWave);
+        if (tid % kWave >= off) incl += v;
     }
-    const int incl = scan[tid], excl = incl - c_i;
+    if (tid % kWave == kWave - 1) wsum[tid / kWave] = incl;
+    __syncthreads();
+    for (int v = 0; v < tid / kWave; ++v) incl += wsum[v];
+    const int excl = incl - c_own;
     if (i < B && w >= excl && w < incl) {
         const int li = w - excl;
         role[0] = i * Hkv + li % Hkv;
@@ -485,14 +582,14 @@ void attn_kernel(AttnParams P) {
     const int npiece = G >= 4 ? P.npiece : 1;
     const int per_pair = npiece * P.wpp;
     int pair, sub;
-    // Packed split: every workgroup reads all positions and deals P.pack
-    // workgroups out to the streams in proportion to their valid keys (at
-    // least one each, at most one per chunk of the stream's own size), in
-    // stream order, Hkv consecutive workgroups (one per kv head) per round
-    // of a stream; workgroups past the last stream's exit at once.  Only
-    // the work split follows from it, never a stream's chunks or their
-    // order.  The same integer and double arithmetic in every workgroup
-    // gives every workgroup the same deal.
+    // Packed split: every workgroup reads all positions and deals at most
+    // P.pack workgroups out to the streams (the fewest keys per workgroup
+    // that fit; at least one workgroup each, at most one per chunk of the
+    // stream's own size), in stream order, Hkv consecutive workgroups (one
+    // per kv head) per round of a stream; workgroups past the last
+    // stream's exit at once.  Only the work split follows from it, never a
+    // stream's chunks or their order.  The same integer arithmetic in every
+    // workgroup gives every workgroup the same deal.
     const bool packed = !RING && MODE != kModePartials && P.pack > 0 && npiece == 1;
     int pack_parts = 0, pack_cw = 0, pack_K = 0;
     if (packed) {

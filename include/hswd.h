@@ -149,8 +149,9 @@ typedef struct {
                                library choice (from B and the CU count; for
                                append caches with max_pos >= 32768, at most 256
                                streams and at most 8 query heads per kv head,
-                               dealt on the device in proportion to each
-                               stream's valid keys). */
+                               dealt on the device from each stream's valid
+                               keys: the fewest keys per workgroup whose
+                               workgroups the GPU holds at once). */
     const float* kv_scale;  /* fp8 caches only: DEVICE pointer, float32 [2, Hkv],
                                the K scales then the V scales of the kv heads
                                (NULL = 1 for every head).  Ignored otherwise. */

@@ -466,6 +466,46 @@ def test_small_batch_work_split_never_changes_bits(kind, B, dtype, pos, S, D):
     assert_parity(results[0][0], ref["out"], x, "small-batch split, fused step")
 
 
+@pytest.mark.parametrize("dtype,H", [("bf16", 8), ("fp8", 32)])
+def test_packed_split_never_changes_bits(dtype, H):
+    """Long append caches under the default chunking (a launch bound of
+    32768 keys or more) take the packed split, whose deal gives the streams
+    different workgroup counts from their positions: its bits equal those
+    of one workgroup per chunk and of 64 chunks per workgroup (fixed splits
+    sized for the longest stream), in the fused step and the attention
+    entry, with the written entries; every head matches the oracle (8 kv
+    heads; 32 query heads: the 4-head kernel)."""
+    B, S = 12, 50001
+    spec = inputs.full_spec(B, S, dtype, H=H, Hkv=8, D=128)
+    pos = inputs.ragged_positions(B, 0, S - 1, seed=26)
+    pos[:3] = [S - 1, 0, 3]                  # the capacity, empty, a few keys
+    x = inputs.make_step(spec, pos, seed=27)
+    mp = int(x.pos.max())
+    results = []
+    for cpw in (0, 1, 64):
+        d = to_dev(x)
+        desc = hswd.make_desc(d["k_cache"], n_heads=H, chunks_per_workgroup=cpw,
+                              kv_scale=d["kv_scale"])
+        say("packed split %s H=%d B=%d pos=%s..., cpw=%d" % (dtype, H, B, list(x.pos[:5]), cpw))
+        ws = hswd.workspace(desc, 0, mp)
+        out = hswd.layer_step(d["q"], d["k"], d["v"], d["gate"], d["k_cache"], d["v_cache"],
+                              d["pos"], 0, spec.rot, spec.theta, ws, max_pos=mp, desc=desc)
+        f = to_dev(x)
+        hswd.rope_apply(f["q"], f["k"], f["pos"], spec.rot, spec.theta)
+        o = hswd.decode_attn_full(f["q"], f["k"], f["v"], f["k_cache"], f["v_cache"], f["pos"],
+                                  mp, ws, desc=desc)
+        assert hswd.check_errors(ws) == 0
+        results.append([out.cpu().numpy(), o.cpu().numpy(), cache_to_host(d["k_cache"]),
+                        cache_to_host(d["v_cache"])])
+        del d, f
+    for r in results[1:]:
+        for a, b in zip(results[0], r):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    ref = oracle_step(x)
+    assert_parity(results[0][1], ref["o_pre"], x, "packed split, attention entry")
+    assert_parity(results[0][0], ref["out"], x, "packed split, fused step")
+
+
 def _stream_chunk(n, floor=256):
     """The header's default chunk of an append-cache stream with n valid keys
     (bf16, D = 256, one query head per kv head: floor of four 64-key quanta):

@@ -143,6 +143,17 @@ def test_ragged_long_context_packed_split():
     check_layer(inputs.full_spec(8, 131073, "fp8", H=32), pos[::-1].copy(), 5301)
 
 
+def test_packed_split_more_streams_than_slots():
+    """72 streams over 8 kv heads (more (stream, kv head) pairs than the GPU
+    holds workgroups at once) at ragged positions up to 33000 keys, fp8,
+    128 dims: the packed deal then bounds the launch's workgroups by its
+    pack plus one per pair and still gives the longest streams several;
+    all 576 (stream, head)."""
+    pos = inputs.ragged_positions(72, 0, 33000, seed=5400)
+    pos[0] = 33000
+    check_layer(inputs.full_spec(72, 33001, "fp8", D=128), pos, 5401)
+
+
 def test_ragged_full_layer_64_streams():
     """64 streams with ragged positions in [1, 4096] on a full layer: most
     chunks of the short streams are empty."""
