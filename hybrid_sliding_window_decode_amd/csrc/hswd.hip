@@ -117,8 +117,8 @@ int auto_floor(const hswd_attn_desc* d) {
 // a function of the cache geometry and max_pos only, never of the batch
 // (the chunk size is part of the summation order).  auto_chunk_keys is
 // nondecreasing, so ceil(n / chunk(n)) peaks where a range of constant chunk
-// ends: at 32 * floor and below (32 chunks), at kAutoLongKeys - 1, at the
-// kMaxChunks threshold, or at max_pos itself.
+// ends: at 32 * floor and below (32 chunks), at kAutoLongKeys - 1, at
+// kAutoVeryLongKeys - 1, at the kMaxChunks threshold, or at max_pos itself.
 int auto_chunks_of(int n, int fl) {
     const int k = auto_chunk_keys(n, fl);
     return (int)((n + (long)k - 1) / k);
@@ -127,8 +127,8 @@ int num_chunks(const hswd_attn_desc* d, int ring, int max_pos) {
     const long keys = ring ? d->n_slots : (max_pos > 0 ? max_pos : 0);
     if (auto_chunks(d, ring)) {
         const int fl = auto_floor(d);
-        const long ends[] = {keys, 32l * fl, kAutoLongKeys - 1l,
-                             2l * kAutoChunkKeys * kMaxChunks};
+        const long ends[] = {keys, 32l * fl, kAutoLongKeys - 1l, kAutoVeryLongKeys - 1l,
+                             8l * kAutoChunkKeys * kMaxChunks};
         int n = 1;
         for (long e : ends)
             if (e <= keys) n = max(n, auto_chunks_of((int)e, fl));

@@ -5,8 +5,8 @@
 // Summation order.  The valid key range of each (stream, kv head) is cut into
 // chunks of K keys (K = keys_per_split; by default a ring's from its slot
 // count, 128 to 512, and an append cache stream's from its own position, at
-// most 1024 keys below 131072 and 2048 from there, longer only past 4096
-// chunks).  A chunk's partial (max m, sum l, unnormalised o) is computed the
+// most 1024 keys below 131072, 2048 below 524288 and 8192 from there, longer
+// only past 4096 chunks).  A chunk's partial (max m, sum l, unnormalised o) is computed the
 // same way wherever it runs: the workgroup's waves take the chunk's tiles
 // round robin, keep an online softmax each, and merge through LDS in wave
 // order.  Chunk partials are then
@@ -62,20 +62,25 @@ static_assert(kAttnWaves == 4 || kAttnWaves == 8, "one thread per head dim needs
 constexpr int kMaxChunks = 4096;                     // chunks per (stream, kv head)
 constexpr int kAutoChunkKeys = 1024;                 // cap of a stream's own default chunk
 constexpr int kAutoLongKeys = 1 << 17;               // ... doubled from this many keys on
+constexpr int kAutoVeryLongKeys = 1 << 19;           // ... and 8x from this many keys on
 
 // A stream's default chunk over an append cache, from its n valid keys: the
 // smallest power of two >= n / 32, at least `floor` (four quanta, eight for
-// grouped heads), at most kAutoChunkKeys below kAutoLongKeys keys and twice
-// that from there, then doubled while n would need more than kMaxChunks
-// chunks.  Nondecreasing in n.  About 32 chunks spread a stream far below its
-// cache's capacity over many workgroups; the cap keeps the chunks of long
-// streams fine enough that their workgroups get even shares (a workgroup
-// streams ceil(chunks / workgroups) of them, and one compute unit's bandwidth
-// sets how long the busiest takes).  The host sizes the launch with the same
-// function.
+// grouped heads), at most kAutoChunkKeys below kAutoLongKeys keys, twice
+// that below kAutoVeryLongKeys and 8 times that from there, then doubled
+// while n would need more than kMaxChunks chunks.  Nondecreasing in n.
+// About 32 chunks spread a stream far below its cache's capacity over many
+// workgroups; the cap keeps the chunks of long streams fine enough that
+// their workgroups get even shares (a workgroup streams ceil(chunks /
+// workgroups) of them, and one compute unit's bandwidth sets how long the
+// busiest takes), and is raised for the longest streams, whose partials the
+// last workgroup to arrive folds in sequence (2^20 keys: 128 of them, not
+// 512).  The host sizes the launch with the same function.
 __host__ __device__ inline int auto_chunk_keys(int n, int floor) {
     const int target = (n + 31) >> 5;
-    const int cap = n < kAutoLongKeys ? kAutoChunkKeys : 2 * kAutoChunkKeys;
+    const int cap = n < kAutoLongKeys       ? kAutoChunkKeys
+                    : n < kAutoVeryLongKeys ? 2 * kAutoChunkKeys
+                                            : 8 * kAutoChunkKeys;
     int k = floor;
     while (k < target && k < cap) k <<= 1;
     while ((n + (long)k - 1) / k > kMaxChunks) k <<= 1;

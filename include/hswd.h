@@ -131,8 +131,9 @@ typedef struct {
                                n_kv_heads).  Append cache: each stream's own,
                                from its n = min(pos, max_pos) valid keys: the
                                smallest power of two >= max(F, ceil(n / 32)),
-                               at most 1024 below n = 131072 and 2048 from
-                               there (so about 32 chunks of them), then
+                               at most 1024 below n = 131072, 2048 below
+                               n = 524288 and 8192 from there (so about 32
+                               chunks of them up to 32768 keys), then
                                doubled while n would need more than 4096
                                chunks.  Either way a function of the geometry
                                and the stream's own position, never of the

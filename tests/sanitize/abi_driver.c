@@ -101,7 +101,7 @@ int main(void)
     EXPECT(hswd_layer_step(A, A, A, A, A, A, A, A, 0, 64, 5e6, 10, &big, A, 1 << 24, NULL), HSWD_ERR_UNSUPPORTED);
 
     /* the entry point that allocates nothing: refusals before any device work */
-    hswd_attn_desc h64 = desc(1, 64, 8, 256, (1 << 20) + 1, HSWD_BF16);
+    hswd_attn_desc h64 = desc(2, 64, 8, 256, (1 << 20) + 1, HSWD_BF16);
     EXPECT(hswd_layer_step_noalloc(A, A, A, A, NULL, A, A, A, 0, 64, 5e6, 1 << 20, &h64, NULL, NULL), HSWD_ERR_WORKSPACE);
     hswd_attn_desc many = desc(2049, 8, 8, 256, 511, HSWD_BF16);
     EXPECT(hswd_layer_step_noalloc(A, A, A, A, NULL, A, A, A, 1, 256, 1e4, 0, &many, NULL, NULL), HSWD_ERR_WORKSPACE);

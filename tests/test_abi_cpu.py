@@ -78,9 +78,10 @@ def test_workspace_and_splits():
     # least four quanta (quantum = 32768 / (D * element bytes) keys): 256 keys
     # for a bf16 ring.  An append cache's streams take their own chunk from
     # their n valid keys: the power of two at or above n / 32, at least four
-    # quanta, at most 1024 keys below 131072 keys and 2048 from there; the
-    # launch holds the most chunks a stream up to max_pos can have (32 once
-    # max_pos reaches 32 * the floor, 128 at 131071 keys)
+    # quanta, at most 1024 keys below 131072 keys, 2048 below 524288 and 8192
+    # from there; the launch holds the most chunks a stream up to max_pos can
+    # have (32 once max_pos reaches 32 * the floor, 128 at 131071 keys, 256 at
+    # 524287)
     assert hswd.num_splits(d, 1) == 2
     assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 16              # 256 keys
     assert hswd.num_splits(desc(n_slots=8192), 0, 8191) == 32              # 256 keys
@@ -91,8 +92,10 @@ def test_workspace_and_splits():
     assert hswd.num_splits(desc(n_slots=131073), 0, 131072) == 128         # 2048 keys, 64
     assert hswd.num_splits(desc(n_slots=131073), 0, 5000) == 20            # 256 keys
     assert hswd.num_splits(desc(n_slots=262145), 0, 262144) == 128         # 2048 keys
-    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1), 0, 1 << 20) == 512  # capped: 2048
-    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, kv_dtype=3), 0, 1 << 20) == 512
+    assert hswd.num_splits(desc(n_slots=524289), 0, 524287) == 256         # 2048 keys
+    assert hswd.num_splits(desc(n_slots=524289), 0, 524288) == 256         # 8192 keys, 64
+    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1), 0, 1 << 20) == 256  # 8192: 128
+    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, kv_dtype=3), 0, 1 << 20) == 256
     assert hswd.num_splits(desc(n_slots=4097, head_dim=64), 0, 4096) == 4       # Q = 256
     assert hswd.num_splits(desc(n_slots=4097, kv_dtype=0), 0, 4096) == 32       # f32: Q = 32
     assert hswd.num_splits(desc(n_slots=4097, kv_dtype=3), 0, 4096) == 8        # fp8: Q = 128
@@ -312,24 +315,24 @@ def test_binding_refuses_a_descriptor_that_does_not_match_the_tensors():
 
 
 def test_default_chunks_fit_the_chunk_limit_on_very_long_caches():
-    """Past 2^23 rows the default chunk doubles beyond its 2048-key cap, so
-    every cache the attention entries accept fits in 4096 chunks; an explicit
-    chunk size that would need more is refused by num_splits and gets no
-    workspace size."""
+    """Past 2^25 keys the default chunk doubles beyond its 8192-key cap, so
+    every cache fits in 4096 chunks; an explicit chunk size that would need
+    more is refused by num_splits and gets no workspace size."""
     L = binding.lib()
-    for n_slots, dt, D in [((1 << 23) + 2, 3, 256), ((1 << 24) - 1, 2, 128),
+    for n_slots, dt, D in [((1 << 25) + 2, 3, 128), ((1 << 26) - 1, 2, 64),
                            ((1 << 24) - 1, 3, 128), (1 << 23, 2, 256)]:
         d = desc(n_slots=n_slots, kv_dtype=dt, head_dim=D)
         n = hswd.num_splits(d, 0, n_slots - 1)
         assert 1 <= n <= 4096, (n_slots, dt, D, n)
         assert hswd.workspace_bytes(d, 0, n_slots - 1) > 0
-    # a stream's chunk follows its valid keys: 2^23 of them still take
-    # 2048-key chunks (4096 of them), one more takes 4096-key chunks; the
-    # launch is sized for 4096 chunks from 2^23 keys on
-    assert hswd.num_splits(desc(n_slots=1 << 23), 0, (1 << 23) - 1) == 4096
-    assert hswd.num_splits(desc(n_slots=(1 << 23) + 1), 0, 1 << 23) == 4096
-    assert hswd.num_splits(desc(n_slots=(1 << 23) + 2), 0, (1 << 23) + 1) == 4096
-    assert hswd.num_splits(desc(n_slots=(1 << 23) + 1), 0, 5000) == 20
+    # a stream's chunk follows its valid keys: 2^25 of them still take
+    # 8192-key chunks (4096 of them), one more takes 16384-key chunks; the
+    # launch is sized for 4096 chunks from 2^25 keys on
+    assert hswd.num_splits(desc(n_slots=1 << 25), 0, (1 << 25) - 1) == 4096
+    assert hswd.num_splits(desc(n_slots=(1 << 25) + 1), 0, 1 << 25) == 4096
+    assert hswd.num_splits(desc(n_slots=(1 << 25) + 2), 0, (1 << 25) + 1) == 4096
+    assert hswd.num_splits(desc(n_slots=(1 << 25) + 1), 0, 5000) == 20
+    assert hswd.num_splits(desc(n_slots=1 << 23), 0, (1 << 23) - 1) == 1024
     # an explicit chunk that needs more than 4096 chunks
     big = desc(n_slots=(1 << 20) + 1, keys_per_split=128)
     assert L.hswd_num_splits(ctypes.byref(big), 0, 1 << 20) == -1
@@ -341,8 +344,8 @@ def test_default_chunks_fit_the_chunk_limit_on_very_long_caches():
 def test_noalloc_step_refuses_what_its_array_cannot_hold():
     """hswd_layer_step_noalloc checks, before it touches the device, that the
     call fits the library's 32 MiB array: a call needing more (chunk
-    partials of 64 query heads over a 2^20-row cache on a few workgroups per
-    kv head, or more arrival counters than its 64 KiB region) returns
+    partials of 2 streams of 64 query heads over 2^20-row caches, or more
+    arrival counters than its 64 KiB region) returns
     HSWD_ERR_WORKSPACE (on this GPU-less host a device access would have
     returned HSWD_ERR_HIP instead); a misaligned error word is refused."""
     L = binding.lib()
@@ -351,7 +354,7 @@ def test_noalloc_step_refuses_what_its_array_cannot_hold():
     def call(d, ring=0, max_pos=0, err=None, rot=64):
         return f(A, A, A, A, None, A, A, A, ring, rot, 5e6, max_pos, ctypes.byref(d), err, None)
 
-    big = desc(batch=1, n_heads=64, n_slots=(1 << 20) + 1)      # 33.8 MB of partials
+    big = desc(batch=2, n_heads=64, n_slots=(1 << 20) + 1)      # 33.8 MB of partials
     assert call(big, max_pos=1 << 20) == -3
     many = desc(batch=2049, n_slots=511)                        # 16392 counters
     assert call(many, ring=1, rot=256) == -3

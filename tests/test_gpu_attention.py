@@ -510,12 +510,51 @@ def _stream_chunk(n, floor=256):
     """The header's default chunk of an append-cache stream with n valid keys
     (bf16, D = 256, one query head per kv head: floor of four 64-key quanta):
     the smallest power of two >= max(floor, ceil(n / 32)), at most 1024 below
-    131072 keys and 2048 from there."""
-    cap = 1024 if n < 131072 else 2048
+    131072 keys, 2048 below 524288 and 8192 from there."""
+    cap = 1024 if n < 131072 else (2048 if n < 524288 else 8192)
     k = floor
     while k < -(-n // 32) and k < cap:
         k *= 2
     return k
+
+
+def test_very_long_streams_take_longer_chunks():
+    """Streams of 2^19 keys or more take 8192-key chunks (fewer partials for
+    the last workgroup to fold), the stream one key below them 2048-key
+    chunks: in one batch with shorter streams each stream gives the bits it
+    gives decoded alone and under a fixed split (one workgroup per chunk),
+    and every head matches the oracle (bf16, 128 dims)."""
+    S = (1 << 19) + 1
+    pos = np.array([1 << 19, (1 << 19) - 1, 70000, 0], np.int32)
+    spec = inputs.full_spec(len(pos), S, "bf16", D=128)
+    t = inputs.device_step(spec, pos, seed=28, device="cuda")
+    kc_host, vc_host = cache_to_host(t["k_cache"]), cache_to_host(t["v_cache"])
+    q, k, v, gate = (t[n].cpu().numpy() for n in ("q", "k", "v", "gate"))
+    mp = int(pos.max())
+    q_rot, k_rot = t["q"].clone(), t["k"].clone()
+    hswd.rope_apply(q_rot, k_rot, t["pos"], spec.rot, spec.theta)
+    outs = []
+    for cpw in (0, 1):
+        desc = hswd.make_desc(t["k_cache"], chunks_per_workgroup=cpw)
+        say("very long streams: pos %s, %d chunks, cpw=%d" % (list(pos), hswd.num_splits(desc, 0, mp),
+                                                              cpw))
+        ws = hswd.workspace(desc, 0, mp)
+        outs.append(hswd.decode_attn_full(q_rot, k_rot, t["v"], t["k_cache"], t["v_cache"],
+                                          t["pos"], mp, ws, desc=desc).cpu().numpy())
+        assert hswd.check_errors(ws) == 0
+    assert np.array_equal(outs[0].view(np.uint8), outs[1].view(np.uint8))
+    for b, p in enumerate(pos):
+        sl = slice(b, b + 1)
+        d1 = hswd.make_desc(t["k_cache"][sl])
+        ws1 = hswd.workspace(d1, 0, max(int(p), 1))
+        o1 = hswd.decode_attn_full(q_rot[sl].contiguous(), k_rot[sl].contiguous(),
+                                   t["v"][sl].contiguous(), t["k_cache"][sl], t["v_cache"][sl],
+                                   t["pos"][sl].contiguous(), max(int(p), 1), ws1, desc=d1)
+        assert np.array_equal(o1.cpu().numpy()[0], outs[0][b]), b
+    r = oracle.layer_step(q, k, v, gate, kc_host, vc_host, pos, CODE["bf16"], 0, spec.rot,
+                          spec.theta, write=False)
+    x = inputs.StepInputs(spec, pos, q, k, v, gate, kc_host, vc_host)
+    assert_parity(outs[0], r["o_pre"], x, "very long streams")
 
 
 def test_stream_chunks_follow_their_own_positions():

@@ -190,7 +190,7 @@ def test_grouped_step_layers_64x4096_h64():
 
 
 def test_max_context_1x1048576():
-    """One stream at context 2^20 on a full layer (8.6 GB of cache, 512
-    chunks of 2048 keys, 64 workgroups per kv head merged by the last to
+    """One stream at context 2^20 on a full layer (8.6 GB of cache, 128
+    chunks of 8192 keys, 64 workgroups per kv head merged by the last to
     arrive): the largest context the tests exercise; all 8 heads."""
     check_layer(inputs.full_spec(1, (1 << 20) + 1, "bf16"), 1 << 20, 5100)
