@@ -119,19 +119,20 @@ int auto_floor(const hswd_attn_desc* d) {
 // nondecreasing, so ceil(n / chunk(n)) peaks where a range of constant chunk
 // ends: at 32 * floor and below (32 chunks), at kAutoLongKeys - 1, at
 // kAutoVeryLongKeys - 1, at the kMaxChunks threshold, or at max_pos itself.
-int auto_chunks_of(int n, int fl) {
-    const int k = auto_chunk_keys(n, fl);
+int auto_chunks_of(int n, int fl, int hkv) {
+    const int k = auto_chunk_keys(n, fl, hkv);
     return (int)((n + (long)k - 1) / k);
 }
 int num_chunks(const hswd_attn_desc* d, int ring, int max_pos) {
     const long keys = ring ? d->n_slots : (max_pos > 0 ? max_pos : 0);
     if (auto_chunks(d, ring)) {
         const int fl = auto_floor(d);
+        const int hkv = d->n_kv_heads;
         const long ends[] = {keys, 32l * fl, kAutoLongKeys - 1l, kAutoVeryLongKeys - 1l,
-                             8l * kAutoChunkKeys * kMaxChunks};
+                             (long)auto_very_long_cap(hkv) * kMaxChunks};
         int n = 1;
         for (long e : ends)
-            if (e <= keys) n = max(n, auto_chunks_of((int)e, fl));
+            if (e <= keys) n = max(n, auto_chunks_of((int)e, fl, hkv));
         return n;
     }
     const long K = chunk_keys(d);
@@ -300,7 +301,7 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     // per-stream chunks: the launch's K and cpw are those of a stream at
     // max_pos (its chunks spread over the pair's wpp workgroups unless the
     // caller fixed the chunks per workgroup)
-    const int K = autok ? auto_chunk_keys(max_pos, auto_floor(d)) : chunk_keys(d);
+    const int K = autok ? auto_chunk_keys(max_pos, auto_floor(d), d->n_kv_heads) : chunk_keys(d);
     if (autok && d->chunks_per_workgroup == 0) {
         const int nb = max_pos > 0 ? (max_pos + K - 1) / K : 1;
         cpw = (nb + wpp - 1) / wpp;

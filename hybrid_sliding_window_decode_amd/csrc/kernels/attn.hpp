@@ -5,8 +5,8 @@
 // Summation order.  The valid key range of each (stream, kv head) is cut into
 // chunks of K keys (K = keys_per_split; by default a ring's from its slot
 // count, 128 to 512, and an append cache stream's from its own position, at
-// most 1024 keys below 131072, 2048 below 524288 and 8192 from there, longer
-// only past 4096 chunks).  A chunk's partial (max m, sum l, unnormalised o) is computed the
+// most 1024 keys below 131072, 2048 below 524288 and from there 1024 per kv
+// head within [2048, 8192], longer only past 4096 chunks).  A chunk's partial (max m, sum l, unnormalised o) is computed the
 // same way wherever it runs: the workgroup's waves take the chunk's tiles
 // round robin, keep an online softmax each, and merge through LDS in wave
 // order.  Chunk partials are then
@@ -64,23 +64,33 @@ constexpr int kAutoChunkKeys = 1024;                 // cap of a stream's own de
 constexpr int kAutoLongKeys = 1 << 17;               // ... doubled from this many keys on
 constexpr int kAutoVeryLongKeys = 1 << 19;           // ... and 8x from this many keys on
 
+// The cap from kAutoVeryLongKeys keys on: kAutoChunkKeys per kv head, 2 to
+// 8 of them (a power of two), so that a lone stream there still has at
+// least 512 chunks over its kv heads (one compute unit streams too little
+// of the GPU's bandwidth for fewer workgroups to keep it busy), or as many
+// as below that tier (fewer than 4 kv heads).
+__host__ __device__ inline int auto_very_long_cap(int hkv) {
+    return (hkv >= 8 ? 8 : hkv >= 4 ? 4 : 2) * kAutoChunkKeys;
+}
+
 // A stream's default chunk over an append cache, from its n valid keys: the
 // smallest power of two >= n / 32, at least `floor` (four quanta, eight for
 // grouped heads), at most kAutoChunkKeys below kAutoLongKeys keys, twice
-// that below kAutoVeryLongKeys and 8 times that from there, then doubled
-// while n would need more than kMaxChunks chunks.  Nondecreasing in n.
+// that below kAutoVeryLongKeys and auto_very_long_cap(hkv) from there, then
+// doubled while n would need more than kMaxChunks chunks.  Nondecreasing in
+// n.
 // About 32 chunks spread a stream far below its cache's capacity over many
 // workgroups; the cap keeps the chunks of long streams fine enough that
 // their workgroups get even shares (a workgroup streams ceil(chunks /
 // workgroups) of them, and one compute unit's bandwidth sets how long the
 // busiest takes), and is raised for the longest streams, whose partials the
-// last workgroup to arrive folds in sequence (2^20 keys: 128 of them, not
-// 512).  The host sizes the launch with the same function.
-__host__ __device__ inline int auto_chunk_keys(int n, int floor) {
+// last workgroup to arrive folds in sequence (2^20 keys over 8 kv heads:
+// 128 of them, not 512).  The host sizes the launch with the same function.
+__host__ __device__ inline int auto_chunk_keys(int n, int floor, int hkv) {
     const int target = (n + 31) >> 5;
     const int cap = n < kAutoLongKeys       ? kAutoChunkKeys
                     : n < kAutoVeryLongKeys ? 2 * kAutoChunkKeys
-                                            : 8 * kAutoChunkKeys;
+                                            : auto_very_long_cap(hkv);
     int k = floor;
     while (k < target && k < cap) k <<= 1;
     while ((n + (long)k - 1) / k > kMaxChunks) k <<= 1;
@@ -408,7 +418,7 @@ __device__ __attribute__((noinline)) void pack_deal(const int32_t* pos, int B, i
         nv_i = p_i < 0 ? 0 : (p_i < S ? p_i : S);
         if (nv_i > max_pos) nv_i = max_pos;
     }
-    const int K_i = auto_chunk_keys(nv_i, k_floor);
+    const int K_i = auto_chunk_keys(nv_i, k_floor, Hkv);
     const int nb_i = (nv_i + K_i - 1) / K_i;
     const long long keys_i = (long long)nb_i * K_i;  // keys of its chunks
     if (tid == 0) role[0] = -1;
@@ -798,7 +808,7 @@ void attn_kernel(AttnParams P) {
             // launch's cpw): a shorter stream never needs to finish sooner
             // than the longest, and leaves compute units whose bandwidth the
             // longest streams' workgroups then have to themselves
-            const int k = auto_chunk_keys(nv, P.k_floor);
+            const int k = auto_chunk_keys(nv, P.k_floor, P.Hkv);
             const int nb = max(1, (nv + k - 1) / k);
             const int cw = P.auto_k == 2 ? cpw : max(cpw, (nb + P.wpp - 1) / P.wpp);   // 2: caller's split
             if (k != K || cw != cpw) {

@@ -132,10 +132,10 @@ typedef struct {
                                from its n = min(pos, max_pos) valid keys: the
                                smallest power of two >= max(F, ceil(n / 32)),
                                at most 1024 below n = 131072, 2048 below
-                               n = 524288 and 8192 from there (so about 32
-                               chunks of them up to 32768 keys), then
-                               doubled while n would need more than 4096
-                               chunks.  Either way a function of the geometry
+                               n = 524288 and from there 1024 * n_kv_heads
+                               within [2048, 8192] (so about 32 chunks of
+                               them up to 32768 keys), then doubled while n
+                               would need more than 4096 chunks.  Either way a function of the geometry
                                and the stream's own position, never of the
                                batch.
                                Else a multiple of the quantum Q = 32768 /

@@ -78,10 +78,10 @@ def test_workspace_and_splits():
     # least four quanta (quantum = 32768 / (D * element bytes) keys): 256 keys
     # for a bf16 ring.  An append cache's streams take their own chunk from
     # their n valid keys: the power of two at or above n / 32, at least four
-    # quanta, at most 1024 keys below 131072 keys, 2048 below 524288 and 8192
-    # from there; the launch holds the most chunks a stream up to max_pos can
-    # have (32 once max_pos reaches 32 * the floor, 128 at 131071 keys, 256 at
-    # 524287)
+    # quanta, at most 1024 keys below 131072 keys, 2048 below 524288 and from
+    # there 1024 per kv head within [2048, 8192]; the launch holds the most
+    # chunks a stream up to max_pos can have (32 once max_pos reaches 32 * the
+    # floor, 128 at 131071 keys, 256 at 524287)
     assert hswd.num_splits(d, 1) == 2
     assert hswd.num_splits(desc(n_slots=4097), 0, 4096) == 16              # 256 keys
     assert hswd.num_splits(desc(n_slots=8192), 0, 8191) == 32              # 256 keys
@@ -96,6 +96,11 @@ def test_workspace_and_splits():
     assert hswd.num_splits(desc(n_slots=524289), 0, 524288) == 256         # 8192 keys, 64
     assert hswd.num_splits(desc(n_slots=(1 << 20) + 1), 0, 1 << 20) == 256  # 8192: 128
     assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, kv_dtype=3), 0, 1 << 20) == 256
+    # fewer kv heads, smaller chunks there: 4096 keys for 4 (256 chunks at
+    # 2^20), 2048 for 2 and for 1 (512)
+    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, n_heads=4, n_kv_heads=4), 0, 1 << 20) == 256
+    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, n_heads=2, n_kv_heads=2), 0, 1 << 20) == 512
+    assert hswd.num_splits(desc(n_slots=(1 << 20) + 1, n_heads=8, n_kv_heads=1), 0, 1 << 20) == 512
     assert hswd.num_splits(desc(n_slots=4097, head_dim=64), 0, 4096) == 4       # Q = 256
     assert hswd.num_splits(desc(n_slots=4097, kv_dtype=0), 0, 4096) == 32       # f32: Q = 32
     assert hswd.num_splits(desc(n_slots=4097, kv_dtype=3), 0, 4096) == 8        # fp8: Q = 128

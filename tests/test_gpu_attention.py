@@ -508,9 +508,9 @@ def test_packed_split_never_changes_bits(dtype, H):
 
 def _stream_chunk(n, floor=256):
     """The header's default chunk of an append-cache stream with n valid keys
-    (bf16, D = 256, one query head per kv head: floor of four 64-key quanta):
-    the smallest power of two >= max(floor, ceil(n / 32)), at most 1024 below
-    131072 keys, 2048 below 524288 and 8192 from there."""
+    (bf16, D = 256, 8 kv heads, one query head per each: floor of four 64-key
+    quanta): the smallest power of two >= max(floor, ceil(n / 32)), at most
+    1024 below 131072 keys, 2048 below 524288 and 8192 from there."""
     cap = 1024 if n < 131072 else (2048 if n < 524288 else 8192)
     k = floor
     while k < -(-n // 32) and k < cap:

@@ -189,6 +189,14 @@ def test_grouped_step_layers_64x4096_h64():
     check_layer(inputs.full_spec(64, 4097, "fp8", H=64), 4096, 4301)
 
 
+def test_very_long_stream_four_kv_heads():
+    """One stream at 2^19 + 1000 keys over 4 kv heads (128 dims): past the
+    2^19-key tier its chunk is 4096 keys (1024 per kv head), so the lone
+    stream still spreads over 512 chunks; every head."""
+    check_layer(inputs.full_spec(1, (1 << 19) + 1001, "bf16", H=4, Hkv=4, D=128),
+                (1 << 19) + 1000, 5500)
+
+
 def test_max_context_1x1048576():
     """One stream at context 2^20 on a full layer (8.6 GB of cache, 128
     chunks of 8192 keys, 64 workgroups per kv head merged by the last to
