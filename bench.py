@@ -171,6 +171,9 @@ SINGLE_LAYER = {
     "gqa8_full_64x4096_bf16": ("full", 64, "bf16", 4096, 12, 64),
     "gqa8_sliding_64x4096_bf16": ("sliding", 64, "bf16", 4096, 12, 64),
     "gqa8_full_64x4096_fp8": ("full", 64, "fp8", 4096, 13, 64),
+    "gqa4_full_8x131072_fp8": ("full", 8, "fp8", 131072, 14, 32),
+    "gqa4_full_8x131072_bf16": ("full", 8, "bf16", 131072, 15, 32),
+    "long_full_8x131072_fp8": ("full", 8, "fp8", 131072, 16, 8),
 }
 
 

@@ -337,10 +337,11 @@ int32_t attn_setup(AttnParams& P, int& grid, const hswd_attn_desc* d, int ring, 
     P.npiece = group_pieces(d);
     // The packed split: long append caches under the default chunking (one
     // piece per group, at most one stream per thread of the deal) take their
-    // workgroups from the positions on the device, in proportion to each
-    // stream's valid keys, instead of the same count for every stream: with
-    // ragged positions a short stream's pair no longer holds workgroups
-    // idle while the long ones stream.  Only the work split changes.
+    // workgroups from the positions on the device, from each stream's valid
+    // keys (the fewest keys per workgroup whose workgroups fit in the pack),
+    // instead of the same count for every stream: with ragged positions a
+    // short stream's pair no longer holds workgroups idle while the long
+    // ones stream.  Only the work split changes.
     P.pack = 0;
     if (autok && d->chunks_per_workgroup == 0 && wpp > 1 && P.npiece == 1 &&
         max_pos >= kPackMinKeys && d->batch <= kAttnThreads)
